@@ -1,0 +1,162 @@
+"""Pins for the CPU oracle (no GPU needed).
+
+The oracle is the plain definition of the histogram on the page "Distributed
+Shared Memory", section "The cluster histogram": each element adds one to the
+bin it names, so a bin's final value is the number of elements equal to it.
+It is pinned here to things other than itself:
+
+* closed forms: empty input gives zeros, an input that is all one value b
+  gives n at b and zero elsewhere, hand-counted tiny cases;
+* an independent sort-and-run-length count (numpy sort, then run lengths);
+* brute force per bin with pure-Python loops on tiny inputs;
+* invariants: sum(counts) + dropped == n with dropped computed by an
+  independent mask, permutation invariance, split additivity;
+* mutation: planted mistakes in copies of ``oracle_hist.c`` (a wrong bound,
+  a dropped element, a wrong increment, a transposed index, a missing reset,
+  a missing drop count, a truncated value) each fail at least one pin.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+POISON = np.uint32(0xDEADBEEF)
+
+
+def _call(lib, values: np.ndarray, num_bins: int):
+    """Call an oracle build with a poisoned, padded output buffer."""
+    x = np.ascontiguousarray(values, dtype=np.int32)
+    buf = np.full(num_bins + 64, POISON, dtype=np.uint32)
+    dropped = lib.oracle_hist(x.ctypes.data if x.size else None, x.size, num_bins,
+                              buf.ctypes.data)
+    return buf[:num_bins].copy(), int(dropped)
+
+
+def _sort_rle(values: np.ndarray, num_bins: int) -> np.ndarray:
+    """Independent count: keep in-range values, sort, measure run lengths."""
+    v = np.sort(values[(values >= 0) & (values < num_bins)].astype(np.int64))
+    out = np.zeros(num_bins, dtype=np.int64)
+    if v.size:
+        starts = np.flatnonzero(np.concatenate(([True], v[1:] != v[:-1])))
+        ends = np.concatenate((starts[1:], [v.size]))
+        out[v[starts]] = ends - starts
+    return out
+
+
+def _brute(values, num_bins):
+    """counts[b] = sum over i of [values[i] == b], in pure Python."""
+    vals = [int(v) for v in values]
+    return [sum(1 for v in vals if v == b) for b in range(num_bins)]
+
+
+def _rng_values(seed, n, lo, hi):
+    return np.random.default_rng(seed).integers(lo, hi, size=n, dtype=np.int64).astype(np.int32)
+
+
+def pin_failures(lib) -> list[str]:
+    """Run every pin against one oracle build; return the names that fail."""
+    failed = []
+
+    def check(name, ok):
+        if not ok:
+            failed.append(name)
+
+    # Closed form: empty input.
+    c, d = _call(lib, np.zeros(0, np.int32), 17)
+    check("empty", np.all(c == 0) and d == 0)
+
+    # Closed form: all elements in one bin, at the edges and inside.
+    for num_bins, b, n in [(1, 0, 5), (64, 0, 1000), (64, 63, 999), (1000, 517, 4097)]:
+        c, d = _call(lib, np.full(n, b, np.int32), num_bins)
+        want = np.zeros(num_bins, np.uint32)
+        want[b] = n
+        check(f"one-bin B={num_bins} b={b}", np.array_equal(c, want) and d == 0)
+
+    # Hand-counted tiny case: values 3,1,3,0,7,3,-1,8 into 8 bins -> bin0:1,
+    # bin1:1, bin3:3, bin7:1; -1 and 8 name no bin.
+    c, d = _call(lib, np.array([3, 1, 3, 0, 7, 3, -1, 8], np.int32), 8)
+    check("hand", list(c) == [1, 1, 0, 3, 0, 0, 0, 1] and d == 2)
+
+    # Brute force on tiny inputs, including out-of-range values.
+    for seed in range(6):
+        num_bins = [1, 2, 5, 16, 33, 64][seed]
+        x = _rng_values(seed, 300 + 137 * seed, -3, num_bins + 3)
+        c, d = _call(lib, x, num_bins)
+        check(f"brute seed={seed}", list(c) == _brute(x, num_bins)
+              and d == int(np.sum((x < 0) | (x >= num_bins))))
+
+    # Sort + run-length count on larger inputs with far out-of-range values.
+    for seed, num_bins in [(10, 4096), (11, 65536), (12, 1000003)]:
+        x = _rng_values(seed, 200_000, -(2**31), 2**31 - 1)
+        x[::3] = _rng_values(seed + 100, x[::3].size, 0, num_bins)
+        c, d = _call(lib, x, num_bins)
+        dropped = int(np.sum((x < 0) | (x >= num_bins)))
+        check(f"rle B={num_bins}", np.array_equal(c.astype(np.int64), _sort_rle(x, num_bins)))
+        check(f"sum B={num_bins}", int(c.astype(np.int64).sum()) + d == x.size
+              and d == dropped)
+
+    # Permutation invariance and split additivity.
+    x = _rng_values(20, 50_000, -5, 3000)
+    c, _ = _call(lib, x, 2999)
+    cp, _ = _call(lib, np.random.default_rng(21).permutation(x), 2999)
+    check("permutation", np.array_equal(c, cp))
+    for k in (0, 1, 12_345, 49_999, 50_000):
+        a, da = _call(lib, x[:k], 2999)
+        b, db = _call(lib, x[k:], 2999)
+        check(f"split k={k}", np.array_equal(a.astype(np.int64) + b, c.astype(np.int64)))
+    return failed
+
+
+def test_oracle_passes_every_pin():
+    lib = oracle.load(oracle.build())
+    assert pin_failures(lib) == []
+
+
+def test_oracle_python_wrapper_matches_definition():
+    x = np.array([2, 2, 2, 0, 5, -7, 6], np.int32)
+    counts, dropped = oracle.hist(x, 6)
+    assert counts.dtype == np.uint32
+    assert list(counts) == [1, 0, 3, 0, 0, 1] and dropped == 2
+
+
+def test_oracle_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.hist(np.zeros(3, np.int32), 0)
+
+
+# Each planted mistake is a plausible slip in the loop; every one must be
+# caught by at least one pin above.
+MUTANTS = {
+    "bound-off-by-one": ("x < (int64_t)num_bins", "x <= (int64_t)num_bins"),
+    "bin-zero-lost": ("x >= 0 &&", "x > 0 &&"),
+    "double-increment": ("counts[x] += 1", "counts[x] += 2"),
+    "transposed-index": ("counts[x] += 1", "counts[num_bins - 1 - x] += 1"),
+    "last-element-lost": ("i < n; ++i", "i + 1 < n; ++i"),
+    "first-element-lost": ("for (uint64_t i = 0;", "for (uint64_t i = 1;"),
+    "no-reset": ("memset(counts, 0, (size_t)num_bins * sizeof(uint32_t));", ""),
+    "drop-not-counted": ("dropped += 1;", ";"),
+    "value-truncated": ("int64_t x = input[i];", "int64_t x = input[i] & 0xFFFF;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    src = open(oracle.SOURCE).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutant_c = tmp_path / f"{name}.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(mutant_c), "-o", str(so)],
+                   check=True)
+    lib = ctypes.CDLL(str(so))
+    lib.oracle_hist.restype = ctypes.c_uint64
+    lib.oracle_hist.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
+                                ctypes.c_void_p]
+    assert pin_failures(lib), f"planted mistake {name!r} passed every pin"
