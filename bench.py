@@ -1,0 +1,228 @@
+"""Benchmark of the partitioned LDS histogram on one MI355X.
+
+A step is one hist_run (every kernel of the path) over one batch of the
+65,536-bin uniform workload: n = 67,108,864 int32 indices uniform in
+[0, 65536) from seed 1, 65,536 uint32 bins. The inputs are resident in HBM
+before timing starts. Four device copies of the input are used in rotation,
+so that consecutive steps cannot serve a 256 MiB input from the 256 MB
+Infinity Cache that the previous step filled.
+
+Prints one JSON line (rank 0). Throughput `value` is Gelem/s over the K timed
+steps (wall clock between two device synchronisations). `roofline` is for the
+dominant kernel, timed live with HIP events around its launches inside the
+timed region. `cpu_baseline` is the CPU oracle (a sequential loop, one
+core) timed on a bounded sample of the same input.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCES = ["partitioned_chip_accumulation_amd/csrc/hist_kernels.hpp",
+                  "partitioned_chip_accumulation_amd/csrc/hist_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline)")
+    ap.add_argument("--n", type=int, default=None, help="override the workload length")
+    ap.add_argument("--path", default="auto", choices=["auto", "full", "range", "scatter"])
+    ap.add_argument("--groups", type=int, default=0)
+    ap.add_argument("--range-bins", type=int, default=0)
+    ap.add_argument("--agg", type=int, default=-1)
+    ap.add_argument("--wg", type=int, default=0)
+    ap.add_argument("--xcd-map", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=4, help="input copies used in rotation")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on the CPU-baseline work (0 = skip)")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--comparators", action="store_true",
+                    help="also time the global-atomic fallback and the stream-read ceiling")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(key: str):
+    """Counter-derived HBM bytes per launch from profiles/traffic.json, or None
+    when no entry exists for this kernel and workload or the kernel sources
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(key)
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the histogram would shard by input chunk and reduce-scatter the bins; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from partitioned_chip_accumulation_amd import hist, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.config]
+    n = w.n if args.n is None else args.n
+    B = w.num_bins
+
+    t_gen = time.perf_counter()
+    x = inputs.generate(args.config, n=n)
+    t_gen = time.perf_counter() - t_gen
+    xs = [torch.from_numpy(x).to(dev)]
+    for _ in range(max(0, args.copies - 1)):
+        xs.append(xs[0].clone())
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+
+    plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
+                     range_bins=args.range_bins, agg_rounds=args.agg, wg_size=args.wg,
+                     xcd_map=args.xcd_map)
+    info = plan.info()
+    print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,
+          flush=True)
+
+    plan.timing_enable(args.steps + args.warmup)
+    for k in range(args.warmup):
+        plan.run(xs[k % len(xs)], out)
+    torch.cuda.synchronize(dev)
+    plan.timing_read()  # discard warm-up records
+
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        plan.run(xs[k % len(xs)], out)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    phases = plan.timing_read()
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+        ref, _ = oracle.hist(x, B)
+        parity = bool(np.array_equal(out.view(torch.uint32).cpu().numpy(), ref))
+
+    ms_per_step = elapsed / args.steps * 1e3
+    gelem = n * args.steps / elapsed / 1e9
+    alg_bytes = 4 * n + 4 * B
+    gbps = alg_bytes * args.steps / elapsed / 1e9
+
+    # Dominant kernel: the phase with the most device time.
+    dom = max(phases.items(), key=lambda kv: kv[1][0])
+    dom_name, (dom_ms, dom_launches) = dom
+    dom_avg_s = dom_ms / dom_launches / 1e3
+    # Algorithmic bytes per launch of the dominant kernel: the input sweep
+    # reads each element once (4 bytes); the merges write the 4-byte bins.
+    if dom_name in ("sweep", "partition"):
+        dom_bytes = 4 * n
+    elif dom_name == "owner_hist":
+        dom_bytes = 2 * n
+    else:
+        dom_bytes = 4 * B
+    achieved = dom_bytes / dom_avg_s / 1e9
+    traffic_key = f"{dom_name}:{w.name}:n={n}:{plan.describe()}"
+    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for(traffic_key), "algorithmic_bytes": dom_bytes,
+                "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches": dom_launches}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.hist(x[:1024], B)  # build/load outside the timing
+        reps, spent, t_start = 0, 0.0, time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            oracle.hist(x, B)
+            spent += time.perf_counter() - t1
+            reps += 1
+            if time.perf_counter() - t_start >= args.cpu_seconds or reps >= 100:
+                break
+        cpu = {"value": round(n * reps / spent / 1e9, 4), "unit": "Gelem/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps} full passes of the timed input ({n} elements each), "
+                         f"{spent:.1f} s, sequential loop on one host core "
+                         f"(host has {len(os.sched_getaffinity(0))} usable cores)"}
+
+    comparators = None
+    if args.comparators:
+        comparators = {}
+        torch.cuda.synchronize(dev)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        reps = 20
+        s.record()
+        for k in range(reps):
+            hist.global_atomic(xs[k % len(xs)], B)
+        e.record()
+        torch.cuda.synchronize(dev)
+        comparators["global_atomic_gelem_s"] = round(n * reps / (s.elapsed_time(e) / 1e3) / 1e9, 2)
+        sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+        s.record()
+        for k in range(reps):
+            hist.stream_read(xs[k % len(xs)], sink)
+        e.record()
+        torch.cuda.synchronize(dev)
+        comparators["stream_read_GBps"] = round(4 * n * reps / (s.elapsed_time(e) / 1e3) / 1e9, 1)
+
+    line = {
+        "metric": "Gelem/s and achieved HBM GB/s vs peak, 65,536-bin int32 histogram, 1 MI355X",
+        "value": round(gelem, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "achieved_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "parity_vs_oracle": parity,
+        "config": {"workload": f"{w.name}: {w.recipe}; n={n}, {B} uint32 bins",
+                   "n": n, "num_bins": B, "plan": plan.describe(),
+                   "input_copies": len(xs)},
+        "phases_ms_per_step": {k: round(v[0] / v[1], 5) for k, v in phases.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if comparators is not None:
+        line["comparators"] = comparators
+    print(json.dumps(line), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

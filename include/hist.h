@@ -1,0 +1,160 @@
+/*
+ * hist.h -- partitioned on-chip (LDS) integer histogram for AMD Instinct
+ * MI355X (gfx950). C ABI.
+ *
+ * The operation
+ * -------------
+ * The page "Distributed Shared Memory", section "The cluster histogram",
+ * poses the problem: a histogram with more bins than one block's on-chip
+ * memory holds. Its answer partitions the bins so that each cooperating block
+ * owns a private slice, accumulates into the owner's slice with on-chip
+ * atomics, and after a barrier adds every slice into the global bins. The
+ * value that every such schedule reaches is
+ *
+ *     counts[b] = #{ i in [0, n) : input[i] == b },   0 <= b < num_bins,
+ *
+ * and that is what hist_run() writes. gfx950 has no cross-CU shared memory,
+ * so the partitioning is done by ownership instead of remote atomics: a
+ * workgroup owns a range of bins in its LDS (up to 160 KiB of uint32
+ * counters) and counts only the elements that fall in it (bin-range
+ * ownership); for bin counts far beyond LDS the input is first coarse-
+ * scattered by owning range and then counted per owner (two-phase path).
+ * Per-range results are merged by exclusive owners: each output bin is
+ * written once by one thread, with no global atomics.
+ *
+ * Readings of the page where it is silent:
+ *   - Values outside [0, num_bins) (including negatives) name no bin and are
+ *     skipped. The page's kernel requires the bin count to equal the
+ *     cluster's capacity exactly (same section); here any num_bins >= 1 works.
+ *   - counts is OVERWRITTEN, not accumulated into (the page adds into global
+ *     bins with atomics); a repeated call gives the same result.
+ *   - Counters are uint32; n must be < 2^32 so no counter can wrap.
+ *
+ * Memory and ownership
+ * --------------------
+ * All device buffers belong to the caller. The library never calls
+ * hipMalloc or hipFree. A plan borrows a caller-allocated device workspace
+ * (size from hist_workspace_size) for its whole lifetime. input is read-only
+ * and needs 4-byte alignment only; counts needs 4-byte alignment. counts,
+ * input and the workspace must not overlap. One plan runs one hist_run at a
+ * time: calls that share a plan must be ordered (e.g. on one stream).
+ *
+ * Errors
+ * ------
+ * Every entry point returns a status synchronously, before any work is
+ * queued when arguments are bad; nothing exits, throws or logs. HIST_ERR_HIP
+ * reports a launch error seen right after queuing (hipGetLastError); faults
+ * during execution surface at the caller's next synchronisation, as in HIP.
+ */
+#ifndef PCA_HIST_H
+#define PCA_HIST_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HIST_OK = 0,
+    HIST_ERR_INVALID_ARG = 1, /* null pointer, bad size, overlap, misalignment, wrong device */
+    HIST_ERR_UNSUPPORTED = 2, /* no gfx950 device current, or a size beyond what is supported */
+    HIST_ERR_WORKSPACE = 3,   /* workspace null or smaller than hist_workspace_size reports */
+    HIST_ERR_HIP = 4          /* a HIP call or kernel launch failed */
+} hist_status_t;
+
+/* Which schedule hist_run uses. AUTO picks from num_bins. */
+typedef enum {
+    HIST_PATH_AUTO = 0,
+    HIST_PATH_FULL = 1,    /* every workgroup holds all bins in LDS (num_bins <= LDS capacity) */
+    HIST_PATH_RANGE = 2,   /* bin-range ownership: R workgroups per input chunk, one range each */
+    HIST_PATH_SCATTER = 3  /* two-phase: scatter by owning range, then per-owner LDS histograms */
+} hist_path_t;
+
+/* Plan options. Zero-initialise and set only what you want to force;
+ * 0 (or -1 for agg_rounds) means "choose automatically". */
+typedef struct {
+    int32_t path;       /* hist_path_t */
+    int32_t groups;     /* FULL/RANGE: input chunks G; SCATTER: owner workgroups W */
+    int32_t range_bins; /* RANGE: bins per owned range (multiple of 4, <= LDS capacity) */
+    int32_t agg_rounds; /* wave duplicate aggregation rounds before each LDS add:
+                           -1 auto, 0 off, 1..4 */
+    int32_t wg_size;    /* sweep workgroup size: 256, 512 or 1024 (0 = auto) */
+    int32_t xcd_map;    /* RANGE: 1 = place a chunk's R owners on one XCD (default),
+                           2 = plain order (for measurement) */
+    int32_t reserved[2];
+} hist_plan_opts_t;
+
+/* Numeric description of a plan (for logs and benchmarks). */
+typedef struct {
+    int32_t path;          /* hist_path_t actually used */
+    int32_t device;        /* HIP device ordinal the plan was made on */
+    int32_t cu_count;
+    int32_t xcd_count;
+    uint32_t num_bins;
+    uint32_t range_bins;   /* bins owned by one workgroup (S) */
+    uint32_t ranges;       /* R = ceil(num_bins / S) */
+    uint32_t groups;       /* FULL/RANGE: G chunks; SCATTER: W owner workgroups */
+    uint32_t wg_size;
+    int32_t agg_rounds;
+    uint32_t tile_elems;   /* SCATTER: elements per scatter tile */
+    uint32_t reserved;
+    uint64_t max_n;
+    uint64_t workspace_bytes;
+} hist_plan_info_t;
+
+typedef struct hist_plan hist_plan_t; /* opaque, host memory only */
+
+/* Bytes of device workspace a plan for (num_bins, max_n, opts) needs on the
+ * current device. opts may be NULL. Errors: INVALID_ARG for num_bins == 0,
+ * max_n >= 2^32, bytes == NULL or bad opts; UNSUPPORTED when the current
+ * device is not gfx950 or num_bins exceeds HIST_MAX_BINS. */
+hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n,
+                                  const hist_plan_opts_t *opts, uint64_t *bytes);
+
+/* Largest num_bins any path supports (2^26 bins, 256 MiB of counts). */
+#define HIST_MAX_BINS (1u << 26)
+
+/* Make a plan on the current device. workspace must be device memory of at
+ * least hist_workspace_size() bytes, 256-byte aligned; it may be NULL when
+ * that size is 0. The plan keeps the pointer until hist_plan_destroy. */
+hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
+                               const hist_plan_opts_t *opts, void *workspace,
+                               uint64_t workspace_bytes);
+
+/* Queue the histogram of input[0..n) into counts[0..num_bins) on stream
+ * (0 = the null stream). num_bins must equal the plan's and n <= max_n.
+ * n == 0 is valid and writes num_bins zeros. input may be NULL when n == 0.
+ * The call is asynchronous; counts is complete when the stream reaches it. */
+hist_status_t hist_run(hist_plan_t *plan, uint32_t *counts, const int32_t *input, uint64_t n,
+                       uint32_t num_bins, hipStream_t stream);
+
+/* Fill *info. */
+hist_status_t hist_plan_info(const hist_plan_t *plan, hist_plan_info_t *info);
+
+/* Write a one-line description ("path=range R=2 S=32768 G=128 ...") into
+ * buf (always NUL-terminated when len > 0). */
+hist_status_t hist_plan_describe(const hist_plan_t *plan, char *buf, uint64_t len);
+
+/* Per-kernel timing for measurement. When enabled, hist_run records a pair
+ * of HIP events around each kernel it launches, on the stream it is given.
+ * hist_plan_timing_read waits for the recorded events and returns, for each
+ * phase p < HIST_MAX_PHASES, the summed milliseconds and the launch count,
+ * then clears the record. Phase names come from hist_plan_phase_name.
+ * capacity bounds the number of hist_run calls recorded (older ones beyond
+ * it are not recorded). Enabling allocates host-side HIP events only. */
+#define HIST_MAX_PHASES 6
+hist_status_t hist_plan_timing_enable(hist_plan_t *plan, uint32_t capacity);
+hist_status_t hist_plan_timing_read(hist_plan_t *plan, double *ms, uint32_t *launches);
+const char *hist_plan_phase_name(const hist_plan_t *plan, uint32_t phase);
+
+void hist_plan_destroy(hist_plan_t *plan);
+
+const char *hist_status_str(hist_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PCA_HIST_H */

@@ -1,0 +1,581 @@
+// hist_api.hip -- host side of libpca_hist.so: plans, argument checks and
+// kernel launches for the partitioned LDS histogram (declared in hist.h).
+//
+// Path choice follows the page "Distributed Shared Memory": when the bins fit
+// one workgroup's on-chip memory every workgroup privatises all of them
+// (FULL); when they do not, the bins are partitioned so that each workgroup
+// owns a slice (section "The cluster histogram") -- on gfx950 by bin-range
+// ownership (RANGE) or, when the ranges get many, by routing elements to
+// their owners first (SCATTER). Section "When it beats global atomics" gives
+// the capacity argument: R cooperating workgroups hold R slices on-chip.
+#include "hist.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "hist_kernels.hpp"
+
+namespace {
+
+constexpr uint32_t kMaxLdsBins = 40960;      // 160 KiB of uint32 counters
+constexpr uint32_t kScatterShift = 15;       // SCATTER range = 32768 bins (128 KiB)
+constexpr uint32_t kScatterWG = 1024;
+constexpr uint32_t kScatterVPT = 4;          // vectors per thread in a scatter tile
+constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elements
+constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slots per tile
+constexpr uint32_t kRangeMaxR = 8;           // RANGE up to this many ranges (AUTO)
+constexpr uint32_t kMinElemsPerGroup = 32768;
+constexpr int kMaxWavesPerCU = 32;
+
+enum Phase { PH_SWEEP = 0, PH_MERGE = 1, PH_PART = 2, PH_SCAN = 3, PH_OWNER = 4, PH_SLOTS = 5 };
+const char *kPhaseNames[HIST_MAX_PHASES] = {"sweep", "merge", "partition", "range_scan",
+                                            "owner_hist", "slot_merge"};
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+struct DeviceInfo {
+    int device = -1;
+    int cu = 0;
+    int xcd = 1;
+    uint32_t lds = 0;  // bytes per workgroup
+};
+
+hist_status_t query_device(DeviceInfo *d)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_UNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_UNSUPPORTED;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return HIST_ERR_UNSUPPORTED;
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_UNSUPPORTED;
+    }
+    d->device = dev;
+    d->cu = prop.multiProcessorCount;
+    d->xcd = std::max(1, d->cu / 32);  // gfx950: 32 CUs per XCD
+    d->lds = (uint32_t)std::min<int>(lds, (int)(kMaxLdsBins * 4));
+    return HIST_OK;
+}
+
+}  // namespace
+
+struct hist_plan {
+    DeviceInfo dev;
+    uint32_t num_bins = 0;
+    uint64_t max_n = 0;
+    int path = 0;
+    int agg = 0;
+    uint32_t wg = 0;
+    uint32_t xcd_map = 1;
+    // FULL / RANGE
+    uint32_t range_bins = 0, ranges = 0, groups = 0;
+    uint64_t row = 0;  // partial row stride (bins, multiple of 4)
+    // SCATTER
+    uint32_t tiles = 0, owners = 0;
+    // workspace
+    char *ws = nullptr;
+    uint64_t ws_bytes = 0, need = 0;
+    uint64_t off_partials = 0, off_stage = 0, off_tcnt = 0, off_tbase = 0, off_tpre = 0,
+             off_totals = 0;
+    // timing
+    uint32_t tcap = 0, truns = 0;
+    std::vector<hipEvent_t> ev;  // [tcap][HIST_MAX_PHASES][2]
+    std::vector<uint8_t> used;   // [tcap][HIST_MAX_PHASES]
+};
+
+namespace {
+
+hist_status_t check_opts(const hist_plan_opts_t *o)
+{
+    if (!o) return HIST_OK;
+    if (o->path < 0 || o->path > 3) return HIST_ERR_INVALID_ARG;
+    if (o->groups < 0 || o->groups > 65536) return HIST_ERR_INVALID_ARG;
+    if (o->range_bins < 0 || (o->range_bins % 4) != 0 || o->range_bins > (int)kMaxLdsBins)
+        return HIST_ERR_INVALID_ARG;
+    if (o->agg_rounds < -1 || o->agg_rounds > 4 || o->agg_rounds == 3) return HIST_ERR_INVALID_ARG;
+    if (o->wg_size != 0 && o->wg_size != 256 && o->wg_size != 512 && o->wg_size != 1024)
+        return HIST_ERR_INVALID_ARG;
+    if (o->xcd_map < 0 || o->xcd_map > 2) return HIST_ERR_INVALID_ARG;
+    return HIST_OK;
+}
+
+// Fill every plan field that depends only on (num_bins, max_n, opts, device).
+hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *o)
+{
+    hist_plan_opts_t opts{};
+    opts.agg_rounds = -1;
+    if (o) opts = *o;
+    const DeviceInfo &d = p->dev;
+    const uint32_t lds_bins = std::min<uint32_t>(kMaxLdsBins, d.lds / 4) & ~3u;
+    p->num_bins = num_bins;
+    p->max_n = max_n;
+    p->xcd_map = opts.xcd_map == 0 ? 1 : (uint32_t)opts.xcd_map;
+
+    int path = opts.path;
+    if (path == HIST_PATH_AUTO) {
+        if (num_bins <= lds_bins) path = HIST_PATH_FULL;
+        else if (num_bins <= kRangeMaxR * lds_bins) path = HIST_PATH_RANGE;
+        else path = HIST_PATH_SCATTER;
+    }
+    if (path == HIST_PATH_FULL && num_bins > lds_bins) return HIST_ERR_UNSUPPORTED;
+    p->path = path;
+    p->agg = opts.agg_rounds < 0 ? 0 : opts.agg_rounds;
+
+    if (path == HIST_PATH_FULL || path == HIST_PATH_RANGE) {
+        uint32_t S, R;
+        if (path == HIST_PATH_FULL) {
+            R = 1;
+            S = (num_bins + 3) & ~3u;
+        } else if (opts.range_bins > 0) {
+            S = (uint32_t)opts.range_bins;
+            R = ceil_div(num_bins, S);
+        } else {
+            // Smallest R that fits LDS, then the one among R..2R that keeps the
+            // most CUs busy per element read (R owners read every element).
+            const uint32_t rmin = std::max<uint32_t>(2, ceil_div(num_bins, lds_bins));
+            double best = 1e30;
+            R = rmin;
+            for (uint32_t r = rmin; r <= 2 * rmin; ++r) {
+                uint32_t g = (uint32_t)d.cu / r;
+                if (g >= (uint32_t)d.xcd) g = g / d.xcd * d.xcd;
+                if (g == 0) g = 1;
+                const double cost = (double)r / ((double)g * r / d.cu);
+                if (cost < best - 1e-9) { best = cost; R = r; }
+            }
+            S = (ceil_div(num_bins, R) + 3) & ~3u;
+        }
+        if (S > lds_bins || S == 0) return HIST_ERR_UNSUPPORTED;
+        const uint32_t occ_lds = std::max<uint32_t>(1, d.lds / (S * 4));
+        uint32_t wg = (uint32_t)opts.wg_size;
+        if (wg == 0) wg = occ_lds >= 2 ? 512 : 1024;
+        const uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
+        uint32_t G = (uint32_t)opts.groups;
+        if (G == 0) {
+            G = (uint32_t)d.cu * occ / R;
+            if (G >= (uint32_t)d.xcd) G = G / d.xcd * d.xcd;
+            // Keep the merge traffic (G * num_bins * 4 bytes) a small fraction of the
+            // input (4 * n bytes), and every chunk a useful size.
+            const uint64_t by_merge = std::max<uint64_t>(1, max_n / (4ull * num_bins));
+            const uint64_t by_size = std::max<uint64_t>(1, max_n / kMinElemsPerGroup);
+            G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
+        }
+        p->range_bins = S;
+        p->ranges = R;
+        p->groups = G;
+        p->wg = wg;
+        p->row = ((uint64_t)num_bins + 3) & ~3ull;
+        uint64_t off = 0;
+        p->off_partials = off;
+        off += G > 1 ? align_up((uint64_t)G * p->row * 4, 256) : 0;
+        p->need = off;
+    } else {
+        const uint32_t S = 1u << kScatterShift;
+        const uint32_t R = ceil_div(num_bins, S);
+        const uint64_t nvec_max = max_n / 4;
+        const uint32_t T = std::max<uint32_t>(1, ceil_div(nvec_max, kScatterWG * kScatterVPT));
+        uint32_t W = (uint32_t)opts.groups;
+        if (W == 0) W = (uint32_t)d.cu;
+        p->range_bins = S;
+        p->ranges = R;
+        p->tiles = T;
+        p->owners = W;
+        p->groups = W;
+        p->wg = kScatterWG;
+        uint64_t off = 0;
+        p->off_stage = off;
+        off += align_up((uint64_t)T * kScatterCap * 2, 256);
+        p->off_tcnt = off;
+        off += align_up((uint64_t)R * T * 4, 256);
+        p->off_tbase = off;
+        off += align_up((uint64_t)R * T * 4, 256);
+        p->off_tpre = off;
+        off += align_up((uint64_t)R * T * 4, 256);
+        p->off_totals = off;
+        off += align_up((uint64_t)R * 4, 256);
+        p->off_partials = off;
+        off += align_up((uint64_t)(W + R) * S * 4, 256);
+        p->need = off;
+    }
+    return HIST_OK;
+}
+
+bool overlaps(const void *a, uint64_t an, const void *b, uint64_t bn)
+{
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+template <typename K>
+hipError_t allow_lds(K kernel, uint32_t bytes)
+{
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int WG, int AGG, bool NT>
+hipError_t launch_sweep_t(const hist_plan *p, pca::InputView in, uint32_t G, uint32_t xcds,
+                          uint32_t *dst, uint64_t row, hipStream_t s)
+{
+    auto k = pca::k_sweep<WG, 4, AGG, NT>;
+    const uint32_t bytes = p->range_bins * 4;
+    hipError_t e = allow_lds(k, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(G * p->ranges), dim3(WG), bytes, s, in, p->num_bins, p->range_bins,
+                       p->ranges, G, xcds, dst, row);
+    return hipGetLastError();
+}
+
+template <int WG, bool NT>
+hipError_t launch_sweep_agg(const hist_plan *p, pca::InputView in, uint32_t G, uint32_t xcds,
+                            uint32_t *dst, uint64_t row, hipStream_t s)
+{
+    switch (p->agg) {
+    case 0: return launch_sweep_t<WG, 0, NT>(p, in, G, xcds, dst, row, s);
+    case 1: return launch_sweep_t<WG, 1, NT>(p, in, G, xcds, dst, row, s);
+    case 2: return launch_sweep_t<WG, 2, NT>(p, in, G, xcds, dst, row, s);
+    default: return launch_sweep_t<WG, 4, NT>(p, in, G, xcds, dst, row, s);
+    }
+}
+
+template <bool NT>
+hipError_t launch_sweep_nt(const hist_plan *p, pca::InputView in, uint32_t G, uint32_t xcds,
+                           uint32_t *dst, uint64_t row, hipStream_t s)
+{
+    switch (p->wg) {
+    case 256: return launch_sweep_agg<256, NT>(p, in, G, xcds, dst, row, s);
+    case 512: return launch_sweep_agg<512, NT>(p, in, G, xcds, dst, row, s);
+    default: return launch_sweep_agg<1024, NT>(p, in, G, xcds, dst, row, s);
+    }
+}
+
+template <int AGG>
+hipError_t launch_partition_t(const hist_plan *p, pca::InputView in, uint32_t T, hipStream_t s)
+{
+    auto k = pca::k_partition<kScatterWG, kScatterVPT, AGG>;
+    const uint32_t rpad = (p->ranges + 3u) & ~3u;
+    const uint32_t bytes = (2 * rpad + 4) * 4 + kScatterCap * 2;
+    hipError_t e = allow_lds(k, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(T), dim3(kScatterWG), bytes, s, in, p->num_bins, kScatterShift,
+                       p->ranges, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage), kScatterCap,
+                       reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
+                       reinterpret_cast<uint32_t *>(p->ws + p->off_tbase));
+    return hipGetLastError();
+}
+
+template <int AGG>
+hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
+{
+    auto k = pca::k_bucket_hist<kScatterWG, 4, AGG>;
+    const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8;
+    hipError_t e = allow_lds(k, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(p->owners), dim3(kScatterWG), bytes, s,
+                       reinterpret_cast<const uint16_t *>(p->ws + p->off_stage), kScatterCap,
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt),
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase),
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T,
+                       p->range_bins, p->num_bins, p->owners,
+                       reinterpret_cast<uint32_t *>(p->ws + p->off_partials));
+    return hipGetLastError();
+}
+
+struct PhaseTimer {
+    hist_plan *p;
+    hipStream_t s;
+    uint32_t slot;
+    bool on;
+    PhaseTimer(hist_plan *p_, hipStream_t s_) : p(p_), s(s_)
+    {
+        on = p->tcap > 0 && p->truns < p->tcap;
+        slot = p->truns;
+        if (on) {
+            std::fill(p->used.begin() + (size_t)slot * HIST_MAX_PHASES,
+                      p->used.begin() + (size_t)(slot + 1) * HIST_MAX_PHASES, 0);
+            p->truns++;
+        }
+    }
+    hipEvent_t &event(int ph, int which)
+    {
+        return p->ev[((size_t)slot * HIST_MAX_PHASES + ph) * 2 + which];
+    }
+    void begin(int ph)
+    {
+        if (on) (void)hipEventRecord(event(ph, 0), s);
+    }
+    void end(int ph)
+    {
+        if (on) {
+            (void)hipEventRecord(event(ph, 1), s);
+            p->used[(size_t)slot * HIST_MAX_PHASES + ph] = 1;
+        }
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *hist_status_str(hist_status_t s)
+{
+    switch (s) {
+    case HIST_OK: return "ok";
+    case HIST_ERR_INVALID_ARG: return "invalid argument";
+    case HIST_ERR_UNSUPPORTED: return "unsupported (no gfx950 device current, or size too large)";
+    case HIST_ERR_WORKSPACE: return "workspace missing or too small";
+    case HIST_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *opts,
+                                  uint64_t *bytes)
+{
+    if (!bytes || num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
+    hist_status_t st = check_opts(opts);
+    if (st != HIST_OK) return st;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    hist_plan p;
+    st = query_device(&p.dev);
+    if (st != HIST_OK) return st;
+    st = design(&p, num_bins, max_n, opts);
+    if (st != HIST_OK) return st;
+    *bytes = p.need;
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
+                               const hist_plan_opts_t *opts, void *workspace,
+                               uint64_t workspace_bytes)
+{
+    if (!plan) return HIST_ERR_INVALID_ARG;
+    *plan = nullptr;
+    if (num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
+    hist_status_t st = check_opts(opts);
+    if (st != HIST_OK) return st;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    if (((uintptr_t)workspace & 255u) != 0) return HIST_ERR_INVALID_ARG;
+    hist_plan *p = new (std::nothrow) hist_plan();
+    if (!p) return HIST_ERR_INVALID_ARG;
+    st = query_device(&p->dev);
+    if (st == HIST_OK) st = design(p, num_bins, max_n, opts);
+    if (st == HIST_OK && p->need > 0 && (!workspace || workspace_bytes < p->need))
+        st = HIST_ERR_WORKSPACE;
+    if (st != HIST_OK) {
+        delete p;
+        return st;
+    }
+    p->ws = static_cast<char *>(workspace);
+    p->ws_bytes = workspace_bytes;
+    *plan = p;
+    return HIST_OK;
+}
+
+hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
+                       uint32_t num_bins, hipStream_t stream)
+{
+    if (!p || !counts) return HIST_ERR_INVALID_ARG;
+    if (n > 0 && !input) return HIST_ERR_INVALID_ARG;
+    if (num_bins != p->num_bins || n > p->max_n) return HIST_ERR_INVALID_ARG;
+    if (((uintptr_t)counts & 3u) != 0 || ((uintptr_t)input & 3u) != 0) return HIST_ERR_INVALID_ARG;
+    const uint64_t cbytes = (uint64_t)num_bins * 4, ibytes = n * 4;
+    if (overlaps(counts, cbytes, input, ibytes) || overlaps(counts, cbytes, p->ws, p->need) ||
+        overlaps(input, ibytes, p->ws, p->need))
+        return HIST_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HIST_ERR_HIP;
+    if (dev != p->dev.device) return HIST_ERR_INVALID_ARG;
+
+    PhaseTimer tm(p, stream);
+    hipError_t e = hipSuccess;
+    if (n == 0) {
+        tm.begin(PH_SWEEP);
+        hipLaunchKernelGGL(pca::k_fill_zero, dim3(std::max<uint32_t>(1, std::min<uint32_t>(1024, ceil_div(num_bins, 256)))),
+                           dim3(256), 0, stream, counts, (uint64_t)num_bins);
+        tm.end(PH_SWEEP);
+        return hipGetLastError() == hipSuccess ? HIST_OK : HIST_ERR_HIP;
+    }
+
+    pca::InputView in;
+    in.ptr = input;
+    const uint64_t mis = ((uintptr_t)input & 15u) / 4;
+    in.head = (uint32_t)std::min<uint64_t>(n, mis ? 4 - mis : 0);
+    in.nvec = (n - in.head) / 4;
+    in.tail = (uint32_t)(n - in.head - 4 * in.nvec);
+
+    if (p->path == HIST_PATH_FULL || p->path == HIST_PATH_RANGE) {
+        // Fewer chunks for a small call: keep the merge a small fraction of the work.
+        uint32_t G = p->groups;
+        const uint64_t by_merge = std::max<uint64_t>(1, n / (4ull * num_bins));
+        const uint64_t by_size = std::max<uint64_t>(1, n / kMinElemsPerGroup);
+        G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
+        const uint32_t xcds = (p->xcd_map == 1 && p->ranges > 1 && G % p->dev.xcd == 0) ? p->dev.xcd : 1;
+        uint32_t *dst = G > 1 ? reinterpret_cast<uint32_t *>(p->ws + p->off_partials) : counts;
+        const uint64_t row = G > 1 ? p->row : 0;
+        const bool nt = p->ranges == 1;
+        tm.begin(PH_SWEEP);
+        e = nt ? launch_sweep_nt<true>(p, in, G, xcds, dst, row, stream)
+               : launch_sweep_nt<false>(p, in, G, xcds, dst, row, stream);
+        tm.end(PH_SWEEP);
+        if (e != hipSuccess) return HIST_ERR_HIP;
+        if (G > 1) {
+            tm.begin(PH_MERGE);
+            const uint32_t grid = ceil_div(p->row, 256);
+            if (G >= 64)
+                hipLaunchKernelGGL(pca::k_merge<16>, dim3(grid), dim3(1024), 0, stream, dst, G, p->row,
+                                   num_bins, counts);
+            else
+                hipLaunchKernelGGL(pca::k_merge<4>, dim3(grid), dim3(256), 0, stream, dst, G, p->row,
+                                   num_bins, counts);
+            tm.end(PH_MERGE);
+            if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+        }
+        return HIST_OK;
+    }
+
+    // SCATTER
+    const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kScatterWG * kScatterVPT));
+    if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
+    tm.begin(PH_PART);
+    switch (p->agg) {
+    case 0: e = launch_partition_t<0>(p, in, T, stream); break;
+    case 1: e = launch_partition_t<1>(p, in, T, stream); break;
+    case 2: e = launch_partition_t<2>(p, in, T, stream); break;
+    default: e = launch_partition_t<4>(p, in, T, stream); break;
+    }
+    tm.end(PH_PART);
+    if (e != hipSuccess) return HIST_ERR_HIP;
+    tm.begin(PH_SCAN);
+    hipLaunchKernelGGL(pca::k_bucket_scan<1024>, dim3(p->ranges), dim3(1024), 0, stream,
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt), T,
+                       reinterpret_cast<uint32_t *>(p->ws + p->off_tpre),
+                       reinterpret_cast<uint32_t *>(p->ws + p->off_totals));
+    tm.end(PH_SCAN);
+    if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+    tm.begin(PH_OWNER);
+    switch (p->agg) {
+    case 0: e = launch_owner_t<0>(p, T, stream); break;
+    case 1: e = launch_owner_t<1>(p, T, stream); break;
+    case 2: e = launch_owner_t<2>(p, T, stream); break;
+    default: e = launch_owner_t<4>(p, T, stream); break;
+    }
+    tm.end(PH_OWNER);
+    if (e != hipSuccess) return HIST_ERR_HIP;
+    tm.begin(PH_SLOTS);
+    hipLaunchKernelGGL(pca::k_merge_slots<16>, dim3(ceil_div(num_bins, 256)), dim3(1024), 0, stream,
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_partials),
+                       reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges,
+                       p->range_bins, num_bins, p->owners, counts);
+    tm.end(PH_SLOTS);
+    if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_info(const hist_plan_t *p, hist_plan_info_t *info)
+{
+    if (!p || !info) return HIST_ERR_INVALID_ARG;
+    std::memset(info, 0, sizeof(*info));
+    info->path = p->path;
+    info->device = p->dev.device;
+    info->cu_count = p->dev.cu;
+    info->xcd_count = p->dev.xcd;
+    info->num_bins = p->num_bins;
+    info->range_bins = p->range_bins;
+    info->ranges = p->ranges;
+    info->groups = p->groups;
+    info->wg_size = p->wg;
+    info->agg_rounds = p->agg;
+    info->tile_elems = p->path == HIST_PATH_SCATTER ? kScatterTile : 0;
+    info->max_n = p->max_n;
+    info->workspace_bytes = p->need;
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_describe(const hist_plan_t *p, char *buf, uint64_t len)
+{
+    if (!p || !buf || len == 0) return HIST_ERR_INVALID_ARG;
+    static const char *names[] = {"auto", "full", "range", "scatter"};
+    std::snprintf(buf, len,
+                  "path=%s bins=%u S=%u R=%u %s=%u wg=%u agg=%d tile=%u cu=%d xcd=%d lds=%u ws=%llu",
+                  names[p->path], p->num_bins, p->range_bins, p->ranges,
+                  p->path == HIST_PATH_SCATTER ? "W" : "G", p->groups, p->wg, p->agg,
+                  p->path == HIST_PATH_SCATTER ? kScatterTile : 0u, p->dev.cu, p->dev.xcd,
+                  p->dev.lds, (unsigned long long)p->need);
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_timing_enable(hist_plan_t *p, uint32_t capacity)
+{
+    if (!p || capacity > (1u << 16)) return HIST_ERR_INVALID_ARG;
+    for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
+    p->ev.clear();
+    p->used.clear();
+    p->tcap = 0;
+    p->truns = 0;
+    if (capacity == 0) return HIST_OK;
+    p->ev.resize((size_t)capacity * HIST_MAX_PHASES * 2);
+    for (auto &e : p->ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            (void)hipGetLastError();
+            return HIST_ERR_HIP;
+        }
+    }
+    p->used.assign((size_t)capacity * HIST_MAX_PHASES, 0);
+    p->tcap = capacity;
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_timing_read(hist_plan_t *p, double *ms, uint32_t *launches)
+{
+    if (!p || !ms || !launches) return HIST_ERR_INVALID_ARG;
+    for (int k = 0; k < HIST_MAX_PHASES; ++k) {
+        ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    for (uint32_t r = 0; r < p->truns; ++r) {
+        for (int k = 0; k < HIST_MAX_PHASES; ++k) {
+            if (!p->used[(size_t)r * HIST_MAX_PHASES + k]) continue;
+            hipEvent_t a = p->ev[((size_t)r * HIST_MAX_PHASES + k) * 2];
+            hipEvent_t b = p->ev[((size_t)r * HIST_MAX_PHASES + k) * 2 + 1];
+            float t = 0.f;
+            if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&t, a, b) != hipSuccess)
+                return HIST_ERR_HIP;
+            ms[k] += t;
+            launches[k] += 1;
+        }
+    }
+    p->truns = 0;
+    return HIST_OK;
+}
+
+const char *hist_plan_phase_name(const hist_plan_t *p, uint32_t phase)
+{
+    (void)p;
+    return phase < HIST_MAX_PHASES ? kPhaseNames[phase] : "";
+}
+
+void hist_plan_destroy(hist_plan_t *p)
+{
+    if (!p) return;
+    for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
+    delete p;
+}
+
+}  // extern "C"

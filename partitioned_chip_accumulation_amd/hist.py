@@ -1,0 +1,257 @@
+"""Python binding of libpca_hist.so (the C ABI in include/hist.h).
+
+Argument marshalling only: every step of the histogram runs in the library's
+HIP kernels. PyTorch provides device memory (input, output, workspace) and
+the stream (``torch.cuda.current_stream().cuda_stream``, a hipStream_t on
+ROCm builds). There is no fallback: if the library is missing or the device
+is not gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libpca_hist.so")
+
+HIST_OK, HIST_ERR_INVALID_ARG, HIST_ERR_UNSUPPORTED, HIST_ERR_WORKSPACE, HIST_ERR_HIP = range(5)
+PATHS = {"auto": 0, "full": 1, "range": 2, "scatter": 3}
+PATH_NAMES = {v: k for k, v in PATHS.items()}
+MAX_PHASES = 6
+MAX_BINS = 1 << 26
+
+
+class HistError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+
+
+class LibraryMissing(ImportError):
+    pass
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("groups", ctypes.c_int32),
+                ("range_bins", ctypes.c_int32), ("agg_rounds", ctypes.c_int32),
+                ("wg_size", ctypes.c_int32), ("xcd_map", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("cu_count", ctypes.c_int32), ("xcd_count", ctypes.c_int32),
+                ("num_bins", ctypes.c_uint32), ("range_bins", ctypes.c_uint32),
+                ("ranges", ctypes.c_uint32), ("groups", ctypes.c_uint32),
+                ("wg_size", ctypes.c_uint32), ("agg_rounds", ctypes.c_int32),
+                ("tile_elems", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("max_n", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def load(path: str = LIBRARY):
+    """Load the library and declare its signatures. Raises LibraryMissing."""
+    if not os.path.exists(path):
+        raise LibraryMissing(
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
+    P = ctypes.POINTER
+    sigs = {
+        "hist_status_str": (ctypes.c_char_p, [i32]),
+        "hist_workspace_size": (i32, [u32, u64, P(PlanOpts), P(u64)]),
+        "hist_plan_create": (i32, [P(vp), u32, u64, P(PlanOpts), vp, u64]),
+        "hist_run": (i32, [vp, vp, vp, u64, u32, vp]),
+        "hist_plan_info": (i32, [vp, P(PlanInfo)]),
+        "hist_plan_describe": (i32, [vp, ctypes.c_char_p, u64]),
+        "hist_plan_timing_enable": (i32, [vp, u32]),
+        "hist_plan_timing_read": (i32, [vp, P(ctypes.c_double), P(u32)]),
+        "hist_plan_phase_name": (ctypes.c_char_p, [vp, u32]),
+        "hist_plan_destroy": (None, [vp]),
+        "hist_bench_global_atomic": (i32, [vp, vp, u64, u32, vp]),
+        "hist_bench_read": (i32, [vp, u64, vp, vp]),
+        "hist_bench_copy": (i32, [vp, vp, u64, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def library():
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return library().hist_status_str(status).decode()
+    except LibraryMissing:
+        return "library missing"
+
+
+def _check(status: int, what: str):
+    if status != HIST_OK:
+        raise HistError(status, what)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _opts(path="auto", groups=0, range_bins=0, agg_rounds=-1, wg_size=0, xcd_map=0) -> PlanOpts:
+    o = PlanOpts()
+    o.path = PATHS[path] if isinstance(path, str) else int(path)
+    o.groups, o.range_bins, o.agg_rounds = int(groups), int(range_bins), int(agg_rounds)
+    o.wg_size, o.xcd_map = int(wg_size), int(xcd_map)
+    return o
+
+
+def workspace_size(num_bins: int, max_n: int, **opts) -> int:
+    o = _opts(**opts)
+    n = ctypes.c_uint64(0)
+    _check(library().hist_workspace_size(num_bins, max_n, ctypes.byref(o), ctypes.byref(n)),
+           "hist_workspace_size")
+    return int(n.value)
+
+
+@dataclass
+class Info:
+    path: str
+    device: int
+    cu_count: int
+    xcd_count: int
+    num_bins: int
+    range_bins: int
+    ranges: int
+    groups: int
+    wg_size: int
+    agg_rounds: int
+    tile_elems: int
+    max_n: int
+    workspace_bytes: int
+
+
+class Plan:
+    """A histogram plan for ``num_bins`` bins and inputs of up to ``max_n``
+    elements on one device; owns its device workspace (a torch tensor)."""
+
+    def __init__(self, num_bins: int, max_n: int, device=None, **opts):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        self.num_bins, self.max_n = int(num_bins), int(max_n)
+        self._plan = ctypes.c_void_p()
+        lib = library()
+        o = _opts(**opts)
+        with torch.cuda.device(self.device):
+            n = ctypes.c_uint64(0)
+            _check(lib.hist_workspace_size(self.num_bins, self.max_n, ctypes.byref(o),
+                                           ctypes.byref(n)), "hist_workspace_size")
+            self.workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8,
+                                         device=self.device)
+            _check(lib.hist_plan_create(ctypes.byref(self._plan), self.num_bins, self.max_n,
+                                        ctypes.byref(o),
+                                        self.workspace.data_ptr() if n.value else None,
+                                        int(n.value)), "hist_plan_create")
+
+    def run(self, input: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Histogram of an int32 CUDA tensor into a uint32 tensor of num_bins."""
+        if input.dtype != torch.int32 or input.device != self.device:
+            raise ValueError("input must be an int32 tensor on the plan's device")
+        if not input.is_contiguous():
+            raise ValueError("input must be contiguous")
+        if out is None:
+            out = torch.empty(self.num_bins, dtype=torch.int32, device=self.device)
+        if out.device != self.device or out.numel() != self.num_bins or \
+                out.element_size() != 4 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous 4-byte tensor of num_bins on the device")
+        n = input.numel()
+        with torch.cuda.device(self.device):
+            _check(library().hist_run(self._plan, out.data_ptr(),
+                                      input.data_ptr() if n else None, n, self.num_bins,
+                                      _stream_handle(self.device)), "hist_run")
+        return out.view(torch.uint32) if out.dtype == torch.int32 else out
+
+    __call__ = run
+
+    def info(self) -> Info:
+        i = PlanInfo()
+        _check(library().hist_plan_info(self._plan, ctypes.byref(i)), "hist_plan_info")
+        return Info(PATH_NAMES[i.path], i.device, i.cu_count, i.xcd_count, i.num_bins,
+                    i.range_bins, i.ranges, i.groups, i.wg_size, i.agg_rounds, i.tile_elems,
+                    i.max_n, i.workspace_bytes)
+
+    def describe(self) -> str:
+        buf = ctypes.create_string_buffer(512)
+        _check(library().hist_plan_describe(self._plan, buf, len(buf)), "hist_plan_describe")
+        return buf.value.decode()
+
+    def timing_enable(self, capacity: int):
+        _check(library().hist_plan_timing_enable(self._plan, capacity), "hist_plan_timing_enable")
+
+    def timing_read(self) -> dict[str, tuple[float, int]]:
+        ms = (ctypes.c_double * MAX_PHASES)()
+        cnt = (ctypes.c_uint32 * MAX_PHASES)()
+        _check(library().hist_plan_timing_read(self._plan, ms, cnt), "hist_plan_timing_read")
+        lib = library()
+        return {lib.hist_plan_phase_name(self._plan, k).decode(): (ms[k], cnt[k])
+                for k in range(MAX_PHASES) if cnt[k]}
+
+    def close(self):
+        if self._plan:
+            library().hist_plan_destroy(self._plan)
+            self._plan = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_cache: dict = {}
+
+
+def run(input: torch.Tensor, num_bins: int, **opts) -> torch.Tensor:
+    """One-call histogram with a cached plan (max_n rounded up to a power of two)."""
+    n = max(1, input.numel())
+    max_n = 1 << (n - 1).bit_length()
+    max_n = min(max_n, 2**32 - 1)
+    key = (input.device, int(num_bins), max_n, tuple(sorted(opts.items())))
+    plan = _cache.get(key)
+    if plan is None:
+        plan = _cache[key] = Plan(num_bins, max_n, device=input.device, **opts)
+    return plan.run(input)
+
+
+# Measurement-only kernels (include/hist_bench.h).
+
+def global_atomic(input: torch.Tensor, num_bins: int) -> torch.Tensor:
+    out = torch.empty(num_bins, dtype=torch.int32, device=input.device)
+    with torch.cuda.device(input.device):
+        _check(library().hist_bench_global_atomic(out.data_ptr(), input.data_ptr(), input.numel(),
+                                                  num_bins, _stream_handle(input.device)),
+               "hist_bench_global_atomic")
+    return out.view(torch.uint32)
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor):
+    with torch.cuda.device(src.device):
+        _check(library().hist_bench_read(src.data_ptr(), src.numel() * src.element_size(),
+                                         sink.data_ptr(), _stream_handle(src.device)),
+               "hist_bench_read")
+
+
+def copy(dst: torch.Tensor, src: torch.Tensor):
+    with torch.cuda.device(src.device):
+        _check(library().hist_bench_copy(dst.data_ptr(), src.data_ptr(),
+                                         src.numel() * src.element_size(),
+                                         _stream_handle(src.device)), "hist_bench_copy")

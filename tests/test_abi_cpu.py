@@ -1,0 +1,95 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+that include/*.h declares, and rejects bad arguments with the documented
+status before touching a device."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from partitioned_chip_accumulation_amd import hist
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"\b(hist_[a-z_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_headers_declare_the_expected_calls():
+    names = declared_functions()
+    for must in ["hist_plan_create", "hist_run", "hist_workspace_size", "hist_plan_destroy",
+                 "hist_status_str", "hist_bench_global_atomic"]:
+        assert must in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(name):
+    lib = ctypes.CDLL(hist.LIBRARY)
+    assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = hist.library()
+    for s in range(5):
+        assert lib.hist_status_str(s)
+    assert lib.hist_status_str(99) == b"unknown status"
+
+
+def test_argument_errors_before_any_device_call():
+    lib = hist.library()
+    n = ctypes.c_uint64(0)
+    assert lib.hist_workspace_size(0, 10, None, ctypes.byref(n)) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_workspace_size(10, 10, None, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_workspace_size(10, 2**32, None, ctypes.byref(n)) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_workspace_size(hist.MAX_BINS + 1, 10, None,
+                                   ctypes.byref(n)) == hist.HIST_ERR_UNSUPPORTED
+    for field, bad in [("path", 7), ("groups", -1), ("range_bins", 6), ("agg_rounds", 3),
+                       ("agg_rounds", -2), ("wg_size", 100), ("xcd_map", 5)]:
+        o = hist.PlanOpts()
+        o.agg_rounds = -1
+        setattr(o, field, bad)
+        assert lib.hist_workspace_size(10, 10, ctypes.byref(o),
+                                       ctypes.byref(n)) == hist.HIST_ERR_INVALID_ARG, field
+    p = ctypes.c_void_p()
+    assert lib.hist_plan_create(None, 10, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan_create(ctypes.byref(p), 0, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan_create(ctypes.byref(p), 10, 10, None, 3, 0) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_run(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan_info(None, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan_timing_enable(None, 4) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_bench_global_atomic(None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_bench_copy(None, None, 16, None) == hist.HIST_ERR_INVALID_ARG
+    lib.hist_plan_destroy(None)
+
+
+def test_no_device_is_unsupported_not_a_crash():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = hist.library()
+    n = ctypes.c_uint64(0)
+    assert lib.hist_workspace_size(65536, 1 << 20, None,
+                                   ctypes.byref(n)) == hist.HIST_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(hist.LibraryMissing):
+        hist.load(str(tmp_path / "missing.so"))
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "partitioned_chip_accumulation_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*.*"), recursive=True):
+        if path.endswith((".py", ".hip", ".hpp", ".c", ".h")):
+            text = open(path).read()
+            assert "import oracle" not in text and "from oracle" not in text, path
+            assert "oracle_hist" not in text, path

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path against the CPU oracle, bit for bit.
+
+Histogram counts are integers and every schedule reaches the same counts
+(page "Distributed Shared Memory", section "The cluster histogram": each
+element adds exactly one to its bin, slices are summed), so the bar is exact
+equality for every bin, with no tolerance. All calls go through the C ABI via
+the binding; the oracle runs on the host over the same bytes.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from partitioned_chip_accumulation_amd import hist, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(DEV)
+    yield
+
+
+def check(x: np.ndarray, num_bins: int, label: str, offset: int = 0, **opts):
+    """Run one plan over x (placed `offset` elements into a device buffer, to
+    exercise misaligned starts) and compare with the oracle."""
+    ref, dropped = oracle.hist(x, num_bins)
+    say(f"case {label}: n={x.size} bins={num_bins} offset={offset} opts={opts}")
+    buf = torch.empty(x.size + offset + 4, dtype=torch.int32, device=DEV)
+    buf.fill_(-1)
+    xt = buf[offset:offset + x.size]
+    xt.copy_(torch.from_numpy(x))
+    plan = hist.Plan(num_bins, max(1, x.size), device=DEV, **opts)
+    got = plan.run(xt).cpu().numpy()
+    torch.cuda.synchronize(DEV)
+    if not np.array_equal(got, ref):
+        bad = np.flatnonzero(got != ref)
+        raise AssertionError(f"{label} ({plan.describe()}): {bad.size} bins differ, first "
+                             f"{bad[:5].tolist()} got {got[bad[:5]].tolist()} "
+                             f"want {ref[bad[:5]].tolist()}")
+    assert int(got.astype(np.int64).sum()) + dropped == x.size
+    plan.close()
+
+
+def rnd(seed, n, lo, hi):
+    return np.random.default_rng(seed).integers(lo, hi, size=n, dtype=np.int64).astype(np.int32)
+
+
+# --- small and ragged ------------------------------------------------------
+
+PATH_CASES = [
+    ("full", {}),
+    ("full-agg2", {"agg_rounds": 2}),
+    ("range", {"path": "range", "range_bins": 2048}),
+    ("range-agg4", {"path": "range", "range_bins": 1000, "agg_rounds": 4}),
+    ("scatter", {"path": "scatter"}),
+    ("scatter-agg1", {"path": "scatter", "agg_rounds": 1}),
+]
+
+
+@pytest.mark.parametrize("label,opts", PATH_CASES, ids=[c[0] for c in PATH_CASES])
+def test_small_uniform_every_path(label, opts):
+    x = inputs.generate(1, n=1_000_003)  # several tiles and chunks, ragged tail
+    check(x, 8192, label, **opts)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("path", ["auto", "range", "scatter"])
+def test_small_workloads(cfg, path):
+    w = inputs.WORKLOADS[cfg]
+    x = inputs.generate(cfg, n=(1 << 20) + 12345)
+    opts = {"path": path}
+    if path == "range" and w.num_bins <= 40960:
+        opts["range_bins"] = 4096
+    check(x, w.num_bins, f"wl{cfg}-{path}", **opts)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 4, 5, 7, 63, 64, 65, 1023, 16383, 16384, 16385,
+                               16384 * 3 + 5, 262_147])
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_lengths_and_alignment(n, offset):
+    x = rnd(n + offset, n, -2, 70_000)
+    for opts in ({}, {"path": "range"}, {"path": "scatter"}):
+        check(x, 65536, f"len{n}", offset=offset, **opts)
+
+
+@pytest.mark.parametrize("num_bins", [1, 2, 3, 5, 255, 4095, 8191, 8193, 32767, 32768, 32769,
+                                      40959, 40960, 40961, 65535, 65537, 100_003, 262_145])
+def test_bin_counts(num_bins):
+    x = rnd(num_bins, 300_007, -3, num_bins + 5)
+    paths = ["auto", "scatter"]
+    if num_bins <= 40960:
+        paths.append("full")
+    if num_bins > 8:
+        paths.append("range")
+    for p in paths:
+        check(x, num_bins, f"bins{num_bins}-{p}", path=p)
+
+
+def test_out_of_range_and_negative_values():
+    x = rnd(5, 500_000, -(2**31), 2**31 - 1)
+    x[::2] = rnd(6, x[::2].size, 0, 70_000)
+    for p in ["auto", "range", "scatter"]:
+        check(x, 70_000, f"oor-{p}", path=p)
+
+
+@pytest.mark.parametrize("b", [0, 32767, 32768, 65535])
+def test_all_one_bin(b):
+    x = np.full(1 << 22, b, np.int32)
+    for p, agg in [("range", 0), ("range", 2), ("scatter", 0), ("scatter", 4)]:
+        check(x, 65536, f"one{b}-{p}-agg{agg}", path=p, agg_rounds=agg)
+
+
+def test_groups_and_wg_sizes():
+    x = inputs.generate(2, n=(1 << 21) + 7)
+    for opts in [{"groups": 1}, {"groups": 3}, {"groups": 8}, {"groups": 256},
+                 {"wg_size": 256}, {"wg_size": 512}, {"xcd_map": 2},
+                 {"path": "scatter", "groups": 1}, {"path": "scatter", "groups": 7},
+                 {"path": "scatter", "groups": 1000}]:
+        check(x, 65536, f"opts{opts}", **opts)
+
+
+def test_misaligned_output_buffer():
+    x = inputs.generate(2, n=1 << 20)
+    ref, _ = oracle.hist(x, 65536)
+    plan = hist.Plan(65536, x.size, device=DEV)
+    out = torch.empty(65536 + 1, dtype=torch.int32, device=DEV)
+    got = plan.run(torch.from_numpy(x).to(DEV), out[1:]).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_argument_errors_on_device():
+    plan = hist.Plan(1000, 100, device=DEV)
+    # every buffer is large enough for any call below, so a missed check
+    # could not write out of bounds
+    x = torch.zeros(2000, dtype=torch.int32, device=DEV)[:101]
+    with pytest.raises(hist.HistError) as e:
+        plan.run(x)  # n > max_n
+    assert e.value.status == hist.HIST_ERR_INVALID_ARG
+    lib = hist.library()
+    out = torch.empty(1000, dtype=torch.int32, device=DEV)
+    s = torch.cuda.current_stream(DEV).cuda_stream
+    assert lib.hist_run(plan._plan, out.data_ptr(), x.data_ptr(), 10, 999, s) == \
+        hist.HIST_ERR_INVALID_ARG  # num_bins differs from the plan
+    assert lib.hist_run(plan._plan, out.data_ptr(), x.data_ptr() + 2, 10, 1000, s) == \
+        hist.HIST_ERR_INVALID_ARG  # misaligned input
+    assert lib.hist_run(plan._plan, x.data_ptr(), x.data_ptr(), 10, 1000, s) == \
+        hist.HIST_ERR_INVALID_ARG  # output overlaps input
+    small = hist.PlanOpts()
+    small.agg_rounds = -1
+    p = __import__("ctypes").c_void_p()
+    big = hist.workspace_size(65536, 1 << 24)
+    assert big > 0
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    assert lib.hist_plan_create(__import__("ctypes").byref(p), 65536, 1 << 24, None,
+                                ws.data_ptr(), 16) == hist.HIST_ERR_WORKSPACE
+
+
+def test_repeat_is_idempotent():
+    x = torch.from_numpy(inputs.generate(3, n=1 << 22)).to(DEV)
+    plan = hist.Plan(262_144, x.numel(), device=DEV)
+    first = plan.run(x).clone()
+    for _ in range(20):
+        assert torch.equal(plan.run(x), first)
+
+
+def test_timing_records_phases():
+    x = torch.from_numpy(inputs.generate(2, n=1 << 22)).to(DEV)
+    plan = hist.Plan(65536, x.numel(), device=DEV)
+    plan.timing_enable(8)
+    for _ in range(5):
+        plan.run(x)
+    ph = plan.timing_read()
+    assert ph["sweep"][1] == 5 and ph["sweep"][0] > 0
+    plan = hist.Plan(1 << 20, x.numel(), device=DEV, path="scatter")
+    plan.timing_enable(8)
+    plan.run(x)
+    assert set(plan.timing_read()) == {"partition", "range_scan", "owner_hist", "slot_merge"}
+
+
+def test_global_atomic_comparator():
+    x = inputs.generate(4, n=1 << 21)
+    ref, _ = oracle.hist(x, 1 << 20)
+    got = hist.global_atomic(torch.from_numpy(x).to(DEV), 1 << 20).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+# --- the published sizes ---------------------------------------------------
+
+_full_cache = {}
+
+
+def full(cfg):
+    if cfg not in _full_cache:
+        _full_cache.clear()
+        w = inputs.WORKLOADS[cfg]
+        say(f"generating workload {cfg} ({w.n} elements)")
+        x = inputs.generate(cfg)
+        ref, dropped = oracle.hist(x, w.num_bins)
+        _full_cache[cfg] = (x, ref, dropped, torch.from_numpy(x).to(DEV))
+    return _full_cache[cfg]
+
+
+FULL_CASES = [
+    (1, {}), (1, {"agg_rounds": 2}), (1, {"path": "scatter"}),
+    (2, {}), (2, {"agg_rounds": 1}), (2, {"path": "scatter"}),
+    (3, {}), (3, {"agg_rounds": 4}), (3, {"path": "scatter", "agg_rounds": 2}),
+    (4, {}), (4, {"agg_rounds": 4}), (4, {"path": "range"}),
+    (5, {}), (5, {"agg_rounds": 2}), (5, {"path": "range"}),
+]
+
+
+@pytest.mark.parametrize("cfg,opts", FULL_CASES,
+                         ids=[f"wl{c}-{'-'.join(f'{k}{v}' for k, v in o.items()) or 'auto'}"
+                              for c, o in FULL_CASES])
+def test_full_size_workloads(cfg, opts):
+    x, ref, dropped, xt = full(cfg)
+    w = inputs.WORKLOADS[cfg]
+    plan = hist.Plan(w.num_bins, w.n, device=DEV, **opts)
+    say(f"full workload {cfg}: {plan.describe()}")
+    got = plan.run(xt).cpu().numpy()
+    torch.cuda.synchronize(DEV)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} bins differ, first {bad[:5].tolist()}"
+    assert int(got.astype(np.int64).sum()) + dropped == w.n
+    plan.close()
