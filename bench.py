@@ -8,10 +8,12 @@ so that consecutive steps cannot serve a 256 MiB input from the 256 MB
 Infinity Cache that the previous step filled.
 
 Prints one JSON line (rank 0). Throughput `value` is Gelem/s over the K timed
-steps (wall clock between two device synchronisations). `roofline` is for the
-dominant kernel, timed live with HIP events around its launches inside the
-timed region. `cpu_baseline` is the CPU oracle (a sequential loop, one
-core) timed on a bounded sample of the same input.
+steps (wall clock between two device synchronisations, no instrumentation in
+between). `roofline` is for the dominant kernel, timed live with HIP events
+around each of its launches over a second run of K steps (events between
+kernels cost ~1-2 us per step of their own, so they stay out of `value`).
+`cpu_baseline` is the CPU oracle (a sequential loop, one core) timed on a
+bounded sample of the same input.
 """
 from __future__ import annotations
 
@@ -38,6 +40,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline)")
     ap.add_argument("--n", type=int, default=None, help="override the workload length")
+    ap.add_argument("--uniform-bins", type=int, default=0,
+                    help="instead of a workload, uniform int32 over this many bins (sweeps)")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run one plain copy of this many MiB (for counter scaling)")
     ap.add_argument("--path", default="auto", choices=["auto", "full", "range", "scatter"])
     ap.add_argument("--groups", type=int, default=0)
     ap.add_argument("--range-bins", type=int, default=0)
@@ -96,9 +102,13 @@ def main():
     w = inputs.WORKLOADS[args.config]
     n = w.n if args.n is None else args.n
     B = w.num_bins
-
     t_gen = time.perf_counter()
-    x = inputs.generate(args.config, n=n)
+    if args.uniform_bins:
+        B = args.uniform_bins
+        w = inputs.Workload(0, f"uniform-{B}", n, B, 1, f"int32 uniform in [0, {B}), seed 1")
+        x = inputs.uniform(1, n, B)
+    else:
+        x = inputs.generate(args.config, n=n)
     t_gen = time.perf_counter() - t_gen
     xs = [torch.from_numpy(x).to(dev)]
     for _ in range(max(0, args.copies - 1)):
@@ -112,19 +122,35 @@ def main():
     print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,
           flush=True)
 
-    plan.timing_enable(args.steps + args.warmup)
-    for k in range(args.warmup):
-        plan.run(xs[k % len(xs)], out)
-    torch.cuda.synchronize(dev)
-    plan.timing_read()  # discard warm-up records
+    if args.copy_calibration:
+        a = torch.empty(args.copy_calibration << 18, dtype=torch.int32, device=dev)
+        bcopy = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize(dev)
+        hist.copy(bcopy, a)
+        torch.cuda.synchronize(dev)
+        del a, bcopy
 
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        plan.run(xs[k % len(xs)], out)
-    torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
-    phases = plan.timing_read()
+    def timed(events: bool):
+        plan.timing_enable(args.steps + args.warmup if events else 0)
+        for k in range(args.warmup):
+            plan.run(xs[k % len(xs)], out)
+        torch.cuda.synchronize(dev)
+        if events:
+            plan.timing_read()  # discard warm-up records
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            plan.run(xs[k % len(xs)], out)
+        torch.cuda.synchronize(dev)
+        dt = time.perf_counter() - t0
+        return dt, (plan.timing_read() if events else None)
+
+    # The headline region runs without per-kernel events (they add host and
+    # device work between kernels); a second region of the same length records
+    # HIP events around every kernel for the roofline figures.
+    elapsed, _ = timed(False)
+    elapsed_events, phases = timed(True)
 
     parity = None
     if not args.no_parity:
@@ -153,7 +179,8 @@ def main():
     traffic_key = f"{dom_name}:{w.name}:n={n}:{plan.describe()}"
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(traffic_key), "algorithmic_bytes": dom_bytes,
+                "traffic": traffic_for(traffic_key), "traffic_key": traffic_key,
+                "algorithmic_bytes": dom_bytes,
                 "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches": dom_launches}
 
     cpu = None
@@ -166,7 +193,7 @@ def main():
             oracle.hist(x, B)
             spent += time.perf_counter() - t1
             reps += 1
-            if time.perf_counter() - t_start >= args.cpu_seconds or reps >= 100:
+            if time.perf_counter() - t_start >= args.cpu_seconds or reps >= 10000:
                 break
         cpu = {"value": round(n * reps / spent / 1e9, 4), "unit": "Gelem/s", "cores": 1,
                "kind": "oracle",
@@ -215,6 +242,7 @@ def main():
                    "n": n, "num_bins": B, "plan": plan.describe(),
                    "input_copies": len(xs)},
         "phases_ms_per_step": {k: round(v[0] / v[1], 5) for k, v in phases.items()},
+        "ms_per_step_with_events": round(elapsed_events / args.steps * 1e3, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

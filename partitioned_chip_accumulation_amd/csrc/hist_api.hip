@@ -429,10 +429,11 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         const uint32_t xcds = (p->xcd_map == 1 && p->ranges > 1 && G % p->dev.xcd == 0) ? p->dev.xcd : 1;
         uint32_t *dst = G > 1 ? reinterpret_cast<uint32_t *>(p->ws + p->off_partials) : counts;
         const uint64_t row = G > 1 ? p->row : 0;
-        const bool nt = p->ranges == 1;
+        // Non-temporal loads also for R > 1: the chunk's other owners still find
+        // the lines in the XCD's L2 (measured: 50% L2 hits, one HBM fetch per
+        // element) and the stream evicts less useful data.
         tm.begin(PH_SWEEP);
-        e = nt ? launch_sweep_nt<true>(p, in, G, xcds, dst, row, stream)
-               : launch_sweep_nt<false>(p, in, G, xcds, dst, row, stream);
+        e = launch_sweep_nt<true>(p, in, G, xcds, dst, row, stream);
         tm.end(PH_SWEEP);
         if (e != hipSuccess) return HIST_ERR_HIP;
         if (G > 1) {

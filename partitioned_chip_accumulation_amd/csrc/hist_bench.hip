@@ -5,7 +5,7 @@
 
 #include <algorithm>
 
-namespace {
+namespace pca_bench {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -64,7 +64,9 @@ int grid_for(uint64_t work, int per_block)
     return (int)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cu * 16));
 }
 
-}  // namespace
+}  // namespace pca_bench
+
+using namespace pca_bench;
 
 extern "C" {
 

@@ -150,6 +150,7 @@ class Plan:
         self.num_bins, self.max_n = int(num_bins), int(max_n)
         self._plan = ctypes.c_void_p()
         lib = library()
+        self._run = lib.hist_run
         o = _opts(**opts)
         with torch.cuda.device(self.device):
             n = ctypes.c_uint64(0)
@@ -174,10 +175,14 @@ class Plan:
                 out.element_size() != 4 or not out.is_contiguous():
             raise ValueError("out must be a contiguous 4-byte tensor of num_bins on the device")
         n = input.numel()
-        with torch.cuda.device(self.device):
-            _check(library().hist_run(self._plan, out.data_ptr(),
-                                      input.data_ptr() if n else None, n, self.num_bins,
-                                      _stream_handle(self.device)), "hist_run")
+        if torch.cuda.current_device() == self.device.index:
+            st = self._run(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
+                           self.num_bins, torch.cuda.current_stream().cuda_stream)
+        else:
+            with torch.cuda.device(self.device):
+                st = self._run(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
+                               self.num_bins, torch.cuda.current_stream().cuda_stream)
+        _check(st, "hist_run")
         return out.view(torch.uint32) if out.dtype == torch.int32 else out
 
     __call__ = run

@@ -1,0 +1,149 @@
+"""Summaries of rocprofv3 output for the histogram kernels.
+
+    python -m partitioned_chip_accumulation_amd.profiling trace DIR --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling counters DIR [DIR...] --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling traffic --fetch DIR --write DIR \
+        --kernel k_sweep --calib-kernel k_copy --calib-bytes N --key KEY --sources A B --out FILE.json
+
+DIR is a rocprofv3 output directory written with ``--output-format csv``.
+``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE of a kernel by
+what the same counters read for a plain copy kernel of known size in the same
+run (both counters are in KiB per dispatch; on gfx950 FETCH_SIZE reads half
+of a copy's source bytes, so the scaling is needed), and records the hash of
+the kernel sources so that a later change of the kernels invalidates it.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+
+def _csvs(d: str, suffix: str) -> list[str]:
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def short(name: str) -> str:
+    base = name.split("(")[0].strip()
+    return base.replace("void ", "")
+
+
+def kernel_durations(d: str) -> dict[str, list[float]]:
+    by = collections.defaultdict(list)
+    for f in _csvs(d, "kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            by[short(r["Kernel_Name"])].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return by
+
+
+def trace_table(d: str) -> str:
+    by = kernel_durations(d)
+    lines = ["| kernel | calls | avg us | median us | min us | total ms |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {statistics.mean(v):.2f} | "
+                     f"{statistics.median(v):.2f} | {min(v):.2f} | {sum(v) / 1e3:.3f} |")
+    return "\n".join(lines)
+
+
+def counters_per_dispatch(d: str) -> dict[str, dict[str, float]]:
+    """Median over dispatches of each counter (summed over its dimensions)."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for f in _csvs(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            acc[short(r["Kernel_Name"])][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: {c: statistics.median(v.values()) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def counters_table(dirs: list[str]) -> str:
+    merged = collections.defaultdict(dict)
+    for d in dirs:
+        for k, cs in counters_per_dispatch(d).items():
+            merged[k].update(cs)
+    lines = ["| kernel | counter | median per dispatch |", "|---|---|---:|"]
+    for k in sorted(merged):
+        for c in sorted(merged[k]):
+            lines.append(f"| `{k}` | {c} | {merged[k][c]:.6g} |")
+    return "\n".join(lines)
+
+
+def _match(cs: dict, pat: str) -> dict:
+    hits = {k: v for k, v in cs.items() if pat in k}
+    if not hits:
+        raise SystemExit(f"no kernel matching {pat!r} in {sorted(cs)}")
+    return next(iter(hits.values()))
+
+
+def sources_sha(paths: list[str]) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--title", default="Kernel trace")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--cmd", required=True, action="append")
+    c.add_argument("--out", required=True)
+    c.add_argument("--title", default="Hardware counters")
+    tr = sub.add_parser("traffic")
+    tr.add_argument("--fetch", required=True)
+    tr.add_argument("--write", required=True)
+    tr.add_argument("--kernel", required=True)
+    tr.add_argument("--calib-kernel", required=True)
+    tr.add_argument("--calib-bytes", type=int, required=True)
+    tr.add_argument("--key", required=True)
+    tr.add_argument("--sources", nargs="+", required=True)
+    tr.add_argument("--out", required=True)
+    a = ap.parse_args()
+
+    if a.cmd_ == "trace":
+        text = f"# {a.title}\n\nCommand (rocprofv3 kernel trace):\n\n```\n{a.cmd}\n```\n\n" \
+               f"{trace_table(a.dir)}\n"
+        open(a.out, "w").write(text)
+    elif a.cmd_ == "counters":
+        cmds = "\n".join(a.cmd)
+        text = f"# {a.title}\n\nCommands (one rocprofv3 --pmc pass each):\n\n```\n{cmds}\n```\n\n" \
+               f"{counters_table(a.dirs)}\n"
+        open(a.out, "w").write(text)
+    else:
+        fetch = counters_per_dispatch(a.fetch)
+        write = counters_per_dispatch(a.write)
+        f_k = _match(fetch, a.kernel)["FETCH_SIZE"]
+        w_k = _match(write, a.kernel)["WRITE_SIZE"]
+        f_c = _match(fetch, a.calib_kernel)["FETCH_SIZE"]
+        w_c = _match(write, a.calib_kernel)["WRITE_SIZE"]
+        f_scale = a.calib_bytes / (f_c * 1024.0)
+        w_scale = a.calib_bytes / (w_c * 1024.0)
+        entry = {"fetch_bytes": round(f_k * 1024 * f_scale), "write_bytes": round(w_k * 1024 * w_scale),
+                 "fetch_kib_raw": f_k, "write_kib_raw": w_k, "fetch_scale": f_scale,
+                 "write_scale": w_scale, "calib_kernel": a.calib_kernel,
+                 "calib_bytes": a.calib_bytes, "kernel_source_sha": sources_sha(a.sources)}
+        entry["bytes_per_launch"] = entry["fetch_bytes"] + entry["write_bytes"]
+        data = {}
+        if os.path.exists(a.out):
+            data = json.load(open(a.out))
+        data[a.key] = entry
+        with open(a.out, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+            f.write("\n")
+        print(json.dumps(entry))
+
+
+if __name__ == "__main__":
+    main()
