@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--agg", type=int, default=-1)
     ap.add_argument("--wg", type=int, default=0)
     ap.add_argument("--xcd-map", type=int, default=0)
+    ap.add_argument("--counter-bits", type=int, default=0)
     ap.add_argument("--copies", type=int, default=4, help="input copies used in rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline work (0 = skip)")
@@ -117,7 +118,7 @@ def main():
 
     plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
                      range_bins=args.range_bins, agg_rounds=args.agg, wg_size=args.wg,
-                     xcd_map=args.xcd_map)
+                     xcd_map=args.xcd_map, counter_bits=args.counter_bits)
     info = plan.info()
     print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,
           flush=True)

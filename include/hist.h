@@ -77,13 +77,16 @@ typedef enum {
 typedef struct {
     int32_t path;       /* hist_path_t */
     int32_t groups;     /* FULL/RANGE: input chunks G; SCATTER: owner workgroups W */
-    int32_t range_bins; /* RANGE: bins per owned range (multiple of 4, <= LDS capacity) */
+    int32_t range_bins; /* RANGE: bins per owned range (multiple of 256, <= LDS capacity:
+                           40960 with 32-bit counters, 79616 with 16-bit) */
     int32_t agg_rounds; /* wave duplicate aggregation rounds before each LDS add:
                            -1 auto, 0 off, 1..4 */
     int32_t wg_size;    /* sweep workgroup size: 256, 512 or 1024 (0 = auto) */
     int32_t xcd_map;    /* RANGE: 1 = place a chunk's R owners on one XCD (default),
                            2 = plain order (for measurement) */
-    int32_t reserved[2];
+    int32_t counter_bits; /* FULL/RANGE LDS counters: 32, or 16 (two bins per word, exact
+                             through carry events; twice the bins per workgroup) */
+    int32_t reserved;
 } hist_plan_opts_t;
 
 /* Numeric description of a plan (for logs and benchmarks). */
@@ -99,7 +102,7 @@ typedef struct {
     uint32_t wg_size;
     int32_t agg_rounds;
     uint32_t tile_elems;   /* SCATTER: elements per scatter tile */
-    uint32_t reserved;
+    uint32_t counter_bits; /* FULL/RANGE: 32 or 16 */
     uint64_t max_n;
     uint64_t workspace_bytes;
 } hist_plan_info_t;

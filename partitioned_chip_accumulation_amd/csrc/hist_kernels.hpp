@@ -174,6 +174,190 @@ __global__ void k_fill_zero(uint32_t *__restrict__ dst, uint64_t len)
 }
 
 // ---------------------------------------------------------------------------
+// Partial slices.
+//
+// A workgroup's slice is flushed in blocks of 256 bins, stored bit-planar:
+// plane p (256 bytes) holds byte p of every count of the block, lane l's
+// four counts at bytes 4l..4l+3. A block keeps only as many planes as its
+// largest count needs (1, 2 or 4, chosen by one wave ballot), in a fixed
+// 1 KiB slot. Plane 0 alone is a complete 8-bit block, so the merge can fetch
+// it before it knows the width and go back only for the (rare) wider blocks.
+// A histogram's partial slices hold small counts for most inputs (a
+// 65,536-bin slice of 262,144 uniform elements averages 4 per bin), so this
+// cuts the write-then-read traffic of the merge by up to 4x while staying
+// exact for any count.
+constexpr uint32_t kBlockBins = 256;
+constexpr uint32_t kBlockBytes = 1024;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Partials {
+    uint8_t *data;    // [rows][nblk][4 planes][256 bytes]
+    uint8_t *width;   // [nblk][wstride]: planes - 1 is 0, 1 or 3
+    uint32_t nblk;    // blocks per row = ceil(num_bins / 256)
+    uint32_t wstride; // rows the width table has room for
+};
+
+__device__ __forceinline__ uint32_t plane_of(u32x4 c, uint32_t p)
+{
+    const uint32_t sh = 8u * p;
+    return ((c.x >> sh) & 0xFFu) | (((c.y >> sh) & 0xFFu) << 8) | (((c.z >> sh) & 0xFFu) << 16) |
+           (((c.w >> sh) & 0xFFu) << 24);
+}
+
+// Store one block (lane l holds bins 4l..4l+3). Whole wave, convergent.
+__device__ __forceinline__ void write_block(const Partials &P, uint64_t row, uint32_t blk, u32x4 c)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t mx = max(max(c.x, c.y), max(c.z, c.w));
+    const uint32_t planes = __ballot(mx > 0xFFFFu) ? 4u : (__ballot(mx > 0xFFu) ? 2u : 1u);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+    for (uint32_t p = 0; p < planes; ++p) dst[p * 64 + lane] = plane_of(c, p);
+    if (lane == 0) P.width[(uint64_t)blk * P.wstride + row] = (uint8_t)(planes - 1);
+}
+
+// Add plane p of a block (lane's 4 bytes, as loaded) into acc.
+__device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t p)
+{
+    const uint32_t sh = 8u * p;
+    acc.x += (v & 0xFFu) << sh;
+    acc.y += ((v >> 8) & 0xFFu) << sh;
+    acc.z += ((v >> 16) & 0xFFu) << sh;
+    acc.w += (v >> 24) << sh;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit LDS counters.
+//
+// Two bins share one 32-bit LDS word (bin 2w in the low half, 2w+1 in the
+// high half), which doubles the bins one workgroup can own. Increments are
+// ds_add_rtn_u32 of 1 or 1 << 16 (or k, k << 16 after wave aggregation), and
+// the returned old value exposes the two ways a half can overflow: the low
+// half wrapping (its carry then lands in the high half) and a carry out of
+// the whole word. Each such event is appended to a short LDS list. With A_lo
+// and A_hi the true counts, W the final word, L the low-half wraps and C the
+// carries out of the word:
+//     A_lo = (W & 0xFFFF) + 65536 L,   A_hi = (W >> 16) + 65536 C - L.
+// Each low wrap needs 65536 low increments and each carry out 2^32 of added
+// weight, so a workgroup that counts E elements logs at most 2E / 65536
+// events; the host keeps E <= 2^24, which bounds the list at 512 of its
+// kEventCap entries.
+constexpr uint32_t kEventCap = 1024;
+constexpr uint32_t kEvLoWrap = 0x40000000u;
+constexpr uint32_t kEvCarry = 0x80000000u;
+
+__device__ __forceinline__ void add16(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
+                                      uint32_t s, uint32_t k)
+{
+    const uint32_t w = s >> 1;
+    const bool hi = (s & 1u) != 0;
+    const uint32_t delta = hi ? (k << 16) : k;
+    const uint32_t old = lds_add_rtn(words, w, delta);
+    const bool lo_wrap = !hi && (old & 0xFFFFu) + k > 0xFFFFu;
+    const bool carry = old > 0xFFFFFFFFu - delta;
+    if (lo_wrap || carry) {
+        const uint32_t i = lds_add_rtn(ev_count, 0, 1u);
+        if (i < kEventCap) evlist[i] = w | (lo_wrap ? kEvLoWrap : 0u) | (carry ? kEvCarry : 0u);
+    }
+}
+
+// Unaggregated 16-bit counting of N elements at once: every ds_add_rtn_u32 is
+// issued before any returned value is examined, so the wave waits for LDS
+// once per batch instead of once per element (N <= 15 keeps the batch within
+// the LDS wait counter). An event is possible only when the half being
+// incremented was 0xFFFF, which one bit-field extract tests; the rare
+// events then take one wave-uniform branch.
+template <int N>
+__device__ __forceinline__ void count16_batch(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
+                                              const uint32_t (&s)[N], const bool (&ok)[N])
+{
+    uint32_t old[N], sh[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        sh[e] = (s[e] & 1u) << 4;
+        old[e] = 0u;
+        if (ok[e]) old[e] = lds_add_rtn(words, s[e] >> 1, 1u << sh[e]);
+    }
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        any = any || (ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 16) == 0xFFFFu);
+    if (__ballot(any)) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            if (ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 16) == 0xFFFFu) {
+                // low half full: it wraps, and the whole word carries out if the
+                // high half was full too; high half full: the word carries out.
+                const bool hi = sh[e] != 0u;
+                const uint32_t ev = (hi ? 0u : kEvLoWrap) |
+                                    ((hi || (old[e] >> 16) == 0xFFFFu) ? kEvCarry : 0u);
+                const uint32_t i = lds_add_rtn(ev_count, 0, 1u);
+                if (i < kEventCap) evlist[i] = (s[e] >> 1) | ev;
+            }
+        }
+    }
+}
+
+template <int ROUNDS>
+__device__ __forceinline__ void lds_count16(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
+                                            uint32_t slot, bool valid)
+{
+    if constexpr (ROUNDS == 0) {
+        if (valid) add16(words, evlist, ev_count, slot, 1u);
+    } else {
+        bool pending = valid;
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            const uint64_t act = __ballot(pending);
+            if (act == 0) return;
+            const int leader = __builtin_ctzll(act);
+            const uint32_t lead = __builtin_amdgcn_readlane(slot, leader);
+            const bool mine = pending && slot == lead;
+            const uint64_t m = __ballot(mine);
+            if (mine && lane_id() == (uint32_t)leader)
+                add16(words, evlist, ev_count, lead, (uint32_t)__popcll(m));
+            pending = pending && !mine;
+            if (__popcll(m) == 1) break;
+        }
+        if (pending) add16(words, evlist, ev_count, slot, 1u);
+    }
+}
+
+// Counts of block k of a slice (lane l: bins 4l..4l+3 of the block), from
+// 32-bit or 16-bit LDS counters. Bins at or beyond len read as zero.
+template <int CW>
+__device__ __forceinline__ u32x4 slice_block(const uint32_t *lds, const uint32_t *evlist,
+                                             uint32_t nev, uint32_t k, uint32_t len)
+{
+    const uint32_t lane = lane_id();
+    u32x4 c;
+    if constexpr (CW == 32) {
+        c = reinterpret_cast<const u32x4 *>(lds)[k * 64 + lane];
+    } else {
+        const u32x2 ww = reinterpret_cast<const u32x2 *>(lds)[k * 64 + lane];
+        c = u32x4{ww.x & 0xFFFFu, ww.x >> 16, ww.y & 0xFFFFu, ww.y >> 16};
+        const uint32_t w0 = k * 128 + 2 * lane;
+        for (uint32_t e = 0; e < nev; ++e) {
+            const uint32_t ent = evlist[e];
+            const uint32_t ew = ent & 0x3FFFFFFFu;
+            if (ew == w0) {
+                if (ent & kEvLoWrap) { c.x += 65536u; c.y -= 1u; }
+                if (ent & kEvCarry) c.y += 65536u;
+            } else if (ew == w0 + 1) {
+                if (ent & kEvLoWrap) { c.z += 65536u; c.w -= 1u; }
+                if (ent & kEvCarry) c.w += 65536u;
+            }
+        }
+    }
+    const uint32_t b = k * kBlockBins + lane * 4;
+    if (b + 0 >= len) c.x = 0u;
+    if (b + 1 >= len) c.y = 0u;
+    if (b + 2 >= len) c.z = 0u;
+    if (b + 3 >= len) c.w = 0u;
+    return c;
+}
+
+// ---------------------------------------------------------------------------
 // Sweep: workgroup (g, r) counts chunk g of the input into bin range r.
 //
 // The page's kernel zeroes its slice, synchronises, accumulates, synchronises
@@ -183,21 +367,25 @@ __global__ void k_fill_zero(uint32_t *__restrict__ dst, uint64_t len)
 // workgroup's LDS iff lo <= x < lo + len, at slot x - lo (one unsigned
 // compare, which also rejects negatives and values >= num_bins).
 //
-// With ranges == 1 every workgroup owns all bins (LDS holds num_bins
-// counters). With ranges > 1 the R owners of a chunk all read it; xcds > 1
-// places them on one XCD (workgroups are dispatched to the XCDs round-robin)
-// so that one owner's read brings the lines into the shared L2 for the
-// others. The chunk's slice of range r goes to dst + g * dst_row + lo.
+// With ranges == 1 every workgroup owns all bins. With ranges > 1 the R
+// owners of a chunk all read it; xcds > 1 places them on one XCD
+// (workgroups are dispatched to the XCDs round-robin) so that one owner's
+// read brings the lines into the shared L2 for the others. Counters are
+// 32-bit (CW = 32) or packed 16-bit with carry events (CW = 16).
 //
 // Chunk g is body vectors [g * nvec / groups, (g + 1) * nvec / groups); the
 // head scalars belong to chunk 0 and the tail scalars to the last chunk.
-template <int WG, int UNROLL, int AGG, bool NT>
+// The slice goes to partial row g in 256-bin blocks (range_bins is a multiple
+// of 256), or straight into direct[] (the output) when there is one chunk.
+template <int WG, int UNROLL, int AGG, int CW>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
-                                              uint32_t *__restrict__ dst, uint64_t dst_row)
+                                              Partials out, uint32_t *__restrict__ direct)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
+    uint32_t *ev_count = lds + range_bins / 2;  // CW == 16 only
+    uint32_t *evlist = ev_count + 4;
     const uint32_t tid = threadIdx.x;
     const uint32_t b = blockIdx.x;
     uint32_t g, r;
@@ -212,82 +400,135 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     const uint32_t lo = r * range_bins;
     const uint32_t len = min(range_bins, num_bins - lo);
 
-    zero_lds<WG>(lds, len);
+    zero_lds<WG>(lds, CW == 32 ? len : (len + 1) / 2);
+    if (CW == 16 && tid == 0) *ev_count = 0u;
     __syncthreads();
+
+    auto count1 = [&](uint32_t s, bool ok) {
+        if constexpr (CW == 32) lds_count<AGG>(lds, s, ok);
+        else lds_count16<AGG>(lds, evlist, ev_count, s, ok);
+    };
+    auto count4 = [&](const i32x4 q, bool ok) {
+        uint32_t s;
+        s = (uint32_t)q.x - lo; count1(s, ok && s < len);
+        s = (uint32_t)q.y - lo; count1(s, ok && s < len);
+        s = (uint32_t)q.z - lo; count1(s, ok && s < len);
+        s = (uint32_t)q.w - lo; count1(s, ok && s < len);
+    };
 
     const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
     const uint64_t v0 = (uint64_t)g * in.nvec / groups;
     const uint64_t v1 = (uint64_t)(g + 1) * in.nvec / groups;
-
-    auto count4 = [&](const i32x4 q, bool ok) {
-        uint32_t s;
-        s = (uint32_t)q.x - lo; lds_count<AGG>(lds, s, ok && s < len);
-        s = (uint32_t)q.y - lo; lds_count<AGG>(lds, s, ok && s < len);
-        s = (uint32_t)q.z - lo; lds_count<AGG>(lds, s, ok && s < len);
-        s = (uint32_t)q.w - lo; lds_count<AGG>(lds, s, ok && s < len);
-    };
-
     constexpr uint32_t STEP = WG * UNROLL;
     uint64_t v = v0;
     for (; v + STEP <= v1; v += STEP) {
         i32x4 q[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) q[u] = load_vec<NT>(body + v + u * WG + tid);
+        for (int u = 0; u < UNROLL; ++u) q[u] = load_vec<true>(body + v + u * WG + tid);
+        if constexpr (CW == 16 && AGG == 0) {
+            uint32_t sl[4 * UNROLL];
+            bool ok[4 * UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) count4(q[u], true);
+            for (int u = 0; u < UNROLL; ++u) {
+                sl[4 * u + 0] = (uint32_t)q[u].x - lo;
+                sl[4 * u + 1] = (uint32_t)q[u].y - lo;
+                sl[4 * u + 2] = (uint32_t)q[u].z - lo;
+                sl[4 * u + 3] = (uint32_t)q[u].w - lo;
+            }
+#pragma unroll
+            for (int e = 0; e < 4 * UNROLL; ++e) ok[e] = sl[e] < len;
+            count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) count4(q[u], true);
+        }
     }
     // Remainder with a wave-uniform trip count.
     for (; v < v1; v += WG) {
         const bool ok = v + tid < v1;
-        const i32x4 q = ok ? load_vec<NT>(body + v + tid) : i32x4{0, 0, 0, 0};
+        const i32x4 q = ok ? load_vec<true>(body + v + tid) : i32x4{0, 0, 0, 0};
         count4(q, ok);
     }
     {
         const bool hok = g == 0 && tid < in.head;
         const uint32_t hs = (hok ? (uint32_t)in.ptr[tid] : 0u) - lo;
-        lds_count<AGG>(lds, hs, hok && hs < len);
+        count1(hs, hok && hs < len);
         const bool tok = g == groups - 1 && tid < in.tail;
         const uint32_t ts = (tok ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid] : 0u) - lo;
-        lds_count<AGG>(lds, ts, tok && ts < len);
+        count1(ts, tok && ts < len);
     }
     __syncthreads();
-    store_slice<WG>(dst + (uint64_t)g * dst_row + lo, lds, len);
+
+    const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : 0u;
+    const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
+    for (uint32_t k = tid >> 6; k < nblk; k += WG / 64) {
+        const u32x4 c = slice_block<CW>(lds, evlist, nev, k, len);
+        if (direct) {
+            const uint32_t b0 = lo + k * kBlockBins + lane_id() * 4;
+            if (b0 + 0 < num_bins) direct[b0 + 0] = c.x;
+            if (b0 + 1 < num_bins) direct[b0 + 1] = c.y;
+            if (b0 + 2 < num_bins) direct[b0 + 2] = c.z;
+            if (b0 + 3 < num_bins) direct[b0 + 3] = c.w;
+        } else {
+            write_block(out, g, lo / kBlockBins + k, c);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Exclusive-owner merge: counts[b] = sum over g < groups of partials[g][b].
-// A workgroup owns 256 consecutive bins; lane l holds bins 4l..4l+3 as one
-// 16-byte load per row, the WAVES waves split the rows, and wave 0 adds the
-// waves' sums and writes each of its bins once. row (the partial row
-// stride) is a multiple of 4.
+// Exclusive-owner merge: counts[b] = sum over rows g < rows of partial[g][b].
+// A workgroup owns one 256-bin block; lane l holds bins 4l..4l+3 and the
+// WAVES waves split the rows. A wave loads the width codes of up to 64 of its
+// rows (contiguous per block) together with plane 0 of BATCH rows, so a row
+// of small counts costs no dependent round trip; planes 1..3 are fetched
+// only for rows whose code asks for them. Wave 0 adds the waves' sums and
+// writes each of its bins once.
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_merge(const uint32_t *__restrict__ partials,
-                                                      uint32_t groups, uint64_t row,
-                                                      uint32_t num_bins,
+__global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows, uint32_t num_bins,
                                                       uint32_t *__restrict__ counts)
 {
+    constexpr uint32_t BATCH = 16;
     __shared__ u32x4 red[WAVES][64];
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-    const uint64_t b0 = (uint64_t)blockIdx.x * 256u + lane * 4u;
+    const uint32_t blk = blockIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    if (b0 < row) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(partials + b0);
-        const uint64_t s4 = row >> 2;
-        uint32_t g = w;
-        for (; g + 3 * WAVES < groups; g += 4 * WAVES) {
-            const u32x4 a = p[(uint64_t)g * s4];
-            const u32x4 bq = p[(uint64_t)(g + WAVES) * s4];
-            const u32x4 c = p[(uint64_t)(g + 2 * WAVES) * s4];
-            const u32x4 d = p[(uint64_t)(g + 3 * WAVES) * s4];
-            acc += (a + bq) + (c + d);
+    const uint8_t *codes = P.width + (uint64_t)blk * P.wstride;
+    for (uint32_t base = w; base < rows; base += WAVES * 64) {
+        const uint32_t my_row = base + lane * WAVES;
+        const uint32_t my_code = my_row < rows ? codes[my_row] : 0u;
+        const uint32_t cnt = min(64u, (rows - base + WAVES - 1) / WAVES);
+        for (uint32_t i = 0; i < cnt; i += BATCH) {
+            uint32_t p0[BATCH];
+#pragma unroll
+            for (uint32_t j = 0; j < BATCH; ++j) {
+                const uint64_t row = (uint64_t)base + (uint64_t)(i + j) * WAVES;
+                const uint32_t *src =
+                    reinterpret_cast<const uint32_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+                p0[j] = i + j < cnt ? src[lane] : 0u;
+            }
+            // planes beyond 0: any row of the batch that needs them
+            const uint64_t wide = __ballot(lane >= i && lane < min(i + BATCH, cnt) && my_code != 0u);
+#pragma unroll
+            for (uint32_t j = 0; j < BATCH; ++j) add_plane(acc, p0[j], 0);
+            if (wide) {
+#pragma unroll
+                for (uint32_t j = 0; j < BATCH; ++j) {
+                    if (!((wide >> (i + j)) & 1ull)) continue;
+                    const uint32_t planes = __builtin_amdgcn_readlane(my_code, (int)(i + j)) + 1u;
+                    const uint64_t row = (uint64_t)base + (uint64_t)(i + j) * WAVES;
+                    const uint32_t *src =
+                        reinterpret_cast<const uint32_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+                    for (uint32_t p = 1; p < planes; ++p) add_plane(acc, src[p * 64 + lane], p);
+                }
+            }
         }
-        for (; g < groups; g += WAVES) acc += p[(uint64_t)g * s4];
     }
     red[w][lane] = acc;
     __syncthreads();
     if (w == 0) {
 #pragma unroll
         for (int k = 1; k < WAVES; ++k) acc += red[k][lane];
+        const uint64_t b0 = (uint64_t)blk * kBlockBins + lane * 4u;
         if (b0 + 0 < num_bins) counts[b0 + 0] = acc.x;
         if (b0 + 1 < num_bins) counts[b0 + 1] = acc.y;
         if (b0 + 2 < num_bins) counts[b0 + 2] = acc.z;

@@ -38,7 +38,7 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("groups", ctypes.c_int32),
                 ("range_bins", ctypes.c_int32), ("agg_rounds", ctypes.c_int32),
                 ("wg_size", ctypes.c_int32), ("xcd_map", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("counter_bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -47,7 +47,7 @@ class PlanInfo(ctypes.Structure):
                 ("num_bins", ctypes.c_uint32), ("range_bins", ctypes.c_uint32),
                 ("ranges", ctypes.c_uint32), ("groups", ctypes.c_uint32),
                 ("wg_size", ctypes.c_uint32), ("agg_rounds", ctypes.c_int32),
-                ("tile_elems", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("tile_elems", ctypes.c_uint32), ("counter_bits", ctypes.c_uint32),
                 ("max_n", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -107,11 +107,12 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _opts(path="auto", groups=0, range_bins=0, agg_rounds=-1, wg_size=0, xcd_map=0) -> PlanOpts:
+def _opts(path="auto", groups=0, range_bins=0, agg_rounds=-1, wg_size=0, xcd_map=0,
+          counter_bits=0) -> PlanOpts:
     o = PlanOpts()
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.groups, o.range_bins, o.agg_rounds = int(groups), int(range_bins), int(agg_rounds)
-    o.wg_size, o.xcd_map = int(wg_size), int(xcd_map)
+    o.wg_size, o.xcd_map, o.counter_bits = int(wg_size), int(xcd_map), int(counter_bits)
     return o
 
 
@@ -136,6 +137,7 @@ class Info:
     wg_size: int
     agg_rounds: int
     tile_elems: int
+    counter_bits: int
     max_n: int
     workspace_bytes: int
 
@@ -192,7 +194,7 @@ class Plan:
         _check(library().hist_plan_info(self._plan, ctypes.byref(i)), "hist_plan_info")
         return Info(PATH_NAMES[i.path], i.device, i.cu_count, i.xcd_count, i.num_bins,
                     i.range_bins, i.ranges, i.groups, i.wg_size, i.agg_rounds, i.tile_elems,
-                    i.max_n, i.workspace_bytes)
+                    i.counter_bits, i.max_n, i.workspace_bytes)
 
     def describe(self) -> str:
         buf = ctypes.create_string_buffer(512)

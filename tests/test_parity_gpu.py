@@ -65,7 +65,10 @@ PATH_CASES = [
     ("full", {}),
     ("full-agg2", {"agg_rounds": 2}),
     ("range", {"path": "range", "range_bins": 2048}),
-    ("range-agg4", {"path": "range", "range_bins": 1000, "agg_rounds": 4}),
+    ("range-agg4", {"path": "range", "range_bins": 1024, "agg_rounds": 4}),
+    ("full-cw16", {"counter_bits": 16}),
+    ("full-cw16-agg2", {"counter_bits": 16, "agg_rounds": 2}),
+    ("range-cw16", {"path": "range", "range_bins": 2048, "counter_bits": 16}),
     ("scatter", {"path": "scatter"}),
     ("scatter-agg1", {"path": "scatter", "agg_rounds": 1}),
 ]
@@ -124,9 +127,26 @@ def test_all_one_bin(b):
         check(x, 65536, f"one{b}-{p}-agg{agg}", path=p, agg_rounds=agg)
 
 
+@pytest.mark.parametrize("agg", [0, 1, 4])
+@pytest.mark.parametrize("path,bins", [("full", 65536), ("range", 200_000)])
+def test_counter16_carry_events(agg, path, bins):
+    # Few chunks and many copies of a few bins: every chunk's 16-bit counters
+    # wrap several times, in the low half (even bins) and the high half (odd
+    # bins) of a word, and both halves of one word together.
+    rng = np.random.default_rng(agg)
+    hot = np.array([4, 5, 7, 65534, 65535, bins - 1], np.int32)
+    x = np.concatenate([np.repeat(hot, [400_003, 300_007, 150_001, 350_000, 199_999, 70_000]),
+                        rnd(9, 500_000, 0, bins)])
+    x = x[rng.permutation(x.size)].astype(np.int32)
+    check(x, bins, f"cw16-{path}-agg{agg}", path=path, counter_bits=16, groups=3,
+          agg_rounds=agg)
+
+
 def test_groups_and_wg_sizes():
     x = inputs.generate(2, n=(1 << 21) + 7)
     for opts in [{"groups": 1}, {"groups": 3}, {"groups": 8}, {"groups": 256},
+                 {"counter_bits": 32, "path": "range"}, {"counter_bits": 16, "groups": 1},
+                 {"counter_bits": 16, "groups": 5, "wg_size": 256},
                  {"wg_size": 256}, {"wg_size": 512}, {"xcd_map": 2},
                  {"path": "scatter", "groups": 1}, {"path": "scatter", "groups": 7},
                  {"path": "scatter", "groups": 1000}]:
