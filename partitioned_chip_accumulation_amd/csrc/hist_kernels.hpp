@@ -176,33 +176,34 @@ __global__ void k_fill_zero(uint32_t *__restrict__ dst, uint64_t len)
 // ---------------------------------------------------------------------------
 // Partial slices.
 //
-// A workgroup's slice is flushed in blocks of 256 bins, stored bit-planar:
-// plane p (256 bytes) holds byte p of every count of the block, lane l's
-// four counts at bytes 4l..4l+3. A block keeps only as many planes as its
-// largest count needs (1, 2 or 4, chosen by one wave ballot), in a fixed
-// 1 KiB slot. Plane 0 alone is a complete 8-bit block, so the merge can fetch
-// it before it knows the width and go back only for the (rare) wider blocks.
-// A histogram's partial slices hold small counts for most inputs (a
-// 65,536-bin slice of 262,144 uniform elements averages 4 per bin), so this
-// cuts the write-then-read traffic of the merge by up to 4x while staying
-// exact for any count.
+// A workgroup's slice is flushed in blocks of 256 bins, stored nibble-planar:
+// plane q (128 bytes) holds bits 4q..4q+3 of every count of the block, lane
+// l's four counts as the 16 bits at bytes 2l, 2l+1. A block keeps only as
+// many planes as its largest count needs (1, 2, 4 or 8 planes for 4, 8, 16
+// or 32 bits, chosen by wave ballots), in a fixed 1 KiB slot. Plane 0 alone
+// is a complete 4-bit block, so the merge can fetch it before it knows the
+// width and go back only for wider blocks. A histogram's partial slices hold
+// small counts for most inputs (a 65,536-bin slice of 262,144 uniform
+// elements averages 4 per bin), so this cuts the write-then-read traffic of
+// the merge by up to 8x while staying exact for any count.
 constexpr uint32_t kBlockBins = 256;
 constexpr uint32_t kBlockBytes = 1024;
+constexpr uint32_t kPlaneBytes = 128;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Partials {
-    uint8_t *data;    // [rows][nblk][4 planes][256 bytes]
-    uint8_t *width;   // [nblk][wstride]: planes - 1 is 0, 1 or 3
+    uint8_t *data;    // [rows][nblk][8 planes][128 bytes]
+    uint8_t *width;   // [nblk][wstride]: number of planes - 1 (0, 1, 3 or 7)
     uint32_t nblk;    // blocks per row = ceil(num_bins / 256)
     uint32_t wstride; // rows the width table has room for
 };
 
-__device__ __forceinline__ uint32_t plane_of(u32x4 c, uint32_t p)
+__device__ __forceinline__ uint32_t nibbles_of(u32x4 c, uint32_t q)
 {
-    const uint32_t sh = 8u * p;
-    return ((c.x >> sh) & 0xFFu) | (((c.y >> sh) & 0xFFu) << 8) | (((c.z >> sh) & 0xFFu) << 16) |
-           (((c.w >> sh) & 0xFFu) << 24);
+    const uint32_t sh = 4u * q;
+    return ((c.x >> sh) & 0xFu) | (((c.y >> sh) & 0xFu) << 4) | (((c.z >> sh) & 0xFu) << 8) |
+           (((c.w >> sh) & 0xFu) << 12);
 }
 
 // Store one block (lane l holds bins 4l..4l+3). Whole wave, convergent.
@@ -210,20 +211,23 @@ __device__ __forceinline__ void write_block(const Partials &P, uint64_t row, uin
 {
     const uint32_t lane = lane_id();
     const uint32_t mx = max(max(c.x, c.y), max(c.z, c.w));
-    const uint32_t planes = __ballot(mx > 0xFFFFu) ? 4u : (__ballot(mx > 0xFFu) ? 2u : 1u);
-    uint32_t *dst = reinterpret_cast<uint32_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
-    for (uint32_t p = 0; p < planes; ++p) dst[p * 64 + lane] = plane_of(c, p);
+    const uint32_t planes = __ballot(mx > 0xFFFFu) ? 8u
+                            : __ballot(mx > 0xFFu) ? 4u
+                            : __ballot(mx > 0xFu)  ? 2u
+                                                   : 1u;
+    uint16_t *dst = reinterpret_cast<uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+    for (uint32_t q = 0; q < planes; ++q) dst[q * 64 + lane] = (uint16_t)nibbles_of(c, q);
     if (lane == 0) P.width[(uint64_t)blk * P.wstride + row] = (uint8_t)(planes - 1);
 }
 
-// Add plane p of a block (lane's 4 bytes, as loaded) into acc.
-__device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t p)
+// Add plane q of a block (lane's 16 bits, as loaded) into acc.
+__device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t q)
 {
-    const uint32_t sh = 8u * p;
-    acc.x += (v & 0xFFu) << sh;
-    acc.y += ((v >> 8) & 0xFFu) << sh;
-    acc.z += ((v >> 16) & 0xFFu) << sh;
-    acc.w += (v >> 24) << sh;
+    const uint32_t sh = 4u * q;
+    acc.x += (v & 0xFu) << sh;
+    acc.y += ((v >> 4) & 0xFu) << sh;
+    acc.z += ((v >> 8) & 0xFu) << sh;
+    acc.w += ((v >> 12) & 0xFu) << sh;
 }
 
 // ---------------------------------------------------------------------------
@@ -400,6 +404,21 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     const uint32_t lo = r * range_bins;
     const uint32_t len = min(range_bins, num_bins - lo);
 
+    const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
+    const uint64_t v0 = (uint64_t)g * in.nvec / groups;
+    const uint64_t v1 = (uint64_t)(g + 1) * in.nvec / groups;
+    constexpr uint32_t STEP = WG * UNROLL;
+    uint64_t v = v0;
+
+    // The first batch of loads is in flight while the LDS slice is cleared,
+    // and every later batch is requested before the previous one is counted,
+    // so each wave keeps 2 * UNROLL vector loads outstanding.
+    i32x4 nx[UNROLL];
+    const bool any_full = v + STEP <= v1;
+    if (any_full) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + u * WG + tid);
+    }
     zero_lds<WG>(lds, CW == 32 ? len : (len + 1) / 2);
     if (CW == 16 && tid == 0) *ev_count = 0u;
     __syncthreads();
@@ -416,15 +435,14 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
         s = (uint32_t)q.w - lo; count1(s, ok && s < len);
     };
 
-    const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
-    const uint64_t v0 = (uint64_t)g * in.nvec / groups;
-    const uint64_t v1 = (uint64_t)(g + 1) * in.nvec / groups;
-    constexpr uint32_t STEP = WG * UNROLL;
-    uint64_t v = v0;
-    for (; v + STEP <= v1; v += STEP) {
+    for (; any_full && v + STEP <= v1; v += STEP) {
         i32x4 q[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) q[u] = load_vec<true>(body + v + u * WG + tid);
+        for (int u = 0; u < UNROLL; ++u) q[u] = nx[u];
+        if (v + 2 * STEP <= v1) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + STEP + u * WG + tid);
+        }
         if constexpr (CW == 16 && AGG == 0) {
             uint32_t sl[4 * UNROLL];
             bool ok[4 * UNROLL];
@@ -480,7 +498,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 // A workgroup owns one 256-bin block; lane l holds bins 4l..4l+3 and the
 // WAVES waves split the rows. A wave loads the width codes of up to 64 of its
 // rows (contiguous per block) together with plane 0 of BATCH rows, so a row
-// of small counts costs no dependent round trip; planes 1..3 are fetched
+// of small counts costs no dependent round trip; planes 1..7 are fetched
 // only for rows whose code asks for them. Wave 0 adds the waves' sums and
 // writes each of its bins once.
 template <int WAVES>
@@ -502,8 +520,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows,
 #pragma unroll
             for (uint32_t j = 0; j < BATCH; ++j) {
                 const uint64_t row = (uint64_t)base + (uint64_t)(i + j) * WAVES;
-                const uint32_t *src =
-                    reinterpret_cast<const uint32_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+                const uint16_t *src =
+                    reinterpret_cast<const uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
                 p0[j] = i + j < cnt ? src[lane] : 0u;
             }
             // planes beyond 0: any row of the batch that needs them
@@ -516,9 +534,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows,
                     if (!((wide >> (i + j)) & 1ull)) continue;
                     const uint32_t planes = __builtin_amdgcn_readlane(my_code, (int)(i + j)) + 1u;
                     const uint64_t row = (uint64_t)base + (uint64_t)(i + j) * WAVES;
-                    const uint32_t *src =
-                        reinterpret_cast<const uint32_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
-                    for (uint32_t p = 1; p < planes; ++p) add_plane(acc, src[p * 64 + lane], p);
+                    const uint16_t *src =
+                        reinterpret_cast<const uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+                    for (uint32_t q = 1; q < planes; ++q) add_plane(acc, src[q * 64 + lane], q);
                 }
             }
         }
