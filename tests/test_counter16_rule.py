@@ -31,10 +31,10 @@ def events_k1(old, hi):
     return (not hi), (hi or (old >> 16) == 0xFFFF)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(4))
 def test_decode_rule(seed):
     rnd = random.Random(seed)
-    for _ in range(300):
+    for _ in range(40):
         w, L, C, true = 0, 0, 0, [0, 0]
         if rnd.random() < 0.4:
             lo0, hi0 = rnd.choice([(65535, 65535), (65534, 65535), (65535, 0), (0, 65535)])
