@@ -36,8 +36,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline)")
     ap.add_argument("--n", type=int, default=None, help="override the workload length")
     ap.add_argument("--uniform-bins", type=int, default=0,
@@ -57,7 +57,72 @@ def parse():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--comparators", action="store_true",
                     help="also time the global-atomic fallback and the stream-read ceiling")
+    ap.add_argument("--path-sweep", action="store_true",
+                    help="time every applicable path over bin counts 2^10..2^22 on uniform "
+                         "input of --n (default 2^26) elements; one JSON line per cell")
     return ap.parse_args()
+
+
+def path_sweep(args):
+    """Every schedule the library offers, on uniform input, across bin counts.
+
+    The cells are the evidence behind the plan's automatic choice: for each
+    bin count the fastest bit-exact schedule wins. Timing is the same as the
+    headline's (wall clock over back-to-back runs on rotated input copies).
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    from partitioned_chip_accumulation_amd import hist, inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    n = args.n or (1 << 26)
+    steps = min(args.steps, 100)
+    best = {}
+    for lb in range(10, 23):
+        B = 1 << lb
+        x = inputs.uniform(1, n, B)
+        ref, _ = oracle.hist(x, B)
+        xs = [torch.from_numpy(x).to(dev)]
+        for _ in range(3):
+            xs.append(xs[0].clone())
+        out = torch.empty(B, dtype=torch.int32, device=dev)
+        cells = [("auto", {})]
+        if B <= 40960:
+            cells.append(("full32", {"path": "full", "counter_bits": 32}))
+        if B <= 79616:
+            cells.append(("full16", {"path": "full", "counter_bits": 16}))
+        if B >= 2048:
+            cells.append(("range32", {"path": "range", "counter_bits": 32}))
+            cells.append(("range16", {"path": "range", "counter_bits": 16}))
+        cells.append(("scatter", {"path": "scatter"}))
+        for name, opts in cells:
+            try:
+                plan = hist.Plan(B, n, device=dev, **opts)
+            except hist.HistError as e:
+                print(json.dumps({"bins": B, "cell": name, "error": str(e)}), flush=True)
+                continue
+            for k in range(20):
+                plan.run(xs[k % 4], out)
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            for k in range(steps):
+                plan.run(xs[k % 4], out)
+            torch.cuda.synchronize(dev)
+            dt = (time.perf_counter() - t0) / steps
+            ok = bool(np.array_equal(out.view(torch.uint32).cpu().numpy(), ref))
+            rec = {"bins": B, "n": n, "cell": name, "us_per_run": round(dt * 1e6, 2),
+                   "gelem_s": round(n / dt / 1e9, 1), "parity": ok, "plan": plan.describe()}
+            print(json.dumps(rec), flush=True)
+            if name != "auto" and ok and (B not in best or dt < best[B][1]):
+                best[B] = (name, dt)
+            plan.close()
+        del xs
+    print("# fastest bit-exact schedule per bin count: " +
+          ", ".join(f"2^{B.bit_length() - 1}:{v[0]}" for B, v in sorted(best.items())),
+          file=sys.stderr, flush=True)
 
 
 def kernel_source_sha() -> str:
@@ -92,6 +157,10 @@ def main():
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.path_sweep:
+        path_sweep(args)
+        return
+
     import numpy as np
     import torch
 
@@ -117,7 +186,7 @@ def main():
     out = torch.empty(B, dtype=torch.int32, device=dev)
 
     plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
-                     range_bins=args.range_bins, agg_rounds=args.agg, wg_size=args.wg,
+                     range_bins=args.range_bins, aggregation=args.agg, wg_size=args.wg,
                      xcd_map=args.xcd_map, counter_bits=args.counter_bits)
     info = plan.info()
     print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,

@@ -73,20 +73,24 @@ typedef enum {
 } hist_path_t;
 
 /* Plan options. Zero-initialise and set only what you want to force;
- * 0 (or -1 for agg_rounds) means "choose automatically". */
+ * 0 (or -1 for aggregation) means "choose automatically". */
 typedef struct {
     int32_t path;       /* hist_path_t */
     int32_t groups;     /* FULL/RANGE: input chunks G; SCATTER: owner workgroups W */
     int32_t range_bins; /* RANGE: bins per owned range (multiple of 256, <= LDS capacity:
                            40960 with 32-bit counters, 79616 with 16-bit) */
-    int32_t agg_rounds; /* wave duplicate aggregation rounds before each LDS add:
-                           -1 auto, 0 off, 1..4 */
+    int32_t aggregation; /* wave-level duplicate aggregation ahead of the LDS adds, for
+                            skewed inputs: -1 auto, 0 off, 1 hot slot (lanes holding the
+                            wave's current hot value count in registers), 2 or 4 leader-peel
+                            rounds (readfirstlane + ballot, one add per duplicate group) */
     int32_t wg_size;    /* sweep workgroup size: 256, 512 or 1024 (0 = auto) */
     int32_t xcd_map;    /* RANGE: 1 = place a chunk's R owners on one XCD (default),
                            2 = plain order (for measurement) */
     int32_t counter_bits; /* FULL/RANGE LDS counters: 32, or 16 (two bins per word, exact
                              through carry events; twice the bins per workgroup) */
-    int32_t reserved;
+    int32_t lds_copies;   /* FULL/RANGE with 32-bit counters: interleaved LDS copies of the
+                             slice (1, 2, 4, 8, 16); a lane adds to copy lane mod copies,
+                             which spreads same-bin lanes of a wave over words and banks */
 } hist_plan_opts_t;
 
 /* Numeric description of a plan (for logs and benchmarks). */
@@ -100,7 +104,7 @@ typedef struct {
     uint32_t ranges;       /* R = ceil(num_bins / S) */
     uint32_t groups;       /* FULL/RANGE: G chunks; SCATTER: W owner workgroups */
     uint32_t wg_size;
-    int32_t agg_rounds;
+    int32_t aggregation;
     uint32_t tile_elems;   /* SCATTER: elements per scatter tile */
     uint32_t counter_bits; /* FULL/RANGE: 32 or 16 */
     uint64_t max_n;

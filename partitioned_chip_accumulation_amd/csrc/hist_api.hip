@@ -30,7 +30,10 @@ constexpr uint32_t kScatterWG = 1024;
 constexpr uint32_t kScatterVPT = 4;          // vectors per thread in a scatter tile
 constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elements
 constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slots per tile
-constexpr uint32_t kRangeMaxR = 8;           // RANGE up to this many ranges (AUTO)
+// AUTO uses RANGE up to this many 16-bit ranges and SCATTER beyond: on 2^26
+// uniform elements RANGE wins at 2^17 and 2^18 bins (71.9, 123.0 us vs 146.7,
+// 150.8 us) and SCATTER from 2^19 on (165.0 vs 221.3 us).
+constexpr uint32_t kRangeMaxR = 4;
 constexpr uint32_t kMinElemsPerGroup = 32768;
 constexpr int kMaxWavesPerCU = 32;
 
@@ -86,15 +89,16 @@ struct hist_plan {
     // FULL / RANGE
     uint32_t range_bins = 0, ranges = 0, groups = 0;
     uint32_t cw = 32;    // LDS counter bits
+    uint32_t kshift = 0; // 2^kshift interleaved LDS copies (32-bit counters)
     uint32_t nblk = 0;   // 256-bin blocks per partial row
     uint64_t off_width = 0;
     // SCATTER
-    uint32_t tiles = 0, owners = 0;
+    uint32_t tiles = 0, owners = 0, qlog = 0;
     // workspace
     char *ws = nullptr;
     uint64_t ws_bytes = 0, need = 0;
     uint64_t off_partials = 0, off_stage = 0, off_tcnt = 0, off_tbase = 0, off_tpre = 0,
-             off_totals = 0;
+             off_totals = 0, off_segtot = 0;
     // timing
     uint32_t tcap = 0, truns = 0;
     std::vector<hipEvent_t> ev;  // [tcap][HIST_MAX_PHASES][2]
@@ -112,10 +116,12 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
         return HIST_ERR_INVALID_ARG;
     if (o->counter_bits != 0 && o->counter_bits != 16 && o->counter_bits != 32)
         return HIST_ERR_INVALID_ARG;
-    if (o->agg_rounds < -1 || o->agg_rounds > 4 || o->agg_rounds == 3) return HIST_ERR_INVALID_ARG;
+    if (o->aggregation < -1 || o->aggregation > 4 || o->aggregation == 3) return HIST_ERR_INVALID_ARG;
     if (o->wg_size != 0 && o->wg_size != 256 && o->wg_size != 512 && o->wg_size != 1024)
         return HIST_ERR_INVALID_ARG;
     if (o->xcd_map < 0 || o->xcd_map > 2) return HIST_ERR_INVALID_ARG;
+    if (o->lds_copies < 0 || o->lds_copies > 16 || (o->lds_copies & (o->lds_copies - 1)) != 0)
+        return HIST_ERR_INVALID_ARG;
     return HIST_OK;
 }
 
@@ -123,7 +129,7 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
 hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *o)
 {
     hist_plan_opts_t opts{};
-    opts.agg_rounds = -1;
+    opts.aggregation = -1;
     if (o) opts = *o;
     const DeviceInfo &d = p->dev;
     const uint32_t lds_bins = std::min<uint32_t>(kMaxLdsBins, d.lds / 4) & ~3u;
@@ -137,17 +143,19 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
     int path = opts.path;
     if (path == HIST_PATH_AUTO) {
         if (num_bins <= lds_bins16) path = HIST_PATH_FULL;
-        else if (num_bins <= kRangeMaxR * lds_bins16) path = HIST_PATH_RANGE;
+        else if (num_bins <= kRangeMaxR * lds_bins16) path = HIST_PATH_RANGE;  // see kRangeMaxR
         else path = HIST_PATH_SCATTER;
     }
     p->path = path;
-    p->agg = opts.agg_rounds < 0 ? 0 : opts.agg_rounds;
+    p->agg = opts.aggregation < 0 ? 0 : opts.aggregation;
 
     if (path == HIST_PATH_FULL || path == HIST_PATH_RANGE) {
         // Counter width: 32-bit while a workgroup's slice fits, else 16-bit.
         uint32_t cw = (uint32_t)opts.counter_bits;
         if (cw == 0) {
-            if (path == HIST_PATH_FULL) cw = num_bins <= cap32 ? 32 : 16;
+            // measured on 2^26 uniform elements: 32-bit wins up to 2^14 bins
+            // (59.4 vs 67.2 us), 16-bit from 2^15 (57.9 vs 59.4 us)
+            if (path == HIST_PATH_FULL) cw = num_bins <= 16384 ? 32 : 16;
             else if (opts.range_bins > 0) cw = (uint32_t)opts.range_bins <= cap32 ? 32 : 16;
             else cw = 16;
         }
@@ -176,30 +184,59 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             R = ceil_div(num_bins, S);
         }
         if (S > cap || S == 0) return HIST_ERR_UNSUPPORTED;
-        const uint32_t lds_bytes = cw == 32 ? S * 4 : S * 2 + (4 + pca::kEventCap) * 4;
-        const uint32_t occ_lds = std::max<uint32_t>(1, d.lds / lds_bytes);
-        uint32_t wg = (uint32_t)opts.wg_size;
-        if (wg == 0) wg = occ_lds >= 2 ? 512 : 1024;
-        const uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
-        uint32_t G = (uint32_t)opts.groups;
-        if (G == 0) {
-            G = (uint32_t)d.cu * occ / R;
-            if (G >= (uint32_t)d.xcd) G = G / d.xcd * d.xcd;
-            // Keep the merge traffic (G * num_bins counts) a small fraction of the
-            // input (n elements), and every chunk a useful size.
-            const uint64_t by_merge = std::max<uint64_t>(1, max_n / (4ull * num_bins));
-            const uint64_t by_size = std::max<uint64_t>(1, max_n / kMinElemsPerGroup);
-            G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
+        // Interleaved copies for small 32-bit slices: up to 16, within 128 KiB,
+        // and only while a workgroup counts at least 4 elements per copied
+        // counter (clearing and summing the copies costs LDS time per counter).
+        auto chunks_for = [&](uint32_t lds_bytes, uint32_t *wg_out) {
+            const uint32_t occ_lds = std::max<uint32_t>(1, d.lds / lds_bytes);
+            uint32_t wg = (uint32_t)opts.wg_size;
+            if (wg == 0) wg = occ_lds >= 2 ? 512 : 1024;
+            const uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
+            uint32_t G = (uint32_t)opts.groups;
+            if (G == 0) {
+                G = (uint32_t)d.cu * occ / R;
+                if (G >= (uint32_t)d.xcd) G = G / d.xcd * d.xcd;
+                // Keep the merge traffic (G * num_bins counts) a small fraction of the
+                // input (n elements), and every chunk a useful size.
+                const uint64_t by_merge = std::max<uint64_t>(1, max_n / (4ull * num_bins));
+                const uint64_t by_size = std::max<uint64_t>(1, max_n / kMinElemsPerGroup);
+                G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
+            }
+            if (cw == 16) {
+                // Enough chunks that no workgroup counts more than 2^24 elements.
+                G = std::max<uint32_t>(G, ceil_div(max_n, kMaxElemsPerWG16));
+            }
+            *wg_out = wg;
+            return G;
+        };
+        uint32_t kshift = 0, wg = 0, G = 0;
+        if (cw == 32) {
+            if (opts.lds_copies > 0) {
+                while ((1u << (kshift + 1)) <= (uint32_t)opts.lds_copies) ++kshift;
+            } else {
+                for (uint32_t k = 4;; --k) {
+                    const uint32_t bytes = (S << k) * 4;
+                    if (bytes <= 131072u) {
+                        const uint32_t g = chunks_for(bytes, &wg);
+                        if (k == 0 || max_n / g >= 4ull * ((uint64_t)S << k)) {
+                            kshift = k;
+                            break;
+                        }
+                    }
+                    if (k == 0) break;
+                }
+            }
+            if ((S << kshift) * 4 > d.lds) return HIST_ERR_UNSUPPORTED;
         }
-        if (cw == 16) {
-            // Enough chunks that no workgroup counts more than 2^24 elements.
-            G = std::max<uint32_t>(G, ceil_div(max_n, kMaxElemsPerWG16));
-        }
+        const uint32_t lds_bytes =
+            cw == 32 ? (S << kshift) * 4 : S * 2 + (4 + pca::kEventCap) * 4;
+        G = chunks_for(lds_bytes, &wg);
         p->range_bins = S;
         p->ranges = R;
         p->groups = G;
         p->wg = wg;
         p->cw = cw;
+        p->kshift = kshift;
         p->nblk = ceil_div(num_bins, pca::kBlockBins);
         uint64_t off = 0;
         p->off_partials = off;
@@ -214,11 +251,17 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         const uint32_t T = std::max<uint32_t>(1, ceil_div(nvec_max, kScatterWG * kScatterVPT));
         uint32_t W = (uint32_t)opts.groups;
         if (W == 0) W = (uint32_t)d.cu;
+        // Sub-counters per range in the partition's rank atomics: up to 16,
+        // within 2,048 counters per tile.
+        uint32_t qlog = 4;
+        while (qlog > 0 && (R << qlog) > 2048) --qlog;
         p->range_bins = S;
         p->ranges = R;
         p->tiles = T;
         p->owners = W;
         p->groups = W;
+        p->qlog = qlog;
+        p->nblk = S / pca::kBlockBins;
         p->wg = kScatterWG;
         uint64_t off = 0;
         p->off_stage = off;
@@ -231,8 +274,12 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         off += align_up((uint64_t)R * T * 4, 256);
         p->off_totals = off;
         off += align_up((uint64_t)R * 4, 256);
+        p->off_segtot = off;
+        off += align_up((uint64_t)R * ceil_div(T, pca::kScanSeg) * 4, 256);
         p->off_partials = off;
         off += align_up((uint64_t)(W + R) * S * 4, 256);
+        p->off_width = off;
+        off += align_up((uint64_t)(W + R) * p->nblk, 256);  // width codes [nblk][W + R]
         p->need = off;
     }
     return HIST_OK;
@@ -266,12 +313,13 @@ hipError_t launch_sweep_t(const hist_plan *p, const SweepArgs &a, hipStream_t s)
     // 16-bit counters: 2 vectors (8 returning LDS atomics) per thread per
     // iteration stay within the LDS wait counter; measured 12% faster than 4.
     auto k = pca::k_sweep<WG, CW == 16 ? 2 : 4, AGG, CW>;
-    const uint32_t bytes =
-        CW == 32 ? p->range_bins * 4 : p->range_bins * 2 + (4 + pca::kEventCap) * 4;
+    const uint32_t bytes = CW == 32 ? (p->range_bins << p->kshift) * 4
+                                    : p->range_bins * 2 + (4 + pca::kEventCap) * 4;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, a.in, p->num_bins,
-                       p->range_bins, p->ranges, a.G, a.xcds, a.out, a.direct);
+                       p->range_bins, p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, a.out,
+                       a.direct);
     return hipGetLastError();
 }
 
@@ -296,26 +344,37 @@ hipError_t launch_sweep_wg(const hist_plan *p, const SweepArgs &a, hipStream_t s
     }
 }
 
-template <int AGG>
-hipError_t launch_partition_t(const hist_plan *p, pca::InputView in, uint32_t T, hipStream_t s)
+hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, hipStream_t s)
 {
-    auto k = pca::k_partition<kScatterWG, kScatterVPT, AGG>;
-    const uint32_t rpad = (p->ranges + 3u) & ~3u;
-    const uint32_t bytes = (2 * rpad + 4) * 4 + kScatterCap * 2;
+    auto k = pca::k_partition<kScatterWG, kScatterVPT>;
+    const uint32_t npad = ((p->ranges << p->qlog) + 3u) & ~3u;
+    const uint32_t bytes = (2 * npad + 64) * 4 + kScatterCap * 2;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(T), dim3(kScatterWG), bytes, s, in, p->num_bins, kScatterShift,
-                       p->ranges, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage), kScatterCap,
-                       reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
+    // persistent: two workgroups per CU (32 waves), each walking tiles
+    const uint32_t grid = std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kScatterWG), bytes, s, in, p->num_bins, kScatterShift,
+                       p->ranges, p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage),
+                       kScatterCap, reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
                        reinterpret_cast<uint32_t *>(p->ws + p->off_tbase));
     return hipGetLastError();
+}
+
+pca::Partials slot_partials(const hist_plan *p)
+{
+    pca::Partials P;
+    P.data = reinterpret_cast<uint8_t *>(p->ws + p->off_partials);
+    P.width = reinterpret_cast<uint8_t *>(p->ws + p->off_width);
+    P.nblk = p->nblk;
+    P.wstride = p->owners + p->ranges;
+    return P;
 }
 
 template <int AGG>
 hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
 {
     auto k = pca::k_bucket_hist<kScatterWG, 4, AGG>;
-    const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8;
+    const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + (5 * 64 + 4) * 4;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(p->owners), dim3(kScatterWG), bytes, s,
@@ -324,8 +383,7 @@ hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T,
-                       p->range_bins, p->num_bins, p->owners,
-                       reinterpret_cast<uint32_t *>(p->ws + p->off_partials));
+                       p->range_bins, p->num_bins, p->owners, slot_partials(p));
     return hipGetLastError();
 }
 
@@ -493,19 +551,20 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kScatterWG * kScatterVPT));
     if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
     tm.begin(PH_PART);
-    switch (p->agg) {
-    case 0: e = launch_partition_t<0>(p, in, T, stream); break;
-    case 1: e = launch_partition_t<1>(p, in, T, stream); break;
-    case 2: e = launch_partition_t<2>(p, in, T, stream); break;
-    default: e = launch_partition_t<4>(p, in, T, stream); break;
-    }
+    e = launch_partition(p, in, T, stream);
     tm.end(PH_PART);
     if (e != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_SCAN);
-    hipLaunchKernelGGL(pca::k_bucket_scan<1024>, dim3(p->ranges), dim3(1024), 0, stream,
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt), T,
-                       reinterpret_cast<uint32_t *>(p->ws + p->off_tpre),
-                       reinterpret_cast<uint32_t *>(p->ws + p->off_totals));
+    {
+        const uint32_t nseg = ceil_div(T, pca::kScanSeg);
+        uint32_t *tpre = reinterpret_cast<uint32_t *>(p->ws + p->off_tpre);
+        uint32_t *segtot = reinterpret_cast<uint32_t *>(p->ws + p->off_segtot);
+        hipLaunchKernelGGL(pca::k_seg_scan<1024>, dim3(p->ranges * nseg), dim3(1024), 0, stream,
+                           reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt), T, nseg, tpre,
+                           segtot);
+        hipLaunchKernelGGL(pca::k_seg_fix<256>, dim3(p->ranges * nseg), dim3(256), 0, stream, T, nseg,
+                           tpre, segtot, reinterpret_cast<uint32_t *>(p->ws + p->off_totals));
+    }
     tm.end(PH_SCAN);
     if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_OWNER);
@@ -519,7 +578,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     if (e != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_SLOTS);
     hipLaunchKernelGGL(pca::k_merge_slots<16>, dim3(ceil_div(num_bins, 256)), dim3(1024), 0, stream,
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_partials),
+                       slot_partials(p),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges,
                        p->range_bins, num_bins, p->owners, counts);
     tm.end(PH_SLOTS);
@@ -540,7 +599,7 @@ hist_status_t hist_plan_info(const hist_plan_t *p, hist_plan_info_t *info)
     info->ranges = p->ranges;
     info->groups = p->groups;
     info->wg_size = p->wg;
-    info->agg_rounds = p->agg;
+    info->aggregation = p->agg;
     info->tile_elems = p->path == HIST_PATH_SCATTER ? kScatterTile : 0;
     info->counter_bits = p->path == HIST_PATH_SCATTER ? 32 : p->cw;
     info->max_n = p->max_n;
@@ -553,11 +612,11 @@ hist_status_t hist_plan_describe(const hist_plan_t *p, char *buf, uint64_t len)
     if (!p || !buf || len == 0) return HIST_ERR_INVALID_ARG;
     static const char *names[] = {"auto", "full", "range", "scatter"};
     std::snprintf(buf, len,
-                  "path=%s bins=%u S=%u R=%u %s=%u cw=%u wg=%u agg=%d tile=%u cu=%d xcd=%d lds=%u "
-                  "ws=%llu",
+                  "path=%s bins=%u S=%u R=%u %s=%u cw=%u copies=%u wg=%u agg=%d tile=%u cu=%d xcd=%d "
+                  "lds=%u ws=%llu",
                   names[p->path], p->num_bins, p->range_bins, p->ranges,
                   p->path == HIST_PATH_SCATTER ? "W" : "G", p->groups,
-                  p->path == HIST_PATH_SCATTER ? 32u : p->cw, p->wg, p->agg,
+                  p->path == HIST_PATH_SCATTER ? 32u : p->cw, 1u << p->kshift, p->wg, p->agg,
                   p->path == HIST_PATH_SCATTER ? kScatterTile : 0u, p->dev.cu, p->dev.xcd,
                   p->dev.lds, (unsigned long long)p->need);
     return HIST_OK;

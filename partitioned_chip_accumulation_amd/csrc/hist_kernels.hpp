@@ -101,34 +101,57 @@ __device__ __forceinline__ void lds_count(uint32_t *lds, uint32_t slot, bool val
     }
 }
 
-// Like lds_count, but returns each valid lane's rank: the value lds[slot]
-// had before this lane's increment (distinct lanes of one slot get distinct,
-// consecutive ranks). Invalid lanes get 0.
-template <int ROUNDS>
-__device__ __forceinline__ uint32_t lds_rank(uint32_t *lds, uint32_t slot, bool valid)
+// Wave-level duplicate aggregation by a hot slot kept in registers.
+//
+// A wave holds one wave-uniform "hot" slot h and a per-lane count c. Lanes
+// whose element is h add to c instead of issuing an LDS atomic; the wave
+// flushes c (one wave reduction, one LDS add) when h changes and at the end.
+// h is chosen from the data as it streams: once per vector the wave takes the
+// first active lane's slot (readfirstlane) as a candidate and counts, with two
+// ballots, how many lanes hold it and how many hold h; the candidate replaces
+// h only when it holds at least 8 of the 64 lanes and clearly more than h.
+// A hot bin (a tenth of the input on one value) is then counted almost
+// entirely in registers, while uniform data never selects a slot and pays
+// one compare per element.
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+
+struct HotSlot {
+    uint32_t h = kNoSlot;  // wave-uniform
+    uint32_t c = 0;        // per lane
+    uint32_t tick = 0;     // wave-uniform: candidates are checked every 4th vector
+};
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
-    uint32_t rank = 0;
-    bool pending = valid;
-    if constexpr (ROUNDS > 0) {
 #pragma unroll
-        for (int k = 0; k < ROUNDS; ++k) {
-            const uint64_t act = __ballot(pending);
-            if (act == 0) return rank;
-            const int leader = __builtin_ctzll(act);
-            const uint32_t lead = __builtin_amdgcn_readlane(slot, leader);
-            const bool mine = pending && slot == lead;
-            const uint64_t m = __ballot(mine);
-            uint32_t base = 0;
-            if (mine && lane_id() == (uint32_t)leader)
-                base = lds_add_rtn(lds, lead, (uint32_t)__popcll(m));
-            base = __builtin_amdgcn_readlane(base, leader);
-            if (mine) rank = base + lanes_below(m);
-            pending = pending && !mine;
-            if (__popcll(m) == 1) break;
-        }
-    }
-    if (pending) rank = lds_add_rtn(lds, slot, 1u);
-    return rank;
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+// The wave's pending count for h, summed (whole wave, convergent).
+__device__ __forceinline__ uint32_t hot_take(HotSlot &hs)
+{
+    const uint32_t total = hs.h == kNoSlot ? 0u : wave_sum(hs.c);
+    hs.c = 0;
+    return total;
+}
+
+// Returns true when the wave must flush its old hot slot (call hot_take and
+// add the total to the old slot, then set hs.h = *next). Whole wave.
+__device__ __forceinline__ bool hot_should_switch(HotSlot &hs, uint32_t s0, bool v0,
+                                                  uint32_t *next)
+{
+    if ((hs.tick++ & 3u) != 0u) return false;
+    const uint64_t act = __ballot(v0);
+    if (act == 0) return false;
+    const uint32_t cand = __builtin_amdgcn_readlane(s0, __builtin_ctzll(act));
+    if (cand == hs.h) return false;
+    const uint32_t mc = (uint32_t)__popcll(__ballot(v0 && s0 == cand));
+    if (mc < 8) return false;
+    const uint32_t mh = (uint32_t)__popcll(__ballot(v0 && s0 == hs.h));
+    if (mc <= mh + 4) return false;
+    *next = cand;
+    return true;
 }
 
 template <bool NT>
@@ -136,24 +159,6 @@ __device__ __forceinline__ i32x4 load_vec(const i32x4 *p)
 {
     if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
-}
-
-// Copy lds[0..len) to dst[0..len). 16-byte stores when dst is aligned; the
-// store never writes past dst[len - 1].
-template <int WG>
-__device__ __forceinline__ void store_slice(uint32_t *__restrict__ dst, const uint32_t *lds,
-                                            uint32_t len)
-{
-    const uint32_t tid = threadIdx.x;
-    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-        const uint32_t full = len >> 2;
-        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(lds);
-        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
-        for (uint32_t i = tid; i < full; i += WG) d4[i] = s4[i];
-        for (uint32_t i = full * 4 + tid; i < len; i += WG) dst[i] = lds[i];
-    } else {
-        for (uint32_t i = tid; i < len; i += WG) dst[i] = lds[i];
-    }
 }
 
 template <int WG>
@@ -331,12 +336,23 @@ __device__ __forceinline__ void lds_count16(uint32_t *words, uint32_t *evlist, u
 // 32-bit or 16-bit LDS counters. Bins at or beyond len read as zero.
 template <int CW>
 __device__ __forceinline__ u32x4 slice_block(const uint32_t *lds, const uint32_t *evlist,
-                                             uint32_t nev, uint32_t k, uint32_t len)
+                                             uint32_t nev, uint32_t k, uint32_t len,
+                                             uint32_t kshift = 0)
 {
     const uint32_t lane = lane_id();
     u32x4 c;
     if constexpr (CW == 32) {
-        c = reinterpret_cast<const u32x4 *>(lds)[k * 64 + lane];
+        if (kshift == 0) {
+            c = reinterpret_cast<const u32x4 *>(lds)[k * 64 + lane];
+        } else {
+            // K = 2^kshift interleaved copies: bin s, copy j at word s*K + j
+            const uint32_t K = 1u << kshift;
+            const uint32_t b = (k * kBlockBins + lane * 4) << kshift;
+            uint32_t a[4] = {0u, 0u, 0u, 0u};
+            for (uint32_t j = 0; j < 4; ++j)
+                for (uint32_t cp = 0; cp < K; ++cp) a[j] += lds[b + j * K + cp];
+            c = u32x4{a[0], a[1], a[2], a[3]};
+        }
     } else {
         const u32x2 ww = reinterpret_cast<const u32x2 *>(lds)[k * 64 + lane];
         c = u32x4{ww.x & 0xFFFFu, ww.x >> 16, ww.y & 0xFFFFu, ww.y >> 16};
@@ -384,7 +400,8 @@ __device__ __forceinline__ u32x4 slice_block(const uint32_t *lds, const uint32_t
 template <int WG, int UNROLL, int AGG, int CW>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
-                                              Partials out, uint32_t *__restrict__ direct)
+                                              uint32_t kshift, Partials out,
+                                              uint32_t *__restrict__ direct)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
@@ -419,13 +436,46 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + u * WG + tid);
     }
-    zero_lds<WG>(lds, CW == 32 ? len : (len + 1) / 2);
+    zero_lds<WG>(lds, CW == 32 ? (len << kshift) : (len + 1) / 2);
     if (CW == 16 && tid == 0) *ev_count = 0u;
     __syncthreads();
+    // 32-bit counters may keep 2^kshift interleaved copies of the slice; a lane
+    // adds to copy (lane mod 2^kshift), so lanes of one wave that hit the same
+    // bin mostly touch different words and banks.
+    const uint32_t rep = lane_id() & ((1u << kshift) - 1u);
 
+    // AGG == 1: hot-slot register aggregation in the main loop; the ragged
+    // remainder counts plainly. AGG >= 2: leader-peel rounds everywhere.
+    constexpr int PEEL = AGG >= 2 ? AGG : 0;
     auto count1 = [&](uint32_t s, bool ok) {
-        if constexpr (CW == 32) lds_count<AGG>(lds, s, ok);
-        else lds_count16<AGG>(lds, evlist, ev_count, s, ok);
+        if constexpr (CW == 32) lds_count<PEEL>(lds, (s << kshift) | rep, ok);
+        else lds_count16<PEEL>(lds, evlist, ev_count, s, ok);
+    };
+    HotSlot hs;
+    auto hot_flush = [&]() {
+        if constexpr (AGG == 1) {
+            uint32_t t = hot_take(hs);
+            if (lane_id() == 0 && t != 0u) {
+                if constexpr (CW == 32) {
+                    lds_add(lds, hs.h << kshift, t);
+                } else {
+                    while (t != 0u) {
+                        const uint32_t kk = min(t, 32768u);
+                        add16(lds, evlist, ev_count, hs.h, kk);
+                        t -= kk;
+                    }
+                }
+            }
+        }
+    };
+    auto hot_check = [&](uint32_t s0, bool v0) {
+        if constexpr (AGG == 1) {
+            uint32_t nxt;
+            if (hot_should_switch(hs, s0, v0, &nxt)) {
+                hot_flush();
+                hs.h = nxt;
+            }
+        }
     };
     auto count4 = [&](const i32x4 q, bool ok) {
         uint32_t s;
@@ -443,7 +493,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + STEP + u * WG + tid);
         }
-        if constexpr (CW == 16 && AGG == 0) {
+        if constexpr (AGG <= 1) {
             uint32_t sl[4 * UNROLL];
             bool ok[4 * UNROLL];
 #pragma unroll
@@ -455,7 +505,24 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
             }
 #pragma unroll
             for (int e = 0; e < 4 * UNROLL; ++e) ok[e] = sl[e] < len;
-            count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
+            if constexpr (AGG == 1) {
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) hot_check(sl[4 * u], ok[4 * u]);
+                if (hs.h != kNoSlot) {
+#pragma unroll
+                    for (int e = 0; e < 4 * UNROLL; ++e) {
+                        const bool m = ok[e] && sl[e] == hs.h;
+                        hs.c += m ? 1u : 0u;
+                        ok[e] = ok[e] && !m;
+                    }
+                }
+            }
+            if constexpr (CW == 16) {
+                count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4 * UNROLL; ++e) lds_count<0>(lds, (sl[e] << kshift) | rep, ok[e]);
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) count4(q[u], true);
@@ -475,12 +542,13 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
         const uint32_t ts = (tok ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid] : 0u) - lo;
         count1(ts, tok && ts < len);
     }
+    hot_flush();
     __syncthreads();
 
     const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : 0u;
     const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
     for (uint32_t k = tid >> 6; k < nblk; k += WG / 64) {
-        const u32x4 c = slice_block<CW>(lds, evlist, nev, k, len);
+        const u32x4 c = slice_block<CW>(lds, evlist, nev, k, len, kshift);
         if (direct) {
             const uint32_t b0 = lo + k * kBlockBins + lane_id() * 4;
             if (b0 + 0 < num_bins) direct[b0 + 0] = c.x;
@@ -555,90 +623,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows,
 }
 
 // ---------------------------------------------------------------------------
-// Two-phase path, phase 1: route every element of a tile to its owning range.
-//
-// Tile t is body vectors [t * WG * VPT, ...) (tile 0 also takes the head
-// scalars, the last tile the tail scalars). Each valid element x (x <
-// num_bins) is owned by range r = x >> shift, where it is slot x & mask. The
-// workgroup counts its elements per range in LDS, and each element's LDS
-// atomic returns its rank among the tile's elements of that range; an
-// exclusive scan of the counts gives each range's start, so the tile's
-// slots can be written to an LDS staging buffer grouped by range and copied
-// to stage[t * stage_cap ...] with full 16-byte stores. Only the 16-bit slot
-// is kept: the range is implied by the position. Per tile and range the
-// kernel writes the count and the start of its run (tcnt, tbase; layout
-// [range][tile]). Element order inside a run is whatever the atomics gave;
-// counts do not depend on it.
-template <int WG, int VPT, int AGG>
-__global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
-                                                  uint32_t ranges, uint32_t tiles,
-                                                  uint16_t *__restrict__ stage, uint32_t stage_cap,
-                                                  uint32_t *__restrict__ tcnt,
-                                                  uint32_t *__restrict__ tbase)
-{
-    extern __shared__ u32x4 smem4[];
-    const uint32_t rpad = (ranges + 3u) & ~3u;
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem4);
-    uint32_t *base = cnt + rpad;
-    uint32_t *nvalid = base + rpad;  // one word, padded to 16 bytes
-    uint16_t *st = reinterpret_cast<uint16_t *>(nvalid + 4);
-    const uint32_t tid = threadIdx.x, t = blockIdx.x;
-    const uint32_t mask = (1u << shift) - 1u;
-
-    for (uint32_t i = tid; i < ranges; i += WG) cnt[i] = 0u;
-    __syncthreads();
-
-    constexpr int E = VPT * 4;
-    uint32_t x[E + 2], rk[E + 2];
-    const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
-    const uint64_t vb = (uint64_t)t * (WG * VPT);
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const uint64_t v = vb + (uint64_t)u * WG + tid;
-        const i32x4 q = v < in.nvec ? body[v] : i32x4{-1, -1, -1, -1};
-        x[4 * u + 0] = (uint32_t)q.x;
-        x[4 * u + 1] = (uint32_t)q.y;
-        x[4 * u + 2] = (uint32_t)q.z;
-        x[4 * u + 3] = (uint32_t)q.w;
-    }
-    x[E] = (t == 0 && tid < in.head) ? (uint32_t)in.ptr[tid] : 0xFFFFFFFFu;
-    x[E + 1] = (t == tiles - 1 && tid < in.tail) ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid]
-                                                 : 0xFFFFFFFFu;
-#pragma unroll
-    for (int e = 0; e < E + 2; ++e) {
-        const bool ok = x[e] < num_bins;
-        rk[e] = lds_rank<AGG>(cnt, ok ? x[e] >> shift : 0u, ok);
-    }
-    __syncthreads();
-
-    if (tid < 64) {
-        uint32_t carry = 0;
-        for (uint32_t c = 0; c < ranges; c += 64) {
-            const uint32_t i = c + tid;
-            const uint32_t v = i < ranges ? cnt[i] : 0u;
-            const uint32_t incl = wave_inclusive_scan(v);
-            if (i < ranges) {
-                base[i] = carry + incl - v;
-                tcnt[(uint64_t)i * tiles + t] = v;
-                tbase[(uint64_t)i * tiles + t] = carry + incl - v;
-            }
-            carry += __shfl(incl, 63, 64);
-        }
-        if (tid == 0) *nvalid = carry;
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int e = 0; e < E + 2; ++e)
-        if (x[e] < num_bins) st[base[x[e] >> shift] + rk[e]] = (uint16_t)(x[e] & mask);
-    __syncthreads();
-
-    const uint32_t nv = (*nvalid + 7u) >> 3;
-    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(st);
-    u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)t * stage_cap);
-    for (uint32_t i = tid; i < nv; i += WG) d4[i] = s4[i];
-}
-
+// Two-phase path.
 // WG-wide exclusive scan of one value per thread; returns this thread's
 // exclusive prefix and writes the total to *total (all threads).
 template <int WG>
@@ -662,27 +647,56 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
 }
 
 // Phase 1b: per range r, tpre[r][t] = sum of tcnt[r][t'] over t' < t, and
-// totals[r] = the range's element count. One workgroup per range.
+// totals[r] = the range's element count. Two passes, both spread over
+// (range, segment of kScanSeg tiles) workgroups so that every CU takes part:
+// k_seg_scan writes each segment's local exclusive prefix and its total,
+// k_seg_fix adds the totals of the range's earlier segments (and the last
+// segment's workgroup writes the range total).
+constexpr uint32_t kScanSeg = 4096;
+
 template <int WG>
-__global__ __launch_bounds__(WG) void k_bucket_scan(const uint32_t *__restrict__ tcnt,
-                                                    uint32_t tiles, uint32_t *__restrict__ tpre,
-                                                    uint32_t *__restrict__ totals)
+__global__ __launch_bounds__(WG) void k_seg_scan(const uint32_t *__restrict__ tcnt, uint32_t tiles,
+                                                 uint32_t nseg, uint32_t *__restrict__ tpre,
+                                                 uint32_t *__restrict__ segtot)
 {
     __shared__ uint32_t scratch[2 * (WG / 64) + 1];
-    const uint32_t r = blockIdx.x, tid = threadIdx.x;
+    const uint32_t r = blockIdx.x / nseg, sg = blockIdx.x % nseg, tid = threadIdx.x;
+    const uint32_t s0 = sg * kScanSeg, s1 = min(s0 + kScanSeg, tiles);
     const uint32_t *c = tcnt + (uint64_t)r * tiles;
     uint32_t *p = tpre + (uint64_t)r * tiles;
-    const uint32_t per = (tiles + WG - 1) / WG;
-    const uint32_t t0 = min(tid * per, tiles), t1 = min(t0 + per, tiles);
-    uint32_t s = 0;
-    for (uint32_t t = t0; t < t1; ++t) s += c[t];
-    uint32_t total;
-    uint32_t run = block_exclusive_scan<WG>(s, scratch, &total);
-    for (uint32_t t = t0; t < t1; ++t) {
-        p[t] = run;
-        run += c[t];
+    constexpr uint32_t PER = kScanSeg / WG;
+    const uint32_t t0 = s0 + tid * PER;
+    uint32_t v[PER], sum = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        v[k] = t0 + k < s1 ? c[t0 + k] : 0u;
+        sum += v[k];
     }
-    if (tid == 0) totals[r] = total;
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<WG>(sum, scratch, &total);
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        if (t0 + k < s1) p[t0 + k] = run;
+        run += v[k];
+    }
+    if (tid == 0) segtot[(uint64_t)r * nseg + sg] = total;
+}
+
+template <int WG>
+__global__ __launch_bounds__(WG) void k_seg_fix(uint32_t tiles, uint32_t nseg,
+                                                uint32_t *__restrict__ tpre,
+                                                const uint32_t *__restrict__ segtot,
+                                                uint32_t *__restrict__ totals)
+{
+    const uint32_t r = blockIdx.x / nseg, sg = blockIdx.x % nseg, tid = threadIdx.x;
+    const uint32_t *st = segtot + (uint64_t)r * nseg;
+    uint32_t off = 0;
+    for (uint32_t k = 0; k < sg; ++k) off += st[k];
+    if (sg == nseg - 1 && tid == 0) totals[r] = off + st[sg];
+    if (off == 0) return;
+    uint32_t *p = tpre + (uint64_t)r * tiles;
+    const uint32_t s0 = sg * kScanSeg, s1 = min(s0 + kScanSeg, tiles);
+    for (uint32_t t = s0 + tid; t < s1; t += WG) p[t] += off;
 }
 
 // Exclusive prefix of totals[0..ranges) into bs[0..ranges], by wave 0.
@@ -710,6 +724,132 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
     return (uint32_t)(((p + 1) * W - 1) / N);
 }
 
+// Phase 1: route every element of a tile to its owning range.
+//
+// Tile t is body vectors [t * WG * VPT, ...) (tile 0 also takes the head
+// scalars, the last tile the tail scalars). Each valid element x (x <
+// num_bins) is owned by range r = x >> shift, where it is slot x & mask. The
+// workgroup counts its elements per range in LDS; each element's returning
+// LDS atomic gives its rank among the tile's elements of that range, and an
+// exclusive scan of the counts gives each range's start, so the tile's slots
+// are grouped by range in an LDS staging buffer and copied out with full
+// 16-byte stores to stage[t * stage_cap ...]. Only the 16-bit slot is kept:
+// the range is implied by the position.
+//
+// Returning atomics on one LDS word are served one lane at a time (each lane
+// needs its own rank), so every range's counter is split into 2^qlog
+// sub-counters chosen by lane (lane mod 2^qlog): lanes that route to the same
+// range then rarely share a word. The scan runs over [range][sub] order, so a
+// range's elements stay contiguous. Per tile and range the kernel writes the
+// run's length and start (tcnt, tbase; layout [range][tile]). Element order
+// inside a run is whatever the atomics gave; counts do not depend on it.
+template <int WG, int VPT>
+__global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
+                                                  uint32_t ranges, uint32_t qlog, uint32_t tiles,
+                                                  uint16_t *__restrict__ stage, uint32_t stage_cap,
+                                                  uint32_t *__restrict__ tcnt,
+                                                  uint32_t *__restrict__ tbase)
+{
+    extern __shared__ u32x4 smem4[];
+    const uint32_t nsub = ranges << qlog;  // <= 2 * WG
+    const uint32_t npad = (nsub + 3u) & ~3u;
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem4);
+    uint32_t *base = cnt + npad;
+    uint32_t *scratch = base + npad;  // block scan scratch + total
+    uint16_t *st = reinterpret_cast<uint16_t *>(scratch + 64);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t mask = (1u << shift) - 1u;
+    const uint32_t q = lane_id() & ((1u << qlog) - 1u);
+    constexpr int E = VPT * 4;
+    const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
+
+    // A persistent workgroup walks tiles blockIdx.x, + gridDim.x, ...; the
+    // next tile's elements are loaded while the current one is counted.
+    uint32_t nx[E + 2];
+    auto load_tile = [&](uint32_t t) {
+        const uint64_t vb = (uint64_t)t * (WG * VPT);
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const uint64_t v = vb + (uint64_t)u * WG + tid;
+            const i32x4 qv = v < in.nvec ? body[v] : i32x4{-1, -1, -1, -1};
+            nx[4 * u + 0] = (uint32_t)qv.x;
+            nx[4 * u + 1] = (uint32_t)qv.y;
+            nx[4 * u + 2] = (uint32_t)qv.z;
+            nx[4 * u + 3] = (uint32_t)qv.w;
+        }
+        nx[E] = (t == 0 && tid < in.head) ? (uint32_t)in.ptr[tid] : 0xFFFFFFFFu;
+        nx[E + 1] = (t == tiles - 1 && tid < in.tail) ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid]
+                                                      : 0xFFFFFFFFu;
+    };
+    uint32_t t = blockIdx.x;
+    if (t < tiles) load_tile(t);
+    for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
+    __syncthreads();
+
+    for (; t < tiles; t += gridDim.x) {
+        uint32_t x[E + 2], rk[E + 2];
+#pragma unroll
+        for (int e = 0; e < E + 2; ++e) x[e] = nx[e];
+        if (t + gridDim.x < tiles) load_tile(t + gridDim.x);
+#pragma unroll
+        for (int e = 0; e < E + 2; ++e) {
+            rk[e] = 0u;
+            if (x[e] < num_bins) rk[e] = lds_add_rtn(cnt, ((x[e] >> shift) << qlog) | q, 1u);
+        }
+        __syncthreads();
+
+        {
+            const uint32_t i0 = 2 * tid, i1 = 2 * tid + 1;
+            const uint32_t c0 = i0 < nsub ? cnt[i0] : 0u, c1 = i1 < nsub ? cnt[i1] : 0u;
+            uint32_t total;
+            const uint32_t ex = block_exclusive_scan<WG>(c0 + c1, scratch, &total);
+            if (i0 < nsub) base[i0] = ex;
+            if (i1 < nsub) base[i1] = ex + c0;
+            if (tid == 0) scratch[63] = total;
+        }
+        __syncthreads();
+        const uint32_t nvalid = scratch[63];
+        for (uint32_t r = tid; r < ranges; r += WG) {
+            const uint32_t b0 = base[r << qlog];
+            const uint32_t b1 = r + 1 < ranges ? base[(r + 1) << qlog] : nvalid;
+            tcnt[(uint64_t)r * tiles + t] = b1 - b0;
+            tbase[(uint64_t)r * tiles + t] = b0;
+        }
+#pragma unroll
+        for (int e = 0; e < E + 2; ++e)
+            if (x[e] < num_bins) st[base[((x[e] >> shift) << qlog) | q] + rk[e]] = (uint16_t)(x[e] & mask);
+        __syncthreads();
+
+        // counters are free again: clear them for the next tile while copying out
+        for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
+        const uint32_t nv = (nvalid + 7u) >> 3;
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(st);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)t * stage_cap);
+        for (uint32_t i = tid; i < nv; i += WG) d4[i] = s4[i];
+        __syncthreads();  // staging and counters are reused by the next tile
+    }
+}
+
+// Wave-cooperative search in a non-decreasing array: the last index i in
+// [0, n) with a[i] <= key (0 if none). Each round samples 64 evenly spaced
+// entries with one load per lane, so a search costs log64(n) round trips.
+__device__ __forceinline__ uint32_t wave_find_last_le(const uint32_t *__restrict__ a, uint32_t n,
+                                                      uint32_t key)
+{
+    const uint32_t lane = lane_id();
+    uint32_t lo = 0, hi = n;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const uint32_t step = (hi - lo + 63) / 64;
+        const uint32_t idx = lo + lane * step;
+        const bool le = idx < hi && a[idx] <= key;
+        const uint64_t m = __ballot(le);
+        const uint32_t j = m ? 63u - (uint32_t)__builtin_clzll(m) : 0u;
+        lo = lo + j * step;
+        hi = min(lo + step, hi);
+    }
+    return lo;
+}
+
 // Phase 2: owner workgroups build LDS histograms from the routed slots.
 //
 // All ranges' elements, concatenated in range order, are split evenly over
@@ -719,21 +859,28 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
 // zeroes an LDS slice of the range's bins, counts the overlapped elements,
 // and writes the slice to partial slot i + r (i + r is distinct for every
 // (owner, range) pair that occurs, because both grow along the
-// concatenation). Inside one range the elements are the runs of the tiles in
-// tile order; each wave takes 64 tiles at a time, lays their runs end to end
-// with a wave scan of their vector counts, and spreads the resulting 16-byte
-// vectors over its lanes, so short and long runs both keep every lane busy.
+// concatenation). Inside one range the elements are the tiles' runs in tile
+// order. The workgroup takes 64 tiles at a time: wave 0 lays their runs end
+// to end (a wave scan of their 16-byte vector counts) into LDS, one batch
+// ahead of use, and all threads then split the batch's vectors evenly,
+// finding each vector's run with a 6-step search of the scanned counts, so
+// short runs, long runs and ragged run boundaries all keep every lane busy.
 template <int WG, int UNROLL, int AGG>
 __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint16_t *__restrict__ stage, uint32_t stage_cap, const uint32_t *__restrict__ tcnt,
     const uint32_t *__restrict__ tbase, const uint32_t *__restrict__ tpre,
     const uint32_t *__restrict__ totals, uint32_t ranges, uint32_t tiles, uint32_t range_bins,
-    uint32_t num_bins, uint32_t owners, uint32_t *__restrict__ partials)
+    uint32_t num_bins, uint32_t owners, Partials out)
 {
-    constexpr uint32_t NW = WG / 64;
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
-    uint64_t *bs = reinterpret_cast<uint64_t *>(lds + range_bins);
+    uint64_t *bs = reinterpret_cast<uint64_t *>(lds + range_bins);  // [ranges + 1]
+    uint32_t *mP = reinterpret_cast<uint32_t *>(bs + ranges + 1);   // inclusive vector prefix
+    uint32_t *mE = mP + 64;                                          // exclusive prefix
+    uint32_t *mV = mE + 64;                                          // first vector of the run
+    uint32_t *mS = mV + 64;                                          // elements skipped in it
+    uint32_t *mC = mS + 64;                                          // run elements used
+    uint32_t *misc = mC + 64;                                        // [0] ta [1] tb [2] total
     const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
 
     range_starts(totals, ranges, bs);
@@ -743,8 +890,7 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint64_t e0 = (uint64_t)i * N / owners, e1 = (uint64_t)(i + 1) * N / owners;
     if (e0 >= e1) return;  // whole workgroup: no element to count
 
-    // First range overlapping [e0, e1): the last r with bs[r] <= e0.
-    uint32_t r = 0;
+    uint32_t r;  // first range overlapping [e0, e1): the last r with bs[r] <= e0
     {
         uint32_t lo = 0, hi = ranges - 1;
         while (lo < hi) {
@@ -759,99 +905,135 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
         if (re <= e0 || rb == re) continue;  // uniform
         const uint32_t p0 = (uint32_t)(max(e0, rb) - rb), p1 = (uint32_t)(min(e1, re) - rb);
         const uint32_t len = min(range_bins, num_bins - r * range_bins);
-        zero_lds<WG>(lds, len);
-        __syncthreads();
-
         const uint32_t *rc = tcnt + (uint64_t)r * tiles;
         const uint32_t *rbase = tbase + (uint64_t)r * tiles;
         const uint32_t *rpre = tpre + (uint64_t)r * tiles;
-        // Tiles whose runs overlap [p0, p1): from the last t with rpre[t] <= p0
-        // up to (excluding) the first t with rpre[t] >= p1.
-        uint32_t ta, tb;
-        {
-            uint32_t lo = 0, hi = tiles - 1;
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi + 1) >> 1;
-                if (rpre[mid] <= p0) lo = mid; else hi = mid - 1;
-            }
-            ta = lo;
-            lo = ta;
-            hi = tiles;
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if (rpre[mid] >= p1) hi = mid; else lo = mid + 1;
-            }
-            tb = lo;
-        }
-        for (uint32_t t0 = ta + w * 64; t0 < tb; t0 += NW * 64) {
-            const uint32_t t = t0 + lane;
-            uint32_t vlo = 0, nv = 0, skip = 0, cnt = 0;
-            if (t < tb) {
-                const uint32_t c = rc[t], q = rpre[t];
-                const uint32_t lo_e = max(p0, q) - q;
-                const uint32_t hi_e = min(p1, q + c) - q;
-                if (c != 0 && hi_e > lo_e) {
-                    const uint64_t g_lo = (uint64_t)t * stage_cap + rbase[t] + lo_e;
-                    const uint64_t g_hi = g_lo + (hi_e - lo_e);
-                    vlo = (uint32_t)(g_lo >> 3);
-                    nv = (uint32_t)(((g_hi + 7) >> 3) - (g_lo >> 3));
-                    skip = (uint32_t)(g_lo & 7u);
-                    cnt = hi_e - lo_e;
-                }
-            }
-            const uint32_t P = wave_inclusive_scan(nv);
-            const uint32_t E = P - nv;
-            const uint32_t total = __shfl(P, 63, 64);
-            for (uint32_t u0 = 0; u0 < total; u0 += 64 * UNROLL) {
-                i32x4 q[UNROLL];
-                uint32_t first[UNROLL], last[UNROLL];
-#pragma unroll
-                for (int k = 0; k < UNROLL; ++k) {
-                    const uint32_t u = u0 + k * 64 + lane;
-                    // owner lane j: the first lane whose inclusive prefix exceeds u
-                    uint32_t j = 0;
-#pragma unroll
-                    for (uint32_t step = 32; step >= 1; step >>= 1) {
-                        const uint32_t pj = __shfl(P, (int)(j + step - 1), 64);
-                        if (pj <= u) j += step;
-                    }
-                    const uint32_t jv = __shfl(vlo, (int)j, 64);
-                    const uint32_t je = __shfl(E, (int)j, 64);
-                    const uint32_t js = __shfl(skip, (int)j, 64);
-                    const uint32_t jc = __shfl(cnt, (int)j, 64);
-                    const bool ok = u < total;
-                    const uint32_t k8 = (u - je) * 8u;  // element offset of this vector in the run, + skip
-                    // element e of the vector is run element k8 + e - skip
-                    first[k] = ok ? (k8 < js ? js - k8 : 0u) : 8u;
-                    last[k] = ok ? min(8u, js + jc - k8) : 0u;
-                    q[k] = ok ? stage_vec[jv + (u - je)] : i32x4{0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int k = 0; k < UNROLL; ++k) {
-                    const uint32_t words[4] = {(uint32_t)q[k].x, (uint32_t)q[k].y, (uint32_t)q[k].z,
-                                               (uint32_t)q[k].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t s = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
-                        const bool ok = (uint32_t)e >= first[k] && (uint32_t)e < last[k];
-                        lds_count<AGG>(lds, s, ok);
-                    }
-                }
+        zero_lds<WG>(lds, len);
+        if (w == 0) {
+            // runs overlapping [p0, p1): from the last t with rpre[t] <= p0 to the
+            // first t with rpre[t] >= p1
+            const uint32_t ta = wave_find_last_le(rpre, tiles, p0);
+            uint32_t tb = wave_find_last_le(rpre, tiles, p1 - 1) + 1;
+            if (lane == 0) {
+                misc[0] = ta;
+                misc[1] = tb;
             }
         }
         __syncthreads();
-        store_slice<WG>(partials + (uint64_t)(i + r) * range_bins, lds, len);
+        const uint32_t ta = misc[0], tb = misc[1];
+        HotSlot hs;
+
+        // wave 0's registers hold the metadata of the batch after the current one
+        uint32_t nc = 0, nq = 0, nb = 0;
+        if (w == 0 && ta + lane < tb) {
+            nc = rc[ta + lane];
+            nq = rpre[ta + lane];
+            nb = rbase[ta + lane];
+        }
+        for (uint32_t t0 = ta; t0 < tb; t0 += 64) {
+            if (w == 0) {
+                const uint32_t t = t0 + lane;
+                uint32_t vlo = 0, nv = 0, skip = 0, used = 0;
+                if (t < tb && nc != 0) {
+                    const uint32_t lo_e = max(p0, nq) - nq;
+                    const uint32_t hi_e = min(p1, nq + nc) - nq;
+                    if (hi_e > lo_e) {
+                        const uint64_t g_lo = (uint64_t)t * stage_cap + nb + lo_e;
+                        const uint64_t g_hi = g_lo + (hi_e - lo_e);
+                        vlo = (uint32_t)(g_lo >> 3);
+                        nv = (uint32_t)(((g_hi + 7) >> 3) - (g_lo >> 3));
+                        skip = (uint32_t)(g_lo & 7u);
+                        used = hi_e - lo_e;
+                    }
+                }
+                const uint32_t P = wave_inclusive_scan(nv);
+                mP[lane] = P;
+                mE[lane] = P - nv;
+                mV[lane] = vlo;
+                mS[lane] = skip;
+                mC[lane] = used;
+                if (lane == 63) misc[2] = P;
+                nc = nq = nb = 0;
+                if (t0 + 64 + lane < tb) {
+                    nc = rc[t0 + 64 + lane];
+                    nq = rpre[t0 + 64 + lane];
+                    nb = rbase[t0 + 64 + lane];
+                }
+            }
+            __syncthreads();
+            const uint32_t total = misc[2];
+            for (uint32_t ub = 0; ub < total; ub += WG * UNROLL) {
+                i32x4 qv[UNROLL];
+                uint32_t first[UNROLL], last[UNROLL];
+#pragma unroll
+                for (int k = 0; k < UNROLL; ++k) {
+                    const uint32_t u = ub + k * WG + tid;
+                    const bool ok = u < total;
+                    uint32_t j = 0;
+#pragma unroll
+                    for (uint32_t step = 32; step >= 1; step >>= 1)
+                        if (mP[j + step - 1] <= u) j += step;
+                    const uint32_t d = u - mE[j];
+                    const uint32_t k8 = d * 8u;  // run element of vector element e is k8 + e - skip
+                    const uint32_t js = mS[j], jc = mC[j];
+                    first[k] = ok ? (k8 < js ? js - k8 : 0u) : 8u;
+                    last[k] = ok ? min(8u, js + jc - k8) : 0u;
+                    qv[k] = ok ? stage_vec[(uint64_t)mV[j] + d] : i32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int k = 0; k < UNROLL; ++k) {
+                    const uint32_t words[4] = {(uint32_t)qv[k].x, (uint32_t)qv[k].y,
+                                               (uint32_t)qv[k].z, (uint32_t)qv[k].w};
+                    if constexpr (AGG == 1) {
+                        uint32_t nxt;
+                        if (hot_should_switch(hs, words[0] & 0xFFFFu, first[k] == 0u && last[k] > 0u,
+                                              &nxt)) {
+                            const uint32_t t = hot_take(hs);
+                            if (lane == 0 && t != 0u) lds_add(lds, hs.h, t);
+                            hs.h = nxt;
+                        }
+                    }
+                    if (AGG == 1 && hs.h != kNoSlot) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t s =
+                                (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+                            const bool ok = (uint32_t)e >= first[k] && (uint32_t)e < last[k];
+                            const bool m = ok && s == hs.h;
+                            hs.c += m ? 1u : 0u;
+                            lds_count<0>(lds, s, ok && !m);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t s =
+                                (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+                            const bool ok = (uint32_t)e >= first[k] && (uint32_t)e < last[k];
+                            lds_count<AGG == 1 ? 0 : AGG>(lds, s, ok);
+                        }
+                    }
+                }
+            }
+            __syncthreads();  // the batch metadata is rewritten next
+        }
+        {
+            const uint32_t t = hot_take(hs);
+            if (lane == 0 && t != 0u) lds_add(lds, hs.h, t);
+        }
+        __syncthreads();
+        const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
+        for (uint32_t k = w; k < nblk; k += WG / 64)
+            write_block(out, i + r, k, slice_block<32>(lds, nullptr, 0, k, len));
         __syncthreads();
     }
 }
 
 // Phase 2b: counts[b] for the bins of one range = the sum of the slots that
 // the owners overlapping the range wrote for it (exclusive owner per bin, no
-// global atomics). A workgroup handles 256 bins of one range; range_bins is
-// a multiple of 256. Empty ranges give zeros.
+// global atomics). A workgroup handles one 256-bin block of one range; each
+// slot's block is read at its own width. Empty ranges give zeros.
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_merge_slots(const uint32_t *__restrict__ partials,
-                                                            const uint32_t *__restrict__ totals,
+__global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint32_t *__restrict__ totals,
                                                             uint32_t ranges, uint32_t range_bins,
                                                             uint32_t num_bins, uint32_t owners,
                                                             uint32_t *__restrict__ counts)
@@ -859,9 +1041,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(const uint32_t *__re
     __shared__ u32x4 red[WAVES][64];
     __shared__ uint64_t se[3];
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-    const uint64_t bin0 = (uint64_t)blockIdx.x * 256u;
-    const uint32_t r = (uint32_t)(bin0 / range_bins);
-    const uint32_t s0 = (uint32_t)(bin0 % range_bins) + lane * 4u;
+    const uint32_t bpr = range_bins / kBlockBins;  // blocks per range
+    const uint32_t r = blockIdx.x / bpr, lb = blockIdx.x % bpr;
     if (w == 0) {
         // start of range r, its end, and the grand total
         uint64_t before = 0, all = 0;
@@ -890,8 +1071,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(const uint32_t *__re
         const uint32_t first = owner_of(rb, N, owners), last = owner_of(re - 1, N, owners);
         for (uint32_t i = first + w; i <= last; i += WAVES) {
             const uint64_t a = (uint64_t)i * N / owners, b = (uint64_t)(i + 1) * N / owners;
-            if (a < b)
-                acc += *reinterpret_cast<const u32x4 *>(partials + (uint64_t)(i + r) * range_bins + s0);
+            if (a >= b) continue;
+            const uint64_t row = (uint64_t)i + r;
+            const uint32_t planes = P.width[(uint64_t)lb * P.wstride + row] + 1u;
+            const uint16_t *src =
+                reinterpret_cast<const uint16_t *>(P.data + (row * P.nblk + lb) * kBlockBytes);
+            for (uint32_t qd = 0; qd < planes; ++qd) add_plane(acc, src[qd * 64 + lane], qd);
         }
     }
     red[w][lane] = acc;
@@ -899,7 +1084,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(const uint32_t *__re
     if (w == 0) {
 #pragma unroll
         for (int k = 1; k < WAVES; ++k) acc += red[k][lane];
-        const uint64_t b = (uint64_t)r * range_bins + s0;
+        const uint64_t b = (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u;
         if (b + 0 < num_bins) counts[b + 0] = acc.x;
         if (b + 1 < num_bins) counts[b + 1] = acc.y;
         if (b + 2 < num_bins) counts[b + 2] = acc.z;

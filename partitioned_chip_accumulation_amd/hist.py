@@ -36,9 +36,9 @@ class LibraryMissing(ImportError):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("groups", ctypes.c_int32),
-                ("range_bins", ctypes.c_int32), ("agg_rounds", ctypes.c_int32),
+                ("range_bins", ctypes.c_int32), ("aggregation", ctypes.c_int32),
                 ("wg_size", ctypes.c_int32), ("xcd_map", ctypes.c_int32),
-                ("counter_bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("counter_bits", ctypes.c_int32), ("lds_copies", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -46,7 +46,7 @@ class PlanInfo(ctypes.Structure):
                 ("cu_count", ctypes.c_int32), ("xcd_count", ctypes.c_int32),
                 ("num_bins", ctypes.c_uint32), ("range_bins", ctypes.c_uint32),
                 ("ranges", ctypes.c_uint32), ("groups", ctypes.c_uint32),
-                ("wg_size", ctypes.c_uint32), ("agg_rounds", ctypes.c_int32),
+                ("wg_size", ctypes.c_uint32), ("aggregation", ctypes.c_int32),
                 ("tile_elems", ctypes.c_uint32), ("counter_bits", ctypes.c_uint32),
                 ("max_n", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
 
@@ -107,12 +107,13 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _opts(path="auto", groups=0, range_bins=0, agg_rounds=-1, wg_size=0, xcd_map=0,
-          counter_bits=0) -> PlanOpts:
+def _opts(path="auto", groups=0, range_bins=0, aggregation=-1, wg_size=0, xcd_map=0,
+          counter_bits=0, lds_copies=0) -> PlanOpts:
     o = PlanOpts()
     o.path = PATHS[path] if isinstance(path, str) else int(path)
-    o.groups, o.range_bins, o.agg_rounds = int(groups), int(range_bins), int(agg_rounds)
+    o.groups, o.range_bins, o.aggregation = int(groups), int(range_bins), int(aggregation)
     o.wg_size, o.xcd_map, o.counter_bits = int(wg_size), int(xcd_map), int(counter_bits)
+    o.lds_copies = int(lds_copies)
     return o
 
 
@@ -135,7 +136,7 @@ class Info:
     ranges: int
     groups: int
     wg_size: int
-    agg_rounds: int
+    aggregation: int
     tile_elems: int
     counter_bits: int
     max_n: int
@@ -193,7 +194,7 @@ class Plan:
         i = PlanInfo()
         _check(library().hist_plan_info(self._plan, ctypes.byref(i)), "hist_plan_info")
         return Info(PATH_NAMES[i.path], i.device, i.cu_count, i.xcd_count, i.num_bins,
-                    i.range_bins, i.ranges, i.groups, i.wg_size, i.agg_rounds, i.tile_elems,
+                    i.range_bins, i.ranges, i.groups, i.wg_size, i.aggregation, i.tile_elems,
                     i.counter_bits, i.max_n, i.workspace_bytes)
 
     def describe(self) -> str:

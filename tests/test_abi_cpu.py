@@ -53,10 +53,11 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_workspace_size(hist.MAX_BINS + 1, 10, None,
                                    ctypes.byref(n)) == hist.HIST_ERR_UNSUPPORTED
     for field, bad in [("path", 7), ("groups", -1), ("range_bins", 6), ("range_bins", 1000),
-                       ("counter_bits", 8), ("agg_rounds", 3),
-                       ("agg_rounds", -2), ("wg_size", 100), ("xcd_map", 5)]:
+                       ("counter_bits", 8), ("aggregation", 3), ("lds_copies", 3),
+                       ("lds_copies", 32),
+                       ("aggregation", -2), ("wg_size", 100), ("xcd_map", 5)]:
         o = hist.PlanOpts()
-        o.agg_rounds = -1
+        o.aggregation = -1
         setattr(o, field, bad)
         assert lib.hist_workspace_size(10, 10, ctypes.byref(o),
                                        ctypes.byref(n)) == hist.HIST_ERR_INVALID_ARG, field

@@ -63,14 +63,22 @@ def rnd(seed, n, lo, hi):
 
 PATH_CASES = [
     ("full", {}),
-    ("full-agg2", {"agg_rounds": 2}),
+    ("full-agg2", {"aggregation": 2}),
     ("range", {"path": "range", "range_bins": 2048}),
-    ("range-agg4", {"path": "range", "range_bins": 1024, "agg_rounds": 4}),
+    ("range-agg4", {"path": "range", "range_bins": 1024, "aggregation": 4}),
     ("full-cw16", {"counter_bits": 16}),
-    ("full-cw16-agg2", {"counter_bits": 16, "agg_rounds": 2}),
+    ("full-cw16-agg2", {"counter_bits": 16, "aggregation": 2}),
+    ("full-cw16-hot", {"counter_bits": 16, "aggregation": 1}),
+    ("full-hot", {"aggregation": 1}),
+    ("scatter-hot", {"path": "scatter", "aggregation": 1}),
+    ("full-copies1", {"lds_copies": 1}),
+    ("full-copies2", {"lds_copies": 2}),
+    ("full-copies4-hot", {"lds_copies": 4, "aggregation": 1}),
+    ("full-copies4-agg2", {"lds_copies": 4, "aggregation": 2}),
+    ("range-copies8", {"path": "range", "range_bins": 2048, "lds_copies": 8}),
     ("range-cw16", {"path": "range", "range_bins": 2048, "counter_bits": 16}),
     ("scatter", {"path": "scatter"}),
-    ("scatter-agg1", {"path": "scatter", "agg_rounds": 1}),
+    ("scatter-agg1", {"path": "scatter", "aggregation": 1}),
 ]
 
 
@@ -123,8 +131,9 @@ def test_out_of_range_and_negative_values():
 @pytest.mark.parametrize("b", [0, 32767, 32768, 65535])
 def test_all_one_bin(b):
     x = np.full(1 << 22, b, np.int32)
-    for p, agg in [("range", 0), ("range", 2), ("scatter", 0), ("scatter", 4)]:
-        check(x, 65536, f"one{b}-{p}-agg{agg}", path=p, agg_rounds=agg)
+    for p, agg in [("range", 0), ("range", 1), ("range", 2), ("scatter", 0), ("scatter", 1),
+                   ("scatter", 4), ("full", 1), ("full", 2)]:
+        check(x, 65536, f"one{b}-{p}-agg{agg}", path=p, aggregation=agg)
 
 
 @pytest.mark.parametrize("agg", [0, 1, 4])
@@ -139,7 +148,7 @@ def test_counter16_carry_events(agg, path, bins):
                         rnd(9, 500_000, 0, bins)])
     x = x[rng.permutation(x.size)].astype(np.int32)
     check(x, bins, f"cw16-{path}-agg{agg}", path=path, counter_bits=16, groups=3,
-          agg_rounds=agg)
+          aggregation=agg)
 
 
 def test_groups_and_wg_sizes():
@@ -180,7 +189,7 @@ def test_argument_errors_on_device():
     assert lib.hist_run(plan._plan, x.data_ptr(), x.data_ptr(), 10, 1000, s) == \
         hist.HIST_ERR_INVALID_ARG  # output overlaps input
     small = hist.PlanOpts()
-    small.agg_rounds = -1
+    small.aggregation = -1
     p = __import__("ctypes").c_void_p()
     big = hist.workspace_size(65536, 1 << 24)
     assert big > 0
@@ -235,11 +244,13 @@ def full(cfg):
 
 
 FULL_CASES = [
-    (1, {}), (1, {"agg_rounds": 2}), (1, {"path": "scatter"}),
-    (2, {}), (2, {"agg_rounds": 1}), (2, {"path": "scatter"}),
-    (3, {}), (3, {"agg_rounds": 4}), (3, {"path": "scatter", "agg_rounds": 2}),
-    (4, {}), (4, {"agg_rounds": 4}), (4, {"path": "range"}),
-    (5, {}), (5, {"agg_rounds": 2}), (5, {"path": "range"}),
+    (1, {}), (1, {"aggregation": 2}), (1, {"path": "scatter"}),
+    (2, {}), (2, {"aggregation": 1}), (2, {"path": "scatter"}),
+    (3, {}), (3, {"aggregation": 4}), (3, {"path": "scatter", "aggregation": 2}),
+    (4, {}), (4, {"aggregation": 4}), (4, {"aggregation": 1}), (4, {"path": "range"}),
+    (3, {"path": "scatter", "aggregation": 1}), (3, {"aggregation": 1}),
+    (2, {"aggregation": 1}), (2, {"path": "range", "counter_bits": 32, "aggregation": 1}),
+    (5, {}), (5, {"aggregation": 2}), (5, {"path": "range"}),
 ]
 
 
