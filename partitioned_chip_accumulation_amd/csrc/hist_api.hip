@@ -72,7 +72,7 @@ hist_status_t query_device(DeviceInfo *d)
     d->device = dev;
     d->cu = prop.multiProcessorCount;
     d->xcd = std::max(1, d->cu / 32);  // gfx950: 32 CUs per XCD
-    d->lds = (uint32_t)std::min<int>(lds, (int)(kMaxLdsBins * 4));
+    d->lds = (uint32_t)std::min<int>(lds, 163840);
     return HIST_OK;
 }
 
@@ -132,13 +132,14 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
     opts.aggregation = -1;
     if (o) opts = *o;
     const DeviceInfo &d = p->dev;
-    const uint32_t lds_bins = std::min<uint32_t>(kMaxLdsBins, d.lds / 4) & ~3u;
+    const uint32_t lds_dyn = d.lds;
+    const uint32_t lds_bins = std::min<uint32_t>(kMaxLdsBins, lds_dyn / 4) & ~3u;
     p->num_bins = num_bins;
     p->max_n = max_n;
     p->xcd_map = opts.xcd_map == 0 ? 1 : (uint32_t)opts.xcd_map;
 
     const uint32_t lds_bins16 = std::min<uint32_t>(kMaxLdsBins16,
-                                                   (d.lds - (4 + pca::kEventCap) * 4) / 2) & ~255u;
+                                                   (lds_dyn - (4 + pca::kEventCap) * 4) / 2) & ~255u;
     const uint32_t cap32 = lds_bins & ~255u;
     int path = opts.path;
     if (path == HIST_PATH_AUTO) {
@@ -230,7 +231,7 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
                     if (k == 0) break;
                 }
             }
-            if ((S << kshift) * 4 > d.lds) return HIST_ERR_UNSUPPORTED;
+            if ((S << kshift) * 4 > lds_dyn) return HIST_ERR_UNSUPPORTED;
         }
         const uint32_t lds_bytes =
             cw == 32 ? (S << kshift) * 4 : S * 2 + (4 + pca::kEventCap) * 4;

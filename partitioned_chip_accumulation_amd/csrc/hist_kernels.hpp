@@ -211,7 +211,8 @@ __device__ __forceinline__ uint32_t nibbles_of(u32x4 c, uint32_t q)
            (((c.w >> sh) & 0xFu) << 12);
 }
 
-// Store one block (lane l holds bins 4l..4l+3). Whole wave, convergent.
+// Store one block (lane l holds bins 4l..4l+3) and its width code. Whole wave, convergent. The codes are laid out [block][row]
+// so that the merge reads one block's codes for 64 rows in one load.
 __device__ __forceinline__ void write_block(const Partials &P, uint64_t row, uint32_t blk, u32x4 c)
 {
     const uint32_t lane = lane_id();
@@ -221,6 +222,7 @@ __device__ __forceinline__ void write_block(const Partials &P, uint64_t row, uin
                             : __ballot(mx > 0xFu)  ? 2u
                                                    : 1u;
     uint16_t *dst = reinterpret_cast<uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
+    // plain stores: the merge reads these right after, from the caches
     for (uint32_t q = 0; q < planes; ++q) dst[q * 64 + lane] = (uint16_t)nibbles_of(c, q);
     if (lane == 0) P.width[(uint64_t)blk * P.wstride + row] = (uint8_t)(planes - 1);
 }
@@ -375,6 +377,31 @@ __device__ __forceinline__ u32x4 slice_block(const uint32_t *lds, const uint32_t
     if (b + 2 >= len) c.z = 0u;
     if (b + 3 >= len) c.w = 0u;
     return c;
+}
+
+// Flush blocks [0, nblk_slice) of an LDS slice to partial row `row`, starting
+// at block blk0: each wave takes 4 blocks at a time, their LDS reads issued
+// together. Whole workgroup.
+template <int WG, int CW>
+__device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uint32_t blk0,
+                                            const uint32_t *lds, const uint32_t *evlist,
+                                            uint32_t nev, uint32_t len, uint32_t kshift)
+{
+    const uint32_t nblk_slice = (len + kBlockBins - 1) / kBlockBins;
+    const uint32_t w = threadIdx.x >> 6;
+    constexpr uint32_t NW = WG / 64;
+    for (uint32_t k0 = w * 4; k0 < nblk_slice; k0 += NW * 4) {
+        u32x4 c[4];
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j)
+            c[j] = k0 + j < nblk_slice ? slice_block<CW>(lds, evlist, nev, k0 + j, len, kshift)
+                                       : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j) {
+            if (k0 + j >= nblk_slice) break;  // uniform
+            write_block(P, row, blk0 + k0 + j, c[j]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -546,18 +573,18 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     __syncthreads();
 
     const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : 0u;
-    const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
-    for (uint32_t k = tid >> 6; k < nblk; k += WG / 64) {
-        const u32x4 c = slice_block<CW>(lds, evlist, nev, k, len, kshift);
-        if (direct) {
+    if (direct) {
+        const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
+        for (uint32_t k = tid >> 6; k < nblk; k += WG / 64) {
+            const u32x4 c = slice_block<CW>(lds, evlist, nev, k, len, kshift);
             const uint32_t b0 = lo + k * kBlockBins + lane_id() * 4;
             if (b0 + 0 < num_bins) direct[b0 + 0] = c.x;
             if (b0 + 1 < num_bins) direct[b0 + 1] = c.y;
             if (b0 + 2 < num_bins) direct[b0 + 2] = c.z;
             if (b0 + 3 < num_bins) direct[b0 + 3] = c.w;
-        } else {
-            write_block(out, g, lo / kBlockBins + k, c);
         }
+    } else {
+        flush_slice<WG, CW>(out, g, lo / kBlockBins, lds, evlist, nev, len, kshift);
     }
 }
 
@@ -1021,9 +1048,7 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
             if (lane == 0 && t != 0u) lds_add(lds, hs.h, t);
         }
         __syncthreads();
-        const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
-        for (uint32_t k = w; k < nblk; k += WG / 64)
-            write_block(out, i + r, k, slice_block<32>(lds, nullptr, 0, k, len));
+        flush_slice<WG, 32>(out, i + r, 0, lds, nullptr, 0, len, 0);
         __syncthreads();
     }
 }

@@ -109,11 +109,12 @@ def test_lengths_and_alignment(n, offset):
 
 
 @pytest.mark.parametrize("num_bins", [1, 2, 3, 5, 255, 4095, 8191, 8193, 32767, 32768, 32769,
-                                      40959, 40960, 40961, 65535, 65537, 100_003, 262_145])
+                                      40703, 40704, 40705, 40960, 65535, 65537, 79616, 79617,
+                                      100_003, 262_145])
 def test_bin_counts(num_bins):
     x = rnd(num_bins, 300_007, -3, num_bins + 5)
     paths = ["auto", "scatter"]
-    if num_bins <= 40960:
+    if num_bins <= 79616:
         paths.append("full")
     if num_bins > 8:
         paths.append("range")
