@@ -269,3 +269,54 @@ def test_full_size_workloads(cfg, opts):
     assert bad.size == 0, f"{bad.size} bins differ, first {bad[:5].tolist()}"
     assert int(got.astype(np.int64).sum()) + dropped == w.n
     plan.close()
+
+
+# --- beyond 32-bit element indices, stress, streams -------------------------
+
+def test_more_than_2_pow_31_elements():
+    # 8 GiB of input: element offsets and tile/chunk arithmetic exceed 32 bits.
+    n = (1 << 31) + 7
+    say(f"generating {n} elements")
+    x = inputs.uniform(11, n, 1 << 20)
+    xt = torch.from_numpy(x).to(DEV)
+    for bins, opts in [(65536, {}), (200_000, {"path": "range"}), (1 << 20, {})]:
+        ref, dropped = oracle.hist(x, bins)
+        plan = hist.Plan(bins, n, device=DEV, **opts)
+        say(f"case n=2^31+7 bins={bins}: {plan.describe()}")
+        got = plan.run(xt).cpu().numpy()
+        torch.cuda.synchronize(DEV)
+        assert np.array_equal(got, ref), f"bins={bins}: {np.flatnonzero(got != ref)[:5]}"
+        assert int(got.astype(np.int64).sum()) + dropped == n
+        plan.close()
+    del xt
+
+
+def test_stress_repeated_runs_stay_exact():
+    # Integer counts leave no room for noise: any lost update or race shows as
+    # a mismatch. Alternate plans over the same input many times.
+    x = inputs.generate(4, n=(1 << 22) + 3)
+    ref, _ = oracle.hist(x, 1 << 20)
+    xt = torch.from_numpy(x).to(DEV)
+    plans = [hist.Plan(1 << 20, x.size, device=DEV, **o) for o in
+             ({}, {"aggregation": 0}, {"groups": 37}, {"path": "range"},
+              {"path": "range", "aggregation": 1})]
+    outs = []
+    for k in range(100):
+        outs.append(plans[k % len(plans)].run(xt).clone())
+    torch.cuda.synchronize(DEV)
+    for k, o in enumerate(outs):
+        assert np.array_equal(o.cpu().numpy(), ref), f"run {k} ({plans[k % len(plans)].describe()})"
+
+
+def test_runs_on_a_side_stream():
+    x = inputs.generate(2, n=1 << 22)
+    ref, _ = oracle.hist(x, 65536)
+    xt = torch.from_numpy(x).to(DEV)
+    plan = hist.Plan(65536, x.size, device=DEV)
+    s = torch.cuda.Stream(DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(s):
+        out = torch.empty(65536, dtype=torch.int32, device=DEV)
+        plan.run(xt, out)
+    s.synchronize()
+    assert np.array_equal(out.view(torch.uint32).cpu().numpy(), ref)
