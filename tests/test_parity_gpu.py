@@ -320,3 +320,27 @@ def test_runs_on_a_side_stream():
         plan.run(xt, out)
     s.synchronize()
     assert np.array_equal(out.view(torch.uint32).cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("case", ["one-range", "all-invalid", "sparse-ranges", "tiny-last-range",
+                                  "tile-edges"])
+def test_scatter_edge_cases(case):
+    bins = 1 << 20
+    if case == "one-range":        # every element in range 5: all owners share one range
+        x = rnd(1, 700_001, 5 * 32768, 6 * 32768)
+    elif case == "all-invalid":    # nothing to count: every range empty
+        x = rnd(2, 300_000, bins, bins + 1000)
+    elif case == "sparse-ranges":  # only ranges 0, 7 and 31 hold elements
+        x = np.concatenate([rnd(3, 100_000, 0, 100), rnd(4, 200_000, 7 * 32768, 8 * 32768),
+                            rnd(5, 50_000, bins - 10, bins)])
+        x = x[np.random.default_rng(6).permutation(x.size)].astype(np.int32)
+    elif case == "tiny-last-range":
+        bins = 32768 * 3 + 1       # the last range holds a single bin
+        x = rnd(7, 400_003, 0, bins)
+        x[::97] = bins - 1
+    else:                          # lengths around whole tiles of 16,384 elements
+        for n in (16384 * 5 - 1, 16384 * 5, 16384 * 5 + 1, 16384 * 5 + 7):
+            check(rnd(n, n, 0, bins), bins, f"scatter-{case}-{n}", path="scatter")
+        return
+    for agg in (0, 1):
+        check(x, bins, f"scatter-{case}-agg{agg}", path="scatter", aggregation=agg)
