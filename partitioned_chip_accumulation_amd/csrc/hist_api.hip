@@ -34,7 +34,7 @@ constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slot
 // uniform elements RANGE wins at 2^17 and 2^18 bins (71.9, 123.0 us vs 146.7,
 // 150.8 us) and SCATTER from 2^19 on (165.0 vs 221.3 us).
 constexpr uint32_t kRangeMaxR = 4;
-constexpr uint32_t kMinElemsPerGroup = 32768;
+constexpr uint32_t kMinElemsPerGroup = 4096;
 constexpr int kMaxWavesPerCU = 32;
 
 enum Phase { PH_SWEEP = 0, PH_MERGE = 1, PH_PART = 2, PH_SCAN = 3, PH_OWNER = 4, PH_SLOTS = 5 };
@@ -201,9 +201,10 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             if (G == 0) {
                 G = (uint32_t)d.cu * occ / R;
                 if (G >= (uint32_t)d.xcd) G = G / d.xcd * d.xcd;
-                // Keep the merge traffic (G * num_bins counts) a small fraction of the
-                // input (n elements), and every chunk a useful size.
-                const uint64_t by_merge = std::max<uint64_t>(1, max_n / (4ull * num_bins));
+                // Keep the merge traffic (G rows of num_bins counts, ~4 bits each for
+                // the counts a chunk of n/G elements produces) a small fraction of the
+                // input (4n bytes), and every chunk a useful size.
+                const uint64_t by_merge = std::max<uint64_t>(1, max_n / num_bins);
                 const uint64_t by_size = std::max<uint64_t>(1, max_n / kMinElemsPerGroup);
                 G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
             }
@@ -518,7 +519,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     if (p->path == HIST_PATH_FULL || p->path == HIST_PATH_RANGE) {
         // Fewer chunks for a small call: keep the merge a small fraction of the work.
         uint32_t G = p->groups;
-        const uint64_t by_merge = std::max<uint64_t>(1, n / (4ull * num_bins));
+        const uint64_t by_merge = std::max<uint64_t>(1, n / num_bins);
         const uint64_t by_size = std::max<uint64_t>(1, n / kMinElemsPerGroup);
         G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
         if (p->cw == 16) G = std::max<uint32_t>(G, ceil_div(n, kMaxElemsPerWG16));
