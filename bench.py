@@ -152,9 +152,10 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the histogram would shard by input chunk and reduce-scatter the bins; "
-              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only; there is no multi-GPU path. Sharded, each GPU "
+              "would count a contiguous chunk of the input and a reduce-scatter by bin range "
+              "would make GPU k the owner of bins [kB/g, (k+1)B/g). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.path_sweep:

@@ -58,7 +58,7 @@ def load(path: str = LIBRARY):
     """Load the library and declare its signatures. Raises LibraryMissing."""
     if not os.path.exists(path):
         raise LibraryMissing(
-            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+            f"{path} is not built; run `python -m partitioned_chip_accumulation_amd.build`")
     lib = ctypes.CDLL(path)
     vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
     P = ctypes.POINTER
