@@ -42,6 +42,15 @@ const char *kPhaseNames[HIST_MAX_PHASES] = {"sweep", "merge", "partition", "rang
                                             "owner_hist", "slot_merge"};
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// Workspace bytes of `rows` partial rows of nblk blocks: plane 0, planes 1..7
+// and the width codes, each region 256-byte aligned.
+uint64_t partial_bytes(uint32_t rows, uint32_t nblk)
+{
+    const uint64_t cells = (uint64_t)rows * nblk;
+    return align_up(cells * pca::kPlaneBytes, 256) +
+           align_up(cells * pca::kPlaneBytes * pca::kUpperPlanes, 256) + align_up(cells, 256);
+}
 uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
 
 struct DeviceInfo {
@@ -90,8 +99,8 @@ struct hist_plan {
     uint32_t range_bins = 0, ranges = 0, groups = 0;
     uint32_t cw = 32;    // LDS counter bits
     uint32_t kshift = 0; // 2^kshift interleaved LDS copies (32-bit counters)
-    uint32_t nblk = 0;   // 256-bin blocks per partial row
-    uint64_t off_width = 0;
+    uint32_t nblk = 0;       // 256-bin blocks per partial row
+    uint32_t part_rows = 0;  // partial rows the workspace holds
     // SCATTER
     uint32_t tiles = 0, owners = 0, qlog = 0;
     // workspace
@@ -245,10 +254,9 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         p->kshift = kshift;
         p->nblk = ceil_div(num_bins, pca::kBlockBins);
         uint64_t off = 0;
+        p->part_rows = G > 1 ? G : 0;
         p->off_partials = off;
-        off += G > 1 ? align_up((uint64_t)G * p->nblk * pca::kBlockBytes, 256) : 0;
-        p->off_width = off;
-        off += G > 1 ? align_up((uint64_t)G * p->nblk, 256) : 0;  // width codes [nblk][G]
+        off += partial_bytes(p->part_rows, p->nblk);
         p->need = off;
     } else {
         const uint32_t S = 1u << kScatterShift;
@@ -282,10 +290,9 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         off += align_up((uint64_t)R * 4, 256);
         p->off_segtot = off;
         off += align_up((uint64_t)R * ceil_div(T, pca::kScanSeg) * 4, 256);
+        p->part_rows = W + R;
         p->off_partials = off;
-        off += align_up((uint64_t)(W + R) * S * 4, 256);
-        p->off_width = off;
-        off += align_up((uint64_t)(W + R) * p->nblk, 256);  // width codes [nblk][W + R]
+        off += partial_bytes(p->part_rows, p->nblk);
         p->need = off;
     }
     return HIST_OK;
@@ -366,13 +373,14 @@ hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, h
     return hipGetLastError();
 }
 
-pca::Partials slot_partials(const hist_plan *p)
+pca::Partials plan_partials(const hist_plan *p)
 {
+    const uint64_t cells = (uint64_t)p->part_rows * p->nblk;
     pca::Partials P;
-    P.data = reinterpret_cast<uint8_t *>(p->ws + p->off_partials);
-    P.width = reinterpret_cast<uint8_t *>(p->ws + p->off_width);
+    P.plane0 = reinterpret_cast<uint8_t *>(p->ws + p->off_partials);
+    P.upper = P.plane0 + align_up(cells * pca::kPlaneBytes, 256);
+    P.width = P.upper + align_up(cells * pca::kPlaneBytes * pca::kUpperPlanes, 256);
     P.nblk = p->nblk;
-    P.wstride = p->owners + p->ranges;
     return P;
 }
 
@@ -389,7 +397,7 @@ hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T,
-                       p->range_bins, p->num_bins, p->owners, slot_partials(p));
+                       p->range_bins, p->num_bins, p->owners, plan_partials(p));
     return hipGetLastError();
 }
 
@@ -527,10 +535,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         a.in = in;
         a.G = G;
         a.xcds = (p->xcd_map == 1 && p->ranges > 1 && G % p->dev.xcd == 0) ? p->dev.xcd : 1;
-        a.out.data = reinterpret_cast<uint8_t *>(p->ws + p->off_partials);
-        a.out.width = reinterpret_cast<uint8_t *>(p->ws + p->off_width);
-        a.out.nblk = p->nblk;
-        a.out.wstride = p->groups;
+        a.out = plan_partials(p);
         a.direct = G > 1 ? nullptr : counts;
         // Non-temporal loads also for R > 1: the chunk's other owners still find
         // the lines in the XCD's L2 (measured: 50% L2 hits, one HBM fetch per
@@ -541,11 +546,15 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         if (e != hipSuccess) return HIST_ERR_HIP;
         if (G > 1) {
             tm.begin(PH_MERGE);
-            if (G >= 64)
-                hipLaunchKernelGGL(pca::k_merge<16>, dim3(p->nblk), dim3(1024), 0, stream, a.out, G,
+            // one batch of loads per lane covers 8 rows x 8 rounds per wave
+            if (G <= 256)
+                hipLaunchKernelGGL(pca::k_merge<4>, dim3(p->nblk), dim3(256), 0, stream, a.out, G,
+                                   num_bins, counts);
+            else if (G <= 512)
+                hipLaunchKernelGGL(pca::k_merge<8>, dim3(p->nblk), dim3(512), 0, stream, a.out, G,
                                    num_bins, counts);
             else
-                hipLaunchKernelGGL(pca::k_merge<4>, dim3(p->nblk), dim3(256), 0, stream, a.out, G,
+                hipLaunchKernelGGL(pca::k_merge<16>, dim3(p->nblk), dim3(1024), 0, stream, a.out, G,
                                    num_bins, counts);
             tm.end(PH_MERGE);
             if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
@@ -584,7 +593,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     if (e != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_SLOTS);
     hipLaunchKernelGGL(pca::k_merge_slots<16>, dim3(ceil_div(num_bins, 256)), dim3(1024), 0, stream,
-                       slot_partials(p),
+                       plan_partials(p),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges,
                        p->range_bins, num_bins, p->owners, counts);
     tm.end(PH_SLOTS);

@@ -182,59 +182,74 @@ __global__ void k_fill_zero(uint32_t *__restrict__ dst, uint64_t len)
 // Partial slices.
 //
 // A workgroup's slice is flushed in blocks of 256 bins, stored nibble-planar:
-// plane q (128 bytes) holds bits 4q..4q+3 of every count of the block, lane
-// l's four counts as the 16 bits at bytes 2l, 2l+1. A block keeps only as
+// plane q of a block (128 bytes) holds bits 4q..4q+3 of its 256 counts, bin b
+// of the block in byte b / 2 (low nibble for even b). A block keeps only as
 // many planes as its largest count needs (1, 2, 4 or 8 planes for 4, 8, 16
-// or 32 bits, chosen by wave ballots), in a fixed 1 KiB slot. Plane 0 alone
-// is a complete 4-bit block, so the merge can fetch it before it knows the
-// width and go back only for wider blocks. A histogram's partial slices hold
-// small counts for most inputs (a 65,536-bin slice of 262,144 uniform
-// elements averages 4 per bin), so this cuts the write-then-read traffic of
-// the merge by up to 8x while staying exact for any count.
+// or 32 bits, chosen by wave ballots). Plane 0 of every block of a row is
+// stored densely (row after row, 128 bytes per block), planes 1..7 in a
+// per-block slot of their own, and a byte per block records planes - 1. A
+// histogram's partial slices hold small counts for most inputs (a
+// 65,536-bin slice of 262,144 uniform elements averages 4 per bin), so plane
+// 0 alone carries nearly all of it: an eighth of the 32-bit bytes, written
+// and read as whole cache lines, while staying exact for any count.
 constexpr uint32_t kBlockBins = 256;
-constexpr uint32_t kBlockBytes = 1024;
 constexpr uint32_t kPlaneBytes = 128;
+constexpr uint32_t kUpperPlanes = 7;
+// bytes of partial storage per (row, block): plane 0, planes 1..7, width code
+constexpr uint32_t kBlockStoreBytes = kPlaneBytes * (1 + kUpperPlanes) + 1;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Partials {
-    uint8_t *data;    // [rows][nblk][8 planes][128 bytes]
-    uint8_t *width;   // [nblk][wstride]: number of planes - 1 (0, 1, 3 or 7)
+    uint8_t *plane0;  // [rows][nblk][128 bytes]
+    uint8_t *upper;   // [rows][nblk][7 planes][128 bytes]
+    uint8_t *width;   // [rows][nblk]: number of planes - 1 (0, 1, 3 or 7)
     uint32_t nblk;    // blocks per row = ceil(num_bins / 256)
-    uint32_t wstride; // rows the width table has room for
 };
 
-__device__ __forceinline__ uint32_t nibbles_of(u32x4 c, uint32_t q)
+// Store that writes through the XCD's L2 (device scope): the partial slices
+// are read by other XCDs in the next kernel, and written-through lines leave
+// nothing for the end-of-kernel L2 write-back to do.
+__device__ __forceinline__ void store_through(uint32_t *p, uint32_t v)
 {
-    const uint32_t sh = 4u * q;
-    return ((c.x >> sh) & 0xFu) | (((c.y >> sh) & 0xFu) << 4) | (((c.z >> sh) & 0xFu) << 8) |
-           (((c.w >> sh) & 0xFu) << 12);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Store one block (lane l holds bins 4l..4l+3) and its width code. Whole wave, convergent. The codes are laid out [block][row]
-// so that the merge reads one block's codes for 64 rows in one load.
-__device__ __forceinline__ void write_block(const Partials &P, uint64_t row, uint32_t blk, u32x4 c)
+// Bits 4q..4q+3 of eight counts, packed as the nibbles of one word.
+__device__ __forceinline__ uint32_t plane_word(const uint32_t (&c)[8], uint32_t q)
+{
+    uint32_t d = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d |= ((c[i] >> (4u * q)) & 0xFu) << (4 * i);
+    return d;
+}
+
+// Store a pair of blocks: lane l holds the counts of bins 8l..8l+7 of the
+// pair (lanes 0-31 the even block kb0, lanes 32-63 the odd one). blocks_left
+// is the number of blocks of the pair that exist (1 or 2). Whole wave,
+// convergent.
+__device__ __forceinline__ void write_pair(const Partials &P, uint64_t blk_even,
+                                           uint32_t blocks_left, const uint32_t (&c)[8])
 {
     const uint32_t lane = lane_id();
-    const uint32_t mx = max(max(c.x, c.y), max(c.z, c.w));
-    const uint32_t planes = __ballot(mx > 0xFFFFu) ? 8u
-                            : __ballot(mx > 0xFFu) ? 4u
-                            : __ballot(mx > 0xFu)  ? 2u
-                                                   : 1u;
-    uint16_t *dst = reinterpret_cast<uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
-    // plain stores: the merge reads these right after, from the caches
-    for (uint32_t q = 0; q < planes; ++q) dst[q * 64 + lane] = (uint16_t)nibbles_of(c, q);
-    if (lane == 0) P.width[(uint64_t)blk * P.wstride + row] = (uint8_t)(planes - 1);
-}
-
-// Add plane q of a block (lane's 16 bits, as loaded) into acc.
-__device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t q)
-{
-    const uint32_t sh = 4u * q;
-    acc.x += (v & 0xFu) << sh;
-    acc.y += ((v >> 4) & 0xFu) << sh;
-    acc.z += ((v >> 8) & 0xFu) << sh;
-    acc.w += ((v >> 12) & 0xFu) << sh;
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = max(mx, c[i]);
+    const uint32_t sh = lane & 32u;
+    const uint32_t b4 = (uint32_t)(__ballot(mx > 0xFu) >> sh);
+    const uint32_t b8 = (uint32_t)(__ballot(mx > 0xFFu) >> sh);
+    const uint32_t b16 = (uint32_t)(__ballot(mx > 0xFFFFu) >> sh);
+    const uint32_t planes = b16 ? 8u : b8 ? 4u : b4 ? 2u : 1u;
+    if ((lane >> 5) >= blocks_left) return;
+    const uint64_t blk = blk_even + (lane >> 5);
+    const uint32_t sub = lane & 31u;
+    // both blocks' plane 0 are 256 contiguous bytes
+    store_through(reinterpret_cast<uint32_t *>(P.plane0 + blk_even * kPlaneBytes) + lane,
+                  plane_word(c, 0));
+    for (uint32_t q = 1; q < planes; ++q)
+        store_through(reinterpret_cast<uint32_t *>(P.upper + (blk * kUpperPlanes + q - 1) * kPlaneBytes) + sub,
+                      plane_word(c, q));
+    if (sub == 0) P.width[blk] = (uint8_t)(planes - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -334,72 +349,88 @@ __device__ __forceinline__ void lds_count16(uint32_t *words, uint32_t *evlist, u
     }
 }
 
-// Counts of block k of a slice (lane l: bins 4l..4l+3 of the block), from
-// 32-bit or 16-bit LDS counters. Bins at or beyond len read as zero.
+// Counts of bins 8l..8l+7 (l = lane) of pair p (bins 512p..512p+511) of a
+// slice, from 32-bit or 16-bit LDS counters. Bins at or beyond len read as
+// zero; a lane whose bins all lie beyond len reads no LDS. The slice's LDS
+// holds at least round_up(len, 256) counters, so a partly valid lane stays
+// inside it.
 template <int CW>
-__device__ __forceinline__ u32x4 slice_block(const uint32_t *lds, const uint32_t *evlist,
-                                             uint32_t nev, uint32_t k, uint32_t len,
-                                             uint32_t kshift = 0)
+__device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t *evlist,
+                                            uint32_t nev, uint32_t p, uint32_t len,
+                                            uint32_t kshift, uint32_t (&c)[8])
 {
-    const uint32_t lane = lane_id();
-    u32x4 c;
+    const uint32_t b0 = p * 512u + lane_id() * 8u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = 0u;
+    if (b0 >= len) return;
     if constexpr (CW == 32) {
         if (kshift == 0) {
-            c = reinterpret_cast<const u32x4 *>(lds)[k * 64 + lane];
+            const u32x4 a = reinterpret_cast<const u32x4 *>(lds)[b0 / 4];
+            const u32x4 b = reinterpret_cast<const u32x4 *>(lds)[b0 / 4 + 1];
+            c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
+            c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
         } else {
             // K = 2^kshift interleaved copies: bin s, copy j at word s*K + j
             const uint32_t K = 1u << kshift;
-            const uint32_t b = (k * kBlockBins + lane * 4) << kshift;
-            uint32_t a[4] = {0u, 0u, 0u, 0u};
-            for (uint32_t j = 0; j < 4; ++j)
-                for (uint32_t cp = 0; cp < K; ++cp) a[j] += lds[b + j * K + cp];
-            c = u32x4{a[0], a[1], a[2], a[3]};
+            for (uint32_t i = 0; i < 8; ++i) {
+                const uint32_t *src = lds + ((b0 + i) << kshift);
+                uint32_t t = 0u;
+                for (uint32_t cp = 0; cp < K; ++cp) t += src[cp];
+                c[i] = t;
+            }
         }
     } else {
-        const u32x2 ww = reinterpret_cast<const u32x2 *>(lds)[k * 64 + lane];
-        c = u32x4{ww.x & 0xFFFFu, ww.x >> 16, ww.y & 0xFFFFu, ww.y >> 16};
-        const uint32_t w0 = k * 128 + 2 * lane;
+        const u32x4 ww = reinterpret_cast<const u32x4 *>(lds)[b0 / 8];
+        c[0] = ww.x & 0xFFFFu; c[1] = ww.x >> 16;
+        c[2] = ww.y & 0xFFFFu; c[3] = ww.y >> 16;
+        c[4] = ww.z & 0xFFFFu; c[5] = ww.z >> 16;
+        c[6] = ww.w & 0xFFFFu; c[7] = ww.w >> 16;
+        const uint32_t w0 = b0 / 2;
+        // constant indices only: a variable index would move c[] to scratch memory
         for (uint32_t e = 0; e < nev; ++e) {
             const uint32_t ent = evlist[e];
-            const uint32_t ew = ent & 0x3FFFFFFFu;
-            if (ew == w0) {
-                if (ent & kEvLoWrap) { c.x += 65536u; c.y -= 1u; }
-                if (ent & kEvCarry) c.y += 65536u;
-            } else if (ew == w0 + 1) {
-                if (ent & kEvLoWrap) { c.z += 65536u; c.w -= 1u; }
-                if (ent & kEvCarry) c.w += 65536u;
+            const uint32_t d = (ent & 0x3FFFFFFFu) - w0;
+            const uint32_t add_lo = (ent & kEvLoWrap) ? 65536u : 0u;
+            const uint32_t add_hi = ((ent & kEvCarry) ? 65536u : 0u) - ((ent & kEvLoWrap) ? 1u : 0u);
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                if (d == k) {
+                    c[2 * k] += add_lo;
+                    c[2 * k + 1] += add_hi;
+                }
             }
         }
     }
-    const uint32_t b = k * kBlockBins + lane * 4;
-    if (b + 0 >= len) c.x = 0u;
-    if (b + 1 >= len) c.y = 0u;
-    if (b + 2 >= len) c.z = 0u;
-    if (b + 3 >= len) c.w = 0u;
-    return c;
+#pragma unroll
+    for (uint32_t i = 0; i < 8; ++i)
+        if (b0 + i >= len) c[i] = 0u;
 }
 
-// Flush blocks [0, nblk_slice) of an LDS slice to partial row `row`, starting
-// at block blk0: each wave takes 4 blocks at a time, their LDS reads issued
-// together. Whole workgroup.
+// Flush an LDS slice of len bins to partial row `row`, starting at block
+// blk0 of the row: each wave takes pairs of blocks, FLUSH_BATCH pairs at a
+// time with their LDS reads issued together. Whole workgroup.
+constexpr uint32_t kFlushBatch = 4;
+
 template <int WG, int CW>
 __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uint32_t blk0,
                                             const uint32_t *lds, const uint32_t *evlist,
                                             uint32_t nev, uint32_t len, uint32_t kshift)
 {
     const uint32_t nblk_slice = (len + kBlockBins - 1) / kBlockBins;
+    const uint32_t npairs = (nblk_slice + 1) / 2;
     const uint32_t w = threadIdx.x >> 6;
     constexpr uint32_t NW = WG / 64;
-    for (uint32_t k0 = w * 4; k0 < nblk_slice; k0 += NW * 4) {
-        u32x4 c[4];
+    const uint64_t row_blk = row * P.nblk + blk0;
+    for (uint32_t p0 = w * kFlushBatch; p0 < npairs; p0 += NW * kFlushBatch) {
+        uint32_t c[kFlushBatch][8];
 #pragma unroll
-        for (uint32_t j = 0; j < 4; ++j)
-            c[j] = k0 + j < nblk_slice ? slice_block<CW>(lds, evlist, nev, k0 + j, len, kshift)
-                                       : u32x4{0u, 0u, 0u, 0u};
+        for (uint32_t j = 0; j < kFlushBatch; ++j)
+            slice_octet<CW>(lds, evlist, nev, p0 + j < npairs ? p0 + j : npairs, len, kshift, c[j]);
 #pragma unroll
-        for (uint32_t j = 0; j < 4; ++j) {
-            if (k0 + j >= nblk_slice) break;  // uniform
-            write_block(P, row, blk0 + k0 + j, c[j]);
+        for (uint32_t j = 0; j < kFlushBatch; ++j) {
+            if (p0 + j >= npairs) break;  // uniform
+            const uint32_t kb = 2 * (p0 + j);
+            write_pair(P, row_blk + kb, min(2u, nblk_slice - kb), c[j]);
         }
     }
 }
@@ -574,14 +605,14 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 
     const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : 0u;
     if (direct) {
-        const uint32_t nblk = (len + kBlockBins - 1) / kBlockBins;
-        for (uint32_t k = tid >> 6; k < nblk; k += WG / 64) {
-            const u32x4 c = slice_block<CW>(lds, evlist, nev, k, len, kshift);
-            const uint32_t b0 = lo + k * kBlockBins + lane_id() * 4;
-            if (b0 + 0 < num_bins) direct[b0 + 0] = c.x;
-            if (b0 + 1 < num_bins) direct[b0 + 1] = c.y;
-            if (b0 + 2 < num_bins) direct[b0 + 2] = c.z;
-            if (b0 + 3 < num_bins) direct[b0 + 3] = c.w;
+        const uint32_t npairs = (len + 511) / 512;
+        for (uint32_t p = tid >> 6; p < npairs; p += WG / 64) {
+            uint32_t c[8];
+            slice_octet<CW>(lds, evlist, nev, p, len, kshift, c);
+            const uint32_t b0 = lo + p * 512 + lane_id() * 8;
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i)
+                if (b0 + i < num_bins && b0 + i - lo < len) direct[b0 + i] = c[i];
         }
     } else {
         flush_slice<WG, CW>(out, g, lo / kBlockBins, lds, evlist, nev, len, kshift);
@@ -590,62 +621,111 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 
 // ---------------------------------------------------------------------------
 // Exclusive-owner merge: counts[b] = sum over rows g < rows of partial[g][b].
-// A workgroup owns one 256-bin block; lane l holds bins 4l..4l+3 and the
-// WAVES waves split the rows. A wave loads the width codes of up to 64 of its
-// rows (contiguous per block) together with plane 0 of BATCH rows, so a row
-// of small counts costs no dependent round trip; planes 1..7 are fetched
-// only for rows whose code asks for them. Wave 0 adds the waves' sums and
-// writes each of its bins once.
+//
+// A workgroup owns one 256-bin block and writes each of its bins once. Lane
+// l of wave w reads 16 bytes of a plane per row: the 32 bins of chunk
+// c = l / 8 of the block, from row slot i = l mod 8 of the wave's 8 rows of
+// a round (8 * WAVES rows per round). A batch is kMergeRounds rounds, and
+// all of its loads of one plane are issued before any is used. A lane sums
+// its rows' nibbles bytewise, then widens them into 32 counters. Plane 0
+// exists for every row; planes 1..7 are fetched only when the batch's width
+// codes (one ballot) ask for them, each lane for its own rows. Finally the 8
+// lanes of a chunk are summed with DPP, the waves through LDS.
+constexpr uint32_t kMergeRounds = 8;
+
+// acc[j] += sum over t of nibble j of v[t] (32 nibbles as 4 words), shifted
+// to plane q's weight 16^q. The nibbles are first summed bytewise, even and
+// odd nibbles apart; kMergeRounds * 15 < 256 keeps each byte exact.
+__device__ __forceinline__ void add_nibbles_bytewise(uint32_t (&acc)[32],
+                                                     const u32x4 (&v)[kMergeRounds], uint32_t q)
+{
+    u32x4 se = {0u, 0u, 0u, 0u}, so = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (uint32_t t = 0; t < kMergeRounds; ++t) {
+        se += v[t] & 0x0F0F0F0Fu;
+        so += (v[t] >> 4) & 0x0F0F0F0Fu;
+    }
+    const uint32_t e4[4] = {se.x, se.y, se.z, se.w}, o4[4] = {so.x, so.y, so.z, so.w};
+    const uint32_t sh = 4u * q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            acc[8 * k + 2 * bb] += ((e4[k] >> (8 * bb)) & 0xFFu) << sh;
+            acc[8 * k + 2 * bb + 1] += ((o4[k] >> (8 * bb)) & 0xFFu) << sh;
+        }
+    }
+}
+
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows, uint32_t num_bins,
                                                       uint32_t *__restrict__ counts)
 {
-    constexpr uint32_t BATCH = 16;
+    constexpr uint32_t RPR = 8 * WAVES;  // rows per round
     __shared__ u32x4 red[WAVES][64];
-    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t c = lane >> 3, i = lane & 7u;
     const uint32_t blk = blockIdx.x;
-    u32x4 acc = {0u, 0u, 0u, 0u};
-    const uint8_t *codes = P.width + (uint64_t)blk * P.wstride;
-    for (uint32_t base = w; base < rows; base += WAVES * 64) {
-        const uint32_t my_row = base + lane * WAVES;
-        const uint32_t my_code = my_row < rows ? codes[my_row] : 0u;
-        const uint32_t cnt = min(64u, (rows - base + WAVES - 1) / WAVES);
-        for (uint32_t i = 0; i < cnt; i += BATCH) {
-            uint32_t p0[BATCH];
+    uint32_t acc[32];
 #pragma unroll
-            for (uint32_t j = 0; j < BATCH; ++j) {
-                const uint64_t row = (uint64_t)base + (uint64_t)(i + j) * WAVES;
-                const uint16_t *src =
-                    reinterpret_cast<const uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
-                p0[j] = i + j < cnt ? src[lane] : 0u;
-            }
-            // planes beyond 0: any row of the batch that needs them
-            const uint64_t wide = __ballot(lane >= i && lane < min(i + BATCH, cnt) && my_code != 0u);
+    for (int j = 0; j < 32; ++j) acc[j] = 0u;
+    for (uint32_t base = 0; base < rows; base += kMergeRounds * RPR) {
+        // lane l: the width code of round l / 8, slot l mod 8
+        const uint32_t crow = base + (lane >> 3) * RPR + w * 8 + i;
+        const uint32_t code = crow < rows ? P.width[(uint64_t)crow * P.nblk + blk] : 0u;
+        u32x4 v[kMergeRounds];
 #pragma unroll
-            for (uint32_t j = 0; j < BATCH; ++j) add_plane(acc, p0[j], 0);
-            if (wide) {
+        for (uint32_t t = 0; t < kMergeRounds; ++t) {
+            const uint32_t row = base + t * RPR + w * 8 + i;
+            v[t] = row < rows ? *reinterpret_cast<const u32x4 *>(
+                                    P.plane0 + ((uint64_t)row * P.nblk + blk) * kPlaneBytes + 16u * c)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+        add_nibbles_bytewise(acc, v, 0);
+        // Planes beyond 0: each lane fetches them for its own rows of the batch,
+        // all rows of one plane at once (plane q of a row exists iff q < planes).
+        if (__ballot(code != 0u)) {
+            const uint32_t maxp = __ballot(code == 7u) ? 8u : __ballot(code == 3u) ? 4u : 2u;
+            uint32_t pl[kMergeRounds];
 #pragma unroll
-                for (uint32_t j = 0; j < BATCH; ++j) {
-                    if (!((wide >> (i + j)) & 1ull)) continue;
-                    const uint32_t planes = __builtin_amdgcn_readlane(my_code, (int)(i + j)) + 1u;
-                    const uint64_t row = (uint64_t)base + (uint64_t)(i + j) * WAVES;
-                    const uint16_t *src =
-                        reinterpret_cast<const uint16_t *>(P.data + (row * P.nblk + blk) * kBlockBytes);
-                    for (uint32_t q = 1; q < planes; ++q) add_plane(acc, src[q * 64 + lane], q);
+            for (uint32_t t = 0; t < kMergeRounds; ++t)
+                pl[t] = (uint32_t)__shfl((int)code, (int)(8 * t + i), 64) + 1u;
+            for (uint32_t q = 1; q < maxp; ++q) {
+#pragma unroll
+                for (uint32_t t = 0; t < kMergeRounds; ++t) {
+                    const uint64_t row = base + t * RPR + w * 8 + i;
+                    v[t] = q < pl[t] ? *reinterpret_cast<const u32x4 *>(
+                                           P.upper + ((row * P.nblk + blk) * kUpperPlanes + q - 1) *
+                                                         kPlaneBytes + 16u * c)
+                                     : u32x4{0u, 0u, 0u, 0u};
                 }
+                add_nibbles_bytewise(acc, v, q);
             }
         }
     }
-    red[w][lane] = acc;
+    // sum over the 8 lanes of each chunk: swap pairs, swap pair halves, mirror halves of 8
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        acc[j] += (uint32_t)__builtin_amdgcn_mov_dpp((int)acc[j], 0xB1, 0xF, 0xF, false);
+        acc[j] += (uint32_t)__builtin_amdgcn_mov_dpp((int)acc[j], 0x4E, 0xF, 0xF, false);
+        acc[j] += (uint32_t)__builtin_amdgcn_mov_dpp((int)acc[j], 0x141, 0xF, 0xF, false);
+    }
+    // lane 8c + i keeps bins 32c + 4i .. 32c + 4i + 3: red[w] holds the block in bin order
+    u32x4 mine = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+    for (uint32_t k = 1; k < 8; ++k)
+        if (i == k) mine = u32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
+    red[w][lane] = mine;
     __syncthreads();
     if (w == 0) {
+        u32x4 t = red[0][lane];
 #pragma unroll
-        for (int k = 1; k < WAVES; ++k) acc += red[k][lane];
+        for (int k = 1; k < WAVES; ++k) t += red[k][lane];
         const uint64_t b0 = (uint64_t)blk * kBlockBins + lane * 4u;
-        if (b0 + 0 < num_bins) counts[b0 + 0] = acc.x;
-        if (b0 + 1 < num_bins) counts[b0 + 1] = acc.y;
-        if (b0 + 2 < num_bins) counts[b0 + 2] = acc.z;
-        if (b0 + 3 < num_bins) counts[b0 + 3] = acc.w;
+        if (b0 + 0 < num_bins) counts[b0 + 0] = t.x;
+        if (b0 + 1 < num_bins) counts[b0 + 1] = t.y;
+        if (b0 + 2 < num_bins) counts[b0 + 2] = t.z;
+        if (b0 + 3 < num_bins) counts[b0 + 3] = t.w;
     }
 }
 
@@ -1053,6 +1133,16 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     }
 }
 
+// Add plane q of a block, as lane l's 16 bits (bins 4l..4l+3), into acc.
+__device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t q)
+{
+    const uint32_t sh = 4u * q;
+    acc.x += (v & 0xFu) << sh;
+    acc.y += ((v >> 4) & 0xFu) << sh;
+    acc.z += ((v >> 8) & 0xFu) << sh;
+    acc.w += ((v >> 12) & 0xFu) << sh;
+}
+
 // Phase 2b: counts[b] for the bins of one range = the sum of the slots that
 // the owners overlapping the range wrote for it (exclusive owner per bin, no
 // global atomics). A workgroup handles one 256-bin block of one range; each
@@ -1097,11 +1187,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
         for (uint32_t i = first + w; i <= last; i += WAVES) {
             const uint64_t a = (uint64_t)i * N / owners, b = (uint64_t)(i + 1) * N / owners;
             if (a >= b) continue;
-            const uint64_t row = (uint64_t)i + r;
-            const uint32_t planes = P.width[(uint64_t)lb * P.wstride + row] + 1u;
-            const uint16_t *src =
-                reinterpret_cast<const uint16_t *>(P.data + (row * P.nblk + lb) * kBlockBytes);
-            for (uint32_t qd = 0; qd < planes; ++qd) add_plane(acc, src[qd * 64 + lane], qd);
+            const uint64_t blk = ((uint64_t)i + r) * P.nblk + lb;
+            const uint32_t planes = P.width[blk] + 1u;
+            add_plane(acc, reinterpret_cast<const uint16_t *>(P.plane0 + blk * kPlaneBytes)[lane], 0);
+            for (uint32_t qd = 1; qd < planes; ++qd)
+                add_plane(acc, reinterpret_cast<const uint16_t *>(
+                                   P.upper + (blk * kUpperPlanes + qd - 1) * kPlaneBytes)[lane], qd);
         }
     }
     red[w][lane] = acc;
