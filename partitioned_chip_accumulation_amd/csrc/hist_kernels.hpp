@@ -232,13 +232,14 @@ __device__ __forceinline__ void write_pair(const Partials &P, uint64_t blk_even,
                                            uint32_t blocks_left, const uint32_t (&c)[8])
 {
     const uint32_t lane = lane_id();
-    uint32_t mx = 0;
+    // a count needs more than 4k bits iff the OR of the counts does
+    uint32_t any = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx = max(mx, c[i]);
+    for (int i = 0; i < 8; ++i) any |= c[i];
     const uint32_t sh = lane & 32u;
-    const uint32_t b4 = (uint32_t)(__ballot(mx > 0xFu) >> sh);
-    const uint32_t b8 = (uint32_t)(__ballot(mx > 0xFFu) >> sh);
-    const uint32_t b16 = (uint32_t)(__ballot(mx > 0xFFFFu) >> sh);
+    const uint32_t b4 = (uint32_t)(__ballot(any > 0xFu) >> sh);
+    const uint32_t b8 = (uint32_t)(__ballot(any > 0xFFu) >> sh);
+    const uint32_t b16 = (uint32_t)(__ballot(any > 0xFFFFu) >> sh);
     const uint32_t planes = b16 ? 8u : b8 ? 4u : b4 ? 2u : 1u;
     if ((lane >> 5) >= blocks_left) return;
     const uint64_t blk = blk_even + (lane >> 5);
@@ -249,6 +250,38 @@ __device__ __forceinline__ void write_pair(const Partials &P, uint64_t blk_even,
     for (uint32_t q = 1; q < planes; ++q)
         store_through(reinterpret_cast<uint32_t *>(P.upper + (blk * kUpperPlanes + q - 1) * kPlaneBytes) + sub,
                       plane_word(c, q));
+    if (sub == 0) P.width[blk] = (uint8_t)(planes - 1);
+}
+
+// Plane q of eight 16-bit counts held two per word (count 2k in the low half
+// of word k, count 2k+1 in its high half), as one word of nibbles.
+__device__ __forceinline__ uint32_t plane_word16(u32x4 w, uint32_t q)
+{
+    const uint32_t sh = 4u * q;
+    // y: nibbles of counts 0, 2, 1, 3 at bits 0, 8, 16, 24 (z likewise for 4..7)
+    const uint32_t y = ((w.x >> sh) & 0x000F000Fu) | (((w.y >> sh) & 0x000F000Fu) << 8);
+    const uint32_t z = ((w.z >> sh) & 0x000F000Fu) | (((w.w >> sh) & 0x000F000Fu) << 8);
+    return ((y | (y >> 12)) & 0xFFFFu) | ((z | (z >> 12)) << 16);
+}
+
+// write_pair for counts that are exact in 16 bits, read straight from packed
+// LDS words (lane l: bins 8l..8l+7 of the pair as four words). Both blocks of
+// the pair exist. Whole wave, convergent.
+__device__ __forceinline__ void write_pair16(const Partials &P, uint64_t blk_even, u32x4 w)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t any = w.x | w.y | w.z | w.w;
+    const uint32_t sh = lane & 32u;
+    const uint32_t b4 = (uint32_t)(__ballot((any & 0xFFF0FFF0u) != 0u) >> sh);
+    const uint32_t b8 = (uint32_t)(__ballot((any & 0xFF00FF00u) != 0u) >> sh);
+    const uint32_t planes = b8 ? 4u : b4 ? 2u : 1u;
+    const uint64_t blk = blk_even + (lane >> 5);
+    const uint32_t sub = lane & 31u;
+    store_through(reinterpret_cast<uint32_t *>(P.plane0 + blk_even * kPlaneBytes) + lane,
+                  plane_word16(w, 0));
+    for (uint32_t q = 1; q < planes; ++q)
+        store_through(reinterpret_cast<uint32_t *>(P.upper + (blk * kUpperPlanes + q - 1) * kPlaneBytes) + sub,
+                      plane_word16(w, q));
     if (sub == 0) P.width[blk] = (uint8_t)(planes - 1);
 }
 
@@ -421,6 +454,30 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
     const uint32_t w = threadIdx.x >> 6;
     constexpr uint32_t NW = WG / 64;
     const uint64_t row_blk = row * P.nblk + blk0;
+    if constexpr (CW == 16) {
+        // No carry events: every count is its 16-bit half. Whole pairs inside
+        // the slice go straight from the packed LDS words.
+        if (nev == 0) {
+            const uint32_t full = len / 512;
+            for (uint32_t p0 = w * kFlushBatch; p0 < full; p0 += NW * kFlushBatch) {
+                u32x4 ww[kFlushBatch];
+#pragma unroll
+                for (uint32_t j = 0; j < kFlushBatch; ++j)
+                    ww[j] = reinterpret_cast<const u32x4 *>(lds)[min(p0 + j, full - 1) * 64 + lane_id()];
+#pragma unroll
+                for (uint32_t j = 0; j < kFlushBatch; ++j) {
+                    if (p0 + j >= full) break;  // uniform
+                    write_pair16(P, row_blk + 2 * (p0 + j), ww[j]);
+                }
+            }
+            if (full < npairs && w == (full / kFlushBatch) % NW) {
+                uint32_t c[8];
+                slice_octet<CW>(lds, evlist, nev, full, len, kshift, c);
+                write_pair(P, row_blk + 2 * full, min(2u, nblk_slice - 2 * full), c);
+            }
+            return;
+        }
+    }
     for (uint32_t p0 = w * kFlushBatch; p0 < npairs; p0 += NW * kFlushBatch) {
         uint32_t c[kFlushBatch][8];
 #pragma unroll
