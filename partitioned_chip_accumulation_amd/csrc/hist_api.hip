@@ -388,7 +388,7 @@ template <int AGG>
 hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
 {
     auto k = pca::k_bucket_hist<kScatterWG, 4, AGG>;
-    const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + (5 * 64 + 4) * 4;
+    const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + 4 * 4;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(p->owners), dim3(kScatterWG), bytes, s,
@@ -592,7 +592,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     tm.end(PH_OWNER);
     if (e != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_SLOTS);
-    hipLaunchKernelGGL(pca::k_merge_slots<16>, dim3(ceil_div(num_bins, 256)), dim3(1024), 0, stream,
+    hipLaunchKernelGGL(pca::k_merge_slots<4>, dim3(ceil_div(num_bins, 256)), dim3(256), 0, stream,
                        plan_partials(p),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges,
                        p->range_bins, num_bins, p->owners, counts);

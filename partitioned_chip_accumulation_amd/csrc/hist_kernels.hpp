@@ -1014,6 +1014,31 @@ __device__ __forceinline__ uint32_t wave_find_last_le(const uint32_t *__restrict
     return lo;
 }
 
+// Count the slots of one staged vector (8 uint16 slots as 4 words) whose
+// index e lies in [first, last), through the wave's hot slot when AGG == 1.
+template <int AGG>
+__device__ __forceinline__ void count_slots(uint32_t *lds, HotSlot &hs, const uint32_t (&words)[4],
+                                            uint32_t first, uint32_t last)
+{
+    if (AGG == 1 && hs.h != kNoSlot) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t s = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+            const bool ok = (uint32_t)e >= first && (uint32_t)e < last;
+            const bool m = ok && s == hs.h;
+            hs.c += m ? 1u : 0u;
+            lds_count<0>(lds, s, ok && !m);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t s = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+            const bool ok = (uint32_t)e >= first && (uint32_t)e < last;
+            lds_count<AGG == 1 ? 0 : AGG>(lds, s, ok);
+        }
+    }
+}
+
 // Phase 2: owner workgroups build LDS histograms from the routed slots.
 //
 // All ranges' elements, concatenated in range order, are split evenly over
@@ -1024,11 +1049,14 @@ __device__ __forceinline__ uint32_t wave_find_last_le(const uint32_t *__restrict
 // and writes the slice to partial slot i + r (i + r is distinct for every
 // (owner, range) pair that occurs, because both grow along the
 // concatenation). Inside one range the elements are the tiles' runs in tile
-// order. The workgroup takes 64 tiles at a time: wave 0 lays their runs end
-// to end (a wave scan of their 16-byte vector counts) into LDS, one batch
-// ahead of use, and all threads then split the batch's vectors evenly,
-// finding each vector's run with a 6-step search of the scanned counts, so
-// short runs, long runs and ragged run boundaries all keep every lane busy.
+// order. Each wave works on its own: it takes groups of RPW consecutive
+// tiles (groups w, w + NW, w + 2NW, ... of the owner's span), reads the
+// group's run metadata with one lane per tile, numbers the runs' 16-byte
+// vectors end to end, and finds a vector's run by compares against prefix
+// sums held in scalar registers. With no workgroup barrier until the slice
+// is flushed, the waves drift apart and one wave's loads overlap the
+// others' counting. The runs of one range are about equally long for
+// shuffled inputs, so the waves stay balanced.
 template <int WG, int UNROLL, int AGG>
 __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint16_t *__restrict__ stage, uint32_t stage_cap, const uint32_t *__restrict__ tcnt,
@@ -1039,13 +1067,10 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
     uint64_t *bs = reinterpret_cast<uint64_t *>(lds + range_bins);  // [ranges + 1]
-    uint32_t *mP = reinterpret_cast<uint32_t *>(bs + ranges + 1);   // inclusive vector prefix
-    uint32_t *mE = mP + 64;                                          // exclusive prefix
-    uint32_t *mV = mE + 64;                                          // first vector of the run
-    uint32_t *mS = mV + 64;                                          // elements skipped in it
-    uint32_t *mC = mS + 64;                                          // run elements used
-    uint32_t *misc = mC + 64;                                        // [0] ta [1] tb [2] total
+    uint32_t *misc = reinterpret_cast<uint32_t *>(bs + ranges + 1);  // [0] ta [1] tb
     const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    constexpr uint32_t NW = WG / 64;  // waves
+    constexpr uint32_t RPW = 4;       // tiles (runs) per wave group
 
     range_starts(totals, ranges, bs);
     __syncthreads();
@@ -1087,62 +1112,55 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
         const uint32_t ta = misc[0], tb = misc[1];
         HotSlot hs;
 
-        // wave 0's registers hold the metadata of the batch after the current one
-        uint32_t nc = 0, nq = 0, nb = 0;
-        if (w == 0 && ta + lane < tb) {
-            nc = rc[ta + lane];
-            nq = rpre[ta + lane];
-            nb = rbase[ta + lane];
-        }
-        for (uint32_t t0 = ta; t0 < tb; t0 += 64) {
-            if (w == 0) {
-                const uint32_t t = t0 + lane;
-                uint32_t vlo = 0, nv = 0, skip = 0, used = 0;
-                if (t < tb && nc != 0) {
-                    const uint32_t lo_e = max(p0, nq) - nq;
-                    const uint32_t hi_e = min(p1, nq + nc) - nq;
-                    if (hi_e > lo_e) {
-                        const uint64_t g_lo = (uint64_t)t * stage_cap + nb + lo_e;
-                        const uint64_t g_hi = g_lo + (hi_e - lo_e);
-                        vlo = (uint32_t)(g_lo >> 3);
-                        nv = (uint32_t)(((g_hi + 7) >> 3) - (g_lo >> 3));
-                        skip = (uint32_t)(g_lo & 7u);
-                        used = hi_e - lo_e;
-                    }
-                }
-                const uint32_t P = wave_inclusive_scan(nv);
-                mP[lane] = P;
-                mE[lane] = P - nv;
-                mV[lane] = vlo;
-                mS[lane] = skip;
-                mC[lane] = used;
-                if (lane == 63) misc[2] = P;
-                nc = nq = nb = 0;
-                if (t0 + 64 + lane < tb) {
-                    nc = rc[t0 + 64 + lane];
-                    nq = rpre[t0 + 64 + lane];
-                    nb = rbase[t0 + 64 + lane];
+        for (uint32_t g0 = ta + w * RPW; g0 < tb; g0 += NW * RPW) {
+            // lane m < RPW: the run of tile g0 + m, clipped to [p0, p1)
+            uint32_t vlo = 0, nv = 0, skip = 0, used = 0;
+            const uint32_t t = g0 + lane;
+            if (lane < RPW && t < tb) {
+                const uint32_t c = rc[t], q = rpre[t], bse = rbase[t];
+                const uint32_t lo_e = max(p0, q) - q;
+                const uint32_t hi_e = min(p1, q + c) - q;
+                if (c != 0u && hi_e > lo_e) {
+                    const uint64_t g_lo = (uint64_t)t * stage_cap + bse + lo_e;
+                    const uint64_t g_hi = g_lo + (hi_e - lo_e);
+                    vlo = (uint32_t)(g_lo >> 3);
+                    nv = (uint32_t)(((g_hi + 7) >> 3) - (g_lo >> 3));
+                    skip = (uint32_t)(g_lo & 7u);
+                    used = hi_e - lo_e;
                 }
             }
-            __syncthreads();
-            const uint32_t total = misc[2];
-            for (uint32_t ub = 0; ub < total; ub += WG * UNROLL) {
+            uint32_t pre[RPW + 1], run_v[RPW], run_s[RPW], run_u[RPW];
+            pre[0] = 0u;
+#pragma unroll
+            for (uint32_t m = 0; m < RPW; ++m) {
+                pre[m + 1] = pre[m] + (uint32_t)__builtin_amdgcn_readlane((int)nv, (int)m);
+                run_v[m] = (uint32_t)__builtin_amdgcn_readlane((int)vlo, (int)m);
+                run_s[m] = (uint32_t)__builtin_amdgcn_readlane((int)skip, (int)m);
+                run_u[m] = (uint32_t)__builtin_amdgcn_readlane((int)used, (int)m);
+            }
+            const uint32_t total = pre[RPW];
+            for (uint32_t ub = 0; ub < total; ub += 64 * UNROLL) {
                 i32x4 qv[UNROLL];
                 uint32_t first[UNROLL], last[UNROLL];
 #pragma unroll
                 for (int k = 0; k < UNROLL; ++k) {
-                    const uint32_t u = ub + k * WG + tid;
+                    const uint32_t u = ub + k * 64 + lane;
                     const bool ok = u < total;
-                    uint32_t j = 0;
+                    // the last run m with pre[m] <= u (empty runs are passed over)
+                    uint32_t base = pre[0], vv = run_v[0], js = run_s[0], jc = run_u[0];
 #pragma unroll
-                    for (uint32_t step = 32; step >= 1; step >>= 1)
-                        if (mP[j + step - 1] <= u) j += step;
-                    const uint32_t d = u - mE[j];
+                    for (uint32_t m = 1; m < RPW; ++m) {
+                        const bool after = u >= pre[m];
+                        base = after ? pre[m] : base;
+                        vv = after ? run_v[m] : vv;
+                        js = after ? run_s[m] : js;
+                        jc = after ? run_u[m] : jc;
+                    }
+                    const uint32_t d = u - base;
                     const uint32_t k8 = d * 8u;  // run element of vector element e is k8 + e - skip
-                    const uint32_t js = mS[j], jc = mC[j];
                     first[k] = ok ? (k8 < js ? js - k8 : 0u) : 8u;
                     last[k] = ok ? min(8u, js + jc - k8) : 0u;
-                    qv[k] = ok ? stage_vec[(uint64_t)mV[j] + d] : i32x4{0, 0, 0, 0};
+                    qv[k] = ok ? stage_vec[(uint64_t)vv + d] : i32x4{0, 0, 0, 0};
                 }
 #pragma unroll
                 for (int k = 0; k < UNROLL; ++k) {
@@ -1152,33 +1170,14 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                         uint32_t nxt;
                         if (hot_should_switch(hs, words[0] & 0xFFFFu, first[k] == 0u && last[k] > 0u,
                                               &nxt)) {
-                            const uint32_t t = hot_take(hs);
-                            if (lane == 0 && t != 0u) lds_add(lds, hs.h, t);
+                            const uint32_t tk = hot_take(hs);
+                            if (lane == 0 && tk != 0u) lds_add(lds, hs.h, tk);
                             hs.h = nxt;
                         }
                     }
-                    if (AGG == 1 && hs.h != kNoSlot) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const uint32_t s =
-                                (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
-                            const bool ok = (uint32_t)e >= first[k] && (uint32_t)e < last[k];
-                            const bool m = ok && s == hs.h;
-                            hs.c += m ? 1u : 0u;
-                            lds_count<0>(lds, s, ok && !m);
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const uint32_t s =
-                                (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
-                            const bool ok = (uint32_t)e >= first[k] && (uint32_t)e < last[k];
-                            lds_count<AGG == 1 ? 0 : AGG>(lds, s, ok);
-                        }
-                    }
+                    count_slots<AGG>(lds, hs, words, first[k], last[k]);
                 }
             }
-            __syncthreads();  // the batch metadata is rewritten next
         }
         {
             const uint32_t t = hot_take(hs);
@@ -1203,13 +1202,16 @@ __device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t q)
 // Phase 2b: counts[b] for the bins of one range = the sum of the slots that
 // the owners overlapping the range wrote for it (exclusive owner per bin, no
 // global atomics). A workgroup handles one 256-bin block of one range; each
-// slot's block is read at its own width. Empty ranges give zeros.
+// wave takes a few owner slots at a time, loading their width codes and
+// plane 0 together and then only the planes the codes ask for. Empty ranges
+// give zeros.
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint32_t *__restrict__ totals,
                                                             uint32_t ranges, uint32_t range_bins,
                                                             uint32_t num_bins, uint32_t owners,
                                                             uint32_t *__restrict__ counts)
 {
+    constexpr uint32_t OB = 8;  // owner slots per wave step
     __shared__ u32x4 red[WAVES][64];
     __shared__ uint64_t se[3];
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
@@ -1241,15 +1243,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
     u32x4 acc = {0u, 0u, 0u, 0u};
     if (re > rb) {
         const uint32_t first = owner_of(rb, N, owners), last = owner_of(re - 1, N, owners);
-        for (uint32_t i = first + w; i <= last; i += WAVES) {
-            const uint64_t a = (uint64_t)i * N / owners, b = (uint64_t)(i + 1) * N / owners;
-            if (a >= b) continue;
-            const uint64_t blk = ((uint64_t)i + r) * P.nblk + lb;
-            const uint32_t planes = P.width[blk] + 1u;
-            add_plane(acc, reinterpret_cast<const uint16_t *>(P.plane0 + blk * kPlaneBytes)[lane], 0);
-            for (uint32_t qd = 1; qd < planes; ++qd)
-                add_plane(acc, reinterpret_cast<const uint16_t *>(
-                                   P.upper + (blk * kUpperPlanes + qd - 1) * kPlaneBytes)[lane], qd);
+        // each wave takes OB owners at a time, their loads issued together
+        for (uint32_t i0 = first + w; i0 <= last; i0 += WAVES * OB) {
+            uint32_t code[OB], v[OB];
+            uint64_t blk[OB];
+#pragma unroll
+            for (uint32_t o = 0; o < OB; ++o) {
+                const uint32_t i = i0 + o * WAVES;
+                // an owner that took no element wrote no slot
+                const bool has = i <= last && (uint64_t)i * N / owners < (uint64_t)(i + 1) * N / owners;
+                blk[o] = ((uint64_t)i + r) * P.nblk + lb;
+                code[o] = has ? P.width[blk[o]] : 0u;
+                v[o] = has ? reinterpret_cast<const uint16_t *>(P.plane0 + blk[o] * kPlaneBytes)[lane] : 0u;
+            }
+            uint32_t maxc = 0;
+#pragma unroll
+            for (uint32_t o = 0; o < OB; ++o) {
+                add_plane(acc, v[o], 0);
+                maxc = max(maxc, code[o]);
+            }
+            for (uint32_t q = 1; q <= maxc; ++q) {
+#pragma unroll
+                for (uint32_t o = 0; o < OB; ++o)
+                    v[o] = q <= code[o] ? reinterpret_cast<const uint16_t *>(
+                                              P.upper + (blk[o] * kUpperPlanes + q - 1) * kPlaneBytes)[lane]
+                                        : 0u;
+#pragma unroll
+                for (uint32_t o = 0; o < OB; ++o) add_plane(acc, v[o], q);
+            }
         }
     }
     red[w][lane] = acc;
