@@ -26,8 +26,9 @@
  *   - Values outside [0, num_bins) (including negatives) name no bin and are
  *     skipped. The page's kernel requires the bin count to equal the
  *     cluster's capacity exactly (same section); here any num_bins >= 1 works.
- *   - counts is OVERWRITTEN, not accumulated into (the page adds into global
- *     bins with atomics); a repeated call gives the same result.
+ *   - hist_run OVERWRITES counts (the page adds into global bins with
+ *     atomics); a repeated call gives the same result. hist_run_accumulate
+ *     adds instead.
  *   - Counters are uint32; n must be < 2^32 so no counter can wrap.
  *
  * Memory and ownership
@@ -136,6 +137,16 @@ hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t m
  * The call is asynchronous; counts is complete when the stream reaches it. */
 hist_status_t hist_run(hist_plan_t *plan, uint32_t *counts, const int32_t *input, uint64_t n,
                        uint32_t num_bins, hipStream_t stream);
+
+/* Like hist_run, but adds the histogram into counts instead of overwriting it:
+ * counts[b] += #{ i in [0, n) : input[i] == b }, modulo 2^32. This is the
+ * page's own flush semantics (each block adds its slice into the global
+ * bins, section "The cluster histogram"), and it lets an input be fed in
+ * chunks: successive calls on the pieces of an input leave the histogram of
+ * the whole. Each bin is still read and written by one exclusive owner, with
+ * no atomics. n == 0 queues nothing. Arguments and errors as for hist_run. */
+hist_status_t hist_run_accumulate(hist_plan_t *plan, uint32_t *counts, const int32_t *input,
+                                  uint64_t n, uint32_t num_bins, hipStream_t stream);
 
 /* Fill *info. */
 hist_status_t hist_plan_info(const hist_plan_t *plan, hist_plan_info_t *info);

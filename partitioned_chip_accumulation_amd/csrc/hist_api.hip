@@ -318,6 +318,7 @@ struct SweepArgs {
     uint32_t G, xcds;
     pca::Partials out;
     uint32_t *direct;
+    uint32_t accumulate;
 };
 
 template <int WG, int AGG, int CW>
@@ -332,7 +333,7 @@ hipError_t launch_sweep_t(const hist_plan *p, const SweepArgs &a, hipStream_t s)
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, a.in, p->num_bins,
                        p->range_bins, p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, a.out,
-                       a.direct);
+                       a.direct, a.accumulate);
     return hipGetLastError();
 }
 
@@ -492,8 +493,10 @@ hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t m
     return HIST_OK;
 }
 
-hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
-                       uint32_t num_bins, hipStream_t stream)
+namespace {
+
+hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
+                       uint32_t num_bins, hipStream_t stream, uint32_t accumulate)
 {
     if (!p || !counts) return HIST_ERR_INVALID_ARG;
     if (n > 0 && !input) return HIST_ERR_INVALID_ARG;
@@ -510,6 +513,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     PhaseTimer tm(p, stream);
     hipError_t e = hipSuccess;
     if (n == 0) {
+        if (accumulate) return HIST_OK;  // nothing to add
         tm.begin(PH_SWEEP);
         hipLaunchKernelGGL(pca::k_fill_zero, dim3(std::max<uint32_t>(1, std::min<uint32_t>(1024, ceil_div(num_bins, 256)))),
                            dim3(256), 0, stream, counts, (uint64_t)num_bins);
@@ -537,6 +541,7 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         a.xcds = (p->xcd_map == 1 && p->ranges > 1 && G % p->dev.xcd == 0) ? p->dev.xcd : 1;
         a.out = plan_partials(p);
         a.direct = G > 1 ? nullptr : counts;
+        a.accumulate = accumulate;
         // Non-temporal loads also for R > 1: the chunk's other owners still find
         // the lines in the XCD's L2 (measured: 50% L2 hits, one HBM fetch per
         // element) and the stream evicts less useful data.
@@ -549,13 +554,13 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
             // one batch of loads per lane covers 8 rows x 8 rounds per wave
             if (G <= 256)
                 hipLaunchKernelGGL(pca::k_merge<4>, dim3(p->nblk), dim3(256), 0, stream, a.out, G,
-                                   num_bins, counts);
+                                   num_bins, counts, accumulate);
             else if (G <= 512)
                 hipLaunchKernelGGL(pca::k_merge<8>, dim3(p->nblk), dim3(512), 0, stream, a.out, G,
-                                   num_bins, counts);
+                                   num_bins, counts, accumulate);
             else
                 hipLaunchKernelGGL(pca::k_merge<16>, dim3(p->nblk), dim3(1024), 0, stream, a.out, G,
-                                   num_bins, counts);
+                                   num_bins, counts, accumulate);
             tm.end(PH_MERGE);
             if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
         }
@@ -595,10 +600,24 @@ hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     hipLaunchKernelGGL(pca::k_merge_slots<4>, dim3(ceil_div(num_bins, 256)), dim3(256), 0, stream,
                        plan_partials(p),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges,
-                       p->range_bins, num_bins, p->owners, counts);
+                       p->range_bins, num_bins, p->owners, counts, accumulate);
     tm.end(PH_SLOTS);
     if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
     return HIST_OK;
+}
+
+}  // namespace
+
+hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
+                       uint32_t num_bins, hipStream_t stream)
+{
+    return run_impl(p, counts, input, n, num_bins, stream, 0u);
+}
+
+hist_status_t hist_run_accumulate(hist_plan_t *p, uint32_t *counts, const int32_t *input,
+                                  uint64_t n, uint32_t num_bins, hipStream_t stream)
+{
+    return run_impl(p, counts, input, n, num_bins, stream, 1u);
 }
 
 hist_status_t hist_plan_info(const hist_plan_t *p, hist_plan_info_t *info)

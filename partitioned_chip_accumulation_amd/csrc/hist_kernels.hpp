@@ -511,12 +511,13 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
 // Chunk g is body vectors [g * nvec / groups, (g + 1) * nvec / groups); the
 // head scalars belong to chunk 0 and the tail scalars to the last chunk.
 // The slice goes to partial row g in 256-bin blocks (range_bins is a multiple
-// of 256), or straight into direct[] (the output) when there is one chunk.
+// of 256), or straight into direct[] (the output) when there is one chunk;
+// accumulate != 0 adds to direct[] instead of overwriting it.
 template <int WG, int UNROLL, int AGG, int CW>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
                                               uint32_t kshift, Partials out,
-                                              uint32_t *__restrict__ direct)
+                                              uint32_t *__restrict__ direct, uint32_t accumulate)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
@@ -669,11 +670,23 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
             const uint32_t b0 = lo + p * 512 + lane_id() * 8;
 #pragma unroll
             for (uint32_t i = 0; i < 8; ++i)
-                if (b0 + i < num_bins && b0 + i - lo < len) direct[b0 + i] = c[i];
+                if (b0 + i < num_bins && b0 + i - lo < len)
+                    direct[b0 + i] = (accumulate ? direct[b0 + i] : 0u) + c[i];
         }
     } else {
         flush_slice<WG, CW>(out, g, lo / kBlockBins, lds, evlist, nev, len, kshift);
     }
+}
+
+// The exclusive owner's write of bins b0..b0+3 (those below num_bins):
+// counts = t, or counts += t (mod 2^32) when accumulate != 0.
+__device__ __forceinline__ void store_counts(uint32_t *__restrict__ counts, uint64_t b0,
+                                             uint32_t num_bins, u32x4 t, uint32_t accumulate)
+{
+    const uint32_t v[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (b0 + k < num_bins) counts[b0 + k] = (accumulate ? counts[b0 + k] : 0u) + v[k];
 }
 
 // ---------------------------------------------------------------------------
@@ -716,7 +729,8 @@ __device__ __forceinline__ void add_nibbles_bytewise(uint32_t (&acc)[32],
 
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows, uint32_t num_bins,
-                                                      uint32_t *__restrict__ counts)
+                                                      uint32_t *__restrict__ counts,
+                                                      uint32_t accumulate)
 {
     constexpr uint32_t RPR = 8 * WAVES;  // rows per round
     __shared__ u32x4 red[WAVES][64];
@@ -778,11 +792,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows,
         u32x4 t = red[0][lane];
 #pragma unroll
         for (int k = 1; k < WAVES; ++k) t += red[k][lane];
-        const uint64_t b0 = (uint64_t)blk * kBlockBins + lane * 4u;
-        if (b0 + 0 < num_bins) counts[b0 + 0] = t.x;
-        if (b0 + 1 < num_bins) counts[b0 + 1] = t.y;
-        if (b0 + 2 < num_bins) counts[b0 + 2] = t.z;
-        if (b0 + 3 < num_bins) counts[b0 + 3] = t.w;
+        store_counts(counts, (uint64_t)blk * kBlockBins + lane * 4u, num_bins, t, accumulate);
     }
 }
 
@@ -1209,7 +1219,8 @@ template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint32_t *__restrict__ totals,
                                                             uint32_t ranges, uint32_t range_bins,
                                                             uint32_t num_bins, uint32_t owners,
-                                                            uint32_t *__restrict__ counts)
+                                                            uint32_t *__restrict__ counts,
+                                                            uint32_t accumulate)
 {
     constexpr uint32_t OB = 8;  // owner slots per wave step
     __shared__ u32x4 red[WAVES][64];
@@ -1278,11 +1289,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
     if (w == 0) {
 #pragma unroll
         for (int k = 1; k < WAVES; ++k) acc += red[k][lane];
-        const uint64_t b = (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u;
-        if (b + 0 < num_bins) counts[b + 0] = acc.x;
-        if (b + 1 < num_bins) counts[b + 1] = acc.y;
-        if (b + 2 < num_bins) counts[b + 2] = acc.z;
-        if (b + 3 < num_bins) counts[b + 3] = acc.w;
+        store_counts(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, acc,
+                     accumulate);
     }
 }
 

@@ -67,6 +67,7 @@ def load(path: str = LIBRARY):
         "hist_workspace_size": (i32, [u32, u64, P(PlanOpts), P(u64)]),
         "hist_plan_create": (i32, [P(vp), u32, u64, P(PlanOpts), vp, u64]),
         "hist_run": (i32, [vp, vp, vp, u64, u32, vp]),
+        "hist_run_accumulate": (i32, [vp, vp, vp, u64, u32, vp]),
         "hist_plan_info": (i32, [vp, P(PlanInfo)]),
         "hist_plan_describe": (i32, [vp, ctypes.c_char_p, u64]),
         "hist_plan_timing_enable": (i32, [vp, u32]),
@@ -154,6 +155,7 @@ class Plan:
         self._plan = ctypes.c_void_p()
         lib = library()
         self._run = lib.hist_run
+        self._run_acc = lib.hist_run_accumulate
         o = _opts(**opts)
         with torch.cuda.device(self.device):
             n = ctypes.c_uint64(0)
@@ -166,26 +168,32 @@ class Plan:
                                         self.workspace.data_ptr() if n.value else None,
                                         int(n.value)), "hist_plan_create")
 
-    def run(self, input: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-        """Histogram of an int32 CUDA tensor into a uint32 tensor of num_bins."""
+    def run(self, input: torch.Tensor, out: torch.Tensor | None = None,
+            accumulate: bool = False) -> torch.Tensor:
+        """Histogram of an int32 CUDA tensor into a uint32 tensor of num_bins.
+        accumulate=True adds into ``out`` (required then) instead of
+        overwriting it: out[b] += #{i : input[i] == b}, modulo 2^32."""
         if input.dtype != torch.int32 or input.device != self.device:
             raise ValueError("input must be an int32 tensor on the plan's device")
         if not input.is_contiguous():
             raise ValueError("input must be contiguous")
         if out is None:
+            if accumulate:
+                raise ValueError("accumulate=True needs out")
             out = torch.empty(self.num_bins, dtype=torch.int32, device=self.device)
         if out.device != self.device or out.numel() != self.num_bins or \
                 out.element_size() != 4 or not out.is_contiguous():
             raise ValueError("out must be a contiguous 4-byte tensor of num_bins on the device")
         n = input.numel()
+        fn = self._run_acc if accumulate else self._run
         if torch.cuda.current_device() == self.device.index:
-            st = self._run(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
-                           self.num_bins, torch.cuda.current_stream().cuda_stream)
+            st = fn(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
+                    self.num_bins, torch.cuda.current_stream().cuda_stream)
         else:
             with torch.cuda.device(self.device):
-                st = self._run(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
-                               self.num_bins, torch.cuda.current_stream().cuda_stream)
-        _check(st, "hist_run")
+                st = fn(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
+                        self.num_bins, torch.cuda.current_stream().cuda_stream)
+        _check(st, "hist_run_accumulate" if accumulate else "hist_run")
         return out.view(torch.uint32) if out.dtype == torch.int32 else out
 
     __call__ = run
@@ -228,8 +236,10 @@ class Plan:
 _cache: dict = {}
 
 
-def run(input: torch.Tensor, num_bins: int, **opts) -> torch.Tensor:
-    """One-call histogram with a cached plan (max_n rounded up to a power of two)."""
+def run(input: torch.Tensor, num_bins: int, out: torch.Tensor | None = None,
+        accumulate: bool = False, **opts) -> torch.Tensor:
+    """One-call histogram with a cached plan (max_n rounded up to a power of
+    two). accumulate=True adds into ``out``."""
     n = max(1, input.numel())
     max_n = 1 << (n - 1).bit_length()
     max_n = min(max_n, 2**32 - 1)
@@ -237,7 +247,7 @@ def run(input: torch.Tensor, num_bins: int, **opts) -> torch.Tensor:
     plan = _cache.get(key)
     if plan is None:
         plan = _cache[key] = Plan(num_bins, max_n, device=input.device, **opts)
-    return plan.run(input)
+    return plan.run(input, out=out, accumulate=accumulate)
 
 
 # Measurement-only kernels (include/hist_bench.h).

@@ -66,6 +66,7 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_plan_create(ctypes.byref(p), 0, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_create(ctypes.byref(p), 10, 10, None, 3, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_run(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_run_accumulate(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_info(None, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_timing_enable(None, 4) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_global_atomic(None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG

@@ -207,6 +207,63 @@ def test_repeat_is_idempotent():
         assert torch.equal(plan.run(x), first)
 
 
+ACC_CASES = [
+    ("direct-one-chunk", 4096, 6000, {"path": "full"}),
+    ("full-cw32", 8192, 400_000, {}),
+    ("full-cw16", 65536, 1_000_000, {}),
+    ("range", 200_000, 2_000_000, {"path": "range"}),
+    ("scatter-hot", 300_000, 1_000_000, {"path": "scatter", "aggregation": 1}),
+]
+
+
+@pytest.mark.parametrize("label,num_bins,n,opts", ACC_CASES, ids=[c[0] for c in ACC_CASES])
+def test_accumulate_over_chunks(label, num_bins, n, opts):
+    """hist_run_accumulate over ragged pieces (one of them empty) adds the
+    whole input's histogram to what counts held, modulo 2^32."""
+    x = rnd(31, n, -5, num_bins + 5)
+    ref, _ = oracle.hist(x, num_bins)
+    prefill = np.random.default_rng(32).integers(0, 2**32, size=num_bins,
+                                                 dtype=np.uint64).astype(np.uint32)
+    prefill[:3] = [0xFFFFFFFF, 0xFFFFFFF0, 0]  # wraps
+    want = ((prefill.astype(np.uint64) + ref.astype(np.uint64)) % 2**32).astype(np.uint32)
+    say(f"case accumulate {label}: n={n} bins={num_bins} opts={opts}")
+    xt = torch.from_numpy(x).to(DEV)
+    out = torch.from_numpy(prefill.view(np.int32).copy()).to(DEV)
+    plan = hist.Plan(num_bins, n, device=DEV, **opts)
+    cuts = [0, n // 3, n // 3, n // 3 + 1, 2 * n // 3 + 5, n]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        plan.run(xt[a:b], out=out, accumulate=True)
+    got = out.cpu().numpy().view(np.uint32)
+    torch.cuda.synchronize(DEV)
+    assert np.array_equal(got, want), f"{label} ({plan.describe()}): {np.sum(got != want)} bins differ"
+    plan.close()
+
+
+@pytest.mark.parametrize("path", ["full", "range", "scatter"])
+def test_run_then_accumulate(path):
+    """An overwrite of the first piece followed by accumulation of the rest
+    gives the histogram of the whole input, whatever counts held before."""
+    num_bins, n = (60_000 if path == "full" else 100_000), 700_001
+    x = rnd(33, n, 0, num_bins)
+    ref, _ = oracle.hist(x, num_bins)
+    say(f"case run-then-accumulate: path={path}")
+    xt = torch.from_numpy(x).to(DEV)
+    out = torch.full((num_bins,), 12345, dtype=torch.int32, device=DEV)
+    plan = hist.Plan(num_bins, n, device=DEV, path=path,
+                     range_bins=32768 if path == "range" else 0)
+    plan.run(xt[:250_000], out=out)
+    plan.run(xt[250_000:], out=out, accumulate=True)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref)
+    plan.close()
+
+
+def test_accumulate_needs_an_output():
+    plan = hist.Plan(1024, 100, device=DEV)
+    with pytest.raises(ValueError):
+        plan.run(torch.zeros(10, dtype=torch.int32, device=DEV), accumulate=True)
+    plan.close()
+
+
 def test_timing_records_phases():
     x = torch.from_numpy(inputs.generate(2, n=1 << 22)).to(DEV)
     plan = hist.Plan(65536, x.numel(), device=DEV)
