@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--wg", type=int, default=0)
     ap.add_argument("--xcd-map", type=int, default=0)
     ap.add_argument("--counter-bits", type=int, default=0)
+    ap.add_argument("--lds-copies", type=int, default=0,
+                    help="interleaved LDS copies for 32-bit counters (0 = the plan's choice)")
     ap.add_argument("--copies", type=int, default=4, help="input copies used in rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline work (0 = skip)")
@@ -60,7 +62,76 @@ def parse():
     ap.add_argument("--path-sweep", action="store_true",
                     help="time every applicable path over bin counts 2^10..2^22 on uniform "
                          "input of --n (default 2^26) elements; one JSON line per cell")
+    ap.add_argument("--workload-matrix", action="store_true",
+                    help="time every applicable path on each of the five workloads; one JSON "
+                         "line per cell")
     return ap.parse_args()
+
+
+def time_cells(plan, xs, out, warm: int, steps: int) -> float:
+    """Seconds per run: wall clock over back-to-back runs on rotated inputs."""
+    import torch
+    for k in range(warm):
+        plan.run(xs[k % len(xs)], out)
+    torch.cuda.synchronize(out.device)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        plan.run(xs[k % len(xs)], out)
+    torch.cuda.synchronize(out.device)
+    return (time.perf_counter() - t0) / steps
+
+
+def workload_matrix(args):
+    """Every applicable schedule forced on every workload, each checked bit
+    for bit against the oracle: which path the data itself favours, beside
+    the plan's choice from the bin count alone."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from partitioned_chip_accumulation_amd import hist, inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for cfg in range(1, 6):
+        w = inputs.WORKLOADS[cfg]
+        x = inputs.generate(cfg, n=w.n)
+        ref, _ = oracle.hist(x, w.num_bins)
+        xs = [torch.from_numpy(x).to(dev)]
+        for _ in range(3):
+            xs.append(xs[0].clone())
+        out = torch.empty(w.num_bins, dtype=torch.int32, device=dev)
+        B = w.num_bins
+        cells = [("auto", {})]
+        if B <= 40960:
+            cells.append(("full32", {"path": "full", "counter_bits": 32}))
+        if B <= 79616:
+            cells.append(("full16", {"path": "full", "counter_bits": 16}))
+        if B >= 2048:
+            cells.append(("range32", {"path": "range", "counter_bits": 32}))
+            cells.append(("range16", {"path": "range", "counter_bits": 16}))
+            cells.append(("range16+hot", {"path": "range", "counter_bits": 16,
+                                          "aggregation": 1}))
+        cells.append(("scatter", {"path": "scatter", "aggregation": 0}))
+        cells.append(("scatter+hot", {"path": "scatter", "aggregation": 1}))
+        steps = max(10, min(args.steps, int(4e9 / (4 * w.n))))
+        for name, opts in cells:
+            if B > 4 * 79616 and name.startswith("range32"):
+                continue  # dozens of passes over the input: not a contender
+            try:
+                plan = hist.Plan(B, w.n, device=dev, **opts)
+            except hist.HistError as e:
+                print(json.dumps({"workload": w.name, "cell": name, "error": str(e)}), flush=True)
+                continue
+            dt = time_cells(plan, xs, out, 10, steps)
+            ok = bool(np.array_equal(out.view(torch.uint32).cpu().numpy(), ref))
+            print(json.dumps({"workload": w.name, "n": w.n, "bins": B, "cell": name,
+                              "us_per_run": round(dt * 1e6, 1),
+                              "gelem_s": round(w.n / dt / 1e9, 1), "parity": ok,
+                              "plan": plan.describe()}), flush=True)
+            plan.close()
+        del xs, out
+        torch.cuda.empty_cache()
 
 
 def path_sweep(args):
@@ -158,6 +229,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.workload_matrix:
+        workload_matrix(args)
+        return
     if args.path_sweep:
         path_sweep(args)
         return
@@ -188,7 +262,8 @@ def main():
 
     plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
                      range_bins=args.range_bins, aggregation=args.agg, wg_size=args.wg,
-                     xcd_map=args.xcd_map, counter_bits=args.counter_bits)
+                     xcd_map=args.xcd_map, counter_bits=args.counter_bits,
+                     lds_copies=args.lds_copies)
     info = plan.info()
     print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,
           flush=True)
@@ -222,6 +297,22 @@ def main():
     # HIP events around every kernel for the roofline figures.
     elapsed, _ = timed(False)
     elapsed_events, phases = timed(True)
+
+    # Per-step distribution: a third region with one pair of events around
+    # each run on the launch stream (the events sit between runs).
+    plan.timing_enable(0)
+    nstat = min(args.steps, 2000)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(nstat)]
+    torch.cuda.synchronize(dev)
+    for k in range(nstat):
+        ev[k][0].record()
+        plan.run(xs[k % len(xs)], out)
+        ev[k][1].record()
+    torch.cuda.synchronize(dev)
+    per_step = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    step_us = {"median": round(float(np.median(per_step)), 2), "min": round(float(per_step[0]), 2),
+               "p90": round(float(per_step[int(0.9 * (nstat - 1))]), 2), "samples": nstat}
 
     parity = None
     if not args.no_parity:
@@ -314,6 +405,7 @@ def main():
                    "input_copies": len(xs)},
         "phases_ms_per_step": {k: round(v[0] / v[1], 5) for k, v in phases.items()},
         "ms_per_step_with_events": round(elapsed_events / args.steps * 1e3, 5),
+        "step_us_event_bracketed": step_us,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

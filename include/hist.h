@@ -90,8 +90,9 @@ typedef struct {
     int32_t counter_bits; /* FULL/RANGE LDS counters: 32, or 16 (two bins per word, exact
                              through carry events; twice the bins per workgroup) */
     int32_t lds_copies;   /* FULL/RANGE with 32-bit counters: interleaved LDS copies of the
-                             slice (1, 2, 4, 8, 16); a lane adds to copy lane mod copies,
-                             which spreads same-bin lanes of a wave over words and banks */
+                             slice (1, 2, 4, 8, 16; 0 = one); a lane adds to copy lane mod
+                             copies, which spreads same-bin lanes of a wave over words and
+                             banks at the cost of clearing and summing the copies */
 } hist_plan_opts_t;
 
 /* Numeric description of a plan (for logs and benchmarks). */

@@ -167,9 +167,12 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         // Counter width: 32-bit while a workgroup's slice fits, else 16-bit.
         uint32_t cw = (uint32_t)opts.counter_bits;
         if (cw == 0) {
-            // measured on 2^26 uniform elements: 32-bit wins up to 2^14 bins
-            // (59.4 vs 67.2 us), 16-bit from 2^15 (57.9 vs 59.4 us)
-            if (path == HIST_PATH_FULL) cw = num_bins <= 16384 ? 32 : 16;
+            // Measured on 2^26 uniform elements: 16-bit counters (1024-thread
+            // workgroups, two per CU) take 50-52 us from 2^10 to 2^14 bins and at
+            // 2^16, against 52-55 us for 32-bit ones. 32-bit counters win only
+            // where their slice leaves one workgroup per CU (24,576 bins: 48.8
+            // vs 52.1 us; 32,768: 49.7 vs 52.7 us).
+            if (path == HIST_PATH_FULL) cw = num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
             else if (opts.range_bins > 0) cw = (uint32_t)opts.range_bins <= cap32 ? 32 : 16;
             else cw = 16;
         }
@@ -198,13 +201,13 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             R = ceil_div(num_bins, S);
         }
         if (S > cap || S == 0) return HIST_ERR_UNSUPPORTED;
-        // Interleaved copies for small 32-bit slices: up to 16, within 128 KiB,
-        // and only while a workgroup counts at least 4 elements per copied
-        // counter (clearing and summing the copies costs LDS time per counter).
         auto chunks_for = [&](uint32_t lds_bytes, uint32_t *wg_out) {
             const uint32_t occ_lds = std::max<uint32_t>(1, d.lds / lds_bytes);
             uint32_t wg = (uint32_t)opts.wg_size;
-            if (wg == 0) wg = occ_lds >= 2 ? 512 : 1024;
+            // Measured: 1024 threads, except a 32-bit slice that leaves one
+            // workgroup per CU, which runs best with 512 (32,768 bins: 49.7 vs
+            // 52.6 us; 16-bit at 65,536 bins: 50.8 with 1024 vs 56.4 us).
+            if (wg == 0) wg = cw == 32 && occ_lds == 1 ? 512 : 1024;
             const uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
             uint32_t G = (uint32_t)opts.groups;
             if (G == 0) {
@@ -224,23 +227,14 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             *wg_out = wg;
             return G;
         };
+        // Interleaved LDS copies only when asked for: on uniform input every
+        // copy count above 1 measured slower (2^10 bins: 52.6 us with one copy,
+        // 59.9 with 8, 67.4 with 16), as clearing and summing the copies costs
+        // more than the bank conflicts they spread.
         uint32_t kshift = 0, wg = 0, G = 0;
         if (cw == 32) {
-            if (opts.lds_copies > 0) {
+            if (opts.lds_copies > 0)
                 while ((1u << (kshift + 1)) <= (uint32_t)opts.lds_copies) ++kshift;
-            } else {
-                for (uint32_t k = 4;; --k) {
-                    const uint32_t bytes = (S << k) * 4;
-                    if (bytes <= 131072u) {
-                        const uint32_t g = chunks_for(bytes, &wg);
-                        if (k == 0 || max_n / g >= 4ull * ((uint64_t)S << k)) {
-                            kshift = k;
-                            break;
-                        }
-                    }
-                    if (k == 0) break;
-                }
-            }
             if ((S << kshift) * 4 > lds_dyn) return HIST_ERR_UNSUPPORTED;
         }
         const uint32_t lds_bytes =

@@ -2,6 +2,8 @@
 
     python -m partitioned_chip_accumulation_amd.profiling trace DIR --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling counters DIR [DIR...] --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling matrix FILE.jsonl --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling sweep FILE.jsonl --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling traffic --fetch DIR --write DIR \
         --kernel k_sweep --calib-kernel k_copy --calib-bytes N --key KEY --sources A B --out FILE.json
 
@@ -80,6 +82,72 @@ def _match(cs: dict, pat: str) -> dict:
     return next(iter(hits.values()))
 
 
+def _cells_table(rows: dict, cols: list[str], label) -> list[str]:
+    out = ["| " + label + " | " + " | ".join(cols) + " |", "|---:|" + "---:|" * len(cols)]
+    for key, cells in rows.items():
+        ok = {c: v for c, v in cells.items() if v["parity"] and c != "auto"}
+        best = min(ok, key=lambda c: ok[c]["us_per_run"]) if ok else None
+        tds = []
+        for c in cols:
+            v = cells.get(c)
+            if v is None:
+                tds.append("")
+                continue
+            t = f"{v['us_per_run']:.1f}" + ("" if v["parity"] else " FAIL")
+            tds.append(f"**{t}**" if c == best else t)
+        out.append(f"| {key} | " + " | ".join(tds) + " |")
+    return out
+
+
+def _read_cells(jsonl: str, key: str):
+    rows, cols, plans = collections.OrderedDict(), [], {}
+    for line in open(jsonl):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        r = json.loads(line)
+        if "us_per_run" not in r:
+            continue
+        rows.setdefault(r[key], {})[r["cell"]] = r
+        if r["cell"] not in cols:
+            cols.append(r["cell"])
+        if r["cell"] == "auto":
+            plans[r[key]] = r["plan"]
+    return rows, cols, plans
+
+
+def sweep_markdown(jsonl: str, cmd: str) -> str:
+    """Bin counts x schedules table from ``bench.py --path-sweep``."""
+    rows, cols, plans = _read_cells(jsonl, "bins")
+    n = next(iter(next(iter(rows.values())).values()))["n"]
+    rows = collections.OrderedDict((f"2^{b.bit_length() - 1}", v) for b, v in rows.items())
+    out = [f"# Path selection: every schedule on uniform int32 input, n = {n:,}, one MI355X", "",
+           "Microseconds per histogram: wall clock over back-to-back runs on four rotated input "
+           "copies after 20 warm-up runs. Every cell was checked bit for bit against the CPU "
+           "oracle (a failure would be marked FAIL). The fastest cell of a row is in bold. AUTO "
+           "is the plan's own choice; it runs first in each row, right after the input upload.",
+           "", "Command:", "", "```", cmd, "```", ""]
+    out += _cells_table(rows, cols, "bins")
+    out += ["", "AUTO's plans:", ""] + \
+        [f"- 2^{b.bit_length() - 1}: `{p}`" for b, p in plans.items()]
+    return "\n".join(out) + "\n"
+
+
+def matrix_markdown(jsonl: str, cmd: str) -> str:
+    """Workloads x schedules table (microseconds per histogram) from the JSON
+    lines of ``bench.py --workload-matrix``."""
+    rows, cols, plans = _read_cells(jsonl, "workload")
+    out = ["# Every schedule on every workload, one MI355X", "",
+           "Microseconds per histogram: wall clock over back-to-back runs on four rotated input "
+           "copies after 10 warm-up runs. Every cell was checked bit for bit against the CPU "
+           "oracle (a failure would be marked FAIL). The fastest cell of a row is in bold. "
+           "\"+hot\" is the wave hot-slot aggregation. An empty cell is a schedule the bin "
+           "count does not allow.", "", "Command:", "", "```", cmd, "```", ""]
+    out += _cells_table(rows, cols, "workload")
+    out += ["", "AUTO's plans:", ""] + [f"- {wl}: `{p}`" for wl, p in plans.items()]
+    return "\n".join(out) + "\n"
+
+
 def sources_sha(paths: list[str]) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -101,6 +169,14 @@ def main():
     c.add_argument("--cmd", required=True, action="append")
     c.add_argument("--out", required=True)
     c.add_argument("--title", default="Hardware counters")
+    sw = sub.add_parser("sweep")
+    sw.add_argument("jsonl")
+    sw.add_argument("--cmd", required=True)
+    sw.add_argument("--out", required=True)
+    mx = sub.add_parser("matrix")
+    mx.add_argument("jsonl")
+    mx.add_argument("--cmd", required=True)
+    mx.add_argument("--out", required=True)
     tr = sub.add_parser("traffic")
     tr.add_argument("--fetch", required=True)
     tr.add_argument("--write", required=True)
@@ -112,6 +188,12 @@ def main():
     tr.add_argument("--out", required=True)
     a = ap.parse_args()
 
+    if a.cmd_ == "sweep":
+        open(a.out, "w").write(sweep_markdown(a.jsonl, a.cmd))
+        return
+    if a.cmd_ == "matrix":
+        open(a.out, "w").write(matrix_markdown(a.jsonl, a.cmd))
+        return
     if a.cmd_ == "trace":
         text = f"# {a.title}\n\nCommand (rocprofv3 kernel trace):\n\n```\n{a.cmd}\n```\n\n" \
                f"{trace_table(a.dir)}\n"
