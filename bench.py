@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--path-sweep", action="store_true",
                     help="time every applicable path over bin counts 2^10..2^22 on uniform "
                          "input of --n (default 2^26) elements; one JSON line per cell")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure the machine's ceilings the kernels meet (HBM stream read and "
+                         "copy, LDS atomic rates by address pattern, shared-L2 placement of "
+                         "range owners); one JSON line per measurement")
     ap.add_argument("--workload-matrix", action="store_true",
                     help="time every applicable path on each of the five workloads; one JSON "
                          "line per cell")
@@ -79,6 +83,64 @@ def time_cells(plan, xs, out, warm: int, steps: int) -> float:
         plan.run(xs[k % len(xs)], out)
     torch.cuda.synchronize(out.device)
     return (time.perf_counter() - t0) / steps
+
+
+def calibrate(args):
+    """On-chip and HBM ceilings on this GPU, each a JSON line."""
+    import torch
+
+    from partitioned_chip_accumulation_amd import hist, inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize(dev)
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize(dev)
+        return ev0.elapsed_time(ev1) / 1e3 / reps
+
+    # HBM: 1 GiB read once, and a 512 MiB copy (rotating buffers defeat the 256 MB MALL).
+    src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    t = timed(lambda: hist.stream_read(src, sink), 20)
+    print(json.dumps({"what": "hbm_stream_read", "GBps": round(4 * src.numel() / t / 1e9, 1),
+                      "bytes": 4 * src.numel()}), flush=True)
+    half = 1 << 27
+    t = timed(lambda: hist.copy(dst[:half], src[:half]), 20)
+    print(json.dumps({"what": "hbm_copy", "GBps": round(8 * half / t / 1e9, 1),
+                      "bytes_moved": 8 * half}), flush=True)
+    del src, dst
+    # LDS atomics: time per wave instruction per CU, and cycles at the 2.4 GHz peak clock.
+    iters = 2048
+    lsink = torch.zeros(cu, dtype=torch.int32, device=dev)
+    for pattern in ("distinct", "random", "same", "groups8"):
+        for rtn in (False, True):
+            t = timed(lambda: hist.lds_atomic(pattern, rtn, iters, lsink), 5)
+            per_instr = t / (16 * iters * 16)
+            print(json.dumps({"what": "lds_atomic", "pattern": pattern, "with_return": rtn,
+                              "ns_per_wave_instr_per_cu": round(per_instr * 1e9, 3),
+                              "cycles_at_2p4GHz": round(per_instr * 2.4e9, 2)}), flush=True)
+    # Shared L2: RANGE with the R owners of a chunk on one XCD vs in plain order.
+    n, B = 1 << 26, 1 << 17
+    x = torch.from_numpy(inputs.uniform(1, n, B)).to(dev)
+    xs = [x] + [x.clone() for _ in range(3)]
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    for xcd_map in (1, 2):
+        plan = hist.Plan(B, n, device=dev, path="range", counter_bits=16, xcd_map=xcd_map)
+        dt = time_cells(plan, xs, out, 20, 200)
+        print(json.dumps({"what": "range_owner_placement",
+                          "placement": "one XCD per chunk" if xcd_map == 1 else "plain order",
+                          "bins": B, "n": n, "us_per_run": round(dt * 1e6, 2),
+                          "plan": plan.describe()}), flush=True)
+        plan.close()
 
 
 def workload_matrix(args):
@@ -229,6 +291,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate:
+        calibrate(args)
+        return
     if args.workload_matrix:
         workload_matrix(args)
         return

@@ -77,6 +77,7 @@ def load(path: str = LIBRARY):
         "hist_bench_global_atomic": (i32, [vp, vp, u64, u32, vp]),
         "hist_bench_read": (i32, [vp, u64, vp, vp]),
         "hist_bench_copy": (i32, [vp, vp, u64, vp]),
+        "hist_bench_lds_atomic": (i32, [u32, u32, u32, vp, u32, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -273,3 +274,16 @@ def copy(dst: torch.Tensor, src: torch.Tensor):
         _check(library().hist_bench_copy(dst.data_ptr(), src.data_ptr(),
                                          src.numel() * src.element_size(),
                                          _stream_handle(src.device)), "hist_bench_copy")
+
+
+LDS_PATTERNS = {"distinct": 0, "random": 1, "same": 2, "groups8": 3}
+
+
+def lds_atomic(pattern: str, with_return: bool, iters: int, sink: torch.Tensor):
+    """Queue the LDS-atomic calibration kernel (one 1024-thread workgroup per
+    CU, 16 waves x iters x 16 atomics each) on the current stream."""
+    with torch.cuda.device(sink.device):
+        _check(library().hist_bench_lds_atomic(LDS_PATTERNS[pattern], int(with_return), int(iters),
+                                               sink.data_ptr(), sink.numel(),
+                                               _stream_handle(sink.device)),
+               "hist_bench_lds_atomic")

@@ -4,6 +4,7 @@
     python -m partitioned_chip_accumulation_amd.profiling counters DIR [DIR...] --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling matrix FILE.jsonl --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling sweep FILE.jsonl --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling calib FILE.jsonl --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling traffic --fetch DIR --write DIR \
         --kernel k_sweep --calib-kernel k_copy --calib-bytes N --key KEY --sources A B --out FILE.json
 
@@ -116,6 +117,35 @@ def _read_cells(jsonl: str, key: str):
     return rows, cols, plans
 
 
+def calib_markdown(jsonl: str, cmd: str) -> str:
+    """Tables from ``bench.py --calibrate``."""
+    recs = [json.loads(l) for l in open(jsonl) if l.strip().startswith("{")]
+    out = ["# Calibration: the ceilings the histogram kernels meet, one MI355X", "",
+           "Command:", "", "```", cmd, "```", "", "## HBM", "",
+           "| measurement | GB/s | fraction of 8 TB/s |", "|---|---:|---:|"]
+    for r in recs:
+        if r["what"] in ("hbm_stream_read", "hbm_copy"):
+            out.append(f"| {r['what']} | {r['GBps']:.0f} | {r['GBps'] / 8000:.3f} |")
+    out += ["", "## LDS atomics (one 1024-thread workgroup per CU, 16 waves)", "",
+            "Time per wave instruction per CU; cycles at the 2.4 GHz peak clock.", "",
+            "| address pattern of one wave instruction | form | ns | cycles |",
+            "|---|---|---:|---:|"]
+    names = {"distinct": "64 consecutive words", "random": "random words of 32,768",
+             "same": "all 64 lanes on one word", "groups8": "8 groups of 8 lanes, one word each"}
+    for r in recs:
+        if r["what"] == "lds_atomic":
+            form = "ds_add_rtn_u32" if r["with_return"] else "ds_add_u32"
+            out.append(f"| {names[r['pattern']]} | {form} | {r['ns_per_wave_instr_per_cu']:.2f} | "
+                       f"{r['cycles_at_2p4GHz']:.1f} |")
+    out += ["", "## Owners of a chunk sharing an XCD's L2 (RANGE path)", "",
+            "| placement | bins | n | us per run | plan |", "|---|---:|---:|---:|---|"]
+    for r in recs:
+        if r["what"] == "range_owner_placement":
+            out.append(f"| {r['placement']} | {r['bins']} | {r['n']} | {r['us_per_run']:.1f} | "
+                       f"`{r['plan']}` |")
+    return "\n".join(out) + "\n"
+
+
 def sweep_markdown(jsonl: str, cmd: str) -> str:
     """Bin counts x schedules table from ``bench.py --path-sweep``."""
     rows, cols, plans = _read_cells(jsonl, "bins")
@@ -169,6 +199,10 @@ def main():
     c.add_argument("--cmd", required=True, action="append")
     c.add_argument("--out", required=True)
     c.add_argument("--title", default="Hardware counters")
+    ca = sub.add_parser("calib")
+    ca.add_argument("jsonl")
+    ca.add_argument("--cmd", required=True)
+    ca.add_argument("--out", required=True)
     sw = sub.add_parser("sweep")
     sw.add_argument("jsonl")
     sw.add_argument("--cmd", required=True)
@@ -188,6 +222,9 @@ def main():
     tr.add_argument("--out", required=True)
     a = ap.parse_args()
 
+    if a.cmd_ == "calib":
+        open(a.out, "w").write(calib_markdown(a.jsonl, a.cmd))
+        return
     if a.cmd_ == "sweep":
         open(a.out, "w").write(sweep_markdown(a.jsonl, a.cmd))
         return

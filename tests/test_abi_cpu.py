@@ -71,6 +71,8 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_plan_timing_enable(None, 4) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_global_atomic(None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_copy(None, None, 16, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_bench_lds_atomic(4, 0, 1, None, 0, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_bench_lds_atomic(0, 0, 0, None, 0, None) == hist.HIST_ERR_INVALID_ARG
     lib.hist_plan_destroy(None)
 
 

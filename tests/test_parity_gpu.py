@@ -264,6 +264,24 @@ def test_accumulate_needs_an_output():
     plan.close()
 
 
+@pytest.mark.parametrize("rtn", [False, True])
+def test_lds_atomic_calibration_kernel(rtn):
+    """The calibration kernel does its adds: word 0 is hit by lane 0 of each
+    of the 16 waves per iteration when the lanes' words are distinct, and by
+    all 1024 threads when every lane adds to one word."""
+    cu = torch.cuda.get_device_properties(DEV).multi_processor_count
+    sink = torch.zeros(cu, dtype=torch.int32, device=DEV)
+    iters = 7
+    hist.lds_atomic("distinct", rtn, iters, sink)
+    got = sink.cpu().numpy()
+    if not rtn:
+        assert (got == 16 * iters).all()
+    hist.lds_atomic("same", False, iters, sink)
+    assert (sink.cpu().numpy() == 1024 * iters).all()
+    with pytest.raises(hist.HistError):
+        hist.lds_atomic("same", False, iters, sink[:cu - 1])
+
+
 def test_timing_records_phases():
     x = torch.from_numpy(inputs.generate(2, n=1 << 22)).to(DEV)
     plan = hist.Plan(65536, x.numel(), device=DEV)
