@@ -13,11 +13,12 @@
 //     (k_partition), and owners then read only their own elements
 //     (k_bucket_hist).
 // Slices are merged by exclusive owners (k_merge, k_merge_slots): one thread
-// writes each output bin once, so no global atomics and no memset of the
-// output are needed.
+// writes (or, when accumulating, reads and writes) each output bin once, so
+// no global atomics and no memset of the output are needed.
 //
 // Conventions: wave64 (gfx950), 16-byte (dwordx4) global loads on the input
-// body, uint32 LDS counters, ds_add_u32 for accumulation.
+// body; LDS counters are uint32 (ds_add_u32) or two 16-bit halves of a word
+// kept exact by carry events (ds_add_rtn_u32).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,13 +40,6 @@ struct InputView {
 };
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
-
-// popcount of the bits of m below this lane.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m)
-{
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
 {
@@ -198,7 +192,6 @@ constexpr uint32_t kUpperPlanes = 7;
 // bytes of partial storage per (row, block): plane 0, planes 1..7, width code
 constexpr uint32_t kBlockStoreBytes = kPlaneBytes * (1 + kUpperPlanes) + 1;
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Partials {
     uint8_t *plane0;  // [rows][nblk][128 bytes]
@@ -440,7 +433,7 @@ __device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t 
 }
 
 // Flush an LDS slice of len bins to partial row `row`, starting at block
-// blk0 of the row: each wave takes pairs of blocks, FLUSH_BATCH pairs at a
+// blk0 of the row: each wave takes pairs of blocks, kFlushBatch pairs at a
 // time with their LDS reads issued together. Whole workgroup.
 constexpr uint32_t kFlushBatch = 4;
 
