@@ -122,6 +122,17 @@ def test_bin_counts(num_bins):
         check(x, num_bins, f"bins{num_bins}-{p}", path=p)
 
 
+@pytest.mark.parametrize("num_bins", [hist.MAX_BINS, hist.MAX_BINS - 1])
+def test_maximum_bin_count(num_bins):
+    """The largest supported bin count: 2,048 two-phase ranges (the partition's
+    rank counters and the owners' range table at their LDS limits), a ragged
+    last range, and the RANGE path with one chunk per range."""
+    x = rnd(77, 1_000_003, -3, num_bins + 5)
+    x[:1000] = num_bins - 1  # the last bin, in the last (ragged) range
+    for p in ["auto", "scatter", "range"]:
+        check(x, num_bins, f"maxbins{num_bins}-{p}", path=p)
+
+
 def test_out_of_range_and_negative_values():
     x = rnd(5, 500_000, -(2**31), 2**31 - 1)
     x[::2] = rnd(6, x[::2].size, 0, 70_000)
