@@ -1053,13 +1053,14 @@ __device__ __forceinline__ void count_slots(uint32_t *lds, HotSlot &hs, const ui
 // (owner, range) pair that occurs, because both grow along the
 // concatenation). Inside one range the elements are the tiles' runs in tile
 // order. Each wave works on its own: it takes groups of RPW consecutive
-// tiles (groups w, w + NW, w + 2NW, ... of the owner's span), reads the
-// group's run metadata with one lane per tile, numbers the runs' 16-byte
-// vectors end to end, and finds a vector's run by compares against prefix
-// sums held in scalar registers. With no workgroup barrier until the slice
-// is flushed, the waves drift apart and one wave's loads overlap the
-// others' counting. The runs of one range are about equally long for
-// shuffled inputs, so the waves stay balanced.
+// tiles (groups w, w + NW, w + 2NW, ... of the owner's span) and reads the
+// group's run metadata with one lane per tile. Run m then feeds slot m of
+// every lane's batch of RPW 16-byte loads (lane l takes vectors l, l + 64,
+// ... of each run), so every run parameter is wave-uniform and a vector
+// costs a compare, an address and two bounds. The runs of one range are
+// about equally long for shuffled inputs, so the slots stay busy and the
+// waves balanced. With no workgroup barrier until the slice is flushed, the
+// waves drift apart and one wave's loads overlap the others' counting.
 template <int WG, int UNROLL, int AGG>
 __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint16_t *__restrict__ stage, uint32_t stage_cap, const uint32_t *__restrict__ tcnt,
@@ -1073,7 +1074,7 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     uint32_t *misc = reinterpret_cast<uint32_t *>(bs + ranges + 1);  // [0] ta [1] tb
     const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
     constexpr uint32_t NW = WG / 64;  // waves
-    constexpr uint32_t RPW = 4;       // tiles (runs) per wave group
+    constexpr uint32_t RPW = UNROLL;  // tiles (runs) per wave group = loads in flight per lane
 
     range_starts(totals, ranges, bs);
     __syncthreads();
@@ -1132,41 +1133,31 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                     used = hi_e - lo_e;
                 }
             }
-            uint32_t pre[RPW + 1], run_v[RPW], run_s[RPW], run_u[RPW];
-            pre[0] = 0u;
+            // Run m of the group takes slot m of every lane's batch of RPW vector
+            // loads, so all run parameters stay wave-uniform (scalar registers).
+            uint32_t run_n[RPW], run_v[RPW], run_s[RPW], run_u[RPW], steps = 0;
 #pragma unroll
             for (uint32_t m = 0; m < RPW; ++m) {
-                pre[m + 1] = pre[m] + (uint32_t)__builtin_amdgcn_readlane((int)nv, (int)m);
+                run_n[m] = (uint32_t)__builtin_amdgcn_readlane((int)nv, (int)m);
                 run_v[m] = (uint32_t)__builtin_amdgcn_readlane((int)vlo, (int)m);
                 run_s[m] = (uint32_t)__builtin_amdgcn_readlane((int)skip, (int)m);
                 run_u[m] = (uint32_t)__builtin_amdgcn_readlane((int)used, (int)m);
+                steps = max(steps, (run_n[m] + 63u) / 64u);
             }
-            const uint32_t total = pre[RPW];
-            for (uint32_t ub = 0; ub < total; ub += 64 * UNROLL) {
-                i32x4 qv[UNROLL];
-                uint32_t first[UNROLL], last[UNROLL];
+            for (uint32_t it = 0; it < steps; ++it) {
+                const uint32_t d = it * 64u + lane;  // this lane's vector in each run
+                const uint32_t k8 = d * 8u;          // run element of vector element e is k8 + e - skip
+                i32x4 qv[RPW];
+                uint32_t first[RPW], last[RPW];
 #pragma unroll
-                for (int k = 0; k < UNROLL; ++k) {
-                    const uint32_t u = ub + k * 64 + lane;
-                    const bool ok = u < total;
-                    // the last run m with pre[m] <= u (empty runs are passed over)
-                    uint32_t base = pre[0], vv = run_v[0], js = run_s[0], jc = run_u[0];
-#pragma unroll
-                    for (uint32_t m = 1; m < RPW; ++m) {
-                        const bool after = u >= pre[m];
-                        base = after ? pre[m] : base;
-                        vv = after ? run_v[m] : vv;
-                        js = after ? run_s[m] : js;
-                        jc = after ? run_u[m] : jc;
-                    }
-                    const uint32_t d = u - base;
-                    const uint32_t k8 = d * 8u;  // run element of vector element e is k8 + e - skip
-                    first[k] = ok ? (k8 < js ? js - k8 : 0u) : 8u;
-                    last[k] = ok ? min(8u, js + jc - k8) : 0u;
-                    qv[k] = ok ? stage_vec[(uint64_t)vv + d] : i32x4{0, 0, 0, 0};
+                for (uint32_t m = 0; m < RPW; ++m) {
+                    const bool ok = d < run_n[m];
+                    first[m] = ok ? (k8 < run_s[m] ? run_s[m] - k8 : 0u) : 8u;
+                    last[m] = ok ? min(8u, run_s[m] + run_u[m] - k8) : 0u;
+                    qv[m] = ok ? stage_vec[(uint64_t)run_v[m] + d] : i32x4{0, 0, 0, 0};
                 }
 #pragma unroll
-                for (int k = 0; k < UNROLL; ++k) {
+                for (uint32_t k = 0; k < RPW; ++k) {
                     const uint32_t words[4] = {(uint32_t)qv[k].x, (uint32_t)qv[k].y,
                                                (uint32_t)qv[k].z, (uint32_t)qv[k].w};
                     if constexpr (AGG == 1) {
