@@ -382,7 +382,7 @@ pca::Partials plan_partials(const hist_plan *p)
 template <int AGG>
 hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
 {
-    auto k = pca::k_bucket_hist<kScatterWG, 4, AGG>;
+    auto k = pca::k_bucket_hist<kScatterWG, 8, AGG>;
     const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + 4 * 4;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
