@@ -1023,12 +1023,14 @@ template <int AGG>
 __device__ __forceinline__ void count_slots(uint32_t *lds, HotSlot &hs, const uint32_t (&words)[4],
                                             uint32_t first, uint32_t last)
 {
-    if (AGG == 1 && hs.h != kNoSlot) {
+    // the hot slot is wave-uniform: read it as a scalar so that this test is one branch
+    const uint32_t h = AGG == 1 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)hs.h) : kNoSlot;
+    if (AGG == 1 && h != kNoSlot) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t s = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
             const bool ok = (uint32_t)e >= first && (uint32_t)e < last;
-            const bool m = ok && s == hs.h;
+            const bool m = ok && s == h;
             hs.c += m ? 1u : 0u;
             lds_count<0>(lds, s, ok && !m);
         }
