@@ -39,6 +39,10 @@
  * and needs 4-byte alignment only; counts needs 4-byte alignment. counts,
  * input and the workspace must not overlap. One plan runs one hist_run at a
  * time: calls that share a plan must be ordered (e.g. on one stream).
+ * hist_run and hist_run_accumulate queue kernel launches only (no memset, no
+ * allocation, no synchronisation), so they can be captured into a HIP graph
+ * (with timing disabled) and replayed; each replay reads the captured input
+ * buffer as it is then.
  *
  * Errors
  * ------

@@ -293,6 +293,41 @@ def test_lds_atomic_calibration_kernel(rtn):
         hist.lds_atomic("same", False, iters, sink[:cu - 1])
 
 
+@pytest.mark.parametrize("path,num_bins", [("full", 65536), ("range", 200_000),
+                                           ("scatter", 300_000)])
+def test_graph_capture_and_replay(path, num_bins):
+    """hist_run queues kernels only (no memset, no synchronisation), so a
+    caller can capture it in a graph. Each replay histograms whatever the
+    captured input buffer holds then; between replays the test does eager
+    work of its own (refilling the buffer) and synchronises."""
+    n = 1_000_003
+    say(f"case graph: path={path} bins={num_bins}")
+    plan = hist.Plan(num_bins, n, device=DEV, path=path)
+    xt = torch.empty(n, dtype=torch.int32, device=DEV)
+    out = torch.empty(num_bins, dtype=torch.int32, device=DEV)
+    xt.copy_(torch.from_numpy(rnd(40, n, 0, num_bins)))
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        plan.run(xt, out)  # warm-up on the capture stream (sets kernel attributes)
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize(DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.run(xt, out)
+    for k in range(4):
+        x = rnd(41 + k, n, -2, num_bins + 2)
+        xt.copy_(torch.from_numpy(x))
+        out.fill_(-1)
+        torch.cuda.synchronize(DEV)
+        graph.replay()
+        torch.cuda.synchronize(DEV)
+        ref, _ = oracle.hist(x, num_bins)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref), f"replay {k}"
+    del graph
+    plan.close()
+
+
 def test_timing_records_phases():
     x = torch.from_numpy(inputs.generate(2, n=1 << 22)).to(DEV)
     plan = hist.Plan(65536, x.numel(), device=DEV)
