@@ -266,19 +266,20 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def traffic_for(key: str):
-    """Counter-derived HBM bytes per launch from profiles/traffic.json, or None
-    when no entry exists for this kernel and workload or the kernel sources
-    changed since the counters were taken."""
+def counters_for(key: str) -> dict:
+    """The profiles/traffic.json entry for this kernel and workload (counter-
+    derived HBM bytes per launch, and LDS/occupancy counters where taken), or
+    {} when there is none or the kernel sources changed since the counters
+    were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     e = data.get(key)
     if not e or e.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return e.get("bytes_per_launch")
+        return {}
+    return e
 
 
 def main():
@@ -406,7 +407,9 @@ def main():
     traffic_key = f"{dom_name}:{w.name}:n={n}:{plan.describe()}"
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(traffic_key), "traffic_key": traffic_key,
+                "traffic": counters_for(traffic_key).get("bytes_per_launch"),
+                "traffic_key": traffic_key,
+                "lds_counters": counters_for(traffic_key).get("lds_counters"),
                 "algorithmic_bytes": dom_bytes,
                 "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches": dom_launches}
 

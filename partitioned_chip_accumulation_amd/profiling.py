@@ -220,6 +220,9 @@ def main():
     tr.add_argument("--key", required=True)
     tr.add_argument("--sources", nargs="+", required=True)
     tr.add_argument("--out", required=True)
+    tr.add_argument("--lds", default=None,
+                    help="optional pass with SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE")
+    tr.add_argument("--occ", default=None, help="optional pass with MeanOccupancyPerActiveCU")
     a = ap.parse_args()
 
     if a.cmd_ == "calib":
@@ -254,6 +257,22 @@ def main():
                  "write_scale": w_scale, "calib_kernel": a.calib_kernel,
                  "calib_bytes": a.calib_bytes, "kernel_source_sha": sources_sha(a.sources)}
         entry["bytes_per_launch"] = entry["fetch_bytes"] + entry["write_bytes"]
+        lds = {}
+        if a.lds:
+            c = _match(counters_per_dispatch(a.lds), a.kernel)
+            if c.get("SQ_LDS_IDX_ACTIVE"):
+                # cycles the LDS stalled on bank conflicts, per cycle it was active
+                lds["lds_bank_conflict_per_active_cycle"] = round(
+                    c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"], 4)
+            for name in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAVES"):
+                if name in c:
+                    lds[name] = c[name]
+        if a.occ:
+            c = _match(counters_per_dispatch(a.occ), a.kernel)
+            if "MeanOccupancyPerActiveCU" in c:
+                lds["MeanOccupancyPerActiveCU"] = round(c["MeanOccupancyPerActiveCU"], 4)
+        if lds:
+            entry["lds_counters"] = lds
         data = {}
         if os.path.exists(a.out):
             data = json.load(open(a.out))
