@@ -591,10 +591,21 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     tm.end(PH_OWNER);
     if (e != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_SLOTS);
-    hipLaunchKernelGGL(pca::k_merge_slots<4>, dim3(ceil_div(num_bins, 256)), dim3(256), 0, stream,
-                       plan_partials(p),
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges,
-                       p->range_bins, num_bins, p->owners, counts, accumulate);
+    {
+        // A range's slots are the rows of its overlapping owners, about W / R + 1
+        // of them: one wave per block (64 rows per round trip) once ranges are
+        // many, four (256 rows) when each range has many owners.
+        const pca::Partials P = plan_partials(p);
+        const uint32_t *tot = reinterpret_cast<const uint32_t *>(p->ws + p->off_totals);
+        if (p->ranges >= 16)
+            hipLaunchKernelGGL(pca::k_merge_slots<1>, dim3(ceil_div(num_bins, 256)), dim3(64), 0,
+                               stream, P, tot, p->ranges, p->range_bins, num_bins, p->owners,
+                               counts, accumulate);
+        else
+            hipLaunchKernelGGL(pca::k_merge_slots<4>, dim3(ceil_div(num_bins, 256)), dim3(256), 0,
+                               stream, P, tot, p->ranges, p->range_bins, num_bins, p->owners,
+                               counts, accumulate);
+    }
     tm.end(PH_SLOTS);
     if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
     return HIST_OK;

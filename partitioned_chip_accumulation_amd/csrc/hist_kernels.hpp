@@ -685,7 +685,8 @@ __device__ __forceinline__ void store_counts(uint32_t *__restrict__ counts, uint
 // ---------------------------------------------------------------------------
 // Exclusive-owner merge: counts[b] = sum over rows g < rows of partial[g][b].
 //
-// A workgroup owns one 256-bin block and writes each of its bins once. Lane
+// A workgroup owns one 256-bin block and writes each of its bins once
+// (merge_block does the reading and summing, k_merge_slots uses it too). Lane
 // l of wave w reads 16 bytes of a plane per row: the 32 bins of chunk
 // c = l / 8 of the block, from row slot i = l mod 8 of the wave's 8 rows of
 // a round (8 * WAVES rows per round). A batch is kMergeRounds rounds, and
@@ -720,30 +721,34 @@ __device__ __forceinline__ void add_nibbles_bytewise(uint32_t (&acc)[32],
     }
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows, uint32_t num_bins,
-                                                      uint32_t *__restrict__ counts,
-                                                      uint32_t accumulate)
+// Sum over rows row0 .. row0 + rows - 1 of block blk of the partial rows
+// (rows whose row_ok(k) is false, k the row's index from row0, are skipped).
+// Whole workgroup of WAVES waves, convergent; the sums are valid in wave 0,
+// lane l holding bins 4l..4l+3 of the block.
+template <int WAVES, typename RowOk>
+__device__ __forceinline__ u32x4 merge_block(const Partials &P, uint64_t row0, uint32_t rows,
+                                             uint64_t blk, RowOk row_ok)
 {
     constexpr uint32_t RPR = 8 * WAVES;  // rows per round
     __shared__ u32x4 red[WAVES][64];
     const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
     const uint32_t c = lane >> 3, i = lane & 7u;
-    const uint32_t blk = blockIdx.x;
     uint32_t acc[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = 0u;
     for (uint32_t base = 0; base < rows; base += kMergeRounds * RPR) {
         // lane l: the width code of round l / 8, slot l mod 8
         const uint32_t crow = base + (lane >> 3) * RPR + w * 8 + i;
-        const uint32_t code = crow < rows ? P.width[(uint64_t)crow * P.nblk + blk] : 0u;
+        const uint32_t code =
+            crow < rows && row_ok(crow) ? P.width[(row0 + crow) * P.nblk + blk] : 0u;
         u32x4 v[kMergeRounds];
 #pragma unroll
         for (uint32_t t = 0; t < kMergeRounds; ++t) {
-            const uint32_t row = base + t * RPR + w * 8 + i;
-            v[t] = row < rows ? *reinterpret_cast<const u32x4 *>(
-                                    P.plane0 + ((uint64_t)row * P.nblk + blk) * kPlaneBytes + 16u * c)
-                              : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t k = base + t * RPR + w * 8 + i;
+            v[t] = k < rows && row_ok(k)
+                       ? *reinterpret_cast<const u32x4 *>(
+                             P.plane0 + ((row0 + k) * P.nblk + blk) * kPlaneBytes + 16u * c)
+                       : u32x4{0u, 0u, 0u, 0u};
         }
         add_nibbles_bytewise(acc, v, 0);
         // Planes beyond 0: each lane fetches them for its own rows of the batch,
@@ -757,7 +762,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows,
             for (uint32_t q = 1; q < maxp; ++q) {
 #pragma unroll
                 for (uint32_t t = 0; t < kMergeRounds; ++t) {
-                    const uint64_t row = base + t * RPR + w * 8 + i;
+                    const uint64_t row = row0 + base + t * RPR + w * 8 + i;
                     v[t] = q < pl[t] ? *reinterpret_cast<const u32x4 *>(
                                            P.upper + ((row * P.nblk + blk) * kUpperPlanes + q - 1) *
                                                          kPlaneBytes + 16u * c)
@@ -781,12 +786,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows,
         if (i == k) mine = u32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
     red[w][lane] = mine;
     __syncthreads();
+    u32x4 t = {0u, 0u, 0u, 0u};
     if (w == 0) {
-        u32x4 t = red[0][lane];
 #pragma unroll
-        for (int k = 1; k < WAVES; ++k) t += red[k][lane];
-        store_counts(counts, (uint64_t)blk * kBlockBins + lane * 4u, num_bins, t, accumulate);
+        for (int k = 0; k < WAVES; ++k) t += red[k][lane];
     }
+    return t;
+}
+
+struct AllRows {
+    __device__ bool operator()(uint32_t) const { return true; }
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows, uint32_t num_bins,
+                                                      uint32_t *__restrict__ counts,
+                                                      uint32_t accumulate)
+{
+    const u32x4 t = merge_block<WAVES>(P, 0, rows, blockIdx.x, AllRows{});
+    if ((threadIdx.x >> 6) == 0)
+        store_counts(counts, (uint64_t)blockIdx.x * kBlockBins + lane_id() * 4u, num_bins, t,
+                     accumulate);
 }
 
 // ---------------------------------------------------------------------------
@@ -1054,12 +1074,12 @@ __device__ __forceinline__ void count_slots(uint32_t *lds, HotSlot &hs, const ui
 // and writes the slice to partial slot i + r (i + r is distinct for every
 // (owner, range) pair that occurs, because both grow along the
 // concatenation). Inside one range the elements are the tiles' runs in tile
-// order. Each wave works on its own: it takes groups of RPW consecutive
-// tiles (groups w, w + NW, w + 2NW, ... of the owner's span) and reads the
-// group's run metadata with one lane per tile. Run m then feeds slot m of
-// every lane's batch of RPW 16-byte loads (lane l takes vectors l, l + 64,
-// ... of each run), so every run parameter is wave-uniform and a vector
-// costs a compare, an address and two bounds. The runs of one range are
+// order. Waves work without barriers, in teams: a team takes groups of RPW
+// consecutive tiles (every (NW / S)-th group of the owner's span) and each
+// of its S waves reads the group's run metadata with one lane per tile. Run
+// m then feeds slot m of every lane's batch of RPW 16-byte loads (the team's
+// lanes stripe each run's vectors), so every run parameter is wave-uniform
+// and a vector costs a compare, an address and two bounds. The runs of one range are
 // about equally long for shuffled inputs, so the slots stay busy and the
 // waves balanced. With no workgroup barrier until the slice is flushed, the
 // waves drift apart and one wave's loads overlap the others' counting.
@@ -1118,7 +1138,15 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
         const uint32_t ta = misc[0], tb = misc[1];
         HotSlot hs;
 
-        for (uint32_t g0 = ta + w * RPW; g0 < tb; g0 += NW * RPW) {
+        // Teams of S waves: team w / S takes groups of RPW tiles (every NW / S-th
+        // group), and its S waves stripe each run's vectors. S is the smallest
+        // power of two that still leaves every team two groups, so long runs
+        // (few ranges, or an input piled into one range) keep all waves busy.
+        const uint32_t ngroups = (tb - ta + RPW - 1) / RPW;
+        uint32_t S = 1;
+        while (S < NW && ngroups < 2u * (NW / S)) S *= 2u;
+        const uint32_t team = w / S, member = w % S;
+        for (uint32_t g0 = ta + team * RPW; g0 < tb; g0 += (NW / S) * RPW) {
             // lane m < RPW: the run of tile g0 + m, clipped to [p0, p1)
             uint32_t vlo = 0, nv = 0, skip = 0, used = 0;
             const uint32_t t = g0 + lane;
@@ -1144,10 +1172,10 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                 run_v[m] = (uint32_t)__builtin_amdgcn_readlane((int)vlo, (int)m);
                 run_s[m] = (uint32_t)__builtin_amdgcn_readlane((int)skip, (int)m);
                 run_u[m] = (uint32_t)__builtin_amdgcn_readlane((int)used, (int)m);
-                steps = max(steps, (run_n[m] + 63u) / 64u);
+                steps = max(steps, (run_n[m] + 64u * S - 1u) / (64u * S));
             }
             for (uint32_t it = 0; it < steps; ++it) {
-                const uint32_t d = it * 64u + lane;  // this lane's vector in each run
+                const uint32_t d = (it * S + member) * 64u + lane;  // this lane's vector in each run
                 const uint32_t k8 = d * 8u;          // run element of vector element e is k8 + e - skip
                 i32x4 qv[RPW];
                 uint32_t first[RPW], last[RPW];
@@ -1185,22 +1213,13 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     }
 }
 
-// Add plane q of a block, as lane l's 16 bits (bins 4l..4l+3), into acc.
-__device__ __forceinline__ void add_plane(u32x4 &acc, uint32_t v, uint32_t q)
-{
-    const uint32_t sh = 4u * q;
-    acc.x += (v & 0xFu) << sh;
-    acc.y += ((v >> 4) & 0xFu) << sh;
-    acc.z += ((v >> 8) & 0xFu) << sh;
-    acc.w += ((v >> 12) & 0xFu) << sh;
-}
-
 // Phase 2b: counts[b] for the bins of one range = the sum of the slots that
 // the owners overlapping the range wrote for it (exclusive owner per bin, no
-// global atomics). A workgroup handles one 256-bin block of one range; each
-// wave takes a few owner slots at a time, loading their width codes and
-// plane 0 together and then only the planes the codes ask for. Empty ranges
-// give zeros.
+// global atomics). A workgroup handles one 256-bin block of one range. Owner
+// i wrote the range's slot to row i + r, so the slots of the overlapping
+// owners first..last are consecutive rows, summed by merge_block. An owner
+// that took no element (possible only when there are fewer elements than
+// owners) wrote no slot and is skipped. Empty ranges give zeros.
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint32_t *__restrict__ totals,
                                                             uint32_t ranges, uint32_t range_bins,
@@ -1208,10 +1227,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
                                                             uint32_t *__restrict__ counts,
                                                             uint32_t accumulate)
 {
-    constexpr uint32_t OB = 8;  // owner slots per wave step
-    __shared__ u32x4 red[WAVES][64];
     __shared__ uint64_t se[3];
-    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
     const uint32_t bpr = range_bins / kBlockBins;  // blocks per range
     const uint32_t r = blockIdx.x / bpr, lb = blockIdx.x % bpr;
     if (w == 0) {
@@ -1237,47 +1254,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
     }
     __syncthreads();
     const uint64_t rb = se[0], re = se[1], N = se[2];
-    u32x4 acc = {0u, 0u, 0u, 0u};
+    uint32_t first = 0, rows = 0;
     if (re > rb) {
-        const uint32_t first = owner_of(rb, N, owners), last = owner_of(re - 1, N, owners);
-        // each wave takes OB owners at a time, their loads issued together
-        for (uint32_t i0 = first + w; i0 <= last; i0 += WAVES * OB) {
-            uint32_t code[OB], v[OB];
-            uint64_t blk[OB];
-#pragma unroll
-            for (uint32_t o = 0; o < OB; ++o) {
-                const uint32_t i = i0 + o * WAVES;
-                // an owner that took no element wrote no slot
-                const bool has = i <= last && (uint64_t)i * N / owners < (uint64_t)(i + 1) * N / owners;
-                blk[o] = ((uint64_t)i + r) * P.nblk + lb;
-                code[o] = has ? P.width[blk[o]] : 0u;
-                v[o] = has ? reinterpret_cast<const uint16_t *>(P.plane0 + blk[o] * kPlaneBytes)[lane] : 0u;
-            }
-            uint32_t maxc = 0;
-#pragma unroll
-            for (uint32_t o = 0; o < OB; ++o) {
-                add_plane(acc, v[o], 0);
-                maxc = max(maxc, code[o]);
-            }
-            for (uint32_t q = 1; q <= maxc; ++q) {
-#pragma unroll
-                for (uint32_t o = 0; o < OB; ++o)
-                    v[o] = q <= code[o] ? reinterpret_cast<const uint16_t *>(
-                                              P.upper + (blk[o] * kUpperPlanes + q - 1) * kPlaneBytes)[lane]
-                                        : 0u;
-#pragma unroll
-                for (uint32_t o = 0; o < OB; ++o) add_plane(acc, v[o], q);
-            }
-        }
+        first = owner_of(rb, N, owners);
+        rows = owner_of(re - 1, N, owners) - first + 1;
     }
-    red[w][lane] = acc;
-    __syncthreads();
-    if (w == 0) {
-#pragma unroll
-        for (int k = 1; k < WAVES; ++k) acc += red[k][lane];
-        store_counts(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, acc,
+    // every owner took at least one element when N >= owners
+    const bool all_nonempty = N >= owners;
+    auto row_ok = [&](uint32_t k) {
+        const uint64_t i = (uint64_t)first + k;
+        return all_nonempty || i * N / owners < (i + 1) * N / owners;
+    };
+    const u32x4 t = merge_block<WAVES>(P, (uint64_t)first + r, rows, lb, row_ok);
+    if (w == 0)
+        store_counts(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, t,
                      accumulate);
-    }
 }
 
 }  // namespace pca
