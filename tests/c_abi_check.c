@@ -1,0 +1,62 @@
+/* Plain C99 client of the library's C ABI (include/hist.h, include/hist_bench.h).
+ * Built and run by tests/test_abi_cpu.py with gcc, no GPU needed: every entry
+ * point must link, and calls with bad arguments must return the documented
+ * status without touching a device. Prints "ok" and exits 0 on success. */
+#include "hist.h"
+#include "hist_bench.h"
+
+#include <stdio.h>
+#include <string.h>
+
+static int failures = 0;
+
+static void expect(const char *what, int got, int want)
+{
+    if (got != want) {
+        printf("%s: got %d, want %d\n", what, got, want);
+        ++failures;
+    }
+}
+
+int main(void)
+{
+    uint64_t bytes = 0;
+    hist_plan_t *plan = NULL;
+    hist_plan_info_t info;
+    hist_plan_opts_t opts;
+    double ms[HIST_MAX_PHASES];
+    uint32_t launches[HIST_MAX_PHASES];
+    char buf[64];
+
+    memset(&opts, 0, sizeof(opts));
+    opts.aggregation = -1;
+    expect("workspace_size(num_bins=0)", hist_workspace_size(0, 10, &opts, &bytes),
+           HIST_ERR_INVALID_ARG);
+    expect("workspace_size(bytes=NULL)", hist_workspace_size(10, 10, NULL, NULL),
+           HIST_ERR_INVALID_ARG);
+    opts.path = 9;
+    expect("workspace_size(bad path)", hist_workspace_size(10, 10, &opts, &bytes),
+           HIST_ERR_INVALID_ARG);
+    expect("plan_create(NULL)", hist_plan_create(NULL, 10, 10, NULL, NULL, 0),
+           HIST_ERR_INVALID_ARG);
+    expect("plan_create(num_bins=0)", hist_plan_create(&plan, 0, 10, NULL, NULL, 0),
+           HIST_ERR_INVALID_ARG);
+    expect("run(NULL)", hist_run(NULL, NULL, NULL, 0, 1, NULL), HIST_ERR_INVALID_ARG);
+    expect("run_accumulate(NULL)", hist_run_accumulate(NULL, NULL, NULL, 0, 1, NULL),
+           HIST_ERR_INVALID_ARG);
+    expect("plan_info(NULL)", hist_plan_info(NULL, &info), HIST_ERR_INVALID_ARG);
+    expect("plan_describe(NULL)", hist_plan_describe(NULL, buf, sizeof(buf)), HIST_ERR_INVALID_ARG);
+    expect("timing_enable(NULL)", hist_plan_timing_enable(NULL, 1), HIST_ERR_INVALID_ARG);
+    expect("timing_read(NULL)", hist_plan_timing_read(NULL, ms, launches), HIST_ERR_INVALID_ARG);
+    expect("phase_name(0)", strcmp(hist_plan_phase_name(NULL, 0), "sweep"), 0);
+    expect("bench_global_atomic(NULL)", hist_bench_global_atomic(NULL, NULL, 0, 1, NULL),
+           HIST_ERR_INVALID_ARG);
+    expect("bench_read(NULL)", hist_bench_read(NULL, 16, NULL, NULL), HIST_ERR_INVALID_ARG);
+    expect("bench_copy(NULL)", hist_bench_copy(NULL, NULL, 16, NULL), HIST_ERR_INVALID_ARG);
+    expect("bench_lds_atomic(bad pattern)", hist_bench_lds_atomic(4, 0, 1, NULL, 0, NULL),
+           HIST_ERR_INVALID_ARG);
+    expect("status_str(OK)", strcmp(hist_status_str(HIST_OK), "ok"), 0);
+    hist_plan_destroy(NULL);
+    if (failures == 0) printf("ok\n");
+    return failures == 0 ? 0 : 1;
+}

@@ -7,6 +7,8 @@ import ctypes
 import glob
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -98,3 +100,19 @@ def test_product_path_does_not_import_the_oracle():
             text = open(path).read()
             assert "import oracle" not in text and "from oracle" not in text, path
             assert "oracle_hist" not in text, path
+
+
+def test_plain_c_client_compiles_links_and_gets_documented_errors(tmp_path):
+    """The headers are C: a C99 program includes them, links the library and
+    gets the documented statuses for bad arguments (no device needed)."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    libdir = os.path.dirname(hist.LIBRARY)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "c_abi_check.c"), "-L", libdir, "-lpca_hist",
+                    f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout + out.stderr
