@@ -264,8 +264,16 @@ __device__ __forceinline__ void write_pair16(const Partials &P, uint64_t blk_eve
 {
     const uint32_t lane = lane_id();
     const uint32_t any = w.x | w.y | w.z | w.w;
+    const uint64_t wide = __ballot((any & 0xFFF0FFF0u) != 0u);
+    if (wide == 0) {
+        // the common case: both blocks fit 4 bits, plane 0 only
+        store_through(reinterpret_cast<uint32_t *>(P.plane0 + blk_even * kPlaneBytes) + lane,
+                      plane_word16(w, 0));
+        if ((lane & 31u) == 0) P.width[blk_even + (lane >> 5)] = 0;
+        return;
+    }
     const uint32_t sh = lane & 32u;
-    const uint32_t b4 = (uint32_t)(__ballot((any & 0xFFF0FFF0u) != 0u) >> sh);
+    const uint32_t b4 = (uint32_t)(wide >> sh);
     const uint32_t b8 = (uint32_t)(__ballot((any & 0xFF00FF00u) != 0u) >> sh);
     const uint32_t planes = b8 ? 4u : b4 ? 2u : 1u;
     const uint64_t blk = blk_even + (lane >> 5);
