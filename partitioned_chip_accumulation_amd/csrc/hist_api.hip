@@ -430,64 +430,39 @@ struct PhaseTimer {
 
 }  // namespace
 
-extern "C" {
-
-const char *hist_status_str(hist_status_t s)
-{
-    switch (s) {
-    case HIST_OK: return "ok";
-    case HIST_ERR_INVALID_ARG: return "invalid argument";
-    case HIST_ERR_UNSUPPORTED: return "unsupported (no gfx950 device current, or size too large)";
-    case HIST_ERR_WORKSPACE: return "workspace missing or too small";
-    case HIST_ERR_HIP: return "HIP error";
-    }
-    return "unknown status";
-}
-
-hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *opts,
-                                  uint64_t *bytes)
-{
-    if (!bytes || num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
-    hist_status_t st = check_opts(opts);
-    if (st != HIST_OK) return st;
-    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
-    hist_plan p;
-    st = query_device(&p.dev);
-    if (st != HIST_OK) return st;
-    st = design(&p, num_bins, max_n, opts);
-    if (st != HIST_OK) return st;
-    *bytes = p.need;
-    return HIST_OK;
-}
-
-hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
-                               const hist_plan_opts_t *opts, void *workspace,
-                               uint64_t workspace_bytes)
-{
-    if (!plan) return HIST_ERR_INVALID_ARG;
-    *plan = nullptr;
-    if (num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
-    hist_status_t st = check_opts(opts);
-    if (st != HIST_OK) return st;
-    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
-    if (((uintptr_t)workspace & 255u) != 0) return HIST_ERR_INVALID_ARG;
-    hist_plan *p = new (std::nothrow) hist_plan();
-    if (!p) return HIST_ERR_INVALID_ARG;
-    st = query_device(&p->dev);
-    if (st == HIST_OK) st = design(p, num_bins, max_n, opts);
-    if (st == HIST_OK && p->need > 0 && (!workspace || workspace_bytes < p->need))
-        st = HIST_ERR_WORKSPACE;
-    if (st != HIST_OK) {
-        delete p;
-        return st;
-    }
-    p->ws = static_cast<char *>(workspace);
-    p->ws_bytes = workspace_bytes;
-    *plan = p;
-    return HIST_OK;
-}
-
 namespace {
+
+template <bool ACC>
+hipError_t launch_merge(const pca::Partials &P, uint32_t G, uint32_t num_bins, uint32_t *counts,
+                        uint32_t nblk, hipStream_t s)
+{
+    if (G <= 256)
+        hipLaunchKernelGGL((pca::k_merge<4, ACC>), dim3(nblk), dim3(256), 0, s, P, G, num_bins, counts);
+    else if (G <= 512)
+        hipLaunchKernelGGL((pca::k_merge<8, ACC>), dim3(nblk), dim3(512), 0, s, P, G, num_bins, counts);
+    else
+        hipLaunchKernelGGL((pca::k_merge<16, ACC>), dim3(nblk), dim3(1024), 0, s, P, G, num_bins,
+                           counts);
+    return hipGetLastError();
+}
+
+// A range's slots are the rows of its overlapping owners, about W / R + 1 of
+// them: one wave per block (64 rows per round trip) once ranges are many,
+// four (256 rows) when each range has many owners.
+template <bool ACC>
+hipError_t launch_merge_slots(const hist_plan *p, uint32_t num_bins, uint32_t *counts,
+                              hipStream_t s)
+{
+    const pca::Partials P = plan_partials(p);
+    const uint32_t *tot = reinterpret_cast<const uint32_t *>(p->ws + p->off_totals);
+    if (p->ranges >= 16)
+        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC>), dim3(ceil_div(num_bins, 256)), dim3(64), 0,
+                           s, P, tot, p->ranges, p->range_bins, num_bins, p->owners, counts);
+    else
+        hipLaunchKernelGGL((pca::k_merge_slots<4, ACC>), dim3(ceil_div(num_bins, 256)), dim3(256), 0,
+                           s, P, tot, p->ranges, p->range_bins, num_bins, p->owners, counts);
+    return hipGetLastError();
+}
 
 hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
                        uint32_t num_bins, hipStream_t stream, uint32_t accumulate)
@@ -546,17 +521,10 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         if (G > 1) {
             tm.begin(PH_MERGE);
             // one batch of loads per lane covers 8 rows x 8 rounds per wave
-            if (G <= 256)
-                hipLaunchKernelGGL(pca::k_merge<4>, dim3(p->nblk), dim3(256), 0, stream, a.out, G,
-                                   num_bins, counts, accumulate);
-            else if (G <= 512)
-                hipLaunchKernelGGL(pca::k_merge<8>, dim3(p->nblk), dim3(512), 0, stream, a.out, G,
-                                   num_bins, counts, accumulate);
-            else
-                hipLaunchKernelGGL(pca::k_merge<16>, dim3(p->nblk), dim3(1024), 0, stream, a.out, G,
-                                   num_bins, counts, accumulate);
+            e = accumulate ? launch_merge<true>(a.out, G, num_bins, counts, p->nblk, stream)
+                           : launch_merge<false>(a.out, G, num_bins, counts, p->nblk, stream);
             tm.end(PH_MERGE);
-            if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+            if (e != hipSuccess) return HIST_ERR_HIP;
         }
         return HIST_OK;
     }
@@ -591,27 +559,72 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     tm.end(PH_OWNER);
     if (e != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_SLOTS);
-    {
-        // A range's slots are the rows of its overlapping owners, about W / R + 1
-        // of them: one wave per block (64 rows per round trip) once ranges are
-        // many, four (256 rows) when each range has many owners.
-        const pca::Partials P = plan_partials(p);
-        const uint32_t *tot = reinterpret_cast<const uint32_t *>(p->ws + p->off_totals);
-        if (p->ranges >= 16)
-            hipLaunchKernelGGL(pca::k_merge_slots<1>, dim3(ceil_div(num_bins, 256)), dim3(64), 0,
-                               stream, P, tot, p->ranges, p->range_bins, num_bins, p->owners,
-                               counts, accumulate);
-        else
-            hipLaunchKernelGGL(pca::k_merge_slots<4>, dim3(ceil_div(num_bins, 256)), dim3(256), 0,
-                               stream, P, tot, p->ranges, p->range_bins, num_bins, p->owners,
-                               counts, accumulate);
-    }
+    e = accumulate ? launch_merge_slots<true>(p, num_bins, counts, stream)
+                   : launch_merge_slots<false>(p, num_bins, counts, stream);
     tm.end(PH_SLOTS);
-    if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+    if (e != hipSuccess) return HIST_ERR_HIP;
     return HIST_OK;
 }
 
 }  // namespace
+
+extern "C" {
+
+const char *hist_status_str(hist_status_t s)
+{
+    switch (s) {
+    case HIST_OK: return "ok";
+    case HIST_ERR_INVALID_ARG: return "invalid argument";
+    case HIST_ERR_UNSUPPORTED: return "unsupported (no gfx950 device current, or size too large)";
+    case HIST_ERR_WORKSPACE: return "workspace missing or too small";
+    case HIST_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *opts,
+                                  uint64_t *bytes)
+{
+    if (!bytes || num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
+    hist_status_t st = check_opts(opts);
+    if (st != HIST_OK) return st;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    hist_plan p;
+    st = query_device(&p.dev);
+    if (st != HIST_OK) return st;
+    st = design(&p, num_bins, max_n, opts);
+    if (st != HIST_OK) return st;
+    *bytes = p.need;
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
+                               const hist_plan_opts_t *opts, void *workspace,
+                               uint64_t workspace_bytes)
+{
+    if (!plan) return HIST_ERR_INVALID_ARG;
+    *plan = nullptr;
+    if (num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
+    hist_status_t st = check_opts(opts);
+    if (st != HIST_OK) return st;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    if (((uintptr_t)workspace & 255u) != 0) return HIST_ERR_INVALID_ARG;
+    hist_plan *p = new (std::nothrow) hist_plan();
+    if (!p) return HIST_ERR_INVALID_ARG;
+    st = query_device(&p->dev);
+    if (st == HIST_OK) st = design(p, num_bins, max_n, opts);
+    if (st == HIST_OK && p->need > 0 && (!workspace || workspace_bytes < p->need))
+        st = HIST_ERR_WORKSPACE;
+    if (st != HIST_OK) {
+        delete p;
+        return st;
+    }
+    p->ws = static_cast<char *>(workspace);
+    p->ws_bytes = workspace_bytes;
+    *plan = p;
+    return HIST_OK;
+}
+
 
 hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
                        uint32_t num_bins, hipStream_t stream)

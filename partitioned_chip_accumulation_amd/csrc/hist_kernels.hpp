@@ -680,14 +680,15 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 }
 
 // The exclusive owner's write of bins b0..b0+3 (those below num_bins):
-// counts = t, or counts += t (mod 2^32) when accumulate != 0.
+// counts = t, or counts += t (mod 2^32) when ACC.
+template <bool ACC>
 __device__ __forceinline__ void store_counts(uint32_t *__restrict__ counts, uint64_t b0,
-                                             uint32_t num_bins, u32x4 t, uint32_t accumulate)
+                                             uint32_t num_bins, u32x4 t)
 {
     const uint32_t v[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        if (b0 + k < num_bins) counts[b0 + k] = (accumulate ? counts[b0 + k] : 0u) + v[k];
+        if (b0 + k < num_bins) counts[b0 + k] = (ACC ? counts[b0 + k] : 0u) + v[k];
 }
 
 // ---------------------------------------------------------------------------
@@ -806,15 +807,15 @@ struct AllRows {
     __device__ bool operator()(uint32_t) const { return true; }
 };
 
-template <int WAVES>
+// ACC: add into counts instead of overwriting it (a template parameter, so
+// that the overwriting kernel carries no branch around its stores).
+template <int WAVES, bool ACC>
 __global__ __launch_bounds__(WAVES * 64) void k_merge(Partials P, uint32_t rows, uint32_t num_bins,
-                                                      uint32_t *__restrict__ counts,
-                                                      uint32_t accumulate)
+                                                      uint32_t *__restrict__ counts)
 {
     const u32x4 t = merge_block<WAVES>(P, 0, rows, blockIdx.x, AllRows{});
     if ((threadIdx.x >> 6) == 0)
-        store_counts(counts, (uint64_t)blockIdx.x * kBlockBins + lane_id() * 4u, num_bins, t,
-                     accumulate);
+        store_counts<ACC>(counts, (uint64_t)blockIdx.x * kBlockBins + lane_id() * 4u, num_bins, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -1228,12 +1229,11 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
 // owners first..last are consecutive rows, summed by merge_block. An owner
 // that took no element (possible only when there are fewer elements than
 // owners) wrote no slot and is skipped. Empty ranges give zeros.
-template <int WAVES>
+template <int WAVES, bool ACC>
 __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint32_t *__restrict__ totals,
                                                             uint32_t ranges, uint32_t range_bins,
                                                             uint32_t num_bins, uint32_t owners,
-                                                            uint32_t *__restrict__ counts,
-                                                            uint32_t accumulate)
+                                                            uint32_t *__restrict__ counts)
 {
     __shared__ uint64_t se[3];
     const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
@@ -1275,8 +1275,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
     };
     const u32x4 t = merge_block<WAVES>(P, (uint64_t)first + r, rows, lb, row_ok);
     if (w == 0)
-        store_counts(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, t,
-                     accumulate);
+        store_counts<ACC>(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, t);
 }
 
 }  // namespace pca
