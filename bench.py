@@ -28,8 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCES = ["partitioned_chip_accumulation_amd/csrc/hist_kernels.hpp",
-                  "partitioned_chip_accumulation_amd/csrc/hist_api.hip"]
+KERNEL_SOURCES = [f"partitioned_chip_accumulation_amd/csrc/{f}" for f in (
+    "hist_common.hpp", "hist_counters16.hpp", "hist_partials.hpp", "hist_sweep.hpp",
+    "hist_scatter.hpp", "hist_kernels.hpp", "hist_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

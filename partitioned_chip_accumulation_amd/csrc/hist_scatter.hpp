@@ -1,0 +1,473 @@
+// hist_scatter.hpp -- the two-phase path (SCATTER): partition, range scans,
+// per-owner histograms, slot merge
+//
+// Part of the gfx950 kernels of libpca_hist.so (see hist_kernels.hpp for the
+// overview).
+#pragma once
+
+#include "hist_common.hpp"
+#include "hist_partials.hpp"
+
+namespace pca {
+
+// ---------------------------------------------------------------------------
+// Two-phase path.
+// WG-wide exclusive scan of one value per thread; returns this thread's
+// exclusive prefix and writes the total to *total (all threads).
+template <int WG>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
+                                                         uint32_t *total)
+{
+    constexpr int NW = WG / 64;
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane == 63) scratch[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        const uint32_t s = lane < (uint32_t)NW ? scratch[lane] : 0u;
+        const uint32_t si = wave_inclusive_scan(s);
+        if (lane < (uint32_t)NW) scratch[NW + lane] = si - s;
+        if (lane == 63) scratch[2 * NW] = si;
+    }
+    __syncthreads();
+    *total = scratch[2 * NW];
+    return scratch[NW + w] + incl - v;
+}
+
+// Phase 1b: per range r, tpre[r][t] = sum of tcnt[r][t'] over t' < t, and
+// totals[r] = the range's element count. Two passes, both spread over
+// (range, segment of kScanSeg tiles) workgroups so that every CU takes part:
+// k_seg_scan writes each segment's local exclusive prefix and its total,
+// k_seg_fix adds the totals of the range's earlier segments (and the last
+// segment's workgroup writes the range total).
+constexpr uint32_t kScanSeg = 4096;
+
+template <int WG>
+__global__ __launch_bounds__(WG) void k_seg_scan(const uint32_t *__restrict__ tcnt, uint32_t tiles,
+                                                 uint32_t nseg, uint32_t *__restrict__ tpre,
+                                                 uint32_t *__restrict__ segtot)
+{
+    __shared__ uint32_t scratch[2 * (WG / 64) + 1];
+    const uint32_t r = blockIdx.x / nseg, sg = blockIdx.x % nseg, tid = threadIdx.x;
+    const uint32_t s0 = sg * kScanSeg, s1 = min(s0 + kScanSeg, tiles);
+    const uint32_t *c = tcnt + (uint64_t)r * tiles;
+    uint32_t *p = tpre + (uint64_t)r * tiles;
+    constexpr uint32_t PER = kScanSeg / WG;
+    const uint32_t t0 = s0 + tid * PER;
+    uint32_t v[PER], sum = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        v[k] = t0 + k < s1 ? c[t0 + k] : 0u;
+        sum += v[k];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<WG>(sum, scratch, &total);
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        if (t0 + k < s1) p[t0 + k] = run;
+        run += v[k];
+    }
+    if (tid == 0) segtot[(uint64_t)r * nseg + sg] = total;
+}
+
+template <int WG>
+__global__ __launch_bounds__(WG) void k_seg_fix(uint32_t tiles, uint32_t nseg,
+                                                uint32_t *__restrict__ tpre,
+                                                const uint32_t *__restrict__ segtot,
+                                                uint32_t *__restrict__ totals)
+{
+    const uint32_t r = blockIdx.x / nseg, sg = blockIdx.x % nseg, tid = threadIdx.x;
+    const uint32_t *st = segtot + (uint64_t)r * nseg;
+    uint32_t off = 0;
+    for (uint32_t k = 0; k < sg; ++k) off += st[k];
+    if (sg == nseg - 1 && tid == 0) totals[r] = off + st[sg];
+    if (off == 0) return;
+    uint32_t *p = tpre + (uint64_t)r * tiles;
+    const uint32_t s0 = sg * kScanSeg, s1 = min(s0 + kScanSeg, tiles);
+    for (uint32_t t = s0 + tid; t < s1; t += WG) p[t] += off;
+}
+
+// Exclusive prefix of totals[0..ranges) into bs[0..ranges], by wave 0.
+__device__ __forceinline__ void range_starts(const uint32_t *__restrict__ totals, uint32_t ranges,
+                                             uint64_t *bs)
+{
+    if (threadIdx.x < 64) {
+        const uint32_t lane = threadIdx.x;
+        uint64_t carry = 0;
+        for (uint32_t c = 0; c < ranges; c += 64) {
+            const uint32_t i = c + lane;
+            const uint32_t v = i < ranges ? totals[i] : 0u;
+            const uint32_t incl = wave_inclusive_scan(v);  // < 2^32: sum of <= 64 counts of one call
+            if (i < ranges) bs[i] = carry + incl - v;
+            carry += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) bs[ranges] = carry;
+    }
+}
+
+// Owner workgroup i of W covers positions [i*N/W, (i+1)*N/W) of the
+// concatenation of all ranges' elements; this returns the owner of position p.
+__device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
+{
+    return (uint32_t)(((p + 1) * W - 1) / N);
+}
+
+// Phase 1: route every element of a tile to its owning range.
+//
+// Tile t is body vectors [t * WG * VPT, ...) (tile 0 also takes the head
+// scalars, the last tile the tail scalars). Each valid element x (x <
+// num_bins) is owned by range r = x >> shift, where it is slot x & mask. The
+// workgroup counts its elements per range in LDS; each element's returning
+// LDS atomic gives its rank among the tile's elements of that range, and an
+// exclusive scan of the counts gives each range's start, so the tile's slots
+// are grouped by range in an LDS staging buffer and copied out with full
+// 16-byte stores to stage[t * stage_cap ...]. Only the 16-bit slot is kept:
+// the range is implied by the position.
+//
+// Returning atomics on one LDS word are served one lane at a time (each lane
+// needs its own rank), so every range's counter is split into 2^qlog
+// sub-counters chosen by lane (lane mod 2^qlog): lanes that route to the same
+// range then rarely share a word. The scan runs over [range][sub] order, so a
+// range's elements stay contiguous. Per tile and range the kernel writes the
+// run's length and start (tcnt, tbase; layout [range][tile]). Element order
+// inside a run is whatever the atomics gave; counts do not depend on it.
+template <int WG, int VPT>
+__global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
+                                                  uint32_t ranges, uint32_t qlog, uint32_t tiles,
+                                                  uint16_t *__restrict__ stage, uint32_t stage_cap,
+                                                  uint32_t *__restrict__ tcnt,
+                                                  uint32_t *__restrict__ tbase)
+{
+    extern __shared__ u32x4 smem4[];
+    const uint32_t nsub = ranges << qlog;  // <= 2 * WG
+    const uint32_t npad = (nsub + 3u) & ~3u;
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem4);
+    uint32_t *base = cnt + npad;
+    uint32_t *scratch = base + npad;  // block scan scratch + total
+    uint16_t *st = reinterpret_cast<uint16_t *>(scratch + 64);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t mask = (1u << shift) - 1u;
+    const uint32_t q = lane_id() & ((1u << qlog) - 1u);
+    constexpr int E = VPT * 4;
+    const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
+
+    // A persistent workgroup walks tiles blockIdx.x, + gridDim.x, ...; the
+    // next tile's elements are loaded while the current one is counted.
+    uint32_t nx[E + 2];
+    auto load_tile = [&](uint32_t t) {
+        const uint64_t vb = (uint64_t)t * (WG * VPT);
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const uint64_t v = vb + (uint64_t)u * WG + tid;
+            const i32x4 qv = v < in.nvec ? body[v] : i32x4{-1, -1, -1, -1};
+            nx[4 * u + 0] = (uint32_t)qv.x;
+            nx[4 * u + 1] = (uint32_t)qv.y;
+            nx[4 * u + 2] = (uint32_t)qv.z;
+            nx[4 * u + 3] = (uint32_t)qv.w;
+        }
+        nx[E] = (t == 0 && tid < in.head) ? (uint32_t)in.ptr[tid] : 0xFFFFFFFFu;
+        nx[E + 1] = (t == tiles - 1 && tid < in.tail) ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid]
+                                                      : 0xFFFFFFFFu;
+    };
+    uint32_t t = blockIdx.x;
+    if (t < tiles) load_tile(t);
+    for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
+    __syncthreads();
+
+    for (; t < tiles; t += gridDim.x) {
+        uint32_t x[E + 2], rk[E + 2];
+#pragma unroll
+        for (int e = 0; e < E + 2; ++e) x[e] = nx[e];
+        if (t + gridDim.x < tiles) load_tile(t + gridDim.x);
+#pragma unroll
+        for (int e = 0; e < E + 2; ++e) {
+            rk[e] = 0u;
+            if (x[e] < num_bins) rk[e] = lds_add_rtn(cnt, ((x[e] >> shift) << qlog) | q, 1u);
+        }
+        __syncthreads();
+
+        {
+            const uint32_t i0 = 2 * tid, i1 = 2 * tid + 1;
+            const uint32_t c0 = i0 < nsub ? cnt[i0] : 0u, c1 = i1 < nsub ? cnt[i1] : 0u;
+            uint32_t total;
+            const uint32_t ex = block_exclusive_scan<WG>(c0 + c1, scratch, &total);
+            if (i0 < nsub) base[i0] = ex;
+            if (i1 < nsub) base[i1] = ex + c0;
+            if (tid == 0) scratch[63] = total;
+        }
+        __syncthreads();
+        const uint32_t nvalid = scratch[63];
+        for (uint32_t r = tid; r < ranges; r += WG) {
+            const uint32_t b0 = base[r << qlog];
+            const uint32_t b1 = r + 1 < ranges ? base[(r + 1) << qlog] : nvalid;
+            tcnt[(uint64_t)r * tiles + t] = b1 - b0;
+            tbase[(uint64_t)r * tiles + t] = b0;
+        }
+#pragma unroll
+        for (int e = 0; e < E + 2; ++e)
+            if (x[e] < num_bins) st[base[((x[e] >> shift) << qlog) | q] + rk[e]] = (uint16_t)(x[e] & mask);
+        __syncthreads();
+
+        // counters are free again: clear them for the next tile while copying out
+        for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
+        const uint32_t nv = (nvalid + 7u) >> 3;
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(st);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)t * stage_cap);
+        for (uint32_t i = tid; i < nv; i += WG) d4[i] = s4[i];
+        __syncthreads();  // staging and counters are reused by the next tile
+    }
+}
+
+// Wave-cooperative search in a non-decreasing array: the last index i in
+// [0, n) with a[i] <= key (0 if none). Each round samples 64 evenly spaced
+// entries with one load per lane, so a search costs log64(n) round trips.
+__device__ __forceinline__ uint32_t wave_find_last_le(const uint32_t *__restrict__ a, uint32_t n,
+                                                      uint32_t key)
+{
+    const uint32_t lane = lane_id();
+    uint32_t lo = 0, hi = n;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const uint32_t step = (hi - lo + 63) / 64;
+        const uint32_t idx = lo + lane * step;
+        const bool le = idx < hi && a[idx] <= key;
+        const uint64_t m = __ballot(le);
+        const uint32_t j = m ? 63u - (uint32_t)__builtin_clzll(m) : 0u;
+        lo = lo + j * step;
+        hi = min(lo + step, hi);
+    }
+    return lo;
+}
+
+// Count the slots of one staged vector (8 uint16 slots as 4 words) whose
+// index e lies in [first, last), through the wave's hot slot when AGG == 1.
+template <int AGG>
+__device__ __forceinline__ void count_slots(uint32_t *lds, HotSlot &hs, const uint32_t (&words)[4],
+                                            uint32_t first, uint32_t last)
+{
+    // the hot slot is wave-uniform: read it as a scalar so that this test is one branch
+    const uint32_t h = AGG == 1 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)hs.h) : kNoSlot;
+    if (AGG == 1 && h != kNoSlot) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t s = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+            const bool ok = (uint32_t)e >= first && (uint32_t)e < last;
+            const bool m = ok && s == h;
+            hs.c += m ? 1u : 0u;
+            lds_count<0>(lds, s, ok && !m);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t s = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+            const bool ok = (uint32_t)e >= first && (uint32_t)e < last;
+            lds_count<AGG == 1 ? 0 : AGG>(lds, s, ok);
+        }
+    }
+}
+
+// Phase 2: owner workgroups build LDS histograms from the routed slots.
+//
+// All ranges' elements, concatenated in range order, are split evenly over
+// W owner workgroups, so a range holding most of the input (a hot bin, a
+// Gaussian bump) is shared by as many owners as its size calls for. Owner i
+// takes positions [i*N/W, (i+1)*N/W); for every range r it overlaps it
+// zeroes an LDS slice of the range's bins, counts the overlapped elements,
+// and writes the slice to partial slot i + r (i + r is distinct for every
+// (owner, range) pair that occurs, because both grow along the
+// concatenation). Inside one range the elements are the tiles' runs in tile
+// order. Waves work without barriers, in teams: a team takes groups of RPW
+// consecutive tiles (every (NW / S)-th group of the owner's span) and each
+// of its S waves reads the group's run metadata with one lane per tile. Run
+// m then feeds slot m of every lane's batch of RPW 16-byte loads (the team's
+// lanes stripe each run's vectors), so every run parameter is wave-uniform
+// and a vector costs a compare, an address and two bounds. The runs of one range are
+// about equally long for shuffled inputs, so the slots stay busy and the
+// waves balanced. With no workgroup barrier until the slice is flushed, the
+// waves drift apart and one wave's loads overlap the others' counting.
+template <int WG, int UNROLL, int AGG>
+__global__ __launch_bounds__(WG) void k_bucket_hist(
+    const uint16_t *__restrict__ stage, uint32_t stage_cap, const uint32_t *__restrict__ tcnt,
+    const uint32_t *__restrict__ tbase, const uint32_t *__restrict__ tpre,
+    const uint32_t *__restrict__ totals, uint32_t ranges, uint32_t tiles, uint32_t range_bins,
+    uint32_t num_bins, uint32_t owners, Partials out)
+{
+    extern __shared__ u32x4 lds4[];
+    uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
+    uint64_t *bs = reinterpret_cast<uint64_t *>(lds + range_bins);  // [ranges + 1]
+    uint32_t *misc = reinterpret_cast<uint32_t *>(bs + ranges + 1);  // [0] ta [1] tb
+    const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    constexpr uint32_t NW = WG / 64;  // waves
+    constexpr uint32_t RPW = UNROLL;  // tiles (runs) per wave group = loads in flight per lane
+
+    range_starts(totals, ranges, bs);
+    __syncthreads();
+    const uint64_t N = bs[ranges];
+    const uint32_t i = blockIdx.x;
+    const uint64_t e0 = (uint64_t)i * N / owners, e1 = (uint64_t)(i + 1) * N / owners;
+    if (e0 >= e1) return;  // whole workgroup: no element to count
+
+    uint32_t r;  // first range overlapping [e0, e1): the last r with bs[r] <= e0
+    {
+        uint32_t lo = 0, hi = ranges - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (bs[mid] <= e0) lo = mid; else hi = mid - 1;
+        }
+        r = lo;
+    }
+    const i32x4 *stage_vec = reinterpret_cast<const i32x4 *>(stage);
+    for (; r < ranges && bs[r] < e1; ++r) {
+        const uint64_t rb = bs[r], re = bs[r + 1];
+        if (re <= e0 || rb == re) continue;  // uniform
+        const uint32_t p0 = (uint32_t)(max(e0, rb) - rb), p1 = (uint32_t)(min(e1, re) - rb);
+        const uint32_t len = min(range_bins, num_bins - r * range_bins);
+        const uint32_t *rc = tcnt + (uint64_t)r * tiles;
+        const uint32_t *rbase = tbase + (uint64_t)r * tiles;
+        const uint32_t *rpre = tpre + (uint64_t)r * tiles;
+        zero_lds<WG>(lds, len);
+        if (w == 0) {
+            // runs overlapping [p0, p1): from the last t with rpre[t] <= p0 to the
+            // first t with rpre[t] >= p1
+            const uint32_t ta = wave_find_last_le(rpre, tiles, p0);
+            uint32_t tb = wave_find_last_le(rpre, tiles, p1 - 1) + 1;
+            if (lane == 0) {
+                misc[0] = ta;
+                misc[1] = tb;
+            }
+        }
+        __syncthreads();
+        const uint32_t ta = misc[0], tb = misc[1];
+        HotSlot hs;
+
+        // Teams of S waves: team w / S takes groups of RPW tiles (every NW / S-th
+        // group), and its S waves stripe each run's vectors. S is the smallest
+        // power of two that still leaves every team two groups, so long runs
+        // (few ranges, or an input piled into one range) keep all waves busy.
+        const uint32_t ngroups = (tb - ta + RPW - 1) / RPW;
+        uint32_t S = 1;
+        while (S < NW && ngroups < 2u * (NW / S)) S *= 2u;
+        const uint32_t team = w / S, member = w % S;
+        for (uint32_t g0 = ta + team * RPW; g0 < tb; g0 += (NW / S) * RPW) {
+            // lane m < RPW: the run of tile g0 + m, clipped to [p0, p1)
+            uint32_t vlo = 0, nv = 0, skip = 0, used = 0;
+            const uint32_t t = g0 + lane;
+            if (lane < RPW && t < tb) {
+                const uint32_t c = rc[t], q = rpre[t], bse = rbase[t];
+                const uint32_t lo_e = max(p0, q) - q;
+                const uint32_t hi_e = min(p1, q + c) - q;
+                if (c != 0u && hi_e > lo_e) {
+                    const uint64_t g_lo = (uint64_t)t * stage_cap + bse + lo_e;
+                    const uint64_t g_hi = g_lo + (hi_e - lo_e);
+                    vlo = (uint32_t)(g_lo >> 3);
+                    nv = (uint32_t)(((g_hi + 7) >> 3) - (g_lo >> 3));
+                    skip = (uint32_t)(g_lo & 7u);
+                    used = hi_e - lo_e;
+                }
+            }
+            // Run m of the group takes slot m of every lane's batch of RPW vector
+            // loads, so all run parameters stay wave-uniform (scalar registers).
+            uint32_t run_n[RPW], run_v[RPW], run_s[RPW], run_u[RPW], steps = 0;
+#pragma unroll
+            for (uint32_t m = 0; m < RPW; ++m) {
+                run_n[m] = (uint32_t)__builtin_amdgcn_readlane((int)nv, (int)m);
+                run_v[m] = (uint32_t)__builtin_amdgcn_readlane((int)vlo, (int)m);
+                run_s[m] = (uint32_t)__builtin_amdgcn_readlane((int)skip, (int)m);
+                run_u[m] = (uint32_t)__builtin_amdgcn_readlane((int)used, (int)m);
+                steps = max(steps, (run_n[m] + 64u * S - 1u) / (64u * S));
+            }
+            for (uint32_t it = 0; it < steps; ++it) {
+                const uint32_t d = (it * S + member) * 64u + lane;  // this lane's vector in each run
+                const uint32_t k8 = d * 8u;          // run element of vector element e is k8 + e - skip
+                i32x4 qv[RPW];
+                uint32_t first[RPW], last[RPW];
+#pragma unroll
+                for (uint32_t m = 0; m < RPW; ++m) {
+                    const bool ok = d < run_n[m];
+                    first[m] = ok ? (k8 < run_s[m] ? run_s[m] - k8 : 0u) : 8u;
+                    last[m] = ok ? min(8u, run_s[m] + run_u[m] - k8) : 0u;
+                    qv[m] = ok ? stage_vec[(uint64_t)run_v[m] + d] : i32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (uint32_t k = 0; k < RPW; ++k) {
+                    const uint32_t words[4] = {(uint32_t)qv[k].x, (uint32_t)qv[k].y,
+                                               (uint32_t)qv[k].z, (uint32_t)qv[k].w};
+                    if constexpr (AGG == 1) {
+                        uint32_t nxt;
+                        if (hot_should_switch(hs, words[0] & 0xFFFFu, first[k] == 0u && last[k] > 0u,
+                                              &nxt)) {
+                            const uint32_t tk = hot_take(hs);
+                            if (lane == 0 && tk != 0u) lds_add(lds, hs.h, tk);
+                            hs.h = nxt;
+                        }
+                    }
+                    count_slots<AGG>(lds, hs, words, first[k], last[k]);
+                }
+            }
+        }
+        {
+            const uint32_t t = hot_take(hs);
+            if (lane == 0 && t != 0u) lds_add(lds, hs.h, t);
+        }
+        __syncthreads();
+        flush_slice<WG, 32>(out, i + r, 0, lds, nullptr, 0, len, 0);
+        __syncthreads();
+    }
+}
+
+// Phase 2b: counts[b] for the bins of one range = the sum of the slots that
+// the owners overlapping the range wrote for it (exclusive owner per bin, no
+// global atomics). A workgroup handles one 256-bin block of one range. Owner
+// i wrote the range's slot to row i + r, so the slots of the overlapping
+// owners first..last are consecutive rows, summed by merge_block. An owner
+// that took no element (possible only when there are fewer elements than
+// owners) wrote no slot and is skipped. Empty ranges give zeros.
+template <int WAVES, bool ACC>
+__global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint32_t *__restrict__ totals,
+                                                            uint32_t ranges, uint32_t range_bins,
+                                                            uint32_t num_bins, uint32_t owners,
+                                                            uint32_t *__restrict__ counts)
+{
+    __shared__ uint64_t se[3];
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t bpr = range_bins / kBlockBins;  // blocks per range
+    const uint32_t r = blockIdx.x / bpr, lb = blockIdx.x % bpr;
+    if (w == 0) {
+        // start of range r, its end, and the grand total
+        uint64_t before = 0, all = 0;
+        for (uint32_t c = 0; c < ranges; c += 64) {
+            const uint32_t k = c + lane;
+            const uint64_t v = k < ranges ? totals[k] : 0u;
+            uint64_t a = v, bsum = k < r ? v : 0u;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                a += __shfl_xor(a, d, 64);
+                bsum += __shfl_xor(bsum, d, 64);
+            }
+            all += a;
+            before += bsum;
+        }
+        if (lane == 0) {
+            se[0] = before;
+            se[1] = before + totals[r];
+            se[2] = all;
+        }
+    }
+    __syncthreads();
+    const uint64_t rb = se[0], re = se[1], N = se[2];
+    uint32_t first = 0, rows = 0;
+    if (re > rb) {
+        first = owner_of(rb, N, owners);
+        rows = owner_of(re - 1, N, owners) - first + 1;
+    }
+    // every owner took at least one element when N >= owners
+    const bool all_nonempty = N >= owners;
+    auto row_ok = [&](uint32_t k) {
+        const uint64_t i = (uint64_t)first + k;
+        return all_nonempty || i * N / owners < (i + 1) * N / owners;
+    };
+    const u32x4 t = merge_block<WAVES>(P, (uint64_t)first + r, rows, lb, row_ok);
+    if (w == 0)
+        store_counts<ACC>(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, t);
+}
+
+}  // namespace pca

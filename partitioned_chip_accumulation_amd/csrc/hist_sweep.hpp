@@ -1,0 +1,199 @@
+// hist_sweep.hpp -- the single-pass sweep (FULL and RANGE paths)
+//
+// Part of the gfx950 kernels of libpca_hist.so (see hist_kernels.hpp for the
+// overview).
+#pragma once
+
+#include "hist_common.hpp"
+#include "hist_counters16.hpp"
+#include "hist_partials.hpp"
+
+namespace pca {
+
+// ---------------------------------------------------------------------------
+// Sweep: workgroup (g, r) counts chunk g of the input into bin range r.
+//
+// The page's kernel zeroes its slice, synchronises, accumulates, synchronises
+// and flushes (section "The cluster histogram"); the same zero -> barrier ->
+// accumulate -> barrier -> write shape runs here at workgroup scope, with the
+// owner filter replacing the remote atomic: an element x lands in this
+// workgroup's LDS iff lo <= x < lo + len, at slot x - lo (one unsigned
+// compare, which also rejects negatives and values >= num_bins).
+//
+// With ranges == 1 every workgroup owns all bins. With ranges > 1 the R
+// owners of a chunk all read it; xcds > 1 places them on one XCD
+// (workgroups are dispatched to the XCDs round-robin) so that one owner's
+// read brings the lines into the shared L2 for the others. Counters are
+// 32-bit (CW = 32) or packed 16-bit with carry events (CW = 16).
+//
+// Chunk g is body vectors [g * nvec / groups, (g + 1) * nvec / groups); the
+// head scalars belong to chunk 0 and the tail scalars to the last chunk.
+// The slice goes to partial row g in 256-bin blocks (range_bins is a multiple
+// of 256), or straight into direct[] (the output) when there is one chunk;
+// accumulate != 0 adds to direct[] instead of overwriting it.
+template <int WG, int UNROLL, int AGG, int CW>
+__global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
+                                              uint32_t ranges, uint32_t groups, uint32_t xcds,
+                                              uint32_t kshift, Partials out,
+                                              uint32_t *__restrict__ direct, uint32_t accumulate)
+{
+    extern __shared__ u32x4 lds4[];
+    uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
+    uint32_t *ev_count = lds + range_bins / 2;  // CW == 16 only
+    uint32_t *evlist = ev_count + 4;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t b = blockIdx.x;
+    uint32_t g, r;
+    if (xcds > 1) {
+        const uint32_t x = b % xcds, k = b / xcds;
+        r = k % ranges;
+        g = (k / ranges) * xcds + x;
+    } else {
+        g = b / ranges;
+        r = b % ranges;
+    }
+    const uint32_t lo = r * range_bins;
+    const uint32_t len = min(range_bins, num_bins - lo);
+
+    const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
+    const uint64_t v0 = (uint64_t)g * in.nvec / groups;
+    const uint64_t v1 = (uint64_t)(g + 1) * in.nvec / groups;
+    constexpr uint32_t STEP = WG * UNROLL;
+    uint64_t v = v0;
+
+    // The first batch of loads is in flight while the LDS slice is cleared,
+    // and every later batch is requested before the previous one is counted,
+    // so each wave keeps 2 * UNROLL vector loads outstanding.
+    i32x4 nx[UNROLL];
+    const bool any_full = v + STEP <= v1;
+    if (any_full) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + u * WG + tid);
+    }
+    zero_lds<WG>(lds, CW == 32 ? (len << kshift) : (len + 1) / 2);
+    if (CW == 16 && tid == 0) *ev_count = 0u;
+    __syncthreads();
+    // 32-bit counters may keep 2^kshift interleaved copies of the slice; a lane
+    // adds to copy (lane mod 2^kshift), so lanes of one wave that hit the same
+    // bin mostly touch different words and banks.
+    const uint32_t rep = lane_id() & ((1u << kshift) - 1u);
+
+    // AGG == 1: hot-slot register aggregation in the main loop; the ragged
+    // remainder counts plainly. AGG >= 2: leader-peel rounds everywhere.
+    constexpr int PEEL = AGG >= 2 ? AGG : 0;
+    auto count1 = [&](uint32_t s, bool ok) {
+        if constexpr (CW == 32) lds_count<PEEL>(lds, (s << kshift) | rep, ok);
+        else lds_count16<PEEL>(lds, evlist, ev_count, s, ok);
+    };
+    HotSlot hs;
+    auto hot_flush = [&]() {
+        if constexpr (AGG == 1) {
+            uint32_t t = hot_take(hs);
+            if (lane_id() == 0 && t != 0u) {
+                if constexpr (CW == 32) {
+                    lds_add(lds, hs.h << kshift, t);
+                } else {
+                    while (t != 0u) {
+                        const uint32_t kk = min(t, 32768u);
+                        add16(lds, evlist, ev_count, hs.h, kk);
+                        t -= kk;
+                    }
+                }
+            }
+        }
+    };
+    auto hot_check = [&](uint32_t s0, bool v0) {
+        if constexpr (AGG == 1) {
+            uint32_t nxt;
+            if (hot_should_switch(hs, s0, v0, &nxt)) {
+                hot_flush();
+                hs.h = nxt;
+            }
+        }
+    };
+    auto count4 = [&](const i32x4 q, bool ok) {
+        uint32_t s;
+        s = (uint32_t)q.x - lo; count1(s, ok && s < len);
+        s = (uint32_t)q.y - lo; count1(s, ok && s < len);
+        s = (uint32_t)q.z - lo; count1(s, ok && s < len);
+        s = (uint32_t)q.w - lo; count1(s, ok && s < len);
+    };
+
+    for (; any_full && v + STEP <= v1; v += STEP) {
+        i32x4 q[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) q[u] = nx[u];
+        if (v + 2 * STEP <= v1) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + STEP + u * WG + tid);
+        }
+        if constexpr (AGG <= 1) {
+            uint32_t sl[4 * UNROLL];
+            bool ok[4 * UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                sl[4 * u + 0] = (uint32_t)q[u].x - lo;
+                sl[4 * u + 1] = (uint32_t)q[u].y - lo;
+                sl[4 * u + 2] = (uint32_t)q[u].z - lo;
+                sl[4 * u + 3] = (uint32_t)q[u].w - lo;
+            }
+#pragma unroll
+            for (int e = 0; e < 4 * UNROLL; ++e) ok[e] = sl[e] < len;
+            if constexpr (AGG == 1) {
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) hot_check(sl[4 * u], ok[4 * u]);
+                if (hs.h != kNoSlot) {
+#pragma unroll
+                    for (int e = 0; e < 4 * UNROLL; ++e) {
+                        const bool m = ok[e] && sl[e] == hs.h;
+                        hs.c += m ? 1u : 0u;
+                        ok[e] = ok[e] && !m;
+                    }
+                }
+            }
+            if constexpr (CW == 16) {
+                count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4 * UNROLL; ++e) lds_count<0>(lds, (sl[e] << kshift) | rep, ok[e]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) count4(q[u], true);
+        }
+    }
+    // Remainder with a wave-uniform trip count.
+    for (; v < v1; v += WG) {
+        const bool ok = v + tid < v1;
+        const i32x4 q = ok ? load_vec<true>(body + v + tid) : i32x4{0, 0, 0, 0};
+        count4(q, ok);
+    }
+    {
+        const bool hok = g == 0 && tid < in.head;
+        const uint32_t hs = (hok ? (uint32_t)in.ptr[tid] : 0u) - lo;
+        count1(hs, hok && hs < len);
+        const bool tok = g == groups - 1 && tid < in.tail;
+        const uint32_t ts = (tok ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid] : 0u) - lo;
+        count1(ts, tok && ts < len);
+    }
+    hot_flush();
+    __syncthreads();
+
+    const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : 0u;
+    if (direct) {
+        const uint32_t npairs = (len + 511) / 512;
+        for (uint32_t p = tid >> 6; p < npairs; p += WG / 64) {
+            uint32_t c[8];
+            slice_octet<CW>(lds, evlist, nev, p, len, kshift, c);
+            const uint32_t b0 = lo + p * 512 + lane_id() * 8;
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i)
+                if (b0 + i < num_bins && b0 + i - lo < len)
+                    direct[b0 + i] = (accumulate ? direct[b0 + i] : 0u) + c[i];
+        }
+    } else {
+        flush_slice<WG, CW>(out, g, lo / kBlockBins, lds, evlist, nev, len, kshift);
+    }
+}
+
+}  // namespace pca
