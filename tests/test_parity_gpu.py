@@ -465,3 +465,72 @@ def test_scatter_edge_cases(case):
         return
     for agg in (0, 1):
         check(x, bins, f"scatter-{case}-agg{agg}", path="scatter", aggregation=agg)
+
+
+# --- seeded fuzz over sizes, paths and options -------------------------------
+
+def _fuzz_case(seed):
+    g = np.random.default_rng(1000 + seed)
+    num_bins = int(min(2**20, max(1, round(2 ** g.uniform(0, 20)))))
+    n = int(g.choice([0, 1, 7, int(g.integers(1, 5000)), int(g.integers(5000, 300_000))]))
+    kind = g.choice(["uniform", "skew", "onebin", "wild"])
+    if kind == "uniform":
+        x = g.integers(0, num_bins, size=n)
+    elif kind == "skew":
+        x = np.minimum(g.zipf(1.3, size=n) - 1, num_bins - 1)
+        x = (x * 2654435761) % num_bins  # spread the hot values over the bins
+    elif kind == "onebin":
+        x = np.full(n, int(g.integers(0, num_bins)))
+    else:
+        x = g.integers(-(2**31), 2**31 - 1, size=n)
+        x[::3] = g.integers(0, num_bins, size=x[::3].size)
+    x = x.astype(np.int64).astype(np.int32)
+    paths = ["auto", "scatter"] + (["full"] if num_bins <= 79616 else []) + \
+        (["range", "range"] if num_bins > 1 else [])
+    path = str(g.choice(paths))
+    opts = {"path": path, "aggregation": int(g.choice([-1, 0, 1, 2, 4]))}
+    if path in ("full", "range"):
+        opts["wg_size"] = int(g.choice([0, 256, 512, 1024]))
+        opts["counter_bits"] = int(g.choice([0, 16, 32]))
+        if opts["counter_bits"] == 32 and g.random() < 0.5:
+            opts["lds_copies"] = int(g.choice([1, 2, 4]))
+        if path == "range":
+            cap = 40960 if opts["counter_bits"] == 32 else 79616
+            opts["range_bins"] = int(g.integers(1, cap // 256 + 1)) * 256
+            opts["xcd_map"] = int(g.choice([0, 1, 2]))
+        if g.random() < 0.3:
+            opts["groups"] = int(g.integers(1, 300))
+    elif path == "scatter" and g.random() < 0.3:
+        opts["groups"] = int(g.integers(1, 600))
+    accumulate = bool(g.random() < 0.25)
+    return x, num_bins, opts, accumulate
+
+
+@pytest.mark.parametrize("seed", range(96))
+def test_fuzz_sizes_paths_options(seed):
+    """Random (seeded) bin counts, lengths, input shapes, paths and plan options,
+    each checked bit for bit against the oracle; a quarter of the cases
+    accumulate onto random counts. Combinations a plan does not support must
+    be refused with HIST_ERR_UNSUPPORTED, never run."""
+    x, num_bins, opts, accumulate = _fuzz_case(seed)
+    say(f"case fuzz{seed}: n={x.size} bins={num_bins} opts={opts} accumulate={accumulate}")
+    try:
+        plan = hist.Plan(num_bins, max(1, x.size), device=DEV, **opts)
+    except hist.HistError as e:
+        assert e.status == hist.HIST_ERR_UNSUPPORTED, e
+        return
+    ref, _ = oracle.hist(x, num_bins)
+    xt = torch.from_numpy(x).to(DEV)
+    if accumulate:
+        base = np.random.default_rng(seed).integers(0, 2**32, size=num_bins, dtype=np.uint64)
+        base = base.astype(np.uint32)
+        out = torch.from_numpy(base.view(np.int32).copy()).to(DEV)
+        plan.run(xt, out=out, accumulate=True)
+        want = ((base.astype(np.uint64) + ref) % 2**32).astype(np.uint32)
+    else:
+        out = plan.run(xt)
+        want = ref
+    got = out.cpu().numpy().view(np.uint32)
+    torch.cuda.synchronize(DEV)
+    assert np.array_equal(got, want), f"{plan.describe()}: {int(np.sum(got != want))} bins differ"
+    plan.close()
