@@ -469,10 +469,13 @@ def test_scatter_edge_cases(case):
 
 # --- seeded fuzz over sizes, paths and options -------------------------------
 
-def _fuzz_case(seed):
-    g = np.random.default_rng(1000 + seed)
+def _fuzz_case(seed, large=False):
+    g = np.random.default_rng(1000 + seed + (50_000 if large else 0))
     num_bins = int(min(2**20, max(1, round(2 ** g.uniform(0, 20)))))
     n = int(g.choice([0, 1, 7, int(g.integers(1, 5000)), int(g.integers(5000, 300_000))]))
+    if large:
+        num_bins = int(round(2 ** g.uniform(10, 21)))
+        n = int(g.integers(4_000_000, 20_000_000))
     kind = g.choice(["uniform", "skew", "onebin", "wild"])
     if kind == "uniform":
         x = g.integers(0, num_bins, size=n)
@@ -506,13 +509,14 @@ def _fuzz_case(seed):
     return x, num_bins, opts, accumulate
 
 
-@pytest.mark.parametrize("seed", range(96))
-def test_fuzz_sizes_paths_options(seed):
+@pytest.mark.parametrize("seed,large", [(k, False) for k in range(96)] + [(k, True) for k in range(12)])
+def test_fuzz_sizes_paths_options(seed, large):
     """Random (seeded) bin counts, lengths, input shapes, paths and plan options,
     each checked bit for bit against the oracle; a quarter of the cases
     accumulate onto random counts. Combinations a plan does not support must
-    be refused with HIST_ERR_UNSUPPORTED, never run."""
-    x, num_bins, opts, accumulate = _fuzz_case(seed)
+    be refused with HIST_ERR_UNSUPPORTED, never run. The large cases (4-20
+    million elements, up to 2^21 bins) span many chunks and tiles."""
+    x, num_bins, opts, accumulate = _fuzz_case(seed, large)
     say(f"case fuzz{seed}: n={x.size} bins={num_bins} opts={opts} accumulate={accumulate}")
     try:
         plan = hist.Plan(num_bins, max(1, x.size), device=DEV, **opts)
