@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--path-sweep", action="store_true",
                     help="time every applicable path over bin counts 2^10..2^22 on uniform "
                          "input of --n (default 2^26) elements; one JSON line per cell")
+    ap.add_argument("--sweep-log2", default="10,22",
+                    help="first,last log2 bin count of --path-sweep")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure the machine's ceilings the kernels meet (HBM stream read and "
                          "copy, LDS atomic rates by address pattern, shared-L2 placement of "
@@ -170,11 +172,15 @@ def workload_matrix(args):
             cells.append(("full32", {"path": "full", "counter_bits": 32}))
         if B <= 79616:
             cells.append(("full16", {"path": "full", "counter_bits": 16}))
+        if B <= 155392:
+            cells.append(("full8", {"path": "full", "counter_bits": 8}))
         if B >= 2048:
             cells.append(("range32", {"path": "range", "counter_bits": 32}))
             cells.append(("range16", {"path": "range", "counter_bits": 16}))
             cells.append(("range16+hot", {"path": "range", "counter_bits": 16,
                                           "aggregation": 1}))
+            cells.append(("range8", {"path": "range", "counter_bits": 8}))
+            cells.append(("range8+hot", {"path": "range", "counter_bits": 8, "aggregation": 1}))
         cells.append(("scatter", {"path": "scatter", "aggregation": 0}))
         cells.append(("scatter+hot", {"path": "scatter", "aggregation": 1}))
         steps = max(10, min(args.steps, int(4e9 / (4 * w.n))))
@@ -215,7 +221,8 @@ def path_sweep(args):
     n = args.n or (1 << 26)
     steps = min(args.steps, 100)
     best = {}
-    for lb in range(10, 23):
+    lb0, lb1 = (int(v) for v in args.sweep_log2.split(","))
+    for lb in range(lb0, lb1 + 1):
         B = 1 << lb
         x = inputs.uniform(1, n, B)
         ref, _ = oracle.hist(x, B)
@@ -228,9 +235,12 @@ def path_sweep(args):
             cells.append(("full32", {"path": "full", "counter_bits": 32}))
         if B <= 79616:
             cells.append(("full16", {"path": "full", "counter_bits": 16}))
+        if B <= 155392:
+            cells.append(("full8", {"path": "full", "counter_bits": 8}))
         if B >= 2048:
             cells.append(("range32", {"path": "range", "counter_bits": 32}))
             cells.append(("range16", {"path": "range", "counter_bits": 16}))
+            cells.append(("range8", {"path": "range", "counter_bits": 8}))
         cells.append(("scatter", {"path": "scatter"}))
         for name, opts in cells:
             try:

@@ -83,7 +83,8 @@ typedef struct {
     int32_t path;       /* hist_path_t */
     int32_t groups;     /* FULL/RANGE: input chunks G; SCATTER: owner workgroups W */
     int32_t range_bins; /* RANGE: bins per owned range (multiple of 256, <= LDS capacity:
-                           40960 with 32-bit counters, 79616 with 16-bit) */
+                           40960 with 32-bit counters, 79616 with 16-bit, 155392 with
+                           8-bit) */
     int32_t aggregation; /* wave-level duplicate aggregation ahead of the LDS adds, for
                             skewed inputs: -1 auto, 0 off, 1 hot slot (lanes holding the
                             wave's current hot value count in registers), 2 or 4 leader-peel
@@ -91,8 +92,9 @@ typedef struct {
     int32_t wg_size;    /* sweep workgroup size: 256, 512 or 1024 (0 = auto) */
     int32_t xcd_map;    /* RANGE: 1 = place a chunk's R owners on one XCD (default),
                            2 = plain order (for measurement) */
-    int32_t counter_bits; /* FULL/RANGE LDS counters: 32, or 16 (two bins per word, exact
-                             through carry events; twice the bins per workgroup) */
+    int32_t counter_bits; /* FULL/RANGE LDS counters: 32, 16 (two bins per word) or 8
+                             (four bins per word); the packed widths stay exact through
+                             carry events and hold 2x or 4x the bins per workgroup */
     int32_t lds_copies;   /* FULL/RANGE with 32-bit counters: interleaved LDS copies of the
                              slice (1, 2, 4, 8, 16; 0 = one); a lane adds to copy lane mod
                              copies, which spreads same-bin lanes of a wave over words and
@@ -112,9 +114,15 @@ typedef struct {
     uint32_t wg_size;
     int32_t aggregation;
     uint32_t tile_elems;   /* SCATTER: elements per scatter tile */
-    uint32_t counter_bits; /* FULL/RANGE: 32 or 16 */
+    uint32_t counter_bits; /* FULL/RANGE: 32, 16 or 8 */
     uint64_t max_n;
     uint64_t workspace_bytes;
+    uint64_t max_group_elems; /* FULL/RANGE: the most elements one input chunk may hold;
+                                 a call splits its input into at least
+                                 ceil(n / max_group_elems) chunks (packed counters: this
+                                 bounds each workgroup's carry events) */
+    uint32_t event_cap;       /* FULL/RANGE with 8-bit counters: carry-event list entries
+                                 per workgroup (the LDS its slice leaves); otherwise 0 */
 } hist_plan_info_t;
 
 typedef struct hist_plan hist_plan_t; /* opaque, host memory only */

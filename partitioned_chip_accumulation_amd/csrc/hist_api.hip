@@ -25,14 +25,17 @@ namespace {
 constexpr uint32_t kMaxLdsBins = 40960;      // 160 KiB of uint32 counters
 constexpr uint32_t kMaxLdsBins16 = 79616;    // 16-bit counters + the carry-event list
 constexpr uint64_t kMaxElemsPerWG16 = 1ull << 24;  // bounds the carry-event list
+constexpr uint32_t kMaxLdsBins8 = 155392;    // 8-bit counters + the shortest carry-event list
 constexpr uint32_t kScatterShift = 15;       // SCATTER range = 32768 bins (128 KiB)
 constexpr uint32_t kScatterWG = 1024;
 constexpr uint32_t kScatterVPT = 4;          // vectors per thread in a scatter tile
 constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elements
 constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slots per tile
-// AUTO uses RANGE up to this many 16-bit ranges and SCATTER beyond: on 2^26
-// uniform elements RANGE wins at 2^17 and 2^18 bins (71.9, 123.0 us vs 146.7,
-// 150.8 us) and SCATTER from 2^19 on (165.0 vs 221.3 us).
+// AUTO uses RANGE up to this many 16-bit ranges' worth of bins (318,464) and
+// SCATTER beyond: on 2^26 uniform elements SCATTER wins from 2^19 bins on
+// (141.7 us against 221 with 16-bit and 113 with 8-bit counters, the latter
+// at 1,895 us against 906 on the half-Gaussian 512K-bin workload, whose
+// carry events pile up in a few pairs of blocks).
 constexpr uint32_t kRangeMaxR = 4;
 constexpr uint32_t kMinElemsPerGroup = 4096;
 constexpr int kMaxWavesPerCU = 32;
@@ -52,6 +55,16 @@ uint64_t partial_bytes(uint32_t rows, uint32_t nblk)
            align_up(cells * pca::kPlaneBytes * pca::kUpperPlanes, 256) + align_up(cells, 256);
 }
 uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+// LDS bytes of a sweep workgroup: a slice of S bins in cw-bit counters (with
+// 2^kshift copies of 32-bit ones), plus the carry-event count and list of
+// the packed widths (ev_cap entries for 8-bit counters).
+uint32_t sweep_lds_bytes(uint32_t cw, uint32_t S, uint32_t kshift, uint32_t ev_cap)
+{
+    if (cw == 32) return (S << kshift) * 4;
+    if (cw == 16) return S * 2 + (4 + pca::kEventCap) * 4;
+    return S + (4 + ev_cap) * 4;
+}
 
 struct DeviceInfo {
     int device = -1;
@@ -99,6 +112,8 @@ struct hist_plan {
     uint32_t range_bins = 0, ranges = 0, groups = 0;
     uint32_t cw = 32;    // LDS counter bits
     uint32_t kshift = 0; // 2^kshift interleaved LDS copies (32-bit counters)
+    uint32_t ev_cap = 0; // carry-event list entries (8-bit counters)
+    uint64_t max_elems_wg = 1ull << 40;  // elements one sweep workgroup may count
     uint32_t nblk = 0;       // 256-bin blocks per partial row
     uint32_t part_rows = 0;  // partial rows the workspace holds
     // SCATTER
@@ -121,9 +136,10 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
     if (!o) return HIST_OK;
     if (o->path < 0 || o->path > 3) return HIST_ERR_INVALID_ARG;
     if (o->groups < 0 || o->groups > 65536) return HIST_ERR_INVALID_ARG;
-    if (o->range_bins < 0 || (o->range_bins % 256) != 0 || o->range_bins > (int)kMaxLdsBins16)
+    if (o->range_bins < 0 || (o->range_bins % 256) != 0 || o->range_bins > (int)kMaxLdsBins8)
         return HIST_ERR_INVALID_ARG;
-    if (o->counter_bits != 0 && o->counter_bits != 16 && o->counter_bits != 32)
+    if (o->counter_bits != 0 && o->counter_bits != 8 && o->counter_bits != 16 &&
+        o->counter_bits != 32)
         return HIST_ERR_INVALID_ARG;
     if (o->aggregation < -1 || o->aggregation > 4 || o->aggregation == 3) return HIST_ERR_INVALID_ARG;
     if (o->wg_size != 0 && o->wg_size != 256 && o->wg_size != 512 && o->wg_size != 1024)
@@ -149,10 +165,12 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
 
     const uint32_t lds_bins16 = std::min<uint32_t>(kMaxLdsBins16,
                                                    (lds_dyn - (4 + pca::kEventCap) * 4) / 2) & ~255u;
+    const uint32_t lds_bins8 = std::min<uint32_t>(kMaxLdsBins8,
+                                                  lds_dyn - (4 + pca::kMinEventCap8) * 4) & ~255u;
     const uint32_t cap32 = lds_bins & ~255u;
     int path = opts.path;
     if (path == HIST_PATH_AUTO) {
-        if (num_bins <= lds_bins16) path = HIST_PATH_FULL;
+        if (num_bins <= lds_bins8) path = HIST_PATH_FULL;
         else if (num_bins <= kRangeMaxR * lds_bins16) path = HIST_PATH_RANGE;  // see kRangeMaxR
         else path = HIST_PATH_SCATTER;
     }
@@ -171,12 +189,21 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // workgroups, two per CU) take 50-52 us from 2^10 to 2^14 bins and at
             // 2^16, against 52-55 us for 32-bit ones. 32-bit counters win only
             // where their slice leaves one workgroup per CU (24,576 bins: 48.8
-            // vs 52.1 us; 32,768: 49.7 vs 52.7 us).
-            if (path == HIST_PATH_FULL) cw = num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
-            else if (opts.range_bins > 0) cw = (uint32_t)opts.range_bins <= cap32 ? 32 : 16;
-            else cw = 16;
+            // vs 52.1 us; 32,768: 49.7 vs 52.7 us). 8-bit counters hold the most
+            // bins per workgroup, which saves input passes: 2^17 bins in one
+            // pass (53.9 us against 74.6 for two 16-bit ranges), 2^18 in two
+            // (67.4 against 131.4 for four); at 2^16 they lose to 16-bit ones
+            // (54.1 vs 49.8 us). On skewed input the comparison can turn: Zipf
+            // s = 1.1 over 2^17 bins takes 118 us in one 8-bit pass against 101
+            // in two 16-bit ranges, as a single owner meets more same-word lanes
+            // per LDS instruction.
+            if (path == HIST_PATH_FULL)
+                cw = num_bins > lds_bins16 ? 8 : num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
+            else if (opts.range_bins > 0)
+                cw = (uint32_t)opts.range_bins <= cap32 ? 32 : (uint32_t)opts.range_bins <= lds_bins16 ? 16 : 8;
+            else cw = 8;
         }
-        const uint32_t cap = cw == 32 ? cap32 : lds_bins16;
+        const uint32_t cap = cw == 32 ? cap32 : cw == 16 ? lds_bins16 : lds_bins8;
         uint32_t S, R;
         if (path == HIST_PATH_FULL) {
             R = 1;
@@ -201,7 +228,7 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             R = ceil_div(num_bins, S);
         }
         if (S > cap || S == 0) return HIST_ERR_UNSUPPORTED;
-        auto chunks_for = [&](uint32_t lds_bytes, uint32_t *wg_out) {
+        auto chunks_for = [&](uint32_t lds_bytes, uint64_t max_elems_wg, uint32_t *wg_out) {
             const uint32_t occ_lds = std::max<uint32_t>(1, d.lds / lds_bytes);
             uint32_t wg = (uint32_t)opts.wg_size;
             // Measured: 1024 threads, except a 32-bit slice that leaves one
@@ -209,10 +236,11 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // 52.6 us; 16-bit at 65,536 bins: 50.8 with 1024 vs 56.4 us).
             if (wg == 0) wg = cw == 32 && occ_lds == 1 ? 512 : 1024;
             const uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
-            uint32_t G = (uint32_t)opts.groups;
+            uint32_t G = (uint32_t)opts.groups, slots = 0;
             if (G == 0) {
                 G = (uint32_t)d.cu * occ / R;
                 if (G >= (uint32_t)d.xcd) G = G / d.xcd * d.xcd;
+                slots = std::max<uint32_t>(1, G);  // chunks whose owners are resident at once
                 // Keep the merge traffic (G rows of num_bins counts, ~4 bits each for
                 // the counts a chunk of n/G elements produces) a small fraction of the
                 // input (4n bytes), and every chunk a useful size.
@@ -220,10 +248,10 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
                 const uint64_t by_size = std::max<uint64_t>(1, max_n / kMinElemsPerGroup);
                 G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
             }
-            if (cw == 16) {
-                // Enough chunks that no workgroup counts more than 2^24 elements.
-                G = std::max<uint32_t>(G, ceil_div(max_n, kMaxElemsPerWG16));
-            }
+            // Enough chunks that no workgroup's carry-event list can overflow;
+            // when that takes more chunks than run at once, whole rounds of them.
+            const uint32_t gmin = ceil_div(max_n, max_elems_wg);
+            if (G < gmin) G = slots ? ceil_div(gmin, slots) * slots : gmin;
             *wg_out = wg;
             return G;
         };
@@ -231,21 +259,30 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         // copy count above 1 measured slower (2^10 bins: 52.6 us with one copy,
         // 59.9 with 8, 67.4 with 16), as clearing and summing the copies costs
         // more than the bank conflicts they spread.
-        uint32_t kshift = 0, wg = 0, G = 0;
+        uint32_t kshift = 0, wg = 0, G = 0, ev_cap = 0;
+        uint64_t max_elems_wg = 1ull << 40;  // no list: any n < 2^32
         if (cw == 32) {
             if (opts.lds_copies > 0)
                 while ((1u << (kshift + 1)) <= (uint32_t)opts.lds_copies) ++kshift;
             if ((S << kshift) * 4 > lds_dyn) return HIST_ERR_UNSUPPORTED;
+        } else if (cw == 16) {
+            max_elems_wg = kMaxElemsPerWG16;
+        } else {
+            // The event list takes what LDS the workgroups of a CU leave, so a
+            // large slice (one workgroup per CU) lets a workgroup count more.
+            const uint32_t occ = std::max<uint32_t>(1, lds_dyn / sweep_lds_bytes(8, S, 0, pca::kMinEventCap8));
+            ev_cap = (lds_dyn / occ - S) / 4 - 4;
+            max_elems_wg = 255ull * (ev_cap - 16);
         }
-        const uint32_t lds_bytes =
-            cw == 32 ? (S << kshift) * 4 : S * 2 + (4 + pca::kEventCap) * 4;
-        G = chunks_for(lds_bytes, &wg);
+        G = chunks_for(sweep_lds_bytes(cw, S, kshift, ev_cap), max_elems_wg, &wg);
         p->range_bins = S;
         p->ranges = R;
         p->groups = G;
         p->wg = wg;
         p->cw = cw;
         p->kshift = kshift;
+        p->ev_cap = ev_cap;
+        p->max_elems_wg = max_elems_wg;
         p->nblk = ceil_div(num_bins, pca::kBlockBins);
         uint64_t off = 0;
         p->part_rows = G > 1 ? G : 0;
@@ -318,15 +355,14 @@ struct SweepArgs {
 template <int WG, int AGG, int CW>
 hipError_t launch_sweep_t(const hist_plan *p, const SweepArgs &a, hipStream_t s)
 {
-    // 16-bit counters: 2 vectors (8 returning LDS atomics) per thread per
+    // Packed counters: 2 vectors (8 returning LDS atomics) per thread per
     // iteration stay within the LDS wait counter; measured 12% faster than 4.
-    auto k = pca::k_sweep<WG, CW == 16 ? 2 : 4, AGG, CW>;
-    const uint32_t bytes = CW == 32 ? (p->range_bins << p->kshift) * 4
-                                    : p->range_bins * 2 + (4 + pca::kEventCap) * 4;
+    auto k = pca::k_sweep<WG, CW == 32 ? 4 : 2, AGG, CW>;
+    const uint32_t bytes = sweep_lds_bytes(CW, p->range_bins, CW == 32 ? p->kshift : 0u, p->ev_cap);
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, a.in, p->num_bins,
-                       p->range_bins, p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, a.out,
+                       p->range_bins, p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, p->ev_cap, a.out,
                        a.direct, a.accumulate);
     return hipGetLastError();
 }
@@ -503,7 +539,7 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         const uint64_t by_merge = std::max<uint64_t>(1, n / num_bins);
         const uint64_t by_size = std::max<uint64_t>(1, n / kMinElemsPerGroup);
         G = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>({G, by_merge, by_size}));
-        if (p->cw == 16) G = std::max<uint32_t>(G, ceil_div(n, kMaxElemsPerWG16));
+        G = std::max<uint32_t>(G, ceil_div(n, p->max_elems_wg));  // bounds the carry events
         SweepArgs a;
         a.in = in;
         a.G = G;
@@ -515,7 +551,9 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         // the lines in the XCD's L2 (measured: 50% L2 hits, one HBM fetch per
         // element) and the stream evicts less useful data.
         tm.begin(PH_SWEEP);
-        e = p->cw == 16 ? launch_sweep_wg<16>(p, a, stream) : launch_sweep_wg<32>(p, a, stream);
+        e = p->cw == 32   ? launch_sweep_wg<32>(p, a, stream)
+            : p->cw == 16 ? launch_sweep_wg<16>(p, a, stream)
+                          : launch_sweep_wg<8>(p, a, stream);
         tm.end(PH_SWEEP);
         if (e != hipSuccess) return HIST_ERR_HIP;
         if (G > 1) {
@@ -656,6 +694,8 @@ hist_status_t hist_plan_info(const hist_plan_t *p, hist_plan_info_t *info)
     info->counter_bits = p->path == HIST_PATH_SCATTER ? 32 : p->cw;
     info->max_n = p->max_n;
     info->workspace_bytes = p->need;
+    info->max_group_elems = p->path == HIST_PATH_SCATTER ? 0 : p->max_elems_wg;
+    info->event_cap = p->path == HIST_PATH_SCATTER ? 0 : p->ev_cap;
     return HIST_OK;
 }
 

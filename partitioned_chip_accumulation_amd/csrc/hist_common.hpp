@@ -11,6 +11,7 @@ namespace pca {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // The input split into a 16-byte aligned body of int4 vectors and at most
 // three scalars before (head) and after (tail) it. The host fills this from

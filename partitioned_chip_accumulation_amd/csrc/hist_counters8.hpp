@@ -1,0 +1,216 @@
+// hist_counters8.hpp -- 8-bit LDS counters kept exact by carry events
+//
+// Part of the gfx950 kernels of libpca_hist.so (see hist_kernels.hpp for the
+// overview).
+#pragma once
+
+#include "hist_common.hpp"
+
+namespace pca {
+
+// ---------------------------------------------------------------------------
+// 8-bit LDS counters.
+//
+// Four bins share one 32-bit LDS word, bin 4w + p in byte p of word w, so a
+// workgroup's 160 KiB hold about 155,000 bins. An add of k (1 <= k <= 255) to
+// bin 4w + p is ds_add_rtn_u32 of k << 8p. A byte that overflows carries into
+// the next byte of the word (which can overflow in turn), and a carry out of
+// byte 3 leaves the word. The returned old value shows every carry: with
+// new = old + delta, bit 8q + 8 of old ^ delta ^ new is the carry out of byte
+// q < 3, and new < old is the carry out of byte 3. Each carry out of byte q
+// is appended to an LDS list as the entry 4w + q. With C_q the carries out of
+// byte q of the final word W, the true counts are
+//     A_q = byte_q(W) + 256 C_q - C_(q-1)   (C_(-1) = 0).
+// Every carry out of a byte takes 256 units into it, and the units into byte
+// q are the adds to bin q plus the carries out of byte q - 1, so from zero a
+// workgroup that counts E elements logs at most E / 255 events. The list
+// takes the LDS the slice leaves (at least kMinEventCap8 entries, cap in
+// all), and the host keeps E <= 255 (cap - 16), which bounds it.
+constexpr uint32_t kMinEventCap8 = 2048;
+
+// Bit q set: the add of delta to a word that held old carried out of byte q.
+__device__ __forceinline__ uint32_t carry_bits8(uint32_t old, uint32_t delta)
+{
+    const uint32_t nw = old + delta;
+    const uint32_t x = old ^ delta ^ nw;  // the carry into every bit
+    return ((x >> 8) & 1u) | ((x >> 15) & 2u) | ((x >> 22) & 4u) | (nw < old ? 8u : 0u);
+}
+
+// Log the carries of an add of delta = k << 8p to word w that returned old
+// (one lane on its own).
+__device__ __forceinline__ void log_carries8(uint32_t *evlist, uint32_t *ev_count, uint32_t cap,
+                                             uint32_t w, uint32_t old, uint32_t delta)
+{
+    const uint32_t bits = carry_bits8(old, delta);
+    if (bits == 0u) return;
+    uint32_t i = lds_add_rtn(ev_count, 0, (uint32_t)__popc(bits));
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        if ((bits >> q) & 1u) {
+            if (i < cap) evlist[i] = (w << 2) | q;
+            ++i;
+        }
+    }
+}
+
+__device__ __forceinline__ void add8(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
+                                     uint32_t cap, uint32_t s, uint32_t k)
+{
+    const uint32_t delta = k << ((s & 3u) << 3);
+    const uint32_t old = lds_add_rtn(words, s >> 2, delta);
+    log_carries8(evlist, ev_count, cap, s >> 2, old, delta);
+}
+
+// Unaggregated 8-bit counting of N elements at once (all ds_add_rtn_u32 are
+// issued before any returned value is examined; N <= 15). An add of 1 can
+// carry only when the byte it increments was 0xFF, which one bit-field
+// extract tests. The carries then take one wave-uniform branch that logs all
+// of the wave's events with a single LDS atomic: each lane's offset in the
+// wave's block is the sum of its lower lanes' event counts, taken from one
+// ballot per event a lane has (mostly one). Skewed input, whose hot bins
+// wrap a byte every 256 counts, takes this branch often.
+template <int N>
+__device__ __forceinline__ void count8_batch(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
+                                             uint32_t cap, const uint32_t (&s)[N],
+                                             const bool (&ok)[N])
+{
+    uint32_t old[N], sh[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        sh[e] = (s[e] & 3u) << 3;
+        old[e] = 0u;
+        if (ok[e]) old[e] = lds_add_rtn(words, s[e] >> 2, 1u << sh[e]);
+    }
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        any = any || (ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 8) == 0xFFu);
+    if (__ballot(any)) {
+        uint32_t bits[N], tot = 0;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            bits[e] = ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 8) == 0xFFu
+                          ? carry_bits8(old[e], 1u << sh[e]) : 0u;
+            tot += (uint32_t)__popc(bits[e]);
+        }
+        uint32_t pre = 0, sum = 0;
+        for (uint32_t j = 0;; ++j) {
+            const uint64_t m = __ballot(tot > j);
+            if (m == 0) break;
+            pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            sum += (uint32_t)__popcll(m);
+        }
+        const int first = __builtin_ctzll(__ballot(true));
+        uint32_t b = 0u;
+        if (lane_id() == (uint32_t)first) b = lds_add_rtn(ev_count, 0, sum);
+        uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)b, first) + pre;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            if (__ballot(bits[e] != 0u)) {
+#pragma unroll
+                for (uint32_t q = 0; q < 4; ++q) {
+                    if ((bits[e] >> q) & 1u) {
+                        if (slot < cap) evlist[slot] = (s[e] & ~3u) | q;
+                        ++slot;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int ROUNDS>
+__device__ __forceinline__ void lds_count8(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
+                                           uint32_t cap, uint32_t slot, bool valid)
+{
+    if constexpr (ROUNDS == 0) {
+        if (valid) add8(words, evlist, ev_count, cap, slot, 1u);
+    } else {
+        bool pending = valid;
+#pragma unroll
+        for (int k = 0; k < ROUNDS; ++k) {
+            const uint64_t act = __ballot(pending);
+            if (act == 0) return;
+            const int leader = __builtin_ctzll(act);
+            const uint32_t lead = __builtin_amdgcn_readlane(slot, leader);
+            const bool mine = pending && slot == lead;
+            const uint64_t m = __ballot(mine);
+            if (mine && lane_id() == (uint32_t)leader)
+                add8(words, evlist, ev_count, cap, lead, (uint32_t)__popcll(m));  // <= 64
+            pending = pending && !mine;
+            if (__popcll(m) == 1) break;
+        }
+        if (pending) add8(words, evlist, ev_count, cap, slot, 1u);
+    }
+}
+
+// The counts a lane holds for up to four pairs of blocks, as 32 named
+// scalars rather than an array: the compiler keeps an array of this size as
+// one 32-register tuple, which a branch that changes one element copies
+// whole.
+struct Counts32 {
+    uint32_t v0, v1, v2, v3, v4, v5, v6, v7, v8, v9, v10, v11, v12, v13, v14, v15, v16, v17, v18, v19, v20, v21, v22, v23, v24, v25, v26, v27, v28, v29, v30, v31;
+};
+constexpr uint32_t Counts32::*kCountMember[32] = {
+    &Counts32::v0, &Counts32::v1, &Counts32::v2, &Counts32::v3, &Counts32::v4, &Counts32::v5, &Counts32::v6, &Counts32::v7,
+    &Counts32::v8, &Counts32::v9, &Counts32::v10, &Counts32::v11, &Counts32::v12, &Counts32::v13, &Counts32::v14, &Counts32::v15,
+    &Counts32::v16, &Counts32::v17, &Counts32::v18, &Counts32::v19, &Counts32::v20, &Counts32::v21, &Counts32::v22, &Counts32::v23,
+    &Counts32::v24, &Counts32::v25, &Counts32::v26, &Counts32::v27, &Counts32::v28, &Counts32::v29, &Counts32::v30, &Counts32::v31};
+
+template <int K>
+__device__ __forceinline__ uint32_t &count_at(Counts32 &c)
+{
+    return c.*kCountMember[K];
+}
+
+// c[k] += v for the wave-uniform k in [LO, HI): a binary tree of scalar
+// branches whose every leaf adds to one register. The leaf's add is an
+// opaque instruction so that the compiler cannot merge the leaves back into
+// one add at a run-time register index (GPR indexing mode), which it would
+// otherwise do and which this code must not depend on.
+template <int LO, int HI>
+__device__ __forceinline__ void add_at(Counts32 &c, uint32_t k, uint32_t v)
+{
+    if constexpr (HI - LO == 1) {
+        asm volatile("v_add_u32 %0, %0, %1" : "+v"(count_at<LO>(c)) : "v"(v));
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (k < (uint32_t)MID) add_at<LO, MID>(c, k, v);
+        else add_at<MID, HI>(c, k, v);
+    }
+}
+
+// Apply the carry events to the counts of J <= 4 pairs of blocks that start
+// at word wlo: c[8j + i] is bin 8l + i of pair j (l = lane), byte i % 4 of
+// word wlo + 128 j + 2l + i / 4. The wave reads the list 64 entries at a
+// time and takes only the entries in [wlo, wlo + 128 J); an entry names one
+// count, whose index in c is wave-uniform, so each matching entry costs a
+// few scalar branches and two adds in which only the owning lane's value
+// changes. Whole wave, convergent; wlo uniform.
+template <int J>
+__device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t nev, uint32_t wlo,
+                                              Counts32 &c)
+{
+    const uint32_t lane = lane_id();
+    // uniform in fact (derived from the wave index); said so, the entry index
+    // below is computed in scalar registers
+    wlo = (uint32_t)__builtin_amdgcn_readfirstlane((int)wlo);
+    for (uint32_t e0 = 0; e0 < nev; e0 += 64) {
+        const uint32_t e = e0 + lane;
+        const uint32_t ent = e < nev ? evlist[e] : 0xFFFFFFFFu;
+        uint64_t m = __ballot((ent >> 2) - wlo < 128u * J);
+        while (m != 0) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t ev = (uint32_t)__builtin_amdgcn_readlane((int)ent, k);
+            const uint32_t d = (ev >> 2) - wlo;  // word within the batch
+            const uint32_t idx = (d >> 7) * 8u + (d & 1u) * 4u + (ev & 3u);
+            const uint32_t hit = lane == ((d & 127u) >> 1) ? 1u : 0u;
+            add_at<0, 8 * J>(c, idx, hit << 8);
+            if ((ev & 3u) != 3u) add_at<0, 8 * J>(c, idx + 1, 0u - hit);  // byte 3: leaves the word
+        }
+    }
+}
+
+}  // namespace pca

@@ -17,12 +17,13 @@
 // no global atomics and no memset of the output are needed.
 //
 // Conventions: wave64 (gfx950), 16-byte (dwordx4) global loads on the input
-// body; LDS counters are uint32 (ds_add_u32) or two 16-bit halves of a word
-// kept exact by carry events (ds_add_rtn_u32).
+// body; LDS counters are uint32 (ds_add_u32), or two 16-bit halves or four
+// bytes of a word kept exact by carry events (ds_add_rtn_u32).
 //
 // The kernels live in one header per stage:
 //   hist_common.hpp      input view, wave and LDS helpers, the hot slot
 //   hist_counters16.hpp  16-bit LDS counters with carry events
+//   hist_counters8.hpp   8-bit LDS counters with carry events
 //   hist_partials.hpp    partial-slice layout, flush and exclusive-owner merge
 //   hist_sweep.hpp       the single-pass sweep (FULL, RANGE)
 //   hist_scatter.hpp     the two-phase path (SCATTER)
@@ -30,6 +31,7 @@
 
 #include "hist_common.hpp"
 #include "hist_counters16.hpp"
+#include "hist_counters8.hpp"
 #include "hist_partials.hpp"
 #include "hist_sweep.hpp"
 #include "hist_scatter.hpp"

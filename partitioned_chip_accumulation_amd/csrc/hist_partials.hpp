@@ -7,6 +7,7 @@
 
 #include "hist_common.hpp"
 #include "hist_counters16.hpp"
+#include "hist_counters8.hpp"
 
 namespace pca {
 
@@ -122,17 +123,101 @@ __device__ __forceinline__ void write_pair16(const Partials &P, uint64_t blk_eve
     if (sub == 0) P.width[blk] = (uint8_t)(planes - 1);
 }
 
+// Plane q (0 or 1) of eight 8-bit counts held four per word (count 4k + i in
+// byte i of word k), as one word of nibbles.
+__device__ __forceinline__ uint32_t plane_word8(u32x2 w, uint32_t q)
+{
+    const uint32_t sh = 4u * q;
+    // nibbles of counts 0..3 at bits 0, 8, 16, 24 (z likewise for 4..7), then
+    // each even nibble joined with its odd neighbour and the two bytes packed
+    uint32_t y = (w.x >> sh) & 0x0F0F0F0Fu, z = (w.y >> sh) & 0x0F0F0F0Fu;
+    y |= y >> 4;
+    z |= z >> 4;
+    return (y & 0xFFu) | ((y >> 8) & 0xFF00u) | ((z & 0xFFu) << 16) | ((z << 8) & 0xFF000000u);
+}
+
+// write_pair for counts that are exact in 8 bits, read straight from packed
+// LDS words (lane l: bins 8l..8l+7 of the pair as two words). Both blocks of
+// the pair exist. Whole wave, convergent.
+__device__ __forceinline__ void write_pair8(const Partials &P, uint64_t blk_even, u32x2 w)
+{
+    const uint32_t lane = lane_id();
+    const uint64_t wide = __ballot(((w.x | w.y) & 0xF0F0F0F0u) != 0u);
+    store_through(reinterpret_cast<uint32_t *>(P.plane0 + blk_even * kPlaneBytes) + lane,
+                  plane_word8(w, 0));
+    if (wide == 0) {
+        // the common case: both blocks fit 4 bits, plane 0 only
+        if ((lane & 31u) == 0) P.width[blk_even + (lane >> 5)] = 0;
+        return;
+    }
+    const uint32_t planes = (uint32_t)(wide >> (lane & 32u)) ? 2u : 1u;
+    const uint64_t blk = blk_even + (lane >> 5);
+    if (planes == 2u)
+        store_through(reinterpret_cast<uint32_t *>(P.upper + blk * kUpperPlanes * kPlaneBytes) +
+                          (lane & 31u),
+                      plane_word8(w, 1));
+    if ((lane & 31u) == 0) P.width[blk] = (uint8_t)(planes - 1);
+}
+
+// The eight bytes of bins 8l..8l+7 (l = lane) of pair p, as stored in 8-bit
+// LDS counters (before carry events), into c[8j..8j+7]; zero for a lane
+// whose bins all lie at or beyond len. j is a compile-time index.
+template <int J>
+__device__ __forceinline__ void octet8_raw(const uint32_t *lds, uint32_t p, uint32_t len,
+                                           Counts32 &cv)
+{
+    const uint32_t b0 = p * 512u + lane_id() * 8u;
+    u32x2 w = {0u, 0u};
+    if (b0 < len) w = reinterpret_cast<const u32x2 *>(lds)[b0 / 8];
+    count_at<8 * J + 0>(cv) = w.x & 0xFFu;
+    count_at<8 * J + 1>(cv) = (w.x >> 8) & 0xFFu;
+    count_at<8 * J + 2>(cv) = (w.x >> 16) & 0xFFu;
+    count_at<8 * J + 3>(cv) = w.x >> 24;
+    count_at<8 * J + 4>(cv) = w.y & 0xFFu;
+    count_at<8 * J + 5>(cv) = (w.y >> 8) & 0xFFu;
+    count_at<8 * J + 6>(cv) = (w.y >> 16) & 0xFFu;
+    count_at<8 * J + 7>(cv) = w.y >> 24;
+}
+
+// c[0..7] = counts 8j..8j+7 of cv.
+template <int J>
+__device__ __forceinline__ void octet_of(Counts32 &cv, uint32_t (&c)[8])
+{
+    c[0] = count_at<8 * J + 0>(cv); c[1] = count_at<8 * J + 1>(cv);
+    c[2] = count_at<8 * J + 2>(cv); c[3] = count_at<8 * J + 3>(cv);
+    c[4] = count_at<8 * J + 4>(cv); c[5] = count_at<8 * J + 5>(cv);
+    c[6] = count_at<8 * J + 6>(cv); c[7] = count_at<8 * J + 7>(cv);
+}
+
+__device__ __forceinline__ void mask_octet(uint32_t p, uint32_t len, uint32_t (&c)[8])
+{
+    const uint32_t b0 = p * 512u + lane_id() * 8u;
+#pragma unroll
+    for (uint32_t i = 0; i < 8; ++i)
+        if (b0 + i >= len) c[i] = 0u;
+}
+
 // Counts of bins 8l..8l+7 (l = lane) of pair p (bins 512p..512p+511) of a
-// slice, from 32-bit or 16-bit LDS counters. Bins at or beyond len read as
-// zero; a lane whose bins all lie beyond len reads no LDS. The slice's LDS
-// holds at least round_up(len, 256) counters, so a partly valid lane stays
-// inside it.
+// slice, from 32-bit, 16-bit or 8-bit LDS counters. Bins at or beyond len
+// read as zero; a lane whose bins all lie beyond len reads no LDS. The
+// slice's LDS holds at least round_up(len, 256) counters, so a partly valid
+// lane stays inside it. With 8-bit counters the whole wave must call it
+// (uniform p): the carry events are applied by the wave together.
 template <int CW>
 __device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t *evlist,
                                             uint32_t nev, uint32_t p, uint32_t len,
                                             uint32_t kshift, uint32_t (&c)[8])
 {
     const uint32_t b0 = p * 512u + lane_id() * 8u;
+    if constexpr (CW == 8) {
+        Counts32 cv;
+        octet8_raw<0>(lds, p, len, cv);
+        // a carry out of the last valid byte lands in an invalid one: mask after
+        apply_events8<1>(evlist, nev, p * 128u, cv);
+        octet_of<0>(cv, c);
+        mask_octet(p, len, c);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = 0u;
     if (b0 >= len) return;
@@ -217,6 +302,52 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
             }
             return;
         }
+    }
+    if constexpr (CW == 8) {
+        if (nev == 0) {
+            // no carry events: every count is its byte
+            const uint32_t full = len / 512;
+            for (uint32_t p0 = w * kFlushBatch; p0 < full; p0 += NW * kFlushBatch) {
+                u32x2 ww[kFlushBatch];
+#pragma unroll
+                for (uint32_t j = 0; j < kFlushBatch; ++j)
+                    ww[j] = reinterpret_cast<const u32x2 *>(lds)[min(p0 + j, full - 1) * 64 + lane_id()];
+#pragma unroll
+                for (uint32_t j = 0; j < kFlushBatch; ++j) {
+                    if (p0 + j >= full) break;  // uniform
+                    write_pair8(P, row_blk + 2 * (p0 + j), ww[j]);
+                }
+            }
+            if (full < npairs && w == (full / kFlushBatch) % NW) {
+                uint32_t c[8];
+                slice_octet<CW>(lds, evlist, nev, full, len, kshift, c);
+                write_pair(P, row_blk + 2 * full, min(2u, nblk_slice - 2 * full), c);
+            }
+            return;
+        }
+        // one pass over the event list per batch of pairs
+        for (uint32_t p0 = w * kFlushBatch; p0 < npairs; p0 += NW * kFlushBatch) {
+            static_assert(kFlushBatch == 4, "Counts32 holds four pairs");
+            Counts32 cv;
+            octet8_raw<0>(lds, p0 + 0, len, cv);
+            octet8_raw<1>(lds, p0 + 1, len, cv);
+            octet8_raw<2>(lds, p0 + 2, len, cv);
+            octet8_raw<3>(lds, p0 + 3, len, cv);
+            apply_events8<kFlushBatch>(evlist, nev, p0 * 128u, cv);
+            uint32_t c[kFlushBatch][8];
+            octet_of<0>(cv, c[0]);
+            octet_of<1>(cv, c[1]);
+            octet_of<2>(cv, c[2]);
+            octet_of<3>(cv, c[3]);
+#pragma unroll
+            for (uint32_t j = 0; j < kFlushBatch; ++j) {
+                if (p0 + j >= npairs) break;  // uniform
+                mask_octet(p0 + j, len, c[j]);
+                const uint32_t kb = 2 * (p0 + j);
+                write_pair(P, row_blk + kb, min(2u, nblk_slice - kb), c[j]);
+            }
+        }
+        return;
     }
     for (uint32_t p0 = w * kFlushBatch; p0 < npairs; p0 += NW * kFlushBatch) {
         uint32_t c[kFlushBatch][8];

@@ -6,6 +6,7 @@
 
 #include "hist_common.hpp"
 #include "hist_counters16.hpp"
+#include "hist_counters8.hpp"
 #include "hist_partials.hpp"
 
 namespace pca {
@@ -24,22 +25,24 @@ namespace pca {
 // owners of a chunk all read it; xcds > 1 places them on one XCD
 // (workgroups are dispatched to the XCDs round-robin) so that one owner's
 // read brings the lines into the shared L2 for the others. Counters are
-// 32-bit (CW = 32) or packed 16-bit with carry events (CW = 16).
+// 32-bit (CW = 32), or packed 16-bit or 8-bit ones with carry events
+// (CW = 16, 8).
 //
 // Chunk g is body vectors [g * nvec / groups, (g + 1) * nvec / groups); the
 // head scalars belong to chunk 0 and the tail scalars to the last chunk.
 // The slice goes to partial row g in 256-bin blocks (range_bins is a multiple
 // of 256), or straight into direct[] (the output) when there is one chunk;
-// accumulate != 0 adds to direct[] instead of overwriting it.
+// accumulate != 0 adds to direct[] instead of overwriting it. ev_cap is the
+// length of the 8-bit counters' carry-event list.
 template <int WG, int UNROLL, int AGG, int CW>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
-                                              uint32_t kshift, Partials out,
+                                              uint32_t kshift, uint32_t ev_cap, Partials out,
                                               uint32_t *__restrict__ direct, uint32_t accumulate)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
-    uint32_t *ev_count = lds + range_bins / 2;  // CW == 16 only
+    uint32_t *ev_count = lds + range_bins * CW / 32;  // CW < 32 only
     uint32_t *evlist = ev_count + 4;
     const uint32_t tid = threadIdx.x;
     const uint32_t b = blockIdx.x;
@@ -70,8 +73,8 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + u * WG + tid);
     }
-    zero_lds<WG>(lds, CW == 32 ? (len << kshift) : (len + 1) / 2);
-    if (CW == 16 && tid == 0) *ev_count = 0u;
+    zero_lds<WG>(lds, CW == 32 ? (len << kshift) : CW == 16 ? (len + 1) / 2 : (len + 3) / 4);
+    if (CW != 32 && tid == 0) *ev_count = 0u;
     __syncthreads();
     // 32-bit counters may keep 2^kshift interleaved copies of the slice; a lane
     // adds to copy (lane mod 2^kshift), so lanes of one wave that hit the same
@@ -83,7 +86,8 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     constexpr int PEEL = AGG >= 2 ? AGG : 0;
     auto count1 = [&](uint32_t s, bool ok) {
         if constexpr (CW == 32) lds_count<PEEL>(lds, (s << kshift) | rep, ok);
-        else lds_count16<PEEL>(lds, evlist, ev_count, s, ok);
+        else if constexpr (CW == 16) lds_count16<PEEL>(lds, evlist, ev_count, s, ok);
+        else lds_count8<PEEL>(lds, evlist, ev_count, ev_cap, s, ok);
     };
     HotSlot hs;
     auto hot_flush = [&]() {
@@ -94,8 +98,9 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
                     lds_add(lds, hs.h << kshift, t);
                 } else {
                     while (t != 0u) {
-                        const uint32_t kk = min(t, 32768u);
-                        add16(lds, evlist, ev_count, hs.h, kk);
+                        const uint32_t kk = min(t, CW == 16 ? 32768u : 255u);
+                        if constexpr (CW == 16) add16(lds, evlist, ev_count, hs.h, kk);
+                        else add8(lds, evlist, ev_count, ev_cap, hs.h, kk);
                         t -= kk;
                     }
                 }
@@ -153,6 +158,8 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
             }
             if constexpr (CW == 16) {
                 count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
+            } else if constexpr (CW == 8) {
+                count8_batch<4 * UNROLL>(lds, evlist, ev_count, ev_cap, sl, ok);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4 * UNROLL; ++e) lds_count<0>(lds, (sl[e] << kshift) | rep, ok[e]);
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     hot_flush();
     __syncthreads();
 
-    const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : 0u;
+    const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : CW == 8 ? min(*ev_count, ev_cap) : 0u;
     if (direct) {
         const uint32_t npairs = (len + 511) / 512;
         for (uint32_t p = tid >> 6; p < npairs; p += WG / 64) {

@@ -48,7 +48,8 @@ class PlanInfo(ctypes.Structure):
                 ("ranges", ctypes.c_uint32), ("groups", ctypes.c_uint32),
                 ("wg_size", ctypes.c_uint32), ("aggregation", ctypes.c_int32),
                 ("tile_elems", ctypes.c_uint32), ("counter_bits", ctypes.c_uint32),
-                ("max_n", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+                ("max_n", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
+                ("max_group_elems", ctypes.c_uint64), ("event_cap", ctypes.c_uint32)]
 
 
 _lib = None
@@ -143,6 +144,8 @@ class Info:
     counter_bits: int
     max_n: int
     workspace_bytes: int
+    max_group_elems: int
+    event_cap: int
 
 
 class Plan:
@@ -204,7 +207,8 @@ class Plan:
         _check(library().hist_plan_info(self._plan, ctypes.byref(i)), "hist_plan_info")
         return Info(PATH_NAMES[i.path], i.device, i.cu_count, i.xcd_count, i.num_bins,
                     i.range_bins, i.ranges, i.groups, i.wg_size, i.aggregation, i.tile_elems,
-                    i.counter_bits, i.max_n, i.workspace_bytes)
+                    i.counter_bits, i.max_n, i.workspace_bytes, i.max_group_elems,
+                    i.event_cap)
 
     def describe(self) -> str:
         buf = ctypes.create_string_buffer(512)

@@ -1,10 +1,12 @@
 /* Plain C99 client of the library's C ABI (include/hist.h, include/hist_bench.h).
  * Built and run by tests/test_abi_cpu.py with gcc, no GPU needed: every entry
  * point must link, and calls with bad arguments must return the documented
- * status without touching a device. Prints "ok" and exits 0 on success. */
+ * status without touching a device. Prints the public structs' layout, then
+ * "ok", and exits 0 on success. */
 #include "hist.h"
 #include "hist_bench.h"
 
+#include <stddef.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -57,6 +59,9 @@ int main(void)
            HIST_ERR_INVALID_ARG);
     expect("status_str(OK)", strcmp(hist_status_str(HIST_OK), "ok"), 0);
     hist_plan_destroy(NULL);
+    /* struct layouts, for the Python binding's ctypes mirrors */
+    printf("layout %zu %zu %zu %zu\n", sizeof(hist_plan_info_t), sizeof(hist_plan_opts_t),
+           offsetof(hist_plan_info_t, max_group_elems), offsetof(hist_plan_info_t, event_cap));
     if (failures == 0) printf("ok\n");
     return failures == 0 ? 0 : 1;
 }

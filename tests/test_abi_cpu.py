@@ -55,7 +55,7 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_workspace_size(hist.MAX_BINS + 1, 10, None,
                                    ctypes.byref(n)) == hist.HIST_ERR_UNSUPPORTED
     for field, bad in [("path", 7), ("groups", -1), ("range_bins", 6), ("range_bins", 1000),
-                       ("counter_bits", 8), ("aggregation", 3), ("lds_copies", 3),
+                       ("counter_bits", 12), ("aggregation", 3), ("lds_copies", 3),
                        ("lds_copies", 32),
                        ("aggregation", -2), ("wg_size", 100), ("xcd_map", 5)]:
         o = hist.PlanOpts()
@@ -115,4 +115,9 @@ def test_plain_c_client_compiles_links_and_gets_documented_errors(tmp_path):
                     os.path.join(ROOT, "tests", "c_abi_check.c"), "-L", libdir, "-lpca_hist",
                     f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True)
     out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
-    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout + out.stderr
+    lines = out.stdout.split()
+    assert out.returncode == 0 and lines[-1] == "ok", out.stdout + out.stderr
+    # the ctypes mirrors of the public structs match the C layout
+    layout = [int(v) for v in lines[1:5]]
+    assert layout == [ctypes.sizeof(hist.PlanInfo), ctypes.sizeof(hist.PlanOpts),
+                      hist.PlanInfo.max_group_elems.offset, hist.PlanInfo.event_cap.offset]

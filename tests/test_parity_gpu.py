@@ -77,6 +77,11 @@ PATH_CASES = [
     ("full-copies4-agg2", {"lds_copies": 4, "aggregation": 2}),
     ("range-copies8", {"path": "range", "range_bins": 2048, "lds_copies": 8}),
     ("range-cw16", {"path": "range", "range_bins": 2048, "counter_bits": 16}),
+    ("full-cw8", {"counter_bits": 8}),
+    ("full-cw8-agg2", {"counter_bits": 8, "aggregation": 2}),
+    ("full-cw8-hot", {"counter_bits": 8, "aggregation": 1}),
+    ("range-cw8", {"path": "range", "range_bins": 2048, "counter_bits": 8}),
+    ("range-cw8-wg256", {"path": "range", "range_bins": 1024, "counter_bits": 8, "wg_size": 256}),
     ("scatter", {"path": "scatter"}),
     ("scatter-agg1", {"path": "scatter", "aggregation": 1}),
 ]
@@ -110,11 +115,11 @@ def test_lengths_and_alignment(n, offset):
 
 @pytest.mark.parametrize("num_bins", [1, 2, 3, 5, 255, 4095, 8191, 8193, 32767, 32768, 32769,
                                       40703, 40704, 40705, 40960, 65535, 65537, 79616, 79617,
-                                      100_003, 262_145])
+                                      100_003, 155_391, 155_392, 155_393, 262_145])
 def test_bin_counts(num_bins):
     x = rnd(num_bins, 300_007, -3, num_bins + 5)
     paths = ["auto", "scatter"]
-    if num_bins <= 79616:
+    if num_bins <= 155_392:
         paths.append("full")
     if num_bins > 8:
         paths.append("range")
@@ -161,6 +166,49 @@ def test_counter16_carry_events(agg, path, bins):
     x = x[rng.permutation(x.size)].astype(np.int32)
     check(x, bins, f"cw16-{path}-agg{agg}", path=path, counter_bits=16, groups=3,
           aggregation=agg)
+
+
+@pytest.mark.parametrize("agg", [0, 1, 2, 4])
+@pytest.mark.parametrize("path,bins,groups", [("full", 150_000, 3), ("full", 155_392, 1),
+                                              ("range", 400_000, 2), ("full", 4099, 1)])
+def test_counter8_carry_events(agg, path, bins, groups):
+    # Few chunks and many copies of a few bins: every chunk's 8-bit counters
+    # carry many times, out of every byte of a word (4..7 share a word, so
+    # their carries cascade), out of the word's top byte (11), and in the
+    # last, ragged word of the slice. groups=1 takes the direct write.
+    rng = np.random.default_rng(agg)
+    hot = np.array([4, 5, 6, 7, 8, 11, bins - 1], np.int32)
+    reps = [40_001, 30_007, 25_000, 20_003, 1_000, 9_999, 7_000]
+    x = np.concatenate([np.repeat(hot, reps), rnd(9, 300_000, 0, bins)])
+    x = x[rng.permutation(x.size)].astype(np.int32)
+    check(x, bins, f"cw8-{path}-agg{agg}-g{groups}", path=path, counter_bits=8, groups=groups,
+          aggregation=agg, **({"range_bins": 131_072} if path == "range" else {}))
+
+
+@pytest.mark.parametrize("case,bins", [("one-bin-at-the-limit", 155_392),
+                                       ("one-bin-at-the-limit", 100_000),
+                                       ("one-bin-past-the-limit", 155_392),
+                                       ("every-bin-near-255", 2048)])
+def test_counter8_event_list_bound(case, bins):
+    """The carry-event list at its bound: one workgroup (groups=1) counting
+    the most elements the plan lets one chunk hold, all in one bin, logs about
+    n / 255 events, close to the list's capacity (the LDS its slice leaves:
+    the minimum at 155,392 bins, much more at 100,000); one element more and
+    the plan splits the input. With every bin near 255 copies the events
+    spread over the whole slice."""
+    probe = hist.Plan(bins, 1, device=DEV, path="full", counter_bits=8, groups=1)
+    info = probe.info()
+    probe.close()
+    limit = info.max_group_elems
+    assert limit == 255 * (info.event_cap - 16) and info.event_cap >= 2048
+    if case == "every-bin-near-255":
+        x = np.repeat(np.arange(bins, dtype=np.int32), limit // bins)
+        x = x[np.random.default_rng(5).permutation(x.size)]
+    else:
+        x = np.full(limit + (case == "one-bin-past-the-limit"), bins - 2, np.int32)
+    for agg in (0, 1):
+        check(x, bins, f"cw8-bound-{case}-agg{agg}", path="full", counter_bits=8, groups=1,
+              aggregation=agg)
 
 
 def test_groups_and_wg_sizes():
@@ -222,6 +270,8 @@ ACC_CASES = [
     ("direct-one-chunk", 4096, 6000, {"path": "full"}),
     ("full-cw32", 8192, 400_000, {}),
     ("full-cw16", 65536, 1_000_000, {}),
+    ("full-cw8", 150_000, 1_000_000, {"path": "full"}),
+    ("direct-cw8", 150_000, 400_000, {"path": "full", "groups": 1}),
     ("range", 200_000, 2_000_000, {"path": "range"}),
     ("scatter-hot", 300_000, 1_000_000, {"path": "scatter", "aggregation": 1}),
 ]
@@ -373,6 +423,9 @@ FULL_CASES = [
     (3, {"path": "scatter", "aggregation": 1}), (3, {"aggregation": 1}),
     (2, {"aggregation": 1}), (2, {"path": "range", "counter_bits": 32, "aggregation": 1}),
     (5, {}), (5, {"aggregation": 2}), (5, {"path": "range"}),
+    (2, {"counter_bits": 8}), (3, {"path": "range", "counter_bits": 8}),
+    (3, {"path": "range", "counter_bits": 8, "aggregation": 1}),
+    (5, {"path": "range", "counter_bits": 8}),
 ]
 
 
@@ -488,17 +541,17 @@ def _fuzz_case(seed, large=False):
         x = g.integers(-(2**31), 2**31 - 1, size=n)
         x[::3] = g.integers(0, num_bins, size=x[::3].size)
     x = x.astype(np.int64).astype(np.int32)
-    paths = ["auto", "scatter"] + (["full"] if num_bins <= 79616 else []) + \
+    paths = ["auto", "scatter"] + (["full"] if num_bins <= 155_392 else []) + \
         (["range", "range"] if num_bins > 1 else [])
     path = str(g.choice(paths))
     opts = {"path": path, "aggregation": int(g.choice([-1, 0, 1, 2, 4]))}
     if path in ("full", "range"):
         opts["wg_size"] = int(g.choice([0, 256, 512, 1024]))
-        opts["counter_bits"] = int(g.choice([0, 16, 32]))
+        opts["counter_bits"] = int(g.choice([0, 8, 16, 32]))
         if opts["counter_bits"] == 32 and g.random() < 0.5:
             opts["lds_copies"] = int(g.choice([1, 2, 4]))
         if path == "range":
-            cap = 40960 if opts["counter_bits"] == 32 else 79616
+            cap = {32: 40960, 16: 79616}.get(opts["counter_bits"], 155_392)
             opts["range_bins"] = int(g.integers(1, cap // 256 + 1)) * 256
             opts["xcd_map"] = int(g.choice([0, 1, 2]))
         if g.random() < 0.3:
