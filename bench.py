@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 KERNEL_SOURCES = [f"partitioned_chip_accumulation_amd/csrc/{f}" for f in (
     "hist_common.hpp", "hist_counters16.hpp", "hist_partials.hpp", "hist_sweep.hpp",
-    "hist_scatter.hpp", "hist_kernels.hpp", "hist_api.hip")]
+    "hist_scatter.hpp", "hist_kernels.hpp", "hist_api.hip", "hist_counters8.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -65,6 +65,9 @@ def parse():
                          "input of --n (default 2^26) elements; one JSON line per cell")
     ap.add_argument("--sweep-log2", default="10,22",
                     help="first,last log2 bin count of --path-sweep")
+    ap.add_argument("--sweep-zipf", type=float, default=0.0,
+                    help="--path-sweep on finite Zipf input with this exponent (ranks permuted "
+                         "to bins) instead of uniform input")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure the machine's ceilings the kernels meet (HBM stream read and "
                          "copy, LDS atomic rates by address pattern, shared-L2 placement of "
@@ -167,7 +170,7 @@ def workload_matrix(args):
             xs.append(xs[0].clone())
         out = torch.empty(w.num_bins, dtype=torch.int32, device=dev)
         B = w.num_bins
-        cells = [("auto", {})]
+        cells = []
         if B <= 40960:
             cells.append(("full32", {"path": "full", "counter_bits": 32}))
         if B <= 79616:
@@ -183,6 +186,7 @@ def workload_matrix(args):
             cells.append(("range8+hot", {"path": "range", "counter_bits": 8, "aggregation": 1}))
         cells.append(("scatter", {"path": "scatter", "aggregation": 0}))
         cells.append(("scatter+hot", {"path": "scatter", "aggregation": 1}))
+        cells.append(("auto", {}))  # last: the first cell after an upload runs slow
         steps = max(10, min(args.steps, int(4e9 / (4 * w.n))))
         for name, opts in cells:
             if B > 4 * 79616 and name.startswith("range32"):
@@ -204,7 +208,8 @@ def workload_matrix(args):
 
 
 def path_sweep(args):
-    """Every schedule the library offers, on uniform input, across bin counts.
+    """Every schedule the library offers, on uniform (or --sweep-zipf) input,
+    across bin counts.
 
     The cells are the evidence behind the plan's automatic choice: for each
     bin count the fastest bit-exact schedule wins. Timing is the same as the
@@ -224,13 +229,13 @@ def path_sweep(args):
     lb0, lb1 = (int(v) for v in args.sweep_log2.split(","))
     for lb in range(lb0, lb1 + 1):
         B = 1 << lb
-        x = inputs.uniform(1, n, B)
+        x = inputs.zipf(2, n, B, args.sweep_zipf) if args.sweep_zipf > 0 else inputs.uniform(1, n, B)
         ref, _ = oracle.hist(x, B)
         xs = [torch.from_numpy(x).to(dev)]
         for _ in range(3):
             xs.append(xs[0].clone())
         out = torch.empty(B, dtype=torch.int32, device=dev)
-        cells = [("auto", {})]
+        cells = []
         if B <= 40960:
             cells.append(("full32", {"path": "full", "counter_bits": 32}))
         if B <= 79616:
@@ -242,6 +247,9 @@ def path_sweep(args):
             cells.append(("range16", {"path": "range", "counter_bits": 16}))
             cells.append(("range8", {"path": "range", "counter_bits": 8}))
         cells.append(("scatter", {"path": "scatter"}))
+        if args.sweep_zipf > 0:
+            cells.append(("scatter+hot", {"path": "scatter", "aggregation": 1}))
+        cells.append(("auto", {}))  # last: the first cell after an upload runs slow
         for name, opts in cells:
             try:
                 plan = hist.Plan(B, n, device=dev, **opts)
@@ -258,6 +266,7 @@ def path_sweep(args):
             dt = (time.perf_counter() - t0) / steps
             ok = bool(np.array_equal(out.view(torch.uint32).cpu().numpy(), ref))
             rec = {"bins": B, "n": n, "cell": name, "us_per_run": round(dt * 1e6, 2),
+                   "input": f"zipf s={args.sweep_zipf:g}" if args.sweep_zipf > 0 else "uniform",
                    "gelem_s": round(n / dt / 1e9, 1), "parity": ok, "plan": plan.describe()}
             print(json.dumps(rec), flush=True)
             if name != "auto" and ok and (B not in best or dt < best[B][1]):

@@ -34,7 +34,7 @@ constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slot
 // AUTO uses RANGE up to this many 16-bit ranges' worth of bins (318,464) and
 // SCATTER beyond: on 2^26 uniform elements SCATTER wins from 2^19 bins on
 // (141.7 us against 221 with 16-bit and 113 with 8-bit counters, the latter
-// at 1,895 us against 906 on the half-Gaussian 512K-bin workload, whose
+// at 2,306 us against 904 on the half-Gaussian 512K-bin workload, whose
 // carry events pile up in a few pairs of blocks).
 constexpr uint32_t kRangeMaxR = 4;
 constexpr uint32_t kMinElemsPerGroup = 4096;
@@ -193,10 +193,10 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // bins per workgroup, which saves input passes: 2^17 bins in one
             // pass (53.9 us against 74.6 for two 16-bit ranges), 2^18 in two
             // (67.4 against 131.4 for four); at 2^16 they lose to 16-bit ones
-            // (54.1 vs 49.8 us). On skewed input the comparison can turn: Zipf
-            // s = 1.1 over 2^17 bins takes 118 us in one 8-bit pass against 101
-            // in two 16-bit ranges, as a single owner meets more same-word lanes
-            // per LDS instruction.
+            // (54.1 vs 49.8 us). On skewed input the comparison turns: Zipf
+            // s = 1.1 over 2^17 bins takes 119.4 us in one 8-bit pass against
+            // 105.8 in two 16-bit ranges (hot bytes wrap every 256 counts, and a
+            // single owner meets more same-word lanes per LDS instruction).
             if (path == HIST_PATH_FULL)
                 cw = num_bins > lds_bins16 ? 8 : num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
             else if (opts.range_bins > 0)

@@ -109,6 +109,16 @@ def uniform(seed: int, n: int, num_bins: int, lo: int = 0, out: np.ndarray | Non
     return out
 
 
+def zipf(seed: int, n: int, num_bins: int, s: float) -> np.ndarray:
+    """int32 finite Zipf values: rank k in 1..num_bins with P(k) ~ k^-s, the
+    ranks permuted to bins (the recipe of workload 3, any size and exponent)."""
+    out = np.empty(n, dtype=np.int32)
+    rc = _library().gen_zipf(seed, out.ctypes.data if n else None, n, num_bins, float(s))
+    if rc != 0:
+        raise RuntimeError(f"gen_zipf failed with {rc}")
+    return out
+
+
 def shuffle(seed: int, values: np.ndarray) -> np.ndarray:
     """Fisher-Yates shuffle in place (int32 array); returns the array."""
     assert values.dtype == np.int32 and values.flags.c_contiguous

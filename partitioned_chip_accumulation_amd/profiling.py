@@ -149,13 +149,16 @@ def calib_markdown(jsonl: str, cmd: str) -> str:
 def sweep_markdown(jsonl: str, cmd: str) -> str:
     """Bin counts x schedules table from ``bench.py --path-sweep``."""
     rows, cols, plans = _read_cells(jsonl, "bins")
-    n = next(iter(next(iter(rows.values())).values()))["n"]
+    first = next(iter(next(iter(rows.values())).values()))
+    n, kind = first["n"], first.get("input", "uniform")
+    kind = "uniform" if kind == "uniform" else f"finite Zipf ({kind}, ranks permuted to bins)"
     rows = collections.OrderedDict((f"2^{b.bit_length() - 1}", v) for b, v in rows.items())
-    out = [f"# Path selection: every schedule on uniform int32 input, n = {n:,}, one MI355X", "",
+    out = [f"# Path selection: every schedule on {kind} int32 input, n = {n:,}, one MI355X", "",
            "Microseconds per histogram: wall clock over back-to-back runs on four rotated input "
            "copies after 20 warm-up runs. Every cell was checked bit for bit against the CPU "
            "oracle (a failure would be marked FAIL). The fastest cell of a row is in bold. AUTO "
-           "is the plan's own choice; it runs first in each row, right after the input upload.",
+           "is the plan's own choice; it runs last in each row (the first cell after an input "
+           "upload runs measurably slow).",
            "", "Command:", "", "```", cmd, "```", ""]
     out += _cells_table(rows, cols, "bins")
     out += ["", "AUTO's plans:", ""] + \

@@ -96,3 +96,14 @@ def test_golden_hashes():
     for cfg, entry in golden["inputs"].items():
         x = inputs.generate(int(cfg), n=entry["n"])
         assert hashlib.sha256(x.tobytes()).hexdigest() == entry["sha256"], cfg
+
+
+def test_zipf_any_size_matches_the_workload_recipe():
+    # inputs.zipf is workload 3's generator with its size and exponent free
+    n = 200_003
+    assert np.array_equal(inputs.zipf(2, n, 262_144, 1.1), inputs.generate(3, n=n))
+    x = inputs.zipf(7, 100_000, 1000, 1.5)
+    assert x.min() >= 0 and x.max() < 1000
+    # a heavier exponent concentrates more mass in the top bin
+    top = lambda v: np.bincount(v).max() / v.size  # noqa: E731
+    assert top(x) > top(inputs.zipf(7, 100_000, 1000, 1.1))
