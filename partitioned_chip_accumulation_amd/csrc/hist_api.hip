@@ -150,6 +150,10 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
     return HIST_OK;
 }
 
+// Sweep workgroups of this configuration one CU holds at once (0 if the
+// runtime cannot tell); defined with the launch code below.
+uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes);
+
 // Fill every plan field that depends only on (num_bins, max_n, opts, device).
 hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *o)
 {
@@ -235,7 +239,12 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // workgroup per CU, which runs best with 512 (32,768 bins: 49.7 vs
             // 52.6 us; 16-bit at 65,536 bins: 50.8 with 1024 vs 56.4 us).
             if (wg == 0) wg = cw == 32 && occ_lds == 1 ? 512 : 1024;
-            const uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
+            uint32_t occ = std::min<uint32_t>(occ_lds, kMaxWavesPerCU / (wg / 64));
+            // Registers can bound residency below what LDS allows (a 1024-thread
+            // sweep with more than 64 VGPRs fits once per CU): chunks beyond the
+            // resident ones would run as a second round.
+            const uint32_t res = sweep_resident(cw, wg, p->agg, lds_bytes);
+            if (res > 0) occ = std::max<uint32_t>(1, std::min(occ, res));
             uint32_t G = (uint32_t)opts.groups, slots = 0;
             if (G == 0) {
                 G = (uint32_t)d.cu * occ / R;
@@ -386,6 +395,48 @@ hipError_t launch_sweep_wg(const hist_plan *p, const SweepArgs &a, hipStream_t s
     case 512: return launch_sweep_agg<512, CW>(p, a, s);
     default: return launch_sweep_agg<1024, CW>(p, a, s);
     }
+}
+
+template <int WG, int AGG, int CW>
+uint32_t sweep_resident_t(uint32_t lds_bytes)
+{
+    auto k = pca::k_sweep<WG, CW == 32 ? 4 : 2, AGG, CW>;
+    int blocks = 0;
+    if (allow_lds(k, lds_bytes) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void *>(k), WG,
+                                                     lds_bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return blocks > 0 ? (uint32_t)blocks : 0u;
+}
+
+template <int WG, int CW>
+uint32_t sweep_resident_agg(int agg, uint32_t lds_bytes)
+{
+    switch (agg) {
+    case 0: return sweep_resident_t<WG, 0, CW>(lds_bytes);
+    case 1: return sweep_resident_t<WG, 1, CW>(lds_bytes);
+    case 2: return sweep_resident_t<WG, 2, CW>(lds_bytes);
+    default: return sweep_resident_t<WG, 4, CW>(lds_bytes);
+    }
+}
+
+template <int CW>
+uint32_t sweep_resident_wg(uint32_t wg, int agg, uint32_t lds_bytes)
+{
+    switch (wg) {
+    case 256: return sweep_resident_agg<256, CW>(agg, lds_bytes);
+    case 512: return sweep_resident_agg<512, CW>(agg, lds_bytes);
+    default: return sweep_resident_agg<1024, CW>(agg, lds_bytes);
+    }
+}
+
+uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes)
+{
+    return cw == 32   ? sweep_resident_wg<32>(wg, agg, lds_bytes)
+           : cw == 16 ? sweep_resident_wg<16>(wg, agg, lds_bytes)
+                      : sweep_resident_wg<8>(wg, agg, lds_bytes);
 }
 
 hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, hipStream_t s)
