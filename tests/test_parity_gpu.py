@@ -211,6 +211,26 @@ def test_counter8_event_list_bound(case, bins):
               aggregation=agg)
 
 
+AUTO_CASES = [  # bin count -> (path, counter bits, ranges) the measured thresholds give
+    (8192, ("full", 16, 1)), (20480, ("full", 16, 1)), (20481, ("full", 32, 1)),
+    (40960, ("full", 32, 1)), (40961, ("full", 16, 1)), (79616, ("full", 16, 1)),
+    (79617, ("full", 8, 1)), (155392, ("full", 8, 1)), (155393, ("range", 8, 2)),
+    (262144, ("range", 8, 2)), (318464, ("range", 8, 3)), (318465, ("scatter", 32, 10)),
+    (1 << 20, ("scatter", 32, 32)),
+]
+
+
+@pytest.mark.parametrize("num_bins,want", AUTO_CASES, ids=[str(c[0]) for c in AUTO_CASES])
+def test_auto_plan_follows_the_measured_thresholds(num_bins, want):
+    """AUTO's path, counter width and range count at each threshold of the
+    path-selection sweep, for 2^26 elements (the sweep's n)."""
+    info = hist.Plan(num_bins, 1 << 26, device=DEV).info()
+    assert (info.path, info.counter_bits, info.ranges) == want, info
+    if info.path != "scatter":
+        # one round of resident sweep workgroups
+        assert info.groups * info.ranges <= info.cu_count * 2
+
+
 def test_groups_and_wg_sizes():
     x = inputs.generate(2, n=(1 << 21) + 7)
     for opts in [{"groups": 1}, {"groups": 3}, {"groups": 8}, {"groups": 256},
