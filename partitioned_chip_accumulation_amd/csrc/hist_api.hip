@@ -195,12 +195,13 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // where their slice leaves one workgroup per CU (24,576 bins: 48.8
             // vs 52.1 us; 32,768: 49.7 vs 52.7 us). 8-bit counters hold the most
             // bins per workgroup, which saves input passes: 2^17 bins in one
-            // pass (53.9 us against 74.6 for two 16-bit ranges), 2^18 in two
-            // (67.4 against 131.4 for four); at 2^16 they lose to 16-bit ones
-            // (54.1 vs 49.8 us). On skewed input the comparison turns: Zipf
-            // s = 1.1 over 2^17 bins takes 119.4 us in one 8-bit pass against
-            // 105.8 in two 16-bit ranges (hot bytes wrap every 256 counts, and a
-            // single owner meets more same-word lanes per LDS instruction).
+            // pass (52.9 us against 64.3 for two 16-bit ranges), 2^18 in two
+            // (63.9 against 117.6 for four). Up to 2^16 bins they gain at most
+            // 1.4% over 16-bit ones and lose 2-2.5x on Zipf input. On skewed
+            // input the comparison turns at 2^17 too: Zipf s = 1.1 takes 118.4
+            // us in one 8-bit pass against 106.2 in two 16-bit ranges (hot bytes
+            // wrap every 256 counts, and a single owner meets more same-word
+            // lanes per LDS instruction).
             if (path == HIST_PATH_FULL)
                 cw = num_bins > lds_bins16 ? 8 : num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
             else if (opts.range_bins > 0)

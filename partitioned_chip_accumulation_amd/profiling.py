@@ -157,8 +157,8 @@ def sweep_markdown(jsonl: str, cmd: str) -> str:
            "Microseconds per histogram: wall clock over back-to-back runs on four rotated input "
            "copies after 20 warm-up runs. Every cell was checked bit for bit against the CPU "
            "oracle (a failure would be marked FAIL). The fastest cell of a row is in bold. AUTO "
-           "is the plan's own choice; it runs last in each row (the first cell after an input "
-           "upload runs measurably slow).",
+           "is the plan's own choice; it runs last in each row, and every row starts with 0.3 s "
+           "of untimed runs so that no cell meets unsettled clocks.",
            "", "Command:", "", "```", cmd, "```", ""]
     out += _cells_table(rows, cols, "bins")
     out += ["", "AUTO's plans:", ""] + \
