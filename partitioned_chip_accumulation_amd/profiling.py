@@ -155,8 +155,8 @@ def sweep_markdown(jsonl: str, cmd: str) -> str:
     rows = collections.OrderedDict((f"2^{b.bit_length() - 1}", v) for b, v in rows.items())
     out = [f"# Path selection: every schedule on {kind} int32 input, n = {n:,}, one MI355X", "",
            "Microseconds per histogram: wall clock over back-to-back runs on four rotated input "
-           "copies after 20 warm-up runs. Every cell was checked bit for bit against the CPU "
-           "oracle (a failure would be marked FAIL). The fastest cell of a row is in bold. AUTO "
+           "copies after 20 warm-up runs. Every cell was checked bit for bit against numpy's "
+           "bincount (a failure would be marked FAIL). The fastest cell of a row is in bold. AUTO "
            "is the plan's own choice; it runs last in each row, and every row starts with 0.3 s "
            "of untimed runs so that no cell meets unsettled clocks.",
            "", "Command:", "", "```", cmd, "```", ""]
@@ -172,8 +172,8 @@ def matrix_markdown(jsonl: str, cmd: str) -> str:
     rows, cols, plans = _read_cells(jsonl, "workload")
     out = ["# Every schedule on every workload, one MI355X", "",
            "Microseconds per histogram: wall clock over back-to-back runs on four rotated input "
-           "copies after 10 warm-up runs. Every cell was checked bit for bit against the CPU "
-           "oracle (a failure would be marked FAIL). The fastest cell of a row is in bold. "
+           "copies after 10 warm-up runs. Every cell was checked bit for bit against numpy's "
+           "bincount (a failure would be marked FAIL). The fastest cell of a row is in bold. "
            "\"+hot\" is the wave hot-slot aggregation. An empty cell is a schedule the bin "
            "count does not allow.", "", "Command:", "", "```", cmd, "```", ""]
     out += _cells_table(rows, cols, "workload")
