@@ -164,51 +164,55 @@ __device__ __forceinline__ uint32_t &count_at(Counts32 &c)
     return c.*kCountMember[K];
 }
 
-// c[k] += v for the wave-uniform k in [LO, HI): a binary tree of scalar
-// branches whose every leaf adds to one register. The leaf's add is an
-// opaque instruction so that the compiler cannot merge the leaves back into
-// one add at a run-time register index (GPR indexing mode), which it would
+// One carry event out of count k (wave-uniform, k in [LO, HI)): c[k] += add
+// and, unless k is byte 3 of its word (whose carry leaves the word),
+// c[k + 1] -= sub. A binary tree of scalar branches leads to a leaf that
+// updates its registers by constant names; the updates are opaque
+// instructions so that the compiler cannot merge the leaves back into one
+// update at a run-time register index (GPR indexing mode), which it would
 // otherwise do and which this code must not depend on.
 template <int LO, int HI>
-__device__ __forceinline__ void add_at(Counts32 &c, uint32_t k, uint32_t v)
+__device__ __forceinline__ void carry_at(Counts32 &c, uint32_t k, uint32_t add, uint32_t sub)
 {
     if constexpr (HI - LO == 1) {
-        asm volatile("v_add_u32 %0, %0, %1" : "+v"(count_at<LO>(c)) : "v"(v));
+        asm volatile("v_add_u32 %0, %0, %1" : "+v"(count_at<LO>(c)) : "v"(add));
+        if constexpr ((LO & 3) != 3)
+            asm volatile("v_sub_u32 %0, %0, %1" : "+v"(count_at<LO + 1>(c)) : "v"(sub));
     } else {
         constexpr int MID = (LO + HI) / 2;
-        if (k < (uint32_t)MID) add_at<LO, MID>(c, k, v);
-        else add_at<MID, HI>(c, k, v);
+        if (k < (uint32_t)MID) carry_at<LO, MID>(c, k, add, sub);
+        else carry_at<MID, HI>(c, k, add, sub);
     }
 }
 
-// Apply the carry events to the counts of J <= 4 pairs of blocks that start
-// at word wlo: c[8j + i] is bin 8l + i of pair j (l = lane), byte i % 4 of
-// word wlo + 128 j + 2l + i / 4. The wave reads the list 64 entries at a
-// time and takes only the entries in [wlo, wlo + 128 J); an entry names one
-// count, whose index in c is wave-uniform, so each matching entry costs a
-// few scalar branches and two adds in which only the owning lane's value
-// changes. Whole wave, convergent; wlo uniform.
-template <int J>
-__device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t nev, uint32_t wlo,
+// Apply the carry events to the counts of J <= 4 pairs of blocks, pairs
+// p0 + STRIDE j (j < J): c[8j + i] is bin 8l + i of pair p0 + STRIDE j
+// (l = lane), byte i % 4 of its word 2l + i / 4. The wave reads the list 64
+// entries at a time and takes only the entries in its pairs; an entry names
+// one count, whose index in c is wave-uniform, so each matching entry costs
+// a few scalar branches and two register updates in which only the owning
+// lane's values change. Whole wave, convergent; p0 uniform.
+template <int J, int STRIDE>
+__device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t nev, uint32_t p0,
                                               Counts32 &c)
 {
     const uint32_t lane = lane_id();
     // uniform in fact (derived from the wave index); said so, the entry index
     // below is computed in scalar registers
-    wlo = (uint32_t)__builtin_amdgcn_readfirstlane((int)wlo);
+    p0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)p0);
     for (uint32_t e0 = 0; e0 < nev; e0 += 64) {
         const uint32_t e = e0 + lane;
         const uint32_t ent = e < nev ? evlist[e] : 0xFFFFFFFFu;
-        uint64_t m = __ballot((ent >> 2) - wlo < 128u * J);
+        const uint32_t dp = (ent >> 9) - p0;  // pair of the entry's word, from p0
+        uint64_t m = __ballot(dp < (uint32_t)(STRIDE * J) && dp % STRIDE == 0u);
         while (m != 0) {
             const int k = __builtin_ctzll(m);
             m &= m - 1;
             const uint32_t ev = (uint32_t)__builtin_amdgcn_readlane((int)ent, k);
-            const uint32_t d = (ev >> 2) - wlo;  // word within the batch
-            const uint32_t idx = (d >> 7) * 8u + (d & 1u) * 4u + (ev & 3u);
-            const uint32_t hit = lane == ((d & 127u) >> 1) ? 1u : 0u;
-            add_at<0, 8 * J>(c, idx, hit << 8);
-            if ((ev & 3u) != 3u) add_at<0, 8 * J>(c, idx + 1, 0u - hit);  // byte 3: leaves the word
+            const uint32_t word = ev >> 2;
+            const uint32_t idx = (((ev >> 9) - p0) / STRIDE) * 8u + (word & 1u) * 4u + (ev & 3u);
+            const uint32_t hit = lane == ((word & 127u) >> 1) ? 1u : 0u;
+            carry_at<0, 8 * J>(c, idx, hit << 8, hit);
         }
     }
 }

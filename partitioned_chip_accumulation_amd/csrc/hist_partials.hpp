@@ -213,7 +213,7 @@ __device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t 
         Counts32 cv;
         octet8_raw<0>(lds, p, len, cv);
         // a carry out of the last valid byte lands in an invalid one: mask after
-        apply_events8<1>(evlist, nev, p * 128u, cv);
+        apply_events8<1, 1>(evlist, nev, p, cv);
         octet_of<0>(cv, c);
         mask_octet(p, len, c);
         return;
@@ -325,15 +325,18 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
             }
             return;
         }
-        // one pass over the event list per batch of pairs
-        for (uint32_t p0 = w * kFlushBatch; p0 < npairs; p0 += NW * kFlushBatch) {
+        // One pass over the event list per batch of pairs. A batch is four
+        // pairs NW apart, so that a contiguous run of event-heavy pairs (the
+        // hot core of a skewed input) is spread over up to NW waves, each of
+        // which applies its events one at a time.
+        for (uint32_t p0 = w; p0 < npairs; p0 += NW * kFlushBatch) {
             static_assert(kFlushBatch == 4, "Counts32 holds four pairs");
             Counts32 cv;
-            octet8_raw<0>(lds, p0 + 0, len, cv);
-            octet8_raw<1>(lds, p0 + 1, len, cv);
-            octet8_raw<2>(lds, p0 + 2, len, cv);
-            octet8_raw<3>(lds, p0 + 3, len, cv);
-            apply_events8<kFlushBatch>(evlist, nev, p0 * 128u, cv);
+            octet8_raw<0>(lds, p0 + 0 * NW, len, cv);
+            octet8_raw<1>(lds, p0 + 1 * NW, len, cv);
+            octet8_raw<2>(lds, p0 + 2 * NW, len, cv);
+            octet8_raw<3>(lds, p0 + 3 * NW, len, cv);
+            apply_events8<kFlushBatch, NW>(evlist, nev, p0, cv);
             uint32_t c[kFlushBatch][8];
             octet_of<0>(cv, c[0]);
             octet_of<1>(cv, c[1]);
@@ -341,10 +344,10 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
             octet_of<3>(cv, c[3]);
 #pragma unroll
             for (uint32_t j = 0; j < kFlushBatch; ++j) {
-                if (p0 + j >= npairs) break;  // uniform
-                mask_octet(p0 + j, len, c[j]);
-                const uint32_t kb = 2 * (p0 + j);
-                write_pair(P, row_blk + kb, min(2u, nblk_slice - kb), c[j]);
+                const uint32_t p = p0 + j * NW;
+                if (p >= npairs) break;  // uniform
+                mask_octet(p, len, c[j]);
+                write_pair(P, row_blk + 2 * p, min(2u, nblk_slice - 2 * p), c[j]);
             }
         }
         return;
