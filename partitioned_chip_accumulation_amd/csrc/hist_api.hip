@@ -33,9 +33,8 @@ constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elemen
 constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slots per tile
 // AUTO uses RANGE up to this many 16-bit ranges' worth of bins (318,464) and
 // SCATTER beyond: on 2^26 uniform elements SCATTER wins from 2^19 bins on
-// (141.7 us against 221 with 16-bit and 113 with 8-bit counters, the latter
-// at 2,306 us against 904 on the half-Gaussian 512K-bin workload, whose
-// carry events pile up in a few pairs of blocks).
+// (141 us against 220 with 16-bit and 115 with 8-bit counters, the latter
+// at 1,563 us against 906 on the half-Gaussian 512K-bin workload).
 constexpr uint32_t kRangeMaxR = 4;
 constexpr uint32_t kMinElemsPerGroup = 4096;
 constexpr int kMaxWavesPerCU = 32;
@@ -195,13 +194,12 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // where their slice leaves one workgroup per CU (24,576 bins: 48.8
             // vs 52.1 us; 32,768: 49.7 vs 52.7 us). 8-bit counters hold the most
             // bins per workgroup, which saves input passes: 2^17 bins in one
-            // pass (52.9 us against 64.3 for two 16-bit ranges), 2^18 in two
-            // (63.9 against 117.6 for four). Up to 2^16 bins they gain at most
-            // 1.4% over 16-bit ones and lose 2-2.5x on Zipf input. On skewed
-            // input the comparison turns at 2^17 too: Zipf s = 1.1 takes 118.4
-            // us in one 8-bit pass against 106.2 in two 16-bit ranges (hot bytes
-            // wrap every 256 counts, and a single owner meets more same-word
-            // lanes per LDS instruction).
+            // pass (53.0 us against 65.1 for two 16-bit ranges), 2^18 in two
+            // (64.7 against 118.2 for four), and they stay ahead on Zipf s = 1.1
+            // input there (97.4 vs 105.8, 160.9 vs 166.5 us). Up to 2^16 bins
+            // they gain at most 1.4% on uniform input and lose 1.7x on Zipf
+            // input, whose hot bytes wrap every 256 counts (2^14 bins: 92.8 vs
+            // 55.9 us).
             if (path == HIST_PATH_FULL)
                 cw = num_bins > lds_bins16 ? 8 : num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
             else if (opts.range_bins > 0)
