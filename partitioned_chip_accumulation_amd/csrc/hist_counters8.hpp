@@ -150,13 +150,20 @@ __device__ __forceinline__ void lds_count8(uint32_t *words, uint32_t *evlist, ui
 // one 32-register tuple, which a branch that changes one element copies
 // whole.
 struct Counts32 {
-    uint32_t v0, v1, v2, v3, v4, v5, v6, v7, v8, v9, v10, v11, v12, v13, v14, v15, v16, v17, v18, v19, v20, v21, v22, v23, v24, v25, v26, v27, v28, v29, v30, v31;
+    uint32_t v0, v1, v2, v3, v4, v5, v6, v7;          // pair 0 of the batch
+    uint32_t v8, v9, v10, v11, v12, v13, v14, v15;    // pair 1
+    uint32_t v16, v17, v18, v19, v20, v21, v22, v23;  // pair 2
+    uint32_t v24, v25, v26, v27, v28, v29, v30, v31;  // pair 3
 };
 constexpr uint32_t Counts32::*kCountMember[32] = {
-    &Counts32::v0, &Counts32::v1, &Counts32::v2, &Counts32::v3, &Counts32::v4, &Counts32::v5, &Counts32::v6, &Counts32::v7,
-    &Counts32::v8, &Counts32::v9, &Counts32::v10, &Counts32::v11, &Counts32::v12, &Counts32::v13, &Counts32::v14, &Counts32::v15,
-    &Counts32::v16, &Counts32::v17, &Counts32::v18, &Counts32::v19, &Counts32::v20, &Counts32::v21, &Counts32::v22, &Counts32::v23,
-    &Counts32::v24, &Counts32::v25, &Counts32::v26, &Counts32::v27, &Counts32::v28, &Counts32::v29, &Counts32::v30, &Counts32::v31};
+    &Counts32::v0,  &Counts32::v1,  &Counts32::v2,  &Counts32::v3,
+    &Counts32::v4,  &Counts32::v5,  &Counts32::v6,  &Counts32::v7,
+    &Counts32::v8,  &Counts32::v9,  &Counts32::v10, &Counts32::v11,
+    &Counts32::v12, &Counts32::v13, &Counts32::v14, &Counts32::v15,
+    &Counts32::v16, &Counts32::v17, &Counts32::v18, &Counts32::v19,
+    &Counts32::v20, &Counts32::v21, &Counts32::v22, &Counts32::v23,
+    &Counts32::v24, &Counts32::v25, &Counts32::v26, &Counts32::v27,
+    &Counts32::v28, &Counts32::v29, &Counts32::v30, &Counts32::v31};
 
 template <int K>
 __device__ __forceinline__ uint32_t &count_at(Counts32 &c)
