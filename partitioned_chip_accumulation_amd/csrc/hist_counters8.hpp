@@ -81,17 +81,24 @@ __device__ __forceinline__ void count8_batch(uint32_t *words, uint32_t *evlist, 
         old[e] = 0u;
         if (ok[e]) old[e] = lds_add_rtn(words, s[e] >> 2, 1u << sh[e]);
     }
-    bool any = false;
+    bool hit[N], any = false;
 #pragma unroll
-    for (int e = 0; e < N; ++e)
-        any = any || (ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 8) == 0xFFu);
+    for (int e = 0; e < N; ++e) {
+        hit[e] = ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 8) == 0xFFu;
+        any = any || hit[e];
+    }
     if (__ballot(any)) {
+        // carry bits only for the elements some lane carried on (mostly one or two)
         uint32_t bits[N], tot = 0;
+        uint64_t hm[N];
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            bits[e] = ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 8) == 0xFFu
-                          ? carry_bits8(old[e], 1u << sh[e]) : 0u;
-            tot += (uint32_t)__popc(bits[e]);
+            bits[e] = 0u;
+            hm[e] = __ballot(hit[e]);
+            if (hm[e]) {
+                bits[e] = hit[e] ? carry_bits8(old[e], 1u << sh[e]) : 0u;
+                tot += (uint32_t)__popc(bits[e]);
+            }
         }
         uint32_t pre = 0, sum = 0;
         for (uint32_t j = 0;; ++j) {
@@ -107,7 +114,7 @@ __device__ __forceinline__ void count8_batch(uint32_t *words, uint32_t *evlist, 
         uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)b, first) + pre;
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            if (__ballot(bits[e] != 0u)) {
+            if (hm[e]) {  // a hit has at least the bit of its own byte
 #pragma unroll
                 for (uint32_t q = 0; q < 4; ++q) {
                     if ((bits[e] >> q) & 1u) {
