@@ -185,6 +185,23 @@ def test_counter8_carry_events(agg, path, bins, groups):
           aggregation=agg, **({"range_bins": 131_072} if path == "range" else {}))
 
 
+@pytest.mark.parametrize("wg", [256, 512])
+@pytest.mark.parametrize("path,bins,groups", [("full", 150_000, 3), ("full", 4099, 1),
+                                              ("range", 300_000, 2)])
+def test_counter8_carry_events_smaller_workgroups(wg, path, bins, groups):
+    # The flush gives each wave four pairs of blocks spaced by the wave count
+    # (4 or 8 here), so events in adjacent pairs go to different waves; hot
+    # bins in adjacent blocks (0-7, 256-263, 512-515) and a run of 3,000 bins
+    # with a few hundred copies each put events in many adjacent pairs.
+    rng = np.random.default_rng(wg)
+    hot = np.array([0, 1, 2, 3, 4, 5, 6, 7, 256, 263, 512, 515, bins - 1], np.int32)
+    run = np.repeat(np.arange(1000, 4000, dtype=np.int32) % bins, 300)
+    x = np.concatenate([np.repeat(hot, 20_000), run, rnd(10, 200_000, 0, bins)])
+    x = x[rng.permutation(x.size)].astype(np.int32)
+    check(x, bins, f"cw8-wg{wg}-{path}-g{groups}", path=path, counter_bits=8, groups=groups,
+          wg_size=wg, **({"range_bins": 150_016} if path == "range" else {}))
+
+
 @pytest.mark.parametrize("case,bins", [("one-bin-at-the-limit", 155_392),
                                        ("one-bin-at-the-limit", 100_000),
                                        ("one-bin-past-the-limit", 155_392),
