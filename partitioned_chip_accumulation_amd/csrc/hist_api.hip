@@ -33,8 +33,8 @@ constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elemen
 constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slots per tile
 // AUTO uses RANGE up to this many 16-bit ranges' worth of bins (318,464) and
 // SCATTER beyond: on 2^26 uniform elements SCATTER wins from 2^19 bins on
-// (141 us against 220 with 16-bit and 115 with 8-bit counters, the latter
-// at 1,563 us against 906 on the half-Gaussian 512K-bin workload).
+// (141 us against 220 with 16-bit and 111 with 8-bit counters, the latter
+// at 1,528 us against 912 on the half-Gaussian 512K-bin workload).
 constexpr uint32_t kRangeMaxR = 4;
 constexpr uint32_t kMinElemsPerGroup = 4096;
 constexpr int kMaxWavesPerCU = 32;
@@ -196,10 +196,10 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // bins per workgroup, which saves input passes: 2^17 bins in one
             // pass (53.0 us against 65.1 for two 16-bit ranges), 2^18 in two
             // (64.7 against 118.2 for four), and they stay ahead on Zipf s = 1.1
-            // input there (97.4 vs 105.8, 160.9 vs 166.5 us). Up to 2^16 bins
-            // they gain at most 1.4% on uniform input and lose 1.7x on Zipf
-            // input, whose hot bytes wrap every 256 counts (2^14 bins: 92.8 vs
-            // 55.9 us).
+            // input there (94.3 vs 106.0, 159.8 vs 166.4 us). Up to 2^16 bins
+            // they gain at most 1.4% on uniform input and lose 1.6-1.7x on Zipf
+            // input, whose hot bytes wrap every 256 counts (2^14 bins: 91.4 vs
+            // 56.3 us).
             if (path == HIST_PATH_FULL)
                 cw = num_bins > lds_bins16 ? 8 : num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
             else if (opts.range_bins > 0)
