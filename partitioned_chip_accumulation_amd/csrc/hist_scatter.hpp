@@ -347,12 +347,25 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
         uint32_t S = 1;
         while (S < NW && ngroups < 2u * (NW / S)) S *= 2u;
         const uint32_t team = w / S, member = w % S;
-        for (uint32_t g0 = ta + team * RPW; g0 < tb; g0 += (NW / S) * RPW) {
+        // The next group's run table is requested before this group's vectors,
+        // so both are in flight together and a group costs one memory round trip.
+        const uint32_t gstride = (NW / S) * RPW;
+        uint32_t nc = 0, nq = 0, nb = 0;
+        auto load_runs = [&](uint32_t g) {
+            const uint32_t t = g + lane;
+            if (lane < RPW && t < tb) {
+                nc = rc[t];
+                nq = rpre[t];
+                nb = rbase[t];
+            }
+        };
+        load_runs(ta + team * RPW);
+        for (uint32_t g0 = ta + team * RPW; g0 < tb; g0 += gstride) {
             // lane m < RPW: the run of tile g0 + m, clipped to [p0, p1)
             uint32_t vlo = 0, nv = 0, skip = 0, used = 0;
             const uint32_t t = g0 + lane;
             if (lane < RPW && t < tb) {
-                const uint32_t c = rc[t], q = rpre[t], bse = rbase[t];
+                const uint32_t c = nc, q = nq, bse = nb;
                 const uint32_t lo_e = max(p0, q) - q;
                 const uint32_t hi_e = min(p1, q + c) - q;
                 if (c != 0u && hi_e > lo_e) {
@@ -364,6 +377,7 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                     used = hi_e - lo_e;
                 }
             }
+            load_runs(g0 + gstride);
             // Run m of the group takes slot m of every lane's batch of RPW vector
             // loads, so all run parameters stay wave-uniform (scalar registers).
             uint32_t run_n[RPW], run_v[RPW], run_s[RPW], run_u[RPW], steps = 0;
