@@ -472,8 +472,16 @@ def main():
             reps += 1
             if time.perf_counter() - t_start >= args.cpu_seconds or reps >= 10000:
                 break
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(n * reps / spent / 1e9, 4), "unit": "Gelem/s", "cores": 1,
                "kind": "oracle",
+               "host": {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)),
+                        "cpu_count": os.cpu_count()},
                "sample": f"{reps} full passes of the timed input ({n} elements each), "
                          f"{spent:.1f} s, sequential loop on one host core "
                          f"(host has {len(os.sched_getaffinity(0))} usable cores)"}
