@@ -459,6 +459,11 @@ def main():
                 "lds_counters": counters_for(traffic_key).get("lds_counters"),
                 "algorithmic_bytes": dom_bytes,
                 "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches": dom_launches}
+    if 4 * n * len(xs) <= 256 * 2**20:
+        # all input copies fit the 256 MB Infinity Cache: the steps are served
+        # from it, and kernel launches dominate
+        roofline["note"] = ("input copies fit the 256 MB Infinity Cache; launch- and "
+                            "cache-bound, so the HBM fraction is not meaningful")
 
     cpu = None
     if args.cpu_seconds > 0:
