@@ -244,7 +244,9 @@ _cache: dict = {}
 def run(input: torch.Tensor, num_bins: int, out: torch.Tensor | None = None,
         accumulate: bool = False, **opts) -> torch.Tensor:
     """One-call histogram with a cached plan (max_n rounded up to a power of
-    two). accumulate=True adds into ``out``."""
+    two). accumulate=True adds into ``out``. Calls with the same device, bin
+    count, size class and options share one plan and its workspace, so they
+    must not overlap on different streams (use a Plan per stream for that)."""
     n = max(1, input.numel())
     max_n = 1 << (n - 1).bit_length()
     max_n = min(max_n, 2**32 - 1)
