@@ -248,6 +248,23 @@ def test_auto_plan_follows_the_measured_thresholds(num_bins, want):
         assert info.groups * info.ranges <= info.cu_count * 2
 
 
+@pytest.mark.parametrize("num_bins,opts", [(155_392, {}), (262_144, {}), (65_536, {}),
+                                           (100_000, {"counter_bits": 8, "path": "full"})])
+def test_plan_at_the_largest_n(num_bins, opts):
+    """At n = 2^32 - 1 the carry-event bound sets the chunk count: whole rounds
+    of resident workgroups, each chunk within the per-chunk limit, and a
+    workspace that holds every chunk's partial row."""
+    n = 2**32 - 1
+    info = hist.Plan(num_bins, 1 << 20, device=DEV, **opts).info()  # small: rounds for n
+    big = hist.Plan(num_bins, n, device=DEV, **opts).info()
+    assert big.path == info.path and big.counter_bits == info.counter_bits
+    assert big.groups * big.max_group_elems >= n
+    if big.groups > info.groups:  # rounded up to whole rounds of the resident chunks
+        resident = info.cu_count // big.ranges
+        assert big.groups % (resident // info.xcd_count * info.xcd_count) == 0
+    assert big.workspace_bytes >= big.groups * ((num_bins + 255) // 256) * 128
+
+
 def test_groups_and_wg_sizes():
     x = inputs.generate(2, n=(1 << 21) + 7)
     for opts in [{"groups": 1}, {"groups": 3}, {"groups": 8}, {"groups": 256},
