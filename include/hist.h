@@ -164,6 +164,25 @@ hist_status_t hist_run_accumulate(hist_plan_t *plan, uint32_t *counts, const int
 /* Fill *info. */
 hist_status_t hist_plan_info(const hist_plan_t *plan, hist_plan_info_t *info);
 
+/* A device described by its numbers, for hist_plan_preview. */
+typedef struct {
+    int32_t cu_count;              /* compute units (MI355X: 256) */
+    int32_t xcd_count;             /* L2 domains; cu_count is a multiple of it (MI355X: 8) */
+    uint32_t lds_bytes;            /* LDS one workgroup may use, 65,536 .. 163,840 (MI355X:
+                                      163,840) */
+    uint32_t sweep_waves_per_simd; /* sweep waves one SIMD holds at once as far as registers
+                                      allow (this library on gfx950: 6); 0 = no limit */
+} hist_device_desc_t;
+
+/* The plan hist_plan_create would make for (num_bins, max_n, opts) on the
+ * described device, computed on the host with no device present: the same
+ * path, counter width, ranges, chunks and workspace bytes, for capacity
+ * planning and for tests of the planning rules. info->device is -1.
+ * Errors: as hist_workspace_size, and HIST_ERR_INVALID_ARG for a null
+ * argument or a device description outside the stated bounds. */
+hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins, uint64_t max_n,
+                                const hist_plan_opts_t *opts, hist_plan_info_t *info);
+
 /* Write a one-line description ("path=range R=2 S=32768 G=128 ...") into
  * buf (always NUL-terminated when len > 0). */
 hist_status_t hist_plan_describe(const hist_plan_t *plan, char *buf, uint64_t len);

@@ -70,6 +70,9 @@ struct DeviceInfo {
     int cu = 0;
     int xcd = 1;
     uint32_t lds = 0;  // bytes per workgroup
+    // sweep waves a SIMD holds at once as far as registers allow: 0 = ask the
+    // runtime for the kernel that will run, ~0u = no register limit
+    uint32_t sweep_waves_per_simd = 0;
 };
 
 hist_status_t query_device(DeviceInfo *d)
@@ -242,7 +245,11 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // Registers can bound residency below what LDS allows (a 1024-thread
             // sweep with more than 64 VGPRs fits once per CU): chunks beyond the
             // resident ones would run as a second round.
-            const uint32_t res = sweep_resident(cw, wg, p->agg, lds_bytes);
+            // (4 SIMDs per CU)
+            const uint32_t res = d.sweep_waves_per_simd == 0
+                                     ? sweep_resident(cw, wg, p->agg, lds_bytes)
+                                     : d.sweep_waves_per_simd == ~0u ? ~0u
+                                                                     : d.sweep_waves_per_simd * 4u / (wg / 64u);
             if (res > 0) occ = std::max<uint32_t>(1, std::min(occ, res));
             uint32_t G = (uint32_t)opts.groups, slots = 0;
             if (G == 0) {
@@ -654,6 +661,8 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     return HIST_OK;
 }
 
+void fill_info(const hist_plan *p, hist_plan_info_t *info);
+
 }  // namespace
 
 extern "C" {
@@ -729,6 +738,37 @@ hist_status_t hist_run_accumulate(hist_plan_t *p, uint32_t *counts, const int32_
 hist_status_t hist_plan_info(const hist_plan_t *p, hist_plan_info_t *info)
 {
     if (!p || !info) return HIST_ERR_INVALID_ARG;
+    fill_info(p, info);
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins, uint64_t max_n,
+                                const hist_plan_opts_t *opts, hist_plan_info_t *info)
+{
+    if (!dev || !info || num_bins == 0 || max_n > (uint64_t)UINT32_MAX) return HIST_ERR_INVALID_ARG;
+    if (dev->cu_count <= 0 || dev->xcd_count <= 0 || dev->cu_count % dev->xcd_count != 0 ||
+        dev->lds_bytes < 65536 || dev->lds_bytes > 163840)
+        return HIST_ERR_INVALID_ARG;
+    hist_status_t st = check_opts(opts);
+    if (st != HIST_OK) return st;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    hist_plan p;
+    p.dev.cu = dev->cu_count;
+    p.dev.xcd = dev->xcd_count;
+    p.dev.lds = dev->lds_bytes;
+    p.dev.sweep_waves_per_simd = dev->sweep_waves_per_simd == 0 ? ~0u : dev->sweep_waves_per_simd;
+    st = design(&p, num_bins, max_n, opts);
+    if (st != HIST_OK) return st;
+    fill_info(&p, info);
+    return HIST_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+void fill_info(const hist_plan *p, hist_plan_info_t *info)
+{
     std::memset(info, 0, sizeof(*info));
     info->path = p->path;
     info->device = p->dev.device;
@@ -746,8 +786,11 @@ hist_status_t hist_plan_info(const hist_plan_t *p, hist_plan_info_t *info)
     info->workspace_bytes = p->need;
     info->max_group_elems = p->path == HIST_PATH_SCATTER ? 0 : p->max_elems_wg;
     info->event_cap = p->path == HIST_PATH_SCATTER ? 0 : p->ev_cap;
-    return HIST_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 hist_status_t hist_plan_describe(const hist_plan_t *p, char *buf, uint64_t len)
 {

@@ -52,6 +52,17 @@ class PlanInfo(ctypes.Structure):
                 ("max_group_elems", ctypes.c_uint64), ("event_cap", ctypes.c_uint32)]
 
 
+class DeviceDesc(ctypes.Structure):
+    _fields_ = [("cu_count", ctypes.c_int32), ("xcd_count", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_uint32), ("sweep_waves_per_simd", ctypes.c_uint32)]
+
+
+def mi355x() -> DeviceDesc:
+    """MI355X (gfx950) as this library's kernels see it: 256 CUs in 8 XCDs,
+    160 KiB of LDS per workgroup, 6 sweep waves per SIMD by registers."""
+    return DeviceDesc(256, 8, 163840, 6)
+
+
 _lib = None
 
 
@@ -70,6 +81,7 @@ def load(path: str = LIBRARY):
         "hist_run": (i32, [vp, vp, vp, u64, u32, vp]),
         "hist_run_accumulate": (i32, [vp, vp, vp, u64, u32, vp]),
         "hist_plan_info": (i32, [vp, P(PlanInfo)]),
+        "hist_plan_preview": (i32, [P(DeviceDesc), u32, u64, P(PlanOpts), P(PlanInfo)]),
         "hist_plan_describe": (i32, [vp, ctypes.c_char_p, u64]),
         "hist_plan_timing_enable": (i32, [vp, u32]),
         "hist_plan_timing_read": (i32, [vp, P(ctypes.c_double), P(u32)]),
@@ -148,6 +160,22 @@ class Info:
     event_cap: int
 
 
+def _info(i: PlanInfo) -> "Info":
+    return Info(PATH_NAMES[i.path], i.device, i.cu_count, i.xcd_count, i.num_bins,
+                i.range_bins, i.ranges, i.groups, i.wg_size, i.aggregation, i.tile_elems,
+                i.counter_bits, i.max_n, i.workspace_bytes, i.max_group_elems, i.event_cap)
+
+
+def preview(num_bins: int, max_n: int, device: DeviceDesc | None = None, **opts) -> "Info":
+    """The plan the library would make on the described device (default: an
+    MI355X), computed on the host; needs no GPU."""
+    i = PlanInfo()
+    _check(library().hist_plan_preview(ctypes.byref(device or mi355x()), int(num_bins),
+                                       int(max_n), ctypes.byref(_opts(**opts)), ctypes.byref(i)),
+           "hist_plan_preview")
+    return _info(i)
+
+
 class Plan:
     """A histogram plan for ``num_bins`` bins and inputs of up to ``max_n``
     elements on one device; owns its device workspace (a torch tensor)."""
@@ -205,10 +233,7 @@ class Plan:
     def info(self) -> Info:
         i = PlanInfo()
         _check(library().hist_plan_info(self._plan, ctypes.byref(i)), "hist_plan_info")
-        return Info(PATH_NAMES[i.path], i.device, i.cu_count, i.xcd_count, i.num_bins,
-                    i.range_bins, i.ranges, i.groups, i.wg_size, i.aggregation, i.tile_elems,
-                    i.counter_bits, i.max_n, i.workspace_bytes, i.max_group_elems,
-                    i.event_cap)
+        return _info(i)
 
     def describe(self) -> str:
         buf = ctypes.create_string_buffer(512)

@@ -48,6 +48,16 @@ int main(void)
            HIST_ERR_INVALID_ARG);
     expect("plan_info(NULL)", hist_plan_info(NULL, &info), HIST_ERR_INVALID_ARG);
     expect("plan_describe(NULL)", hist_plan_describe(NULL, buf, sizeof(buf)), HIST_ERR_INVALID_ARG);
+    {
+        /* planning needs no device: an MI355X as the kernels see it */
+        hist_device_desc_t dev = {256, 8, 163840, 6};
+        expect("plan_preview(NULL dev)", hist_plan_preview(NULL, 8, 8, NULL, &info),
+               HIST_ERR_INVALID_ARG);
+        expect("plan_preview(65536 bins)", hist_plan_preview(&dev, 65536, 1u << 26, NULL, &info),
+               HIST_OK);
+        expect("plan_preview path", info.path, HIST_PATH_FULL);
+        expect("plan_preview groups", (int)info.groups, 256);
+    }
     expect("timing_enable(NULL)", hist_plan_timing_enable(NULL, 1), HIST_ERR_INVALID_ARG);
     expect("timing_read(NULL)", hist_plan_timing_read(NULL, ms, launches), HIST_ERR_INVALID_ARG);
     expect("phase_name(0)", strcmp(hist_plan_phase_name(NULL, 0), "sweep"), 0);
@@ -60,8 +70,9 @@ int main(void)
     expect("status_str(OK)", strcmp(hist_status_str(HIST_OK), "ok"), 0);
     hist_plan_destroy(NULL);
     /* struct layouts, for the Python binding's ctypes mirrors */
-    printf("layout %zu %zu %zu %zu\n", sizeof(hist_plan_info_t), sizeof(hist_plan_opts_t),
-           offsetof(hist_plan_info_t, max_group_elems), offsetof(hist_plan_info_t, event_cap));
+    printf("layout %zu %zu %zu %zu %zu\n", sizeof(hist_plan_info_t), sizeof(hist_plan_opts_t),
+           offsetof(hist_plan_info_t, max_group_elems), offsetof(hist_plan_info_t, event_cap),
+           sizeof(hist_device_desc_t));
     if (failures == 0) printf("ok\n");
     return failures == 0 ? 0 : 1;
 }

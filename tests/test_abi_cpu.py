@@ -29,7 +29,8 @@ def declared_functions():
 def test_headers_declare_the_expected_calls():
     names = declared_functions()
     for must in ["hist_plan_create", "hist_run", "hist_workspace_size", "hist_plan_destroy",
-                 "hist_status_str", "hist_bench_global_atomic"]:
+                 "hist_status_str", "hist_bench_global_atomic", "hist_plan_preview",
+                 "hist_run_accumulate"]:
         assert must in names
 
 
@@ -118,6 +119,7 @@ def test_plain_c_client_compiles_links_and_gets_documented_errors(tmp_path):
     lines = out.stdout.split()
     assert out.returncode == 0 and lines[-1] == "ok", out.stdout + out.stderr
     # the ctypes mirrors of the public structs match the C layout
-    layout = [int(v) for v in lines[1:5]]
+    layout = [int(v) for v in lines[lines.index("layout") + 1:lines.index("layout") + 6]]
     assert layout == [ctypes.sizeof(hist.PlanInfo), ctypes.sizeof(hist.PlanOpts),
-                      hist.PlanInfo.max_group_elems.offset, hist.PlanInfo.event_cap.offset]
+                      hist.PlanInfo.max_group_elems.offset, hist.PlanInfo.event_cap.offset,
+                      ctypes.sizeof(hist.DeviceDesc)]

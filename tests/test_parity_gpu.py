@@ -248,6 +248,20 @@ def test_auto_plan_follows_the_measured_thresholds(num_bins, want):
         assert info.groups * info.ranges <= info.cu_count * 2
 
 
+@pytest.mark.parametrize("num_bins,max_n", [(1024, 1 << 26), (8192, 1 << 20), (65536, 1 << 26),
+                                            (100_000, 1 << 26), (262_144, 1 << 28),
+                                            (1 << 20, 1 << 28), (524_288, 1 << 29),
+                                            (262_144, 2**32 - 1)])
+def test_preview_matches_the_device_plan(num_bins, max_n):
+    """hist_plan_preview with the MI355X description gives the plan that
+    hist_plan_create makes on the device (the runtime's occupancy for the
+    1024-thread sweeps is one workgroup per CU, as 6 waves per SIMD say)."""
+    dev = hist.Plan(num_bins, max_n, device=DEV).info()
+    pre = hist.preview(num_bins, max_n)
+    assert dev.cu_count == 256 and dev.xcd_count == 8
+    assert {**pre.__dict__, "device": dev.device} == dev.__dict__
+
+
 @pytest.mark.parametrize("num_bins,opts", [(155_392, {}), (262_144, {}), (65_536, {}),
                                            (100_000, {"counter_bits": 8, "path": "full"})])
 def test_plan_at_the_largest_n(num_bins, opts):
