@@ -78,3 +78,15 @@ def test_trace_table(tmp_path):
         f.write('"void pca::k_merge<4>(x)",5000,9000\n')
     table = profiling.trace_table(str(d))
     assert "| `pca::k_merge<4>` | 2 | 3.00 | 3.00 | 2.00 | 0.006 |" in table
+
+
+def test_sweep_title_names_the_input(tmp_path):
+    f = tmp_path / "z.jsonl"
+    recs = [dict(cell("bins", 1 << 14, "full16", 2.0), input="zipf s=1.1"),
+            dict(cell("bins", 1 << 14, "auto", 2.1), input="zipf s=1.1")]
+    write_lines(f, recs)
+    md = profiling.sweep_markdown(str(f), "cmd")
+    assert "finite Zipf (zipf s=1.1" in md.splitlines()[0]
+    g = tmp_path / "u.jsonl"
+    write_lines(g, [cell("bins", 1 << 14, "full16", 2.0)])  # records without the field
+    assert "uniform int32 input" in profiling.sweep_markdown(str(g), "cmd").splitlines()[0]
