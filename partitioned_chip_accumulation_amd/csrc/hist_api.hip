@@ -452,7 +452,8 @@ hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, h
     const uint32_t bytes = (2 * npad + 64) * 4 + kScatterCap * 2;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
-    // persistent: two workgroups per CU (32 waves), each walking tiles
+    // persistent: a grid of two workgroups per CU, each walking tiles (at its
+    // register count one 1024-thread workgroup is resident per CU at a time)
     const uint32_t grid = std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu);
     hipLaunchKernelGGL(k, dim3(grid), dim3(kScatterWG), bytes, s, in, p->num_bins, kScatterShift,
                        p->ranges, p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage),
