@@ -124,7 +124,7 @@ struct hist_plan {
     char *ws = nullptr;
     uint64_t ws_bytes = 0, need = 0;
     uint64_t off_partials = 0, off_stage = 0, off_tcnt = 0, off_tbase = 0, off_tpre = 0,
-             off_totals = 0, off_segtot = 0;
+             off_totals = 0, off_segtot = 0, off_starts = 0;
     // timing
     uint32_t tcap = 0, truns = 0;
     std::vector<hipEvent_t> ev;  // [tcap][HIST_MAX_PHASES][2]
@@ -336,6 +336,8 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         off += align_up((uint64_t)R * 4, 256);
         p->off_segtot = off;
         off += align_up((uint64_t)R * ceil_div(T, pca::kScanSeg) * 4, 256);
+        p->off_starts = off;  // uint64 start of every range in the concatenation, and the total
+        off += align_up((uint64_t)(R + 1) * 8, 256);
         p->part_rows = W + R;
         p->off_partials = off;
         off += partial_bytes(p->part_rows, p->nblk);
@@ -486,7 +488,8 @@ hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T,
-                       p->range_bins, p->num_bins, p->owners, plan_partials(p));
+                       p->range_bins, p->num_bins, p->owners, plan_partials(p),
+                       reinterpret_cast<uint64_t *>(p->ws + p->off_starts));
     return hipGetLastError();
 }
 
@@ -548,13 +551,18 @@ hipError_t launch_merge_slots(const hist_plan *p, uint32_t num_bins, uint32_t *c
                               hipStream_t s)
 {
     const pca::Partials P = plan_partials(p);
-    const uint32_t *tot = reinterpret_cast<const uint32_t *>(p->ws + p->off_totals);
-    if (p->ranges >= 16)
-        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC>), dim3(ceil_div(num_bins, 256)), dim3(64), 0,
-                           s, P, tot, p->ranges, p->range_bins, num_bins, p->owners, counts);
+    const uint64_t *starts = reinterpret_cast<const uint64_t *>(p->ws + p->off_starts);
+    if (p->ranges >= p->owners)
+        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1>), dim3(ceil_div(num_bins, 256)), dim3(64), 0,
+                           s, P, starts, p->ranges, p->range_bins, num_bins, p->owners, counts);
+    else if (p->ranges >= 16)
+        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, pca::kMergeRounds>), dim3(ceil_div(num_bins, 256)),
+                           dim3(64), 0, s, P, starts, p->ranges, p->range_bins, num_bins, p->owners,
+                           counts);
     else
-        hipLaunchKernelGGL((pca::k_merge_slots<4, ACC>), dim3(ceil_div(num_bins, 256)), dim3(256), 0,
-                           s, P, tot, p->ranges, p->range_bins, num_bins, p->owners, counts);
+        hipLaunchKernelGGL((pca::k_merge_slots<4, ACC, pca::kMergeRounds>), dim3(ceil_div(num_bins, 256)),
+                           dim3(256), 0, s, P, starts, p->ranges, p->range_bins, num_bins, p->owners,
+                           counts);
     return hipGetLastError();
 }
 

@@ -385,7 +385,7 @@ __device__ __forceinline__ void store_counts(uint32_t *__restrict__ counts, uint
 // (merge_block does the reading and summing, k_merge_slots uses it too). Lane
 // l of wave w reads 16 bytes of a plane per row: the 32 bins of chunk
 // c = l / 8 of the block, from row slot i = l mod 8 of the wave's 8 rows of
-// a round (8 * WAVES rows per round). A batch is kMergeRounds rounds, and
+// a round (8 * WAVES rows per round). A batch is kMergeRounds rounds (or fewer), and
 // all of its loads of one plane are issued before any is used. A lane sums
 // its rows' nibbles bytewise, then widens them into 32 counters. Plane 0
 // exists for every row; planes 1..7 are fetched only when the batch's width
@@ -395,13 +395,15 @@ constexpr uint32_t kMergeRounds = 8;
 
 // acc[j] += sum over t of nibble j of v[t] (32 nibbles as 4 words), shifted
 // to plane q's weight 16^q. The nibbles are first summed bytewise, even and
-// odd nibbles apart; kMergeRounds * 15 < 256 keeps each byte exact.
-__device__ __forceinline__ void add_nibbles_bytewise(uint32_t (&acc)[32],
-                                                     const u32x4 (&v)[kMergeRounds], uint32_t q)
+// odd nibbles apart; ROUNDS * 15 < 256 keeps each byte exact.
+template <uint32_t ROUNDS>
+__device__ __forceinline__ void add_nibbles_bytewise(uint32_t (&acc)[32], const u32x4 (&v)[ROUNDS],
+                                                     uint32_t q)
 {
+    static_assert(ROUNDS * 15u < 256u, "bytewise nibble sums must not carry");
     u32x4 se = {0u, 0u, 0u, 0u}, so = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (uint32_t t = 0; t < kMergeRounds; ++t) {
+    for (uint32_t t = 0; t < ROUNDS; ++t) {
         se += v[t] & 0x0F0F0F0Fu;
         so += (v[t] >> 4) & 0x0F0F0F0Fu;
     }
@@ -420,8 +422,10 @@ __device__ __forceinline__ void add_nibbles_bytewise(uint32_t (&acc)[32],
 // Sum over rows row0 .. row0 + rows - 1 of block blk of the partial rows
 // (rows whose row_ok(k) is false, k the row's index from row0, are skipped).
 // Whole workgroup of WAVES waves, convergent; the sums are valid in wave 0,
-// lane l holding bins 4l..4l+3 of the block.
-template <int WAVES, typename RowOk>
+// lane l holding bins 4l..4l+3 of the block. A batch is ROUNDS rounds: fewer
+// rounds hold fewer loads in flight per wave but need fewer registers, so
+// more waves fit when there are few rows to sum.
+template <int WAVES, uint32_t ROUNDS = kMergeRounds, typename RowOk>
 __device__ __forceinline__ u32x4 merge_block(const Partials &P, uint64_t row0, uint32_t rows,
                                              uint64_t blk, RowOk row_ok)
 {
@@ -432,39 +436,40 @@ __device__ __forceinline__ u32x4 merge_block(const Partials &P, uint64_t row0, u
     uint32_t acc[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = 0u;
-    for (uint32_t base = 0; base < rows; base += kMergeRounds * RPR) {
+    for (uint32_t base = 0; base < rows; base += ROUNDS * RPR) {
         // lane l: the width code of round l / 8, slot l mod 8
         const uint32_t crow = base + (lane >> 3) * RPR + w * 8 + i;
-        const uint32_t code =
-            crow < rows && row_ok(crow) ? P.width[(row0 + crow) * P.nblk + blk] : 0u;
-        u32x4 v[kMergeRounds];
+        const uint32_t code = (lane >> 3) < ROUNDS && crow < rows && row_ok(crow)
+                                  ? P.width[(row0 + crow) * P.nblk + blk]
+                                  : 0u;
+        u32x4 v[ROUNDS];
 #pragma unroll
-        for (uint32_t t = 0; t < kMergeRounds; ++t) {
+        for (uint32_t t = 0; t < ROUNDS; ++t) {
             const uint32_t k = base + t * RPR + w * 8 + i;
             v[t] = k < rows && row_ok(k)
                        ? *reinterpret_cast<const u32x4 *>(
                              P.plane0 + ((row0 + k) * P.nblk + blk) * kPlaneBytes + 16u * c)
                        : u32x4{0u, 0u, 0u, 0u};
         }
-        add_nibbles_bytewise(acc, v, 0);
+        add_nibbles_bytewise<ROUNDS>(acc, v, 0);
         // Planes beyond 0: each lane fetches them for its own rows of the batch,
         // all rows of one plane at once (plane q of a row exists iff q < planes).
         if (__ballot(code != 0u)) {
             const uint32_t maxp = __ballot(code == 7u) ? 8u : __ballot(code == 3u) ? 4u : 2u;
-            uint32_t pl[kMergeRounds];
+            uint32_t pl[ROUNDS];
 #pragma unroll
-            for (uint32_t t = 0; t < kMergeRounds; ++t)
+            for (uint32_t t = 0; t < ROUNDS; ++t)
                 pl[t] = (uint32_t)__shfl((int)code, (int)(8 * t + i), 64) + 1u;
             for (uint32_t q = 1; q < maxp; ++q) {
 #pragma unroll
-                for (uint32_t t = 0; t < kMergeRounds; ++t) {
+                for (uint32_t t = 0; t < ROUNDS; ++t) {
                     const uint64_t row = row0 + base + t * RPR + w * 8 + i;
                     v[t] = q < pl[t] ? *reinterpret_cast<const u32x4 *>(
                                            P.upper + ((row * P.nblk + blk) * kUpperPlanes + q - 1) *
                                                          kPlaneBytes + 16u * c)
                                      : u32x4{0u, 0u, 0u, 0u};
                 }
-                add_nibbles_bytewise(acc, v, q);
+                add_nibbles_bytewise<ROUNDS>(acc, v, q);
             }
         }
     }
