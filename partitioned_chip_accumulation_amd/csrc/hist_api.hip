@@ -555,8 +555,9 @@ hipError_t launch_merge_slots(const hist_plan *p, uint32_t num_bins, uint32_t *c
     // With many ranges a range has few owner rows, and one round per batch (78
     // VGPRs, 6 waves per SIMD) beats eight (154 VGPRs, 3 waves): 2^22 uniform
     // bins 31.0 -> 20.3 us. A range holding a hot bin has many rows, which one
-    // round per batch walks slowly: at 32 ranges (workload 4, 256 owners) it
-    // took 24.0 us against 13.9, hence the switch at ranges * 4 >= owners.
+    // round per batch walks slowly: on the 2^20-bin hot-bin input (32 ranges,
+    // 256 owners) it took 24.0 us against 13.9, hence the switch at
+    // ranges * 4 >= owners.
     if (p->ranges * 4u >= p->owners)
         hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1>), dim3(ceil_div(num_bins, 256)), dim3(64), 0,
                            s, P, starts, p->ranges, p->range_bins, num_bins, p->owners, counts);

@@ -111,7 +111,7 @@ def uniform(seed: int, n: int, num_bins: int, lo: int = 0, out: np.ndarray | Non
 
 def zipf(seed: int, n: int, num_bins: int, s: float) -> np.ndarray:
     """int32 finite Zipf values: rank k in 1..num_bins with P(k) ~ k^-s, the
-    ranks permuted to bins (the recipe of workload 3, any size and exponent)."""
+    ranks permuted to bins (the recipe of the 262,144-bin Zipf workload, any size and exponent)."""
     out = np.empty(n, dtype=np.int32)
     rc = _library().gen_zipf(seed, out.ctypes.data if n else None, n, num_bins, float(s))
     if rc != 0:

@@ -99,7 +99,7 @@ def test_golden_hashes():
 
 
 def test_zipf_any_size_matches_the_workload_recipe():
-    # inputs.zipf is workload 3's generator with its size and exponent free
+    # inputs.zipf is the 262,144-bin Zipf workload's generator with its size and exponent free
     n = 200_003
     assert np.array_equal(inputs.zipf(2, n, 262_144, 1.1), inputs.generate(3, n=n))
     x = inputs.zipf(7, 100_000, 1000, 1.5)
