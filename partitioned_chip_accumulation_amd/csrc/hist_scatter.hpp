@@ -243,6 +243,9 @@ __device__ __forceinline__ uint32_t wave_find_last_le(const uint32_t *__restrict
 // 2^26 uniform elements: runs of 128 take 87.6 us one per lane against 103.8
 // striped, runs of 256 take 89.0 against 67.5.
 constexpr uint32_t kSparseRun = 192;
+// In that mode a run of more than this many staged vectors is counted by its
+// whole wave rather than by one lane.
+constexpr uint32_t kLaneRunVecs = 64;
 
 // Count the slots of one staged vector (8 uint16 slots as 4 words) whose
 // index e lies in [first, last), through the wave's hot slot when AGG == 1.
@@ -378,6 +381,12 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                     }
                 }
                 load_run(t0 + WG + lane);
+                // A run far longer than the average (part of the input sorted,
+                // say) would keep one lane busy while the rest of the workgroup
+                // waits: the wave takes such runs together after its own runs.
+                const uint32_t nv_run = nv;
+                uint64_t longm = __ballot(nv > kLaneRunVecs);
+                if (nv > kLaneRunVecs) nv = 0u;
                 for (uint32_t v = 0; v < nv; v += 2u) {
                     const bool two = v + 1u < nv;
                     const i32x4 qa = stage_vec[(uint64_t)vlo + v];
@@ -388,6 +397,23 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                         const uint32_t k8 = (v + k) * 8u;
                         const uint32_t first = k8 < skip ? skip - k8 : 0u;
                         const uint32_t last = (k == 0 || two) ? min(8u, skip + used - k8) : 0u;
+                        const uint32_t words[4] = {(uint32_t)q.x, (uint32_t)q.y, (uint32_t)q.z,
+                                                   (uint32_t)q.w};
+                        count_slots<0>(lds, hs, words, first, last);
+                    }
+                }
+                while (longm) {
+                    const int m = __builtin_ctzll(longm);
+                    longm &= longm - 1u;
+                    const uint32_t lv = (uint32_t)__builtin_amdgcn_readlane((int)vlo, m);
+                    const uint32_t ln = (uint32_t)__builtin_amdgcn_readlane((int)nv_run, m);
+                    const uint32_t ls = (uint32_t)__builtin_amdgcn_readlane((int)skip, m);
+                    const uint32_t lu = (uint32_t)__builtin_amdgcn_readlane((int)used, m);
+                    for (uint32_t d = lane; d < ln; d += 64u) {
+                        const i32x4 q = stage_vec[(uint64_t)lv + d];
+                        const uint32_t k8 = d * 8u;
+                        const uint32_t first = k8 < ls ? ls - k8 : 0u;
+                        const uint32_t last = min(8u, ls + lu - k8);
                         const uint32_t words[4] = {(uint32_t)q.x, (uint32_t)q.y, (uint32_t)q.z,
                                                    (uint32_t)q.w};
                         count_slots<0>(lds, hs, words, first, last);

@@ -565,7 +565,7 @@ def test_runs_on_a_side_stream():
 
 
 @pytest.mark.parametrize("case", ["one-range", "all-invalid", "sparse-ranges", "tiny-last-range",
-                                  "tile-edges", "short-runs", "mixed-runs"])
+                                  "tile-edges", "short-runs", "mixed-runs", "sorted-block"])
 def test_scatter_edge_cases(case):
     bins = 1 << 20
     if case == "short-runs":       # 512 ranges, about 32 elements per (tile, range): one run per lane
@@ -576,6 +576,9 @@ def test_scatter_edge_cases(case):
         x = np.concatenate([rnd(9, 2_000_000, 0, bins), rnd(10, 900_000, 100 * 32768, 101 * 32768),
                             np.full(50_000, bins - 1, np.int32)])
         x = x[np.random.default_rng(11).permutation(x.size)].astype(np.int32)
+    elif case == "sorted-block":   # short runs on average, but each range has one run of ~3,000
+        bins = 1 << 24
+        x = np.concatenate([np.sort(rnd(12, 1_500_000, 0, bins)), rnd(13, 1_500_007, -3, bins + 5)])
     elif case == "one-range":        # every element in range 5: all owners share one range
         x = rnd(1, 700_001, 5 * 32768, 6 * 32768)
     elif case == "all-invalid":    # nothing to count: every range empty
