@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline work (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--tune", action="store_true",
+                    help="time every schedule on the input first (hist_tune) and bench the fastest")
     ap.add_argument("--comparators", action="store_true",
                     help="also time the global-atomic fallback and the stream-read ceiling")
     ap.add_argument("--path-sweep", action="store_true",
@@ -375,10 +377,20 @@ def main():
         xs.append(xs[0].clone())
     out = torch.empty(B, dtype=torch.int32, device=dev)
 
-    plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
-                     range_bins=args.range_bins, aggregation=args.agg, wg_size=args.wg,
-                     xcd_map=args.xcd_map, counter_bits=args.counter_bits,
-                     lds_copies=args.lds_copies)
+    tuned = None
+    if args.tune:
+        # measured schedule choice on this input, before and outside the timed region
+        best, rows = hist.tune(xs[0], B, max_n=n, reps=3)
+        tuned = {"opts": best, "candidates_ms": {
+            f"{r['opts']['path']}{r['opts']['counter_bits'] or ''}"
+            f"{'+hot' if r['opts']['aggregation'] == 1 else ''}": round(r["ms"], 4)
+            for r in rows if r["status"] == hist.HIST_OK}}
+        plan = hist.Plan(B, n, device=dev, **best)
+    else:
+        plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
+                         range_bins=args.range_bins, aggregation=args.agg, wg_size=args.wg,
+                         xcd_map=args.xcd_map, counter_bits=args.counter_bits,
+                         lds_copies=args.lds_copies)
     info = plan.info()
     print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,
           flush=True)
@@ -530,7 +542,7 @@ def main():
         "parity_vs_bincount": parity,
         "config": {"workload": f"{w.name}: {w.recipe}; n={n}, {B} uint32 bins",
                    "n": n, "num_bins": B, "plan": plan.describe(),
-                   "input_copies": len(xs)},
+                   "input_copies": len(xs), **({"tuned": tuned} if tuned else {})},
         "phases_ms_per_step": {k: round(v[0] / v[1], 5) for k, v in phases.items()},
         "ms_per_step_with_events": round(elapsed_events / args.steps * 1e3, 5),
         "step_us_event_bracketed": step_us,

@@ -183,6 +183,57 @@ typedef struct {
 hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins, uint64_t max_n,
                                 const hist_plan_opts_t *opts, hist_plan_info_t *info);
 
+/* Measured schedule choice.
+ *
+ * AUTO picks a schedule from num_bins alone, from sweeps over uniform and
+ * Zipf inputs; the best schedule also depends on the data (a skewed input
+ * can favour the two-phase path with the hot slot where a uniform one
+ * favours bin-range ownership). hist_tune times the candidate schedules on
+ * the caller's own input and reports the fastest, following the cost-guided
+ * selection of "CREDIT: Cost-guided Reduction-reuse with Efficient DSMEM
+ * Inter-CTA Tiling" (its cost model section, Eq. 7: a rate measured at the
+ * same shape replaces a device peak). Its model predicts one schedule's
+ * time from another's; here every candidate is cheap to run, so each is
+ * measured directly.
+ *
+ * Candidates, in this order (those a bin count does not allow are skipped):
+ * FULL with 32-, 16- and 8-bit counters; RANGE with 32-, 16- (plain and hot
+ * slot) and 8-bit counters (plain and hot slot); SCATTER plain and with the
+ * hot slot. Every other option is left to the plan. */
+#define HIST_TUNE_MAX_ENTRIES 10
+
+typedef struct {
+    hist_plan_opts_t opts; /* the options naming the schedule (path, counter_bits,
+                              aggregation; the rest 0) */
+    double ms;             /* mean milliseconds per hist_run over reps runs; -1 if not run */
+    int32_t status;        /* HIST_OK if measured; HIST_ERR_UNSUPPORTED when the bin count
+                              does not allow it; HIST_ERR_WORKSPACE when its plan needs more
+                              workspace than was given */
+    int32_t reserved;
+} hist_tune_entry_t;
+
+/* Bytes of device workspace hist_tune needs to try every candidate for
+ * (num_bins, max_n): the largest hist_workspace_size among them. Errors as
+ * hist_workspace_size. */
+hist_status_t hist_tune_workspace_size(uint32_t num_bins, uint64_t max_n, uint64_t *bytes);
+
+/* Time every candidate schedule for (num_bins, max_n) on input[0..n): for
+ * each, a plan on workspace, one untimed hist_run, then reps hist_runs
+ * between two HIP events on stream. Writes the fastest candidate's options to
+ * *best (pass them to hist_plan_create with the same num_bins and max_n), and
+ * the candidates' entries, in the order above, to entries[0..*count) (at most
+ * capacity of them; entries may be NULL when capacity is 0). counts (device,
+ * num_bins uint32) receives each run's output; on success it holds the
+ * histogram of input. Synchronous: returns after the last run completes. The
+ * workspace's contents are overwritten. Errors: INVALID_ARG for a null input,
+ * counts or best, n == 0, n > max_n, reps outside 1..1000, or a null count
+ * with capacity > 0; UNSUPPORTED as hist_workspace_size; WORKSPACE when no
+ * candidate's plan fits the workspace; HIP when a run or an event fails. */
+hist_status_t hist_tune(uint32_t num_bins, uint64_t max_n, const int32_t *input, uint64_t n,
+                        uint32_t *counts, void *workspace, uint64_t workspace_bytes,
+                        uint32_t reps, hipStream_t stream, hist_plan_opts_t *best,
+                        hist_tune_entry_t *entries, uint32_t capacity, uint32_t *count);
+
 /* Write a one-line description ("path=range R=2 S=32768 G=128 ...") into
  * buf (always NUL-terminated when len > 0). */
 hist_status_t hist_plan_describe(const hist_plan_t *plan, char *buf, uint64_t len);

@@ -57,6 +57,14 @@ class DeviceDesc(ctypes.Structure):
                 ("lds_bytes", ctypes.c_uint32), ("sweep_waves_per_simd", ctypes.c_uint32)]
 
 
+class TuneEntry(ctypes.Structure):
+    _fields_ = [("opts", PlanOpts), ("ms", ctypes.c_double), ("status", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+TUNE_MAX_ENTRIES = 10
+
+
 def mi355x() -> DeviceDesc:
     """MI355X (gfx950) as this library's kernels see it: 256 CUs in 8 XCDs,
     160 KiB of LDS per workgroup, 6 sweep waves per SIMD by registers."""
@@ -83,6 +91,9 @@ def load(path: str = LIBRARY):
         "hist_plan_info": (i32, [vp, P(PlanInfo)]),
         "hist_plan_preview": (i32, [P(DeviceDesc), u32, u64, P(PlanOpts), P(PlanInfo)]),
         "hist_plan_describe": (i32, [vp, ctypes.c_char_p, u64]),
+        "hist_tune_workspace_size": (i32, [u32, u64, P(u64)]),
+        "hist_tune": (i32, [u32, u64, vp, u64, vp, vp, u64, u32, vp, P(PlanOpts), P(TuneEntry),
+                            u32, P(u32)]),
         "hist_plan_timing_enable": (i32, [vp, u32]),
         "hist_plan_timing_read": (i32, [vp, P(ctypes.c_double), P(u32)]),
         "hist_plan_phase_name": (ctypes.c_char_p, [vp, u32]),
@@ -261,6 +272,43 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def _opts_dict(o: PlanOpts) -> dict:
+    """The keyword options (as Plan takes them) that name a tuned schedule."""
+    return {"path": PATH_NAMES[o.path], "counter_bits": int(o.counter_bits),
+            "aggregation": int(o.aggregation)}
+
+
+def tune(input: torch.Tensor, num_bins: int, max_n: int | None = None, reps: int = 3,
+         workspace: torch.Tensor | None = None) -> tuple[dict, list[dict]]:
+    """Time every candidate schedule on ``input`` (hist_tune) and return the
+    fastest one's options, ready for ``Plan(num_bins, max_n, **opts)``, and
+    every candidate as {"opts", "ms", "status"} (ms is -1 and status names the
+    reason when a candidate was not run). Blocks until the runs are done."""
+    if input.dtype != torch.int32 or not input.is_cuda or not input.is_contiguous():
+        raise ValueError("input must be a contiguous int32 CUDA tensor")
+    n = input.numel()
+    max_n = n if max_n is None else int(max_n)
+    lib = library()
+    with torch.cuda.device(input.device):
+        if workspace is None:
+            need = ctypes.c_uint64(0)
+            _check(lib.hist_tune_workspace_size(int(num_bins), max_n, ctypes.byref(need)),
+                   "hist_tune_workspace_size")
+            workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8,
+                                    device=input.device)
+        counts = torch.empty(int(num_bins), dtype=torch.int32, device=input.device)
+        best = PlanOpts()
+        entries = (TuneEntry * TUNE_MAX_ENTRIES)()
+        count = ctypes.c_uint32(0)
+        _check(lib.hist_tune(int(num_bins), max_n, input.data_ptr() if n else None, n,
+                             counts.data_ptr(), workspace.data_ptr(), workspace.numel(), int(reps),
+                             torch.cuda.current_stream().cuda_stream, ctypes.byref(best),
+                             entries, TUNE_MAX_ENTRIES, ctypes.byref(count)), "hist_tune")
+    rows = [{"opts": _opts_dict(e.opts), "ms": float(e.ms), "status": int(e.status)}
+            for e in entries[:count.value]]
+    return _opts_dict(best), rows
 
 
 _cache: dict = {}

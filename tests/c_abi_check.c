@@ -58,6 +58,16 @@ int main(void)
         expect("plan_preview path", info.path, HIST_PATH_FULL);
         expect("plan_preview groups", (int)info.groups, 256);
     }
+    {
+        hist_plan_opts_t best;
+        hist_tune_entry_t entries[HIST_TUNE_MAX_ENTRIES];
+        uint32_t count = 0;
+        expect("tune_workspace_size(bytes=NULL)", hist_tune_workspace_size(10, 10, NULL),
+               HIST_ERR_INVALID_ARG);
+        expect("tune(input=NULL)", hist_tune(10, 10, NULL, 1, NULL, NULL, 0, 1, NULL, &best,
+                                             entries, HIST_TUNE_MAX_ENTRIES, &count),
+               HIST_ERR_INVALID_ARG);
+    }
     expect("timing_enable(NULL)", hist_plan_timing_enable(NULL, 1), HIST_ERR_INVALID_ARG);
     expect("timing_read(NULL)", hist_plan_timing_read(NULL, ms, launches), HIST_ERR_INVALID_ARG);
     expect("phase_name(0)", strcmp(hist_plan_phase_name(NULL, 0), "sweep"), 0);
@@ -70,9 +80,11 @@ int main(void)
     expect("status_str(OK)", strcmp(hist_status_str(HIST_OK), "ok"), 0);
     hist_plan_destroy(NULL);
     /* struct layouts, for the Python binding's ctypes mirrors */
-    printf("layout %zu %zu %zu %zu %zu\n", sizeof(hist_plan_info_t), sizeof(hist_plan_opts_t),
-           offsetof(hist_plan_info_t, max_group_elems), offsetof(hist_plan_info_t, event_cap),
-           sizeof(hist_device_desc_t));
+    printf("layout %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hist_plan_info_t),
+           sizeof(hist_plan_opts_t), offsetof(hist_plan_info_t, max_group_elems),
+           offsetof(hist_plan_info_t, event_cap), sizeof(hist_device_desc_t),
+           sizeof(hist_tune_entry_t), offsetof(hist_tune_entry_t, ms),
+           offsetof(hist_tune_entry_t, status));
     if (failures == 0) printf("ok\n");
     return failures == 0 ? 0 : 1;
 }

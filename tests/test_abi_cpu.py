@@ -30,7 +30,7 @@ def test_headers_declare_the_expected_calls():
     names = declared_functions()
     for must in ["hist_plan_create", "hist_run", "hist_workspace_size", "hist_plan_destroy",
                  "hist_status_str", "hist_bench_global_atomic", "hist_plan_preview",
-                 "hist_run_accumulate"]:
+                 "hist_run_accumulate", "hist_tune", "hist_tune_workspace_size"]:
         assert must in names
 
 
@@ -71,6 +71,23 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_run(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_run_accumulate(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_info(None, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_tune_workspace_size(10, 10, None) == hist.HIST_ERR_INVALID_ARG
+    best = hist.PlanOpts()
+    cnt = ctypes.c_uint32(0)
+    entries = (hist.TuneEntry * hist.TUNE_MAX_ENTRIES)()
+    for args in [(10, 10, None, 5, 8, None, 0, 1),      # no input
+                 (10, 10, 8, 5, None, None, 0, 1),      # no counts
+                 (10, 10, 8, 0, 8, None, 0, 1),         # n == 0
+                 (10, 10, 8, 11, 8, None, 0, 1),        # n > max_n
+                 (10, 10, 8, 5, 8, None, 0, 0),         # reps == 0
+                 (10, 10, 8, 5, 8, None, 0, 1001),      # reps > 1000
+                 (10, 10, 8, 5, 8, 4, 4096, 1)]:        # workspace not 256-byte aligned
+        assert lib.hist_tune(*args, None, ctypes.byref(best), entries, hist.TUNE_MAX_ENTRIES,
+                             ctypes.byref(cnt)) == hist.HIST_ERR_INVALID_ARG, args
+    assert lib.hist_tune(10, 10, 8, 5, 8, None, 0, 1, None, None, entries, 1,
+                         ctypes.byref(cnt)) == hist.HIST_ERR_INVALID_ARG  # no best
+    assert lib.hist_tune(10, 10, 8, 5, 8, None, 0, 1, None, ctypes.byref(best), None, 1,
+                         ctypes.byref(cnt)) == hist.HIST_ERR_INVALID_ARG  # no entries
     assert lib.hist_plan_timing_enable(None, 4) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_global_atomic(None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_copy(None, None, 16, None) == hist.HIST_ERR_INVALID_ARG
@@ -87,6 +104,8 @@ def test_no_device_is_unsupported_not_a_crash():
     n = ctypes.c_uint64(0)
     assert lib.hist_workspace_size(65536, 1 << 20, None,
                                    ctypes.byref(n)) == hist.HIST_ERR_UNSUPPORTED
+    assert lib.hist_tune_workspace_size(65536, 1 << 20,
+                                        ctypes.byref(n)) == hist.HIST_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -119,7 +138,8 @@ def test_plain_c_client_compiles_links_and_gets_documented_errors(tmp_path):
     lines = out.stdout.split()
     assert out.returncode == 0 and lines[-1] == "ok", out.stdout + out.stderr
     # the ctypes mirrors of the public structs match the C layout
-    layout = [int(v) for v in lines[lines.index("layout") + 1:lines.index("layout") + 6]]
+    layout = [int(v) for v in lines[lines.index("layout") + 1:lines.index("layout") + 9]]
     assert layout == [ctypes.sizeof(hist.PlanInfo), ctypes.sizeof(hist.PlanOpts),
                       hist.PlanInfo.max_group_elems.offset, hist.PlanInfo.event_cap.offset,
-                      ctypes.sizeof(hist.DeviceDesc)]
+                      ctypes.sizeof(hist.DeviceDesc), ctypes.sizeof(hist.TuneEntry),
+                      hist.TuneEntry.ms.offset, hist.TuneEntry.status.offset]

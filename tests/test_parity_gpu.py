@@ -670,3 +670,55 @@ def test_fuzz_sizes_paths_options(seed, large):
     torch.cuda.synchronize(DEV)
     assert np.array_equal(got, want), f"{plan.describe()}: {int(np.sum(got != want))} bins differ"
     plan.close()
+
+
+# --- measured schedule choice (hist_tune) ------------------------------------
+
+@pytest.mark.parametrize("num_bins,kind", [(8192, "uniform"), (262_144, "zipf"), (1 << 20, "zipf")])
+def test_tune_measures_every_allowed_schedule_and_picks_the_fastest(num_bins, kind):
+    n = 1 << 22
+    x = inputs.zipf(21, n, num_bins, 1.1) if kind == "zipf" else rnd(22, n, 0, num_bins)
+    say(f"case tune bins={num_bins} {kind}")
+    xt = torch.from_numpy(x).to(DEV)
+    best, rows = hist.tune(xt, num_bins, reps=2)
+    assert len(rows) == hist.TUNE_MAX_ENTRIES
+    for r in rows:
+        o = r["opts"]
+        if o["path"] == "full":  # allowed exactly when the counter width's slice holds all bins
+            cap = {32: 40960, 16: 79616, 8: 155_392}[o["counter_bits"]]
+            assert (r["status"] == hist.HIST_OK) == (num_bins <= cap), r
+        else:
+            assert r["status"] == hist.HIST_OK, r
+    measured = [r for r in rows if r["status"] == hist.HIST_OK]
+    assert all(r["ms"] > 0 for r in measured)
+    assert best == min(measured, key=lambda r: r["ms"])["opts"]
+    ref, _ = oracle.hist(x, num_bins)
+    plan = hist.Plan(num_bins, n, device=DEV, **best)
+    got = plan.run(xt).cpu().numpy()
+    torch.cuda.synchronize(DEV)
+    assert np.array_equal(got, ref), plan.describe()
+    plan.close()
+
+
+def test_tune_skips_schedules_the_workspace_cannot_hold():
+    num_bins, n = 262_144, 1 << 21
+    x = rnd(23, n, 0, num_bins)
+    xt = torch.from_numpy(x).to(DEV)
+    cands = [("range", 32, 0), ("range", 16, 0), ("range", 16, 1), ("range", 8, 0),
+             ("range", 8, 1), ("scatter", 0, 0), ("scatter", 0, 1)]
+    need = {c: hist.workspace_size(num_bins, n, path=c[0], counter_bits=c[1], aggregation=c[2])
+            for c in cands}
+    small = min(need.values())
+    ws = torch.empty(small, dtype=torch.uint8, device=DEV)
+    best, rows = hist.tune(xt, num_bins, reps=1, workspace=ws)
+    for r in rows:
+        o = r["opts"]
+        key = (o["path"], o["counter_bits"], o["aggregation"])
+        if key in need:
+            want = hist.HIST_OK if need[key] <= small else hist.HIST_ERR_WORKSPACE
+            assert r["status"] == want, r
+    assert need[(best["path"], best["counter_bits"], best["aggregation"])] <= small
+    tiny = torch.empty(256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(hist.HistError) as e:
+        hist.tune(xt, num_bins, reps=1, workspace=tiny)
+    assert e.value.status == hist.HIST_ERR_WORKSPACE
