@@ -7,6 +7,14 @@ before timing starts. Four device copies of the input are used in rotation,
 so that consecutive steps cannot serve a 256 MiB input from the 256 MB
 Infinity Cache that the previous step filled.
 
+The steps run on one stream. `two_streams` reports, from the same run, the
+same K steps alternating over two streams, each stream with its own plan,
+workspace and output: two independent histograms are then in flight, and
+one's merge and launch ramp overlap the other's sweep, as for a caller who
+histograms a series of batches with a plan per stream. (`--streams 2` makes
+that the timed mode; the roofline's per-launch durations then include the
+overlap.)
+
 Prints one JSON line (rank 0). Throughput `value` is Gelem/s over the K timed
 steps (wall clock between two device synchronisations, no instrumentation in
 between). `roofline` is for the dominant kernel, timed live with HIP events
@@ -60,6 +68,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline work (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="histograms in flight: consecutive steps alternate over this many "
+                         "streams, each with its own plan, workspace and output")
+    ap.add_argument("--no-two-streams", action="store_true",
+                    help="skip the two-stream region (profiling runs, so that every launch of a "
+                         "kernel is timed alike)")
     ap.add_argument("--tune", action="store_true",
                     help="time every schedule on the input first (hist_tune) and bench the fastest")
     ap.add_argument("--comparators", action="store_true",
@@ -385,12 +399,21 @@ def main():
             f"{r['opts']['path']}{r['opts']['counter_bits'] or ''}"
             f"{'+hot' if r['opts']['aggregation'] == 1 else ''}": round(r["ms"], 4)
             for r in rows if r["status"] == hist.HIST_OK}}
-        plan = hist.Plan(B, n, device=dev, **best)
+        plan_opts = best
     else:
-        plan = hist.Plan(B, n, device=dev, path=args.path, groups=args.groups,
-                         range_bins=args.range_bins, aggregation=args.agg, wg_size=args.wg,
-                         xcd_map=args.xcd_map, counter_bits=args.counter_bits,
-                         lds_copies=args.lds_copies)
+        plan_opts = dict(path=args.path, groups=args.groups, range_bins=args.range_bins,
+                         aggregation=args.agg, wg_size=args.wg, xcd_map=args.xcd_map,
+                         counter_bits=args.counter_bits, lds_copies=args.lds_copies)
+    # One plan (and workspace) and one output per stream: the steps on different
+    # streams are independent histograms, so they may overlap on the device.
+    nstreams = max(1, args.streams)
+    two = nstreams != 2 and not args.no_two_streams
+    nplans = max(2 if two else 1, nstreams)  # the two-stream figure needs a second plan
+    plans = [hist.Plan(B, n, device=dev, **plan_opts) for _ in range(nplans)]
+    plan = plans[0]
+    streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev)
+                                                 for _ in range(nplans - 1)]
+    outs = [out] + [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(nplans - 1)]
     info = plan.info()
     print(f"# plan: {plan.describe()}  (input generated in {t_gen:.1f} s)", file=sys.stderr,
           flush=True)
@@ -404,26 +427,45 @@ def main():
         torch.cuda.synchronize(dev)
         del a, bcopy
 
-    def timed(events: bool):
-        plan.timing_enable(args.steps + args.warmup if events else 0)
+    def step(k: int, ns: int):
+        j = k % ns
+        with torch.cuda.stream(streams[j]):
+            plans[j].run(xs[k % len(xs)], outs[j])
+
+    def timed(events: bool, ns: int):
+        for p in plans[:ns]:
+            p.timing_enable((args.steps + args.warmup) if events else 0)
         for k in range(args.warmup):
-            plan.run(xs[k % len(xs)], out)
+            step(k, ns)
         torch.cuda.synchronize(dev)
         if events:
-            plan.timing_read()  # discard warm-up records
+            for p in plans[:ns]:
+                p.timing_read()  # discard warm-up records
         torch.cuda.synchronize(dev)
         t0 = time.perf_counter()
         for k in range(args.steps):
-            plan.run(xs[k % len(xs)], out)
+            step(k, ns)
         torch.cuda.synchronize(dev)
         dt = time.perf_counter() - t0
-        return dt, (plan.timing_read() if events else None)
+        if not events:
+            return dt, None
+        merged: dict = {}
+        for p in plans[:ns]:
+            for name, (ms, cnt) in p.timing_read().items():
+                m0, c0 = merged.get(name, (0.0, 0))
+                merged[name] = (m0 + ms, c0 + cnt)
+            p.timing_enable(0)
+        return dt, merged
 
     # The headline region runs without per-kernel events (they add host and
     # device work between kernels); a second region of the same length records
-    # HIP events around every kernel for the roofline figures.
-    elapsed, _ = timed(False)
-    elapsed_events, phases = timed(True)
+    # HIP events around every kernel, on its own stream, for the roofline
+    # figures. With several streams a step is still one whole histogram; the
+    # steps of different streams overlap, as a caller's independent histograms
+    # on separate streams would.
+    elapsed, _ = timed(False, nstreams)
+    elapsed_events, phases = timed(True, nstreams)
+    elapsed_2 = timed(False, 2)[0] if two else (elapsed if nstreams == 2 else None)
 
     # Per-step distribution: a third region with one pair of events around
     # each run on the launch stream (the events sit between runs).
@@ -443,7 +485,8 @@ def main():
 
     parity = None
     if not args.no_parity:
-        parity = bool(np.array_equal(out.view(torch.uint32).cpu().numpy(), reference_counts(x, B)))
+        ref = reference_counts(x, B)
+        parity = all(bool(np.array_equal(o.view(torch.uint32).cpu().numpy(), ref)) for o in outs)
 
     ms_per_step = elapsed / args.steps * 1e3
     gelem = n * args.steps / elapsed / 1e9
@@ -542,17 +585,22 @@ def main():
         "parity_vs_bincount": parity,
         "config": {"workload": f"{w.name}: {w.recipe}; n={n}, {B} uint32 bins",
                    "n": n, "num_bins": B, "plan": plan.describe(),
-                   "input_copies": len(xs), **({"tuned": tuned} if tuned else {})},
+                   "input_copies": len(xs), "streams": nstreams,
+                   **({"tuned": tuned} if tuned else {})},
         "phases_ms_per_step": {k: round(v[0] / v[1], 5) for k, v in phases.items()},
         "ms_per_step_with_events": round(elapsed_events / args.steps * 1e3, 5),
         "step_us_event_bracketed": step_us,
+        "two_streams": None if elapsed_2 is None else {
+            "ms_per_step": round(elapsed_2 / args.steps * 1e3, 5),
+            "value": round(n * args.steps / elapsed_2 / 1e9, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if comparators is not None:
         line["comparators"] = comparators
     print(json.dumps(line), flush=True)
-    plan.close()
+    for p in plans:
+        p.close()
 
 
 if __name__ == "__main__":
