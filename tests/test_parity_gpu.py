@@ -602,12 +602,15 @@ def test_scatter_edge_cases(case):
 # --- seeded fuzz over sizes, paths and options -------------------------------
 
 def _fuzz_case(seed, large=False):
-    g = np.random.default_rng(1000 + seed + (50_000 if large else 0))
+    g = np.random.default_rng(1000 + seed + {False: 0, True: 50_000, "huge": 90_000}[large])
     num_bins = int(min(2**20, max(1, round(2 ** g.uniform(0, 20)))))
     n = int(g.choice([0, 1, 7, int(g.integers(1, 5000)), int(g.integers(5000, 300_000))]))
-    if large:
+    if large is True:
         num_bins = int(round(2 ** g.uniform(10, 21)))
         n = int(g.integers(4_000_000, 20_000_000))
+    elif large == "huge":  # far past LDS: hundreds to 2,048 ranges, short runs
+        num_bins = int(min(2**26, round(2 ** g.uniform(21, 26))))
+        n = int(g.integers(500_000, 12_000_000))
     kind = g.choice(["uniform", "skew", "onebin", "wild"])
     if kind == "uniform":
         x = g.integers(0, num_bins, size=n)
@@ -622,6 +625,8 @@ def _fuzz_case(seed, large=False):
     x = x.astype(np.int64).astype(np.int32)
     paths = ["auto", "scatter"] + (["full"] if num_bins <= 155_392 else []) + \
         (["range", "range"] if num_bins > 1 else [])
+    if large == "huge":
+        paths = ["auto", "auto", "scatter", "scatter", "scatter", "range"]
     path = str(g.choice(paths))
     opts = {"path": path, "aggregation": int(g.choice([-1, 0, 1, 2, 4]))}
     if path in ("full", "range"):
@@ -641,13 +646,15 @@ def _fuzz_case(seed, large=False):
     return x, num_bins, opts, accumulate
 
 
-@pytest.mark.parametrize("seed,large", [(k, False) for k in range(96)] + [(k, True) for k in range(12)])
+@pytest.mark.parametrize("seed,large", [(k, False) for k in range(96)] + [(k, True) for k in range(12)]
+                         + [(k, "huge") for k in range(12)])
 def test_fuzz_sizes_paths_options(seed, large):
     """Random (seeded) bin counts, lengths, input shapes, paths and plan options,
     each checked bit for bit against the oracle; a quarter of the cases
     accumulate onto random counts. Combinations a plan does not support must
     be refused with HIST_ERR_UNSUPPORTED, never run. The large cases (4-20
-    million elements, up to 2^21 bins) span many chunks and tiles."""
+    million elements, up to 2^21 bins) span many chunks and tiles; the huge ones
+    (2^21-2^26 bins) reach the two-phase path's short-run regime."""
     x, num_bins, opts, accumulate = _fuzz_case(seed, large)
     say(f"case fuzz{seed}: n={x.size} bins={num_bins} opts={opts} accumulate={accumulate}")
     try:
