@@ -27,6 +27,13 @@ constexpr uint32_t kMaxLdsBins16 = 79616;    // 16-bit counters + the carry-even
 constexpr uint64_t kMaxElemsPerWG16 = 1ull << 24;  // bounds the carry-event list
 constexpr uint32_t kMaxLdsBins8 = 155392;    // 8-bit counters + the shortest carry-event list
 constexpr uint32_t kScatterShift = 15;       // SCATTER range = 32768 bins (128 KiB)
+// From this many ranges the partition writes its run tables tile-major and a
+// transpose makes them range-major. Range-major stores from a tile land a row
+// apart: at 2,048 ranges (2^26 bins) the partition wrote 827 MiB for 192 MiB
+// of slots and tables. Measured on 2^26 uniform elements, tile-major against
+// range-major: 2^26 bins 567 vs 672 us, 2^25 360 vs 404, 2^24 263.3 vs 262.2
+// (the transpose's cost equals the partition's saving there).
+constexpr uint32_t kTileMajorRanges = 1024;
 constexpr uint32_t kScatterWG = 1024;
 constexpr uint32_t kScatterVPT = 4;          // vectors per thread in a scatter tile
 constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elements
@@ -124,7 +131,8 @@ struct hist_plan {
     char *ws = nullptr;
     uint64_t ws_bytes = 0, need = 0;
     uint64_t off_partials = 0, off_stage = 0, off_tcnt = 0, off_tbase = 0, off_tpre = 0,
-             off_totals = 0, off_segtot = 0, off_starts = 0;
+             off_totals = 0, off_segtot = 0, off_starts = 0, off_tbase_tm = 0;
+    bool tile_major = false;  // SCATTER: run tables written tile-major, then transposed
     // timing
     uint32_t tcap = 0, truns = 0;
     std::vector<hipEvent_t> ev;  // [tcap][HIST_MAX_PHASES][2]
@@ -338,6 +346,13 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
         off += align_up((uint64_t)R * ceil_div(T, pca::kScanSeg) * 4, 256);
         p->off_starts = off;  // uint64 start of every range in the concatenation, and the total
         off += align_up((uint64_t)(R + 1) * 8, 256);
+        p->tile_major = R >= kTileMajorRanges;
+        if (p->tile_major) {
+            // tile-major run starts; the tile-major run counts go to the tpre
+            // region, which the range scan overwrites after the transpose
+            p->off_tbase_tm = off;
+            off += align_up((uint64_t)R * T * 4, 256);
+        }
         p->part_rows = W + R;
         p->off_partials = off;
         off += partial_bytes(p->part_rows, p->nblk);
@@ -457,10 +472,13 @@ hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, h
     // persistent: a grid of two workgroups per CU, each walking tiles (at its
     // register count one 1024-thread workgroup is resident per CU at a time)
     const uint32_t grid = std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu);
+    uint32_t *tcnt = reinterpret_cast<uint32_t *>(p->ws + (p->tile_major ? p->off_tpre : p->off_tcnt));
+    uint32_t *tbase =
+        reinterpret_cast<uint32_t *>(p->ws + (p->tile_major ? p->off_tbase_tm : p->off_tbase));
+    const uint32_t rstride = p->tile_major ? 1u : T, tstride = p->tile_major ? p->ranges : 1u;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kScatterWG), bytes, s, in, p->num_bins, kScatterShift,
                        p->ranges, p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage),
-                       kScatterCap, reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
-                       reinterpret_cast<uint32_t *>(p->ws + p->off_tbase));
+                       kScatterCap, tcnt, tbase, rstride, tstride);
     return hipGetLastError();
 }
 
@@ -651,6 +669,12 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         const uint32_t nseg = ceil_div(T, pca::kScanSeg);
         uint32_t *tpre = reinterpret_cast<uint32_t *>(p->ws + p->off_tpre);
         uint32_t *segtot = reinterpret_cast<uint32_t *>(p->ws + p->off_segtot);
+        if (p->tile_major)
+            hipLaunchKernelGGL(pca::k_transpose, dim3(ceil_div(p->ranges, 64), ceil_div(T, 64), 2),
+                               dim3(256), 0, stream, tpre,
+                               reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
+                               reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase_tm),
+                               reinterpret_cast<uint32_t *>(p->ws + p->off_tbase), T, p->ranges);
         hipLaunchKernelGGL(pca::k_seg_scan<1024>, dim3(p->ranges * nseg), dim3(1024), 0, stream,
                            reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt), T, nseg, tpre,
                            segtot);

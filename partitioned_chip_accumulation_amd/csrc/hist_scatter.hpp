@@ -87,6 +87,30 @@ __global__ __launch_bounds__(WG) void k_seg_fix(uint32_t tiles, uint32_t nseg,
     for (uint32_t t = s0 + tid; t < s1; t += WG) p[t] += off;
 }
 
+// Two [rows][cols] uint32 tables (blockIdx.z picks which) to [cols][rows],
+// through LDS in 64 x 64 tiles: reads and writes are both 256-byte rows.
+__global__ __launch_bounds__(256) void k_transpose(const uint32_t *__restrict__ src0,
+                                                   uint32_t *__restrict__ dst0,
+                                                   const uint32_t *__restrict__ src1,
+                                                   uint32_t *__restrict__ dst1, uint32_t rows,
+                                                   uint32_t cols)
+{
+    __shared__ uint32_t tile[64][65];  // padded: a column read hits 64 banks
+    const uint32_t *src = blockIdx.z == 0 ? src0 : src1;
+    uint32_t *dst = blockIdx.z == 0 ? dst0 : dst1;
+    const uint32_t c0 = blockIdx.x * 64u, r0 = blockIdx.y * 64u;
+    const uint32_t tx = threadIdx.x & 63u, ty = threadIdx.x >> 6;
+    for (uint32_t i = ty; i < 64u; i += 4u) {
+        const uint32_t r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) tile[i][tx] = src[(uint64_t)r * cols + c];
+    }
+    __syncthreads();
+    for (uint32_t i = ty; i < 64u; i += 4u) {
+        const uint32_t c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows) dst[(uint64_t)c * rows + r] = tile[tx][i];
+    }
+}
+
 // Exclusive prefix of totals[0..ranges) into bs[0..ranges], by wave 0.
 __device__ __forceinline__ void range_starts(const uint32_t *__restrict__ totals, uint32_t ranges,
                                              uint64_t *bs)
@@ -129,14 +153,19 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
 // sub-counters chosen by lane (lane mod 2^qlog): lanes that route to the same
 // range then rarely share a word. The scan runs over [range][sub] order, so a
 // range's elements stay contiguous. Per tile and range the kernel writes the
-// run's length and start (tcnt, tbase; layout [range][tile]). Element order
-// inside a run is whatever the atomics gave; counts do not depend on it.
+// run's length and start (tcnt, tbase) at r * rstride + t * tstride: range-
+// major ([range][tile], rstride = tiles, tstride = 1) for few ranges. With
+// many ranges those are 4-byte stores a whole row apart, each a partial-line
+// write, so the tables are written tile-major (rstride = 1, tstride = ranges)
+// and k_transpose turns them range-major. Element order inside a run is
+// whatever the atomics gave; counts do not depend on it.
 template <int WG, int VPT>
 __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
                                                   uint32_t ranges, uint32_t qlog, uint32_t tiles,
                                                   uint16_t *__restrict__ stage, uint32_t stage_cap,
                                                   uint32_t *__restrict__ tcnt,
-                                                  uint32_t *__restrict__ tbase)
+                                                  uint32_t *__restrict__ tbase, uint32_t rstride,
+                                                  uint32_t tstride)
 {
     extern __shared__ u32x4 smem4[];
     const uint32_t nsub = ranges << qlog;  // <= 2 * WG
@@ -200,8 +229,9 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
         for (uint32_t r = tid; r < ranges; r += WG) {
             const uint32_t b0 = base[r << qlog];
             const uint32_t b1 = r + 1 < ranges ? base[(r + 1) << qlog] : nvalid;
-            tcnt[(uint64_t)r * tiles + t] = b1 - b0;
-            tbase[(uint64_t)r * tiles + t] = b0;
+            const uint64_t at = (uint64_t)r * rstride + (uint64_t)t * tstride;
+            tcnt[at] = b1 - b0;
+            tbase[at] = b0;
         }
 #pragma unroll
         for (int e = 0; e < E + 2; ++e)
