@@ -212,10 +212,12 @@ class Plan:
                                         int(n.value)), "hist_plan_create")
 
     def run(self, input: torch.Tensor, out: torch.Tensor | None = None,
-            accumulate: bool = False) -> torch.Tensor:
+            accumulate: bool = False, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
         """Histogram of an int32 CUDA tensor into a uint32 tensor of num_bins.
         accumulate=True adds into ``out`` (required then) instead of
-        overwriting it: out[b] += #{i : input[i] == b}, modulo 2^32."""
+        overwriting it: out[b] += #{i : input[i] == b}, modulo 2^32. The
+        kernels go to ``stream`` (default: the current stream of the plan's
+        device)."""
         if input.dtype != torch.int32 or input.device != self.device:
             raise ValueError("input must be an int32 tensor on the plan's device")
         if not input.is_contiguous():
@@ -229,13 +231,18 @@ class Plan:
             raise ValueError("out must be a contiguous 4-byte tensor of num_bins on the device")
         n = input.numel()
         fn = self._run_acc if accumulate else self._run
+        if stream is not None and stream.device != self.device:
+            raise ValueError("stream must be on the plan's device")
         if torch.cuda.current_device() == self.device.index:
+            h = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
             st = fn(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
-                    self.num_bins, torch.cuda.current_stream().cuda_stream)
+                    self.num_bins, h)
         else:
             with torch.cuda.device(self.device):
+                h = stream.cuda_stream if stream is not None else \
+                    torch.cuda.current_stream().cuda_stream
                 st = fn(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
-                        self.num_bins, torch.cuda.current_stream().cuda_stream)
+                        self.num_bins, h)
         _check(st, "hist_run_accumulate" if accumulate else "hist_run")
         return out.view(torch.uint32) if out.dtype == torch.int32 else out
 

@@ -564,6 +564,35 @@ def test_runs_on_a_side_stream():
     assert np.array_equal(out.view(torch.uint32).cpu().numpy(), ref)
 
 
+def test_two_plans_on_two_streams_in_flight():
+    """Independent histograms on two streams, each with its own plan and
+    output, passed as Plan.run(stream=...): alternating runs overlap on the
+    device and every output is exact."""
+    x = inputs.generate(2, n=(1 << 22) + 5)
+    ref, _ = oracle.hist(x, 65536)
+    xt = torch.from_numpy(x).to(DEV)
+    streams = [torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream(DEV))
+    plans = [hist.Plan(65536, x.size, device=DEV) for _ in streams]
+    outs = [torch.empty(65536, dtype=torch.int32, device=DEV) for _ in streams]
+    for k in range(20):
+        plans[k % 2].run(xt, outs[k % 2], stream=streams[k % 2])
+    torch.cuda.synchronize(DEV)
+    for o in outs:
+        assert np.array_equal(o.view(torch.uint32).cpu().numpy(), ref)
+    with pytest.raises(ValueError):
+        plans[0].run(xt, outs[0], stream=_OtherDeviceStream())
+    for p in plans:
+        p.close()
+
+
+class _OtherDeviceStream:
+    """Stands in for a stream of another device (a one-GPU machine has none)."""
+    device = torch.device("cuda", 99)
+    cuda_stream = 0
+
+
 @pytest.mark.parametrize("case", ["one-range", "all-invalid", "sparse-ranges", "tiny-last-range",
                                   "tile-edges", "short-runs", "mixed-runs", "sorted-block"])
 def test_scatter_edge_cases(case):
