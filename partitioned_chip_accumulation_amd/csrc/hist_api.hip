@@ -494,7 +494,8 @@ pca::Partials plan_partials(const hist_plan *p)
 }
 
 template <int AGG>
-hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
+hipError_t launch_owner_t(const hist_plan *p, uint32_t T, uint32_t *counts, uint32_t accumulate,
+                          hipStream_t s)
 {
     auto k = pca::k_bucket_hist<kScatterWG, 8, AGG>;
     const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + 4 * 4;
@@ -507,7 +508,7 @@ hipError_t launch_owner_t(const hist_plan *p, uint32_t T, hipStream_t s)
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
                        reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T,
                        p->range_bins, p->num_bins, p->owners, plan_partials(p),
-                       reinterpret_cast<uint64_t *>(p->ws + p->off_starts));
+                       reinterpret_cast<uint64_t *>(p->ws + p->off_starts), counts, accumulate);
     return hipGetLastError();
 }
 
@@ -576,17 +577,28 @@ hipError_t launch_merge_slots(const hist_plan *p, uint32_t num_bins, uint32_t *c
     // round per batch walks slowly: on the 2^20-bin hot-bin input (32 ranges,
     // 256 owners) it took 24.0 us against 13.9, hence the switch at
     // ranges * 4 >= owners.
-    if (p->ranges * 4u >= p->owners)
-        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1>), dim3(ceil_div(num_bins, 256)), dim3(64), 0,
-                           s, P, starts, p->ranges, p->range_bins, num_bins, p->owners, counts);
+    // From ranges >= 4 * owners most ranges have one owner, which wrote its
+    // counts itself; a workgroup then takes 8 blocks, so that such a range
+    // costs one check per 2,048 bins (2^26 bins: 114 -> 56 us). Where most
+    // ranges are shared the 8 blocks run one after another and it loses
+    // (2^22 bins: 20.3 -> 27.5 us).
+    constexpr uint32_t kManyBPW = 8;
+    if (p->ranges >= 4u * p->owners)
+        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1, kManyBPW>),
+                           dim3(ceil_div(num_bins, 256 * kManyBPW)), dim3(64), 0, s, P, starts,
+                           p->ranges, p->range_bins, num_bins, p->owners, counts);
+    else if (p->ranges * 4u >= p->owners)
+        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1, 1>), dim3(ceil_div(num_bins, 256)),
+                           dim3(64), 0, s, P, starts, p->ranges, p->range_bins, num_bins,
+                           p->owners, counts);
     else if (p->ranges >= 16)
-        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, pca::kMergeRounds>), dim3(ceil_div(num_bins, 256)),
-                           dim3(64), 0, s, P, starts, p->ranges, p->range_bins, num_bins, p->owners,
-                           counts);
+        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, pca::kMergeRounds, 1>),
+                           dim3(ceil_div(num_bins, 256)), dim3(64), 0, s, P, starts, p->ranges,
+                           p->range_bins, num_bins, p->owners, counts);
     else
-        hipLaunchKernelGGL((pca::k_merge_slots<4, ACC, pca::kMergeRounds>), dim3(ceil_div(num_bins, 256)),
-                           dim3(256), 0, s, P, starts, p->ranges, p->range_bins, num_bins, p->owners,
-                           counts);
+        hipLaunchKernelGGL((pca::k_merge_slots<4, ACC, pca::kMergeRounds, 1>),
+                           dim3(ceil_div(num_bins, 256)), dim3(256), 0, s, P, starts, p->ranges,
+                           p->range_bins, num_bins, p->owners, counts);
     return hipGetLastError();
 }
 
@@ -685,10 +697,10 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
     tm.begin(PH_OWNER);
     switch (p->agg) {
-    case 0: e = launch_owner_t<0>(p, T, stream); break;
-    case 1: e = launch_owner_t<1>(p, T, stream); break;
-    case 2: e = launch_owner_t<2>(p, T, stream); break;
-    default: e = launch_owner_t<4>(p, T, stream); break;
+    case 0: e = launch_owner_t<0>(p, T, counts, accumulate, stream); break;
+    case 1: e = launch_owner_t<1>(p, T, counts, accumulate, stream); break;
+    case 2: e = launch_owner_t<2>(p, T, counts, accumulate, stream); break;
+    default: e = launch_owner_t<4>(p, T, counts, accumulate, stream); break;
     }
     tm.end(PH_OWNER);
     if (e != hipSuccess) return HIST_ERR_HIP;

@@ -304,6 +304,38 @@ __device__ __forceinline__ void count_slots(uint32_t *lds, HotSlot &hs, const ui
     }
 }
 
+// An owner's finished slice of one range. When the owner's span holds the
+// whole range it is the range's only owner: it writes the counts itself
+// (adds them when accumulating), and the slot merge skips the range.
+// Otherwise the slice goes to partial slot `row` for the slot merge.
+template <int WG>
+__device__ __forceinline__ void finish_range(const Partials &out, uint32_t row, const uint32_t *lds,
+                                             uint32_t len, uint32_t *__restrict__ dst, bool whole,
+                                             uint32_t accumulate)
+{
+    if (!whole) {
+        flush_slice<WG, 32>(out, row, 0, lds, nullptr, 0, len, 0);
+        return;
+    }
+    // 16-byte stores where the range's counts start 16-byte aligned (counts
+    // itself needs only 4-byte alignment); the tail and other bases by word
+    uint32_t done = 0;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+        const uint32_t nv = len >> 2;
+        const u32x4 *l4 = reinterpret_cast<const u32x4 *>(lds);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
+        if (accumulate)
+            for (uint32_t v = threadIdx.x; v < nv; v += WG) d4[v] = d4[v] + l4[v];
+        else
+            for (uint32_t v = threadIdx.x; v < nv; v += WG) d4[v] = l4[v];
+        done = nv << 2;
+    }
+    if (accumulate)
+        for (uint32_t b = done + threadIdx.x; b < len; b += WG) dst[b] += lds[b];
+    else
+        for (uint32_t b = done + threadIdx.x; b < len; b += WG) dst[b] = lds[b];
+}
+
 // Phase 2: owner workgroups build LDS histograms from the routed slots.
 //
 // All ranges' elements, concatenated in range order, are split evenly over
@@ -328,7 +360,8 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint16_t *__restrict__ stage, uint32_t stage_cap, const uint32_t *__restrict__ tcnt,
     const uint32_t *__restrict__ tbase, const uint32_t *__restrict__ tpre,
     const uint32_t *__restrict__ totals, uint32_t ranges, uint32_t tiles, uint32_t range_bins,
-    uint32_t num_bins, uint32_t owners, Partials out, uint64_t *__restrict__ starts)
+    uint32_t num_bins, uint32_t owners, Partials out, uint64_t *__restrict__ starts,
+    uint32_t *__restrict__ counts, uint32_t accumulate)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
@@ -451,7 +484,8 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                 }
             }
             __syncthreads();
-            flush_slice<WG, 32>(out, i + r, 0, lds, nullptr, 0, len, 0);
+            finish_range<WG>(out, i + r, lds, len, counts + (uint64_t)r * range_bins,
+                             rb >= e0 && re <= e1, accumulate);
             __syncthreads();
             continue;
         }
@@ -540,7 +574,8 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
             if (lane == 0 && t != 0u) lds_add(lds, hs.h, t);
         }
         __syncthreads();
-        flush_slice<WG, 32>(out, i + r, 0, lds, nullptr, 0, len, 0);
+        finish_range<WG>(out, i + r, lds, len, counts + (uint64_t)r * range_bins,
+                         rb >= e0 && re <= e1, accumulate);
         __syncthreads();
     }
 }
@@ -552,21 +587,24 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
 // owners first..last are consecutive rows, summed by merge_block. An owner
 // that took no element (possible only when there are fewer elements than
 // owners) wrote no slot and is skipped. Empty ranges give zeros.
-template <int WAVES, bool ACC, uint32_t ROUNDS>
+template <int WAVES, bool ACC, uint32_t ROUNDS, uint32_t BPW>
 __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint64_t *__restrict__ starts,
                                                             uint32_t ranges, uint32_t range_bins,
                                                             uint32_t num_bins, uint32_t owners,
                                                             uint32_t *__restrict__ counts)
 {
     const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
-    const uint32_t bpr = range_bins / kBlockBins;  // blocks per range
-    const uint32_t r = blockIdx.x / bpr, lb = blockIdx.x % bpr;
+    // a workgroup takes BPW consecutive blocks of one range (BPW divides the
+    // range's 128 blocks), so that a range with one owner is skipped once
+    const uint32_t wpr = range_bins / kBlockBins / BPW;  // workgroups per range
+    const uint32_t r = blockIdx.x / wpr, lb0 = (blockIdx.x % wpr) * BPW;
     // start of range r, its end, and the grand total (the owner phase's prefix)
     const uint64_t rb = starts[r], re = starts[r + 1], N = starts[ranges];
     uint32_t first = 0, rows = 0;
     if (re > rb) {
         first = owner_of(rb, N, owners);
         rows = owner_of(re - 1, N, owners) - first + 1;
+        if (rows == 1) return;  // one owner held the whole range and wrote its counts
     }
     // every owner took at least one element when N >= owners
     const bool all_nonempty = N >= owners;
@@ -574,9 +612,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const ui
         const uint64_t i = (uint64_t)first + k;
         return all_nonempty || i * N / owners < (i + 1) * N / owners;
     };
-    const u32x4 t = merge_block<WAVES, ROUNDS>(P, (uint64_t)first + r, rows, lb, row_ok);
-    if (w == 0)
-        store_counts<ACC>(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins, t);
+    for (uint32_t lb = lb0; lb < lb0 + BPW; ++lb) {
+        const u32x4 t = merge_block<WAVES, ROUNDS>(P, (uint64_t)first + r, rows, lb, row_ok);
+        if (w == 0)
+            store_counts<ACC>(counts, (uint64_t)r * range_bins + lb * kBlockBins + lane * 4u, num_bins,
+                              t);
+        if (BPW > 1) __syncthreads();  // merge_block's LDS is reused by the next block
+    }
 }
 
 }  // namespace pca

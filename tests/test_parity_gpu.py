@@ -299,6 +299,28 @@ def test_misaligned_output_buffer():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_owner_written_ranges_at_any_output_alignment(offset):
+    """With more ranges than owners the owners write most ranges' counts
+    themselves, 16 bytes at a time when the range starts 16-byte aligned and
+    word by word otherwise; run and accumulate, on outputs 0, 4 and 12 bytes
+    past an aligned base."""
+    bins = (1 << 24) + 1000
+    x = rnd(41, 1_500_001, -2, bins + 2)
+    ref, _ = oracle.hist(x, bins)
+    xt = torch.from_numpy(x).to(DEV)
+    plan = hist.Plan(bins, x.size, device=DEV, path="scatter")
+    base = torch.zeros(bins + 3, dtype=torch.int32, device=DEV)
+    out = base[offset:offset + bins]
+    got = plan.run(xt, out).cpu().numpy()
+    assert np.array_equal(got, ref)
+    plan.run(xt, out, accumulate=True)
+    got2 = out.cpu().numpy().view(np.uint32)
+    torch.cuda.synchronize(DEV)
+    assert np.array_equal(got2, (2 * ref.astype(np.uint64)).astype(np.uint32))
+    plan.close()
+
+
 def test_argument_errors_on_device():
     plan = hist.Plan(1000, 100, device=DEV)
     # every buffer is large enough for any call below, so a missed check
@@ -342,6 +364,9 @@ ACC_CASES = [
     ("direct-cw8", 150_000, 400_000, {"path": "full", "groups": 1}),
     ("range", 200_000, 2_000_000, {"path": "range"}),
     ("scatter-hot", 300_000, 1_000_000, {"path": "scatter", "aggregation": 1}),
+    # 512 ranges over 256 owners: most ranges have one owner, which adds its
+    # counts itself; the ranges between owners go through the slot merge
+    ("scatter-whole-ranges", (1 << 24) - 5, 2_000_000, {"path": "scatter"}),
 ]
 
 
