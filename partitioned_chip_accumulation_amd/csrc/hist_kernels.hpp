@@ -12,9 +12,10 @@
 //   * the input is first routed by owner in a cheap coarse pass
 //     (k_partition), and owners then read only their own elements
 //     (k_bucket_hist).
-// Slices are merged by exclusive owners (k_merge, k_merge_slots): one thread
-// writes (or, when accumulating, reads and writes) each output bin once, so
-// no global atomics and no memset of the output are needed.
+// Slices are merged by exclusive owners (k_merge, k_merge_slots; on the
+// two-phase path an owner that holds a whole range writes it itself): one
+// thread writes (or, when accumulating, reads and writes) each output bin
+// once, so no global atomics and no memset of the output are needed.
 //
 // Conventions: wave64 (gfx950), 16-byte (dwordx4) global loads on the input
 // body; LDS counters are uint32 (ds_add_u32), or two 16-bit halves or four

@@ -582,11 +582,13 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
 
 // Phase 2b: counts[b] for the bins of one range = the sum of the slots that
 // the owners overlapping the range wrote for it (exclusive owner per bin, no
-// global atomics). A workgroup handles one 256-bin block of one range. Owner
+// global atomics). A workgroup handles BPW 256-bin blocks of one range. Owner
 // i wrote the range's slot to row i + r, so the slots of the overlapping
 // owners first..last are consecutive rows, summed by merge_block. An owner
 // that took no element (possible only when there are fewer elements than
-// owners) wrote no slot and is skipped. Empty ranges give zeros.
+// owners) wrote no slot and is skipped. A range with a single owner was
+// written to counts by that owner and is skipped whole. Empty ranges give
+// zeros.
 template <int WAVES, bool ACC, uint32_t ROUNDS, uint32_t BPW>
 __global__ __launch_bounds__(WAVES * 64) void k_merge_slots(Partials P, const uint64_t *__restrict__ starts,
                                                             uint32_t ranges, uint32_t range_bins,
