@@ -84,6 +84,31 @@ def test_scatter_sizes():
     assert i.workspace_bytes > partial_bytes(256 + 32, 32768) + tiles * 16392 * 2
 
 
+def scatter_workspace(num_bins, max_n, owners=256):
+    """The SCATTER workspace, region by region, each 256-byte aligned, in the
+    plan's order: staged slots, run tables (counts, starts, prefix), range totals,
+    segment totals, range starts, from 1,024 ranges a tile-major copy of the
+    run starts, then W + R partial rows of 32,768-bin slices."""
+    R = -(-num_bins // 32768)
+    T = max(1, -(-(max_n // 4) // 4096))
+    b = align(T * 16392 * 2) + 3 * align(R * T * 4) + align(R * 4)
+    b += align(R * -(-T // 4096) * 4) + align((R + 1) * 8)
+    if R >= 1024:
+        b += align(R * T * 4)
+    return b + partial_bytes(owners + R, 32768)
+
+
+@pytest.mark.parametrize("num_bins,max_n", [
+    (318_465, N), (1 << 20, 1 << 28), (524_288, 1 << 29), ((1 << 24) - 5, 2_000_000),
+    (1023 * 32768, N), (1024 * 32768, N), (1024 * 32768 + 1, 1 << 20), (hist.MAX_BINS, N),
+    (hist.MAX_BINS, 5), (1 << 21, 2**32 - 1),
+])
+def test_scatter_workspace_layout(num_bins, max_n):
+    i = hist.preview(num_bins, max_n, path="scatter")
+    assert i.ranges == -(-num_bins // 32768)
+    assert i.workspace_bytes == scatter_workspace(num_bins, max_n)
+
+
 def test_forced_options():
     assert hist.preview(8192, N, path="scatter").path == "scatter"
     r = hist.preview(100_000, N, path="range", range_bins=4096)
