@@ -613,7 +613,7 @@ def test_two_plans_on_two_streams_in_flight():
 
 
 class _OtherDeviceStream:
-    """Stands in for a stream of another device (a one-GPU machine has none)."""
+    """Stands in for a stream of another device, which a one-GPU machine lacks."""
     device = torch.device("cuda", 99)
     cuda_stream = 0
 
