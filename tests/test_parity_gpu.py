@@ -761,6 +761,41 @@ def test_tune_measures_every_allowed_schedule_and_picks_the_fastest(num_bins, ki
     plan.close()
 
 
+def test_tune_on_a_sample_shorter_than_max_n_and_its_errors():
+    """Tuning on a sample for plans of a larger max_n: the options it returns
+    make a plan for that max_n which is exact on a full-size input. counts
+    receives the sample's histogram. An output that overlaps the input is
+    refused before anything runs."""
+    import ctypes
+    num_bins, n = 300_000, 1 << 21
+    x = inputs.zipf(24, 4 * n, num_bins, 1.1)
+    xt = torch.from_numpy(x).to(DEV)
+    best, rows = hist.tune(xt[:n], num_bins, max_n=4 * n, reps=1)
+    assert any(r["status"] == hist.HIST_OK for r in rows)
+    plan = hist.Plan(num_bins, 4 * n, device=DEV, **best)
+    ref, _ = oracle.hist(x, num_bins)
+    assert np.array_equal(plan.run(xt).cpu().numpy(), ref)
+    plan.close()
+    lib = hist.library()
+    need = ctypes.c_uint64(0)
+    assert lib.hist_tune_workspace_size(num_bins, 4 * n, ctypes.byref(need)) == hist.HIST_OK
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=DEV)
+    counts = torch.empty(num_bins, dtype=torch.int32, device=DEV)
+    opts, cnt = hist.PlanOpts(), ctypes.c_uint32(0)
+    entries = (hist.TuneEntry * hist.TUNE_MAX_ENTRIES)()
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    assert lib.hist_tune(num_bins, 4 * n, xt.data_ptr(), n, counts.data_ptr(), ws.data_ptr(),
+                         ws.numel(), 1, stream, ctypes.byref(opts), entries,
+                         hist.TUNE_MAX_ENTRIES, ctypes.byref(cnt)) == hist.HIST_OK
+    assert cnt.value == hist.TUNE_MAX_ENTRIES
+    sample_ref, _ = oracle.hist(x[:n], num_bins)
+    assert np.array_equal(counts.view(torch.uint32).cpu().numpy(), sample_ref)
+    # counts overlapping the input: refused with INVALID_ARG, nothing queued
+    assert lib.hist_tune(num_bins, 4 * n, xt.data_ptr(), n, xt.data_ptr() + 4 * 16,
+                         ws.data_ptr(), ws.numel(), 1, stream, ctypes.byref(opts), entries,
+                         hist.TUNE_MAX_ENTRIES, ctypes.byref(cnt)) == hist.HIST_ERR_INVALID_ARG
+
+
 def test_tune_skips_schedules_the_workspace_cannot_hold():
     num_bins, n = 262_144, 1 << 21
     x = rnd(23, n, 0, num_bins)
