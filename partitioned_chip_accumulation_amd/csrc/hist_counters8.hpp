@@ -203,9 +203,10 @@ __device__ __forceinline__ void carry_at(Counts32 &c, uint32_t k, uint32_t add, 
 // p0 + STRIDE j (j < J): c[8j + i] is bin 8l + i of pair p0 + STRIDE j
 // (l = lane), byte i % 4 of its word 2l + i / 4. The wave reads the list 64
 // entries at a time and takes only the entries in its pairs; an entry names
-// one count, whose index in c is wave-uniform, so each matching entry costs
-// a few scalar branches and two register updates in which only the owning
-// lane's values change. Whole wave, convergent; p0 uniform.
+// one count, whose index in c is wave-uniform, so each distinct matching
+// entry of a window costs a few scalar branches and two register updates in
+// which only the owning lane's values change (its copies in the window are
+// added at once). Whole wave, convergent; p0 uniform.
 template <int J, int STRIDE>
 __device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t nev, uint32_t p0,
                                               Counts32 &c)
@@ -221,11 +222,15 @@ __device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t n
         uint64_t m = __ballot(dp < (uint32_t)(STRIDE * J) && dp % STRIDE == 0u);
         while (m != 0) {
             const int k = __builtin_ctzll(m);
-            m &= m - 1;
             const uint32_t ev = (uint32_t)__builtin_amdgcn_readlane((int)ent, k);
+            // the window's copies of this entry (hot bytes repeat) are applied
+            // together: mult events, +256 mult and -mult
+            const uint64_t same = __ballot(ent == ev) & m;
+            m &= ~same;
+            const uint32_t mult = (uint32_t)__popcll(same);
             const uint32_t word = ev >> 2;
             const uint32_t idx = (((ev >> 9) - p0) / STRIDE) * 8u + (word & 1u) * 4u + (ev & 3u);
-            const uint32_t hit = lane == ((word & 127u) >> 1) ? 1u : 0u;
+            const uint32_t hit = lane == ((word & 127u) >> 1) ? mult : 0u;
             carry_at<0, 8 * J>(c, idx, hit << 8, hit);
         }
     }
