@@ -208,9 +208,9 @@ hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist
             // pass (53.0 us against 65.1 for two 16-bit ranges), 2^18 in two
             // (64.7 against 118.2 for four), and they stay ahead on Zipf s = 1.1
             // input there (85.3 vs 105.9, 118.2 vs 167.2 us). Up to 2^16 bins
-            // they gain at most 1.4% on uniform input and lose 1.2-1.3x on Zipf
-            // input, whose hot bytes wrap every 256 counts (2^14 bins: 74.1 vs
-            // 56.3 us).
+            // they gain at most 3.7% on uniform input (2^11-2^12 bins; 1.4% or
+            // less elsewhere) and lose 1.2-1.3x on Zipf input, whose hot bytes
+            // wrap every 256 counts (2^14 bins: 74.1 vs 56.3 us).
             if (path == HIST_PATH_FULL)
                 cw = num_bins > lds_bins16 ? 8 : num_bins > kMaxLdsBins / 2 && num_bins <= cap32 ? 32 : 16;
             else if (opts.range_bins > 0)
