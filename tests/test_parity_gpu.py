@@ -153,6 +153,21 @@ def test_all_one_bin(b):
         check(x, 65536, f"one{b}-{p}-agg{agg}", path=p, aggregation=agg)
 
 
+@pytest.mark.parametrize("path,bins,groups", [("full", 150_000, 1), ("full", 150_000, 3),
+                                              ("range", 262_144, 2)])
+def test_counter8_identical_events_in_a_window(path, bins, groups):
+    """8-bit counters with the input piled onto one bin (and a second bin in
+    the same word): every window of the event list holds up to 64 copies of
+    the same entry, which the flush applies together (+256 m, -m), and the
+    neighbouring byte takes the cascades."""
+    n = 3_000_000
+    b = bins - 6  # byte 2 of its word: its carries cascade into byte 3 (bin b + 1)
+    x = np.full(n, b, np.int32)
+    x[::7] = b + 1
+    x[::1001] = 5
+    check(x, bins, f"identical-events-{path}-g{groups}", path=path, counter_bits=8, groups=groups)
+
+
 @pytest.mark.parametrize("agg", [0, 1, 4])
 @pytest.mark.parametrize("path,bins", [("full", 65536), ("range", 200_000)])
 def test_counter16_carry_events(agg, path, bins):
