@@ -7,7 +7,7 @@ before timing starts. Four device copies of the input are used in rotation,
 so that consecutive steps cannot serve a 256 MiB input from the 256 MB
 Infinity Cache that the previous step filled.
 
-The steps run on one stream. `two_streams` reports, from the same run, the
+The steps run on one stream. `--two-streams` adds, from the same run, the
 same K steps alternating over two streams, each stream with its own plan,
 workspace and output: two independent histograms are then in flight, and
 one's merge and launch ramp overlap the other's sweep, as for a caller who
@@ -17,13 +17,17 @@ overlap.)
 
 Prints one JSON line (rank 0). Throughput `value` is Gelem/s over the K timed
 steps (wall clock between two device synchronisations, no instrumentation in
-between). `roofline` is for the dominant kernel, timed live with HIP events
-around each of its launches over a second run of K steps (events between
-kernels cost ~1-2 us per step of their own, so they stay out of `value`).
+between). `roofline` is for the dominant kernel, timed live over a second run
+of K steps with HIP events attached to the kernels' own dispatches (the
+kernel's start and end, as a profiler's kernel trace reports them);
+`roofline.rocprof` gives the same kernel's average from the committed
+rocprofv3 trace of this command, when the kernel sources still match it.
+`workloads` repeats the measurement (W warm-up and K timed steps, AUTO's
+plan) on the four other workloads at full size, each checked bit for bit.
 `cpu_baseline` is the CPU oracle (a sequential loop, one core) timed on a
 bounded sample of the same input; that is the only use of the oracle here.
-The result checks (`parity_vs_bincount`, the sweeps' `parity`) compare with
-numpy's bincount.
+The result checks (`parity_vs_bincount`, `workloads[*].parity`, the sweeps'
+`parity`) compare with numpy's bincount.
 """
 from __future__ import annotations
 
@@ -38,10 +42,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+# The sources a stored profile entry was taken from, when the entry does not
+# list its own (entries written before they did).
 KERNEL_SOURCES = [f"partitioned_chip_accumulation_amd/csrc/{f}" for f in (
     "hist_common.hpp", "hist_counters16.hpp", "hist_partials.hpp", "hist_sweep.hpp",
     "hist_scatter.hpp", "hist_kernels.hpp", "hist_api.hip", "hist_counters8.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_TIMES_FILE = os.path.join(ROOT, "profiles", "kernel_times.json")
 
 
 def parse():
@@ -71,9 +78,14 @@ def parse():
     ap.add_argument("--streams", type=int, default=1,
                     help="histograms in flight: consecutive steps alternate over this many "
                          "streams, each with its own plan, workspace and output")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="also time the K steps alternating over two streams (two histograms in "
+                         "flight); off by default, so that every launch of a kernel in a trace "
+                         "of the default command is timed alike")
     ap.add_argument("--no-two-streams", action="store_true",
-                    help="skip the two-stream region (profiling runs, so that every launch of a "
-                         "kernel is timed alike)")
+                    help="the default (kept so that older profiling commands still run)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the `workloads` record (the four other workloads at full size)")
     ap.add_argument("--tune", action="store_true",
                     help="time every schedule on the input first (hist_tune) and bench the fastest")
     ap.add_argument("--comparators", action="store_true",
@@ -323,28 +335,157 @@ def path_sweep(args):
           file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources: list[str] | None = None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in sources or KERNEL_SOURCES:
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return "missing:" + rel
     return h.hexdigest()
 
 
-def counters_for(key: str) -> dict:
-    """The profiles/traffic.json entry for this kernel and workload (counter-
-    derived HBM bytes per launch, and LDS/occupancy counters where taken), or
-    {} when there is none or the kernel sources changed since the counters
-    were taken."""
+def stored_entry(path: str, key: str) -> dict:
+    """The entry for this kernel and workload in a committed profile summary
+    (profiles/traffic.json: counter-derived HBM bytes per launch, LDS and
+    occupancy counters; profiles/kernel_times.json: rocprofv3 kernel-trace
+    durations), or {} when there is none or the kernel sources changed since
+    it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return {}
     e = data.get(key)
-    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+    if not e or e.get("kernel_source_sha") != kernel_source_sha(e.get("sources")):
         return {}
     return e
+
+
+def counters_for(key: str) -> dict:
+    return stored_entry(TRAFFIC_FILE, key)
+
+
+def dominant_kernel(phases: dict, n: int, B: int):
+    """(phase name, algorithmic bytes per launch, average launch seconds,
+    launches) of the phase with the most device time. The sweep and the
+    partition read each element once (4 bytes); the owner kernel reads its
+    2-byte routed slots; the merges write the 4-byte bins."""
+    name, (ms, launches) = max(phases.items(), key=lambda kv: kv[1][0])
+    if name in ("sweep", "partition"):
+        nbytes = 4 * n
+    elif name == "owner_hist":
+        nbytes = 2 * n
+    else:
+        nbytes = 4 * B
+    return name, nbytes, ms / launches / 1e3, launches
+
+
+def roofline_for(phases: dict, n: int, B: int, key_tail: str) -> dict:
+    name, nbytes, avg_s, launches = dominant_kernel(phases, n, B)
+    achieved = nbytes / avg_s / 1e9
+    key = f"{name}:{key_tail}"
+    r = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+         "traffic": counters_for(key).get("bytes_per_launch"), "traffic_key": key,
+         "lds_counters": counters_for(key).get("lds_counters"), "algorithmic_bytes": nbytes,
+         "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches}
+    t = stored_entry(KERNEL_TIMES_FILE, key)
+    r["rocprof"] = None if not t else {
+        "avg_launch_us": t["avg_us"], "frac": round(nbytes / (t["avg_us"] * 1e-6) / 1e9 /
+                                                    HBM_PEAK_GBPS, 4),
+        "calls": t["calls"], "kernel": t["kernel"], "profile": t["profile"]}
+    return r
+
+
+def time_workload(cfg: int, steps: int, warmup: int, dev, check: bool = True,
+                  comparators: bool = False) -> dict:
+    """One workload at full size with AUTO's plan: W warm-up and K timed runs
+    (wall clock between device synchronisations), then K runs with kernel
+    events for the dominant kernel, and a bit-exact check against numpy's
+    bincount."""
+    import numpy as np
+    import torch
+
+    from partitioned_chip_accumulation_amd import hist, inputs
+
+    w = inputs.WORKLOADS[cfg]
+    print(f"# workload {w.name}: generating {w.n} elements", file=sys.stderr, flush=True)
+    x = inputs.generate(cfg, n=w.n)
+    xs = [torch.from_numpy(x).to(dev)]
+    if 4 * w.n * 4 <= 256 * 2**20:
+        xs += [xs[0].clone() for _ in range(3)]  # as the headline: four copies in rotation
+    out = torch.empty(w.num_bins, dtype=torch.int32, device=dev)
+    plan = hist.Plan(w.num_bins, w.n, device=dev)
+    for k in range(warmup):
+        plan.run(xs[k % len(xs)], out)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        plan.run(xs[k % len(xs)], out)
+    torch.cuda.synchronize(dev)
+    dt = (time.perf_counter() - t0) / steps
+    plan.timing_enable(steps)
+    for k in range(steps):
+        plan.run(xs[k % len(xs)], out)
+    phases = plan.timing_read()
+    plan.timing_enable(0)
+    rec = {"n": w.n, "num_bins": w.num_bins, "recipe": w.recipe, "plan": plan.describe(),
+           "us_per_histogram": round(dt * 1e6, 2), "gelem_s": round(w.n / dt / 1e9, 2),
+           "achieved_GBps": round((4 * w.n + 4 * w.num_bins) / dt / 1e9, 1),
+           "hbm_frac": round((4 * w.n + 4 * w.num_bins) / dt / 1e9 / HBM_PEAK_GBPS, 4),
+           "phases_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in phases.items()},
+           "roofline": roofline_for(phases, w.n, w.num_bins, f"{w.name}:n={w.n}:{plan.describe()}"),
+           "parity": None}
+    if len(xs) > 1:
+        rec["note"] = ("input copies fit the 256 MB Infinity Cache; launch- and cache-bound, so "
+                       "the HBM fraction is not meaningful")
+    ref = reference_counts(x, w.num_bins) if check or comparators else None
+    if check:
+        rec["parity"] = bool(np.array_equal(out.view(torch.uint32).cpu().numpy(), ref))
+    plan.close()
+    if comparators:
+        rec["comparators"] = comparator_figures(xs, w.num_bins, ref)
+    return rec
+
+
+def comparator_figures(xs, num_bins: int, ref) -> dict:
+    """The global-atomic fallback (page "Distributed Shared Memory", section
+    "When it beats global atomics": every element one atomic add into global
+    memory) and the stream-read ceiling on the same input, both timed with
+    events around a few back-to-back runs; the fallback's counts are checked
+    against the same reference."""
+    import numpy as np
+    import torch
+
+    from partitioned_chip_accumulation_amd import hist
+
+    dev = xs[0].device
+    n = xs[0].numel()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    got = hist.global_atomic(xs[0], num_bins)  # untimed, and checked
+    torch.cuda.synchronize(dev)
+    ok = bool(np.array_equal(got.cpu().numpy(), ref)) if ref is not None else None
+    reps = max(2, min(20, int(2e9 / (4 * n))))
+    s.record()
+    for k in range(reps):
+        hist.global_atomic(xs[k % len(xs)], num_bins)
+    e.record()
+    torch.cuda.synchronize(dev)
+    ga = s.elapsed_time(e) / 1e3 / reps
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    hist.stream_read(xs[0], sink)
+    s.record()
+    for k in range(reps):
+        hist.stream_read(xs[k % len(xs)], sink)
+    e.record()
+    torch.cuda.synchronize(dev)
+    rd = s.elapsed_time(e) / 1e3 / reps
+    return {"global_atomic_us": round(ga * 1e6, 1), "global_atomic_gelem_s": round(n / ga / 1e9, 2),
+            "global_atomic_parity": ok, "stream_read_us": round(rd * 1e6, 1),
+            "stream_read_GBps": round(4 * n / rd / 1e9, 1), "reps": reps}
 
 
 def main():
@@ -407,7 +548,7 @@ def main():
     # One plan (and workspace) and one output per stream: the steps on different
     # streams are independent histograms, so they may overlap on the device.
     nstreams = max(1, args.streams)
-    two = nstreams != 2 and not args.no_two_streams
+    two = nstreams != 2 and args.two_streams
     nplans = max(2 if two else 1, nstreams)  # the two-stream figure needs a second plan
     plans = [hist.Plan(B, n, device=dev, **plan_opts) for _ in range(nplans)]
     plan = plans[0]
@@ -459,10 +600,9 @@ def main():
             p.timing_enable(0)
         return dt, merged
 
-    # The headline region runs without per-kernel events (they add host and
-    # device work between kernels); a second region of the same length records
-    # HIP events around every kernel, on its own stream, for the roofline
-    # figures. With several streams a step is still one whole histogram; the
+    # The headline region runs without per-kernel events (attaching them adds
+    # host work per launch); a second region of the same length attaches HIP
+    # events to every kernel's dispatch, for the roofline figures. With several streams a step is still one whole histogram; the
     # steps of different streams overlap, as a caller's independent histograms
     # on separate streams would.
     elapsed, _ = timed(False, nstreams)
@@ -496,31 +636,25 @@ def main():
     gbps = alg_bytes * args.steps / elapsed / 1e9
 
     # Dominant kernel: the phase with the most device time.
-    dom = max(phases.items(), key=lambda kv: kv[1][0])
-    dom_name, (dom_ms, dom_launches) = dom
-    dom_avg_s = dom_ms / dom_launches / 1e3
-    # Algorithmic bytes per launch of the dominant kernel: the input sweep
-    # reads each element once (4 bytes); the merges write the 4-byte bins.
-    if dom_name in ("sweep", "partition"):
-        dom_bytes = 4 * n
-    elif dom_name == "owner_hist":
-        dom_bytes = 2 * n
-    else:
-        dom_bytes = 4 * B
-    achieved = dom_bytes / dom_avg_s / 1e9
-    traffic_key = f"{dom_name}:{w.name}:n={n}:{plan.describe()}"
-    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": counters_for(traffic_key).get("bytes_per_launch"),
-                "traffic_key": traffic_key,
-                "lds_counters": counters_for(traffic_key).get("lds_counters"),
-                "algorithmic_bytes": dom_bytes,
-                "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches": dom_launches}
+    roofline = roofline_for(phases, n, B, f"{w.name}:n={n}:{plan.describe()}")
     if 4 * n * len(xs) <= 256 * 2**20:
         # all input copies fit the 256 MB Infinity Cache: the steps are served
         # from it, and kernel launches dominate
         roofline["note"] = ("input copies fit the 256 MB Infinity Cache; launch- and "
                             "cache-bound, so the HBM fraction is not meaningful")
+
+    # The other four workloads at full size, AUTO's plan, each checked bit for
+    # bit (after the headline, so that nothing runs between its regions).
+    workloads = None
+    if not args.no_workloads and args.config == 2 and args.n is None and not args.uniform_bins \
+            and nstreams == 1 and not args.tune:
+        workloads = {}
+        for cfg in (1, 3, 4, 5):
+            wk = inputs.WORKLOADS[cfg]
+            workloads[wk.name] = time_workload(cfg, args.steps, args.warmup, dev,
+                                               check=not args.no_parity,
+                                               comparators=args.comparators)
+            torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -550,24 +684,7 @@ def main():
 
     comparators = None
     if args.comparators:
-        comparators = {}
-        torch.cuda.synchronize(dev)
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        reps = 20
-        s.record()
-        for k in range(reps):
-            hist.global_atomic(xs[k % len(xs)], B)
-        e.record()
-        torch.cuda.synchronize(dev)
-        comparators["global_atomic_gelem_s"] = round(n * reps / (s.elapsed_time(e) / 1e3) / 1e9, 2)
-        sink = torch.zeros(4096, dtype=torch.int32, device=dev)
-        s.record()
-        for k in range(reps):
-            hist.stream_read(xs[k % len(xs)], sink)
-        e.record()
-        torch.cuda.synchronize(dev)
-        comparators["stream_read_GBps"] = round(4 * n * reps / (s.elapsed_time(e) / 1e3) / 1e9, 1)
+        comparators = comparator_figures(xs, B, reference_counts(x, B))
 
     line = {
         "metric": "Gelem/s and achieved HBM GB/s vs peak, 65,536-bin int32 histogram, 1 MI355X",
@@ -600,6 +717,7 @@ def main():
     }
     if comparators is not None:
         line["comparators"] = comparators
+    line["workloads"] = workloads
     print(json.dumps(line), flush=True)
     for p in plans:
         p.close()

@@ -125,7 +125,7 @@ typedef struct {
                                  per workgroup (the LDS its slice leaves); otherwise 0 */
 } hist_plan_info_t;
 
-typedef struct hist_plan hist_plan_t; /* opaque, host memory only */
+typedef struct hist_plan_impl hist_plan_t; /* opaque, host memory only */
 
 /* Bytes of device workspace a plan for (num_bins, max_n, opts) needs on the
  * current device. opts may be NULL. Errors: INVALID_ARG for num_bins == 0,
@@ -137,9 +137,30 @@ hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n,
 /* Largest num_bins any path supports (2^26 bins, 256 MiB of counts). */
 #define HIST_MAX_BINS (1u << 26)
 
-/* Make a plan on the current device. workspace must be device memory of at
- * least hist_workspace_size() bytes, 256-byte aligned; it may be NULL when
- * that size is 0. The plan keeps the pointer until hist_plan_destroy. */
+/* Make a plan on the current device for histograms of num_bins bins over
+ * inputs of up to max_n elements (the page "Distributed Shared Memory",
+ * section "The cluster histogram", sizes its cluster from the bin count; here
+ * the plan picks the path, the bins each workgroup owns, the input chunks and
+ * the workspace layout from num_bins, max_n and the device).
+ *   plan            out: the new plan (host memory; free with hist_plan_destroy);
+ *                   *plan is NULL on any error
+ *   num_bins        1 .. HIST_MAX_BINS
+ *   max_n           largest n a hist_run on this plan may take, < 2^32
+ *   opts            NULL, or options to force (see hist_plan_opts_t)
+ *   workspace       device memory of at least hist_workspace_size() bytes,
+ *                   256-byte aligned, owned by the caller; may be NULL when
+ *                   that size is 0. The plan keeps the pointer until
+ *                   hist_plan_destroy and overwrites its contents on every run.
+ *   workspace_bytes its size in bytes
+ * Errors: INVALID_ARG for a null plan, num_bins == 0, max_n >= 2^32, bad
+ * opts or a misaligned workspace; UNSUPPORTED when the current device is not
+ * gfx950 or num_bins > HIST_MAX_BINS; WORKSPACE when workspace is NULL or
+ * smaller than the plan needs. Host-only: queues no device work. */
+hist_status_t hist_plan(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
+                        const hist_plan_opts_t *opts, void *workspace, uint64_t workspace_bytes);
+
+/* The same call as hist_plan under an older name (identical arguments,
+ * behaviour and errors). */
 hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
                                const hist_plan_opts_t *opts, void *workspace,
                                uint64_t workspace_bytes);
@@ -174,7 +195,7 @@ typedef struct {
                                       allow (this library on gfx950: 6); 0 = no limit */
 } hist_device_desc_t;
 
-/* The plan hist_plan_create would make for (num_bins, max_n, opts) on the
+/* The plan hist_plan would make for (num_bins, max_n, opts) on the
  * described device, computed on the host with no device present: the same
  * path, counter width, ranges, chunks and workspace bytes, for capacity
  * planning and for tests of the planning rules. info->device is -1.
@@ -220,7 +241,7 @@ hist_status_t hist_tune_workspace_size(uint32_t num_bins, uint64_t max_n, uint64
 /* Time every candidate schedule for (num_bins, max_n) on input[0..n): for
  * each, a plan on workspace, one untimed hist_run, then reps hist_runs
  * between two HIP events on stream. Writes the fastest candidate's options to
- * *best (pass them to hist_plan_create with the same num_bins and max_n), and
+ * *best (pass them to hist_plan with the same num_bins and max_n), and
  * the candidates' entries, in the order above, to entries[0..*count) (at most
  * capacity of them; entries may be NULL when capacity is 0). counts (device,
  * num_bins uint32) receives each run's output; on success it holds the
@@ -238,8 +259,11 @@ hist_status_t hist_tune(uint32_t num_bins, uint64_t max_n, const int32_t *input,
  * buf (always NUL-terminated when len > 0). */
 hist_status_t hist_plan_describe(const hist_plan_t *plan, char *buf, uint64_t len);
 
-/* Per-kernel timing for measurement. When enabled, hist_run records a pair
- * of HIP events around each kernel it launches, on the stream it is given.
+/* Per-kernel timing for measurement. When enabled, hist_run attaches a pair
+ * of HIP events to the kernels of each phase it launches (hipExtLaunchKernel:
+ * the start of the phase's first kernel and the end of its last), so a
+ * phase's time is its kernels' own execution, as a profiler's kernel trace
+ * reports it, with nothing queued between kernels.
  * hist_plan_timing_read waits for the recorded events and returns, for each
  * phase p < HIST_MAX_PHASES, the summed milliseconds and the launch count,
  * then clears the record. Phase names come from hist_plan_phase_name.

@@ -10,6 +10,7 @@
 // the capacity argument: R cooperating workgroups hold R slices on-chip.
 #include "hist.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -109,7 +110,7 @@ hist_status_t query_device(DeviceInfo *d)
 
 }  // namespace
 
-struct hist_plan {
+struct hist_plan_impl {
     DeviceInfo dev;
     uint32_t num_bins = 0;
     uint64_t max_n = 0;
@@ -165,7 +166,7 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
 uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes);
 
 // Fill every plan field that depends only on (num_bins, max_n, opts, device).
-hist_status_t design(hist_plan *p, uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *o)
+hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const hist_plan_opts_t *o)
 {
     hist_plan_opts_t opts{};
     opts.aggregation = -1;
@@ -376,6 +377,24 @@ hipError_t allow_lds(K kernel, uint32_t bytes)
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// Start and stop events to attach to a kernel's own dispatch (null when timing
+// is off). Attached events take the kernel's start and end timestamps, which
+// is what a profiler's kernel trace reports; no marker packet is queued
+// between kernels.
+struct KEv {
+    hipEvent_t a = nullptr, b = nullptr;
+};
+
+template <typename F, typename... Args>
+void launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, const KEv &ev,
+            Args... args)
+{
+    if (ev.a || ev.b)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.a, ev.b, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
+
 struct SweepArgs {
     pca::InputView in;
     uint32_t G, xcds;
@@ -385,7 +404,7 @@ struct SweepArgs {
 };
 
 template <int WG, int AGG, int CW>
-hipError_t launch_sweep_t(const hist_plan *p, const SweepArgs &a, hipStream_t s)
+hipError_t launch_sweep_t(const hist_plan_impl *p, const SweepArgs &a, hipStream_t s, const KEv &ev)
 {
     // Packed counters: 2 vectors (8 returning LDS atomics) per thread per
     // iteration stay within the LDS wait counter; measured 12% faster than 4.
@@ -393,30 +412,30 @@ hipError_t launch_sweep_t(const hist_plan *p, const SweepArgs &a, hipStream_t s)
     const uint32_t bytes = sweep_lds_bytes(CW, p->range_bins, CW == 32 ? p->kshift : 0u, p->ev_cap);
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, a.in, p->num_bins,
-                       p->range_bins, p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, p->ev_cap, a.out,
-                       a.direct, a.accumulate);
+    launch(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, ev, a.in, p->num_bins, p->range_bins,
+           p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, p->ev_cap, a.out, a.direct,
+           a.accumulate);
     return hipGetLastError();
 }
 
 template <int WG, int CW>
-hipError_t launch_sweep_agg(const hist_plan *p, const SweepArgs &a, hipStream_t s)
+hipError_t launch_sweep_agg(const hist_plan_impl *p, const SweepArgs &a, hipStream_t s, const KEv &ev)
 {
     switch (p->agg) {
-    case 0: return launch_sweep_t<WG, 0, CW>(p, a, s);
-    case 1: return launch_sweep_t<WG, 1, CW>(p, a, s);
-    case 2: return launch_sweep_t<WG, 2, CW>(p, a, s);
-    default: return launch_sweep_t<WG, 4, CW>(p, a, s);
+    case 0: return launch_sweep_t<WG, 0, CW>(p, a, s, ev);
+    case 1: return launch_sweep_t<WG, 1, CW>(p, a, s, ev);
+    case 2: return launch_sweep_t<WG, 2, CW>(p, a, s, ev);
+    default: return launch_sweep_t<WG, 4, CW>(p, a, s, ev);
     }
 }
 
 template <int CW>
-hipError_t launch_sweep_wg(const hist_plan *p, const SweepArgs &a, hipStream_t s)
+hipError_t launch_sweep_wg(const hist_plan_impl *p, const SweepArgs &a, hipStream_t s, const KEv &ev)
 {
     switch (p->wg) {
-    case 256: return launch_sweep_agg<256, CW>(p, a, s);
-    case 512: return launch_sweep_agg<512, CW>(p, a, s);
-    default: return launch_sweep_agg<1024, CW>(p, a, s);
+    case 256: return launch_sweep_agg<256, CW>(p, a, s, ev);
+    case 512: return launch_sweep_agg<512, CW>(p, a, s, ev);
+    default: return launch_sweep_agg<1024, CW>(p, a, s, ev);
     }
 }
 
@@ -462,7 +481,8 @@ uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes)
                       : sweep_resident_wg<8>(wg, agg, lds_bytes);
 }
 
-hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, hipStream_t s)
+hipError_t launch_partition(const hist_plan_impl *p, pca::InputView in, uint32_t T, hipStream_t s,
+                            const KEv &ev)
 {
     auto k = pca::k_partition<kScatterWG, kScatterVPT>;
     const uint32_t npad = ((p->ranges << p->qlog) + 3u) & ~3u;
@@ -476,13 +496,13 @@ hipError_t launch_partition(const hist_plan *p, pca::InputView in, uint32_t T, h
     uint32_t *tbase =
         reinterpret_cast<uint32_t *>(p->ws + (p->tile_major ? p->off_tbase_tm : p->off_tbase));
     const uint32_t rstride = p->tile_major ? 1u : T, tstride = p->tile_major ? p->ranges : 1u;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kScatterWG), bytes, s, in, p->num_bins, kScatterShift,
-                       p->ranges, p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage),
-                       kScatterCap, tcnt, tbase, rstride, tstride);
+    launch(k, dim3(grid), dim3(kScatterWG), bytes, s, ev, in, p->num_bins, kScatterShift, p->ranges,
+           p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage), kScatterCap, tcnt, tbase,
+           rstride, tstride);
     return hipGetLastError();
 }
 
-pca::Partials plan_partials(const hist_plan *p)
+pca::Partials plan_partials(const hist_plan_impl *p)
 {
     const uint64_t cells = (uint64_t)p->part_rows * p->nblk;
     pca::Partials P;
@@ -494,30 +514,30 @@ pca::Partials plan_partials(const hist_plan *p)
 }
 
 template <int AGG>
-hipError_t launch_owner_t(const hist_plan *p, uint32_t T, uint32_t *counts, uint32_t accumulate,
-                          hipStream_t s)
+hipError_t launch_owner_t(const hist_plan_impl *p, uint32_t T, uint32_t *counts, uint32_t accumulate,
+                          hipStream_t s, const KEv &ev)
 {
     auto k = pca::k_bucket_hist<kScatterWG, 8, AGG>;
     const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + 4 * 4;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(p->owners), dim3(kScatterWG), bytes, s,
-                       reinterpret_cast<const uint16_t *>(p->ws + p->off_stage), kScatterCap,
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt),
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase),
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
-                       reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T,
-                       p->range_bins, p->num_bins, p->owners, plan_partials(p),
-                       reinterpret_cast<uint64_t *>(p->ws + p->off_starts), counts, accumulate);
+    launch(k, dim3(p->owners), dim3(kScatterWG), bytes, s, ev,
+           reinterpret_cast<const uint16_t *>(p->ws + p->off_stage), kScatterCap,
+           reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt),
+           reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase),
+           reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
+           reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T, p->range_bins,
+           p->num_bins, p->owners, plan_partials(p),
+           reinterpret_cast<uint64_t *>(p->ws + p->off_starts), counts, accumulate);
     return hipGetLastError();
 }
 
 struct PhaseTimer {
-    hist_plan *p;
+    hist_plan_impl *p;
     hipStream_t s;
     uint32_t slot;
     bool on;
-    PhaseTimer(hist_plan *p_, hipStream_t s_) : p(p_), s(s_)
+    PhaseTimer(hist_plan_impl *p_, hipStream_t s_) : p(p_), s(s_)
     {
         on = p->tcap > 0 && p->truns < p->tcap;
         slot = p->truns;
@@ -531,16 +551,19 @@ struct PhaseTimer {
     {
         return p->ev[((size_t)slot * HIST_MAX_PHASES + ph) * 2 + which];
     }
-    void begin(int ph)
+    // Events to attach to a kernel of phase ph: the phase's first kernel
+    // carries the start event and its last kernel the stop event (a phase of
+    // one kernel carries both).
+    KEv ev(int ph, bool first = true, bool last = true)
     {
-        if (on) (void)hipEventRecord(event(ph, 0), s);
-    }
-    void end(int ph)
-    {
-        if (on) {
-            (void)hipEventRecord(event(ph, 1), s);
+        KEv e;
+        if (!on) return e;
+        if (first) e.a = event(ph, 0);
+        if (last) {
+            e.b = event(ph, 1);
             p->used[(size_t)slot * HIST_MAX_PHASES + ph] = 1;
         }
+        return e;
     }
 };
 
@@ -550,15 +573,14 @@ namespace {
 
 template <bool ACC>
 hipError_t launch_merge(const pca::Partials &P, uint32_t G, uint32_t num_bins, uint32_t *counts,
-                        uint32_t nblk, hipStream_t s)
+                        uint32_t nblk, hipStream_t s, const KEv &ev)
 {
     if (G <= 256)
-        hipLaunchKernelGGL((pca::k_merge<4, ACC>), dim3(nblk), dim3(256), 0, s, P, G, num_bins, counts);
+        launch(pca::k_merge<4, ACC>, dim3(nblk), dim3(256), 0, s, ev, P, G, num_bins, counts);
     else if (G <= 512)
-        hipLaunchKernelGGL((pca::k_merge<8, ACC>), dim3(nblk), dim3(512), 0, s, P, G, num_bins, counts);
+        launch(pca::k_merge<8, ACC>, dim3(nblk), dim3(512), 0, s, ev, P, G, num_bins, counts);
     else
-        hipLaunchKernelGGL((pca::k_merge<16, ACC>), dim3(nblk), dim3(1024), 0, s, P, G, num_bins,
-                           counts);
+        launch(pca::k_merge<16, ACC>, dim3(nblk), dim3(1024), 0, s, ev, P, G, num_bins, counts);
     return hipGetLastError();
 }
 
@@ -566,8 +588,8 @@ hipError_t launch_merge(const pca::Partials &P, uint32_t G, uint32_t num_bins, u
 // them: one wave per block (64 rows per round trip) once ranges are many,
 // four (256 rows) when each range has many owners.
 template <bool ACC>
-hipError_t launch_merge_slots(const hist_plan *p, uint32_t num_bins, uint32_t *counts,
-                              hipStream_t s)
+hipError_t launch_merge_slots(const hist_plan_impl *p, uint32_t num_bins, uint32_t *counts,
+                              hipStream_t s, const KEv &ev)
 {
     const pca::Partials P = plan_partials(p);
     const uint64_t *starts = reinterpret_cast<const uint64_t *>(p->ws + p->off_starts);
@@ -584,21 +606,18 @@ hipError_t launch_merge_slots(const hist_plan *p, uint32_t num_bins, uint32_t *c
     // (2^22 bins: 20.3 -> 27.5 us).
     constexpr uint32_t kManyBPW = 8;
     if (p->ranges >= 4u * p->owners)
-        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1, kManyBPW>),
-                           dim3(ceil_div(num_bins, 256 * kManyBPW)), dim3(64), 0, s, P, starts,
-                           p->ranges, p->range_bins, num_bins, p->owners, counts);
+        launch(pca::k_merge_slots<1, ACC, 1, kManyBPW>, dim3(ceil_div(num_bins, 256 * kManyBPW)),
+               dim3(64), 0, s, ev, P, starts, p->ranges, p->range_bins, num_bins, p->owners, counts);
     else if (p->ranges * 4u >= p->owners)
-        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, 1, 1>), dim3(ceil_div(num_bins, 256)),
-                           dim3(64), 0, s, P, starts, p->ranges, p->range_bins, num_bins,
-                           p->owners, counts);
+        launch(pca::k_merge_slots<1, ACC, 1, 1>, dim3(ceil_div(num_bins, 256)), dim3(64), 0, s, ev,
+               P, starts, p->ranges, p->range_bins, num_bins, p->owners, counts);
     else if (p->ranges >= 16)
-        hipLaunchKernelGGL((pca::k_merge_slots<1, ACC, pca::kMergeRounds, 1>),
-                           dim3(ceil_div(num_bins, 256)), dim3(64), 0, s, P, starts, p->ranges,
-                           p->range_bins, num_bins, p->owners, counts);
+        launch(pca::k_merge_slots<1, ACC, pca::kMergeRounds, 1>, dim3(ceil_div(num_bins, 256)),
+               dim3(64), 0, s, ev, P, starts, p->ranges, p->range_bins, num_bins, p->owners, counts);
     else
-        hipLaunchKernelGGL((pca::k_merge_slots<4, ACC, pca::kMergeRounds, 1>),
-                           dim3(ceil_div(num_bins, 256)), dim3(256), 0, s, P, starts, p->ranges,
-                           p->range_bins, num_bins, p->owners, counts);
+        launch(pca::k_merge_slots<4, ACC, pca::kMergeRounds, 1>, dim3(ceil_div(num_bins, 256)),
+               dim3(256), 0, s, ev, P, starts, p->ranges, p->range_bins, num_bins, p->owners,
+               counts);
     return hipGetLastError();
 }
 
@@ -621,10 +640,8 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     hipError_t e = hipSuccess;
     if (n == 0) {
         if (accumulate) return HIST_OK;  // nothing to add
-        tm.begin(PH_SWEEP);
-        hipLaunchKernelGGL(pca::k_fill_zero, dim3(std::max<uint32_t>(1, std::min<uint32_t>(1024, ceil_div(num_bins, 256)))),
-                           dim3(256), 0, stream, counts, (uint64_t)num_bins);
-        tm.end(PH_SWEEP);
+        launch(pca::k_fill_zero, dim3(std::max<uint32_t>(1, std::min<uint32_t>(1024, ceil_div(num_bins, 256)))),
+               dim3(256), 0, stream, tm.ev(PH_SWEEP), counts, (uint64_t)num_bins);
         return hipGetLastError() == hipSuccess ? HIST_OK : HIST_ERR_HIP;
     }
 
@@ -649,21 +666,22 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         a.out = plan_partials(p);
         a.direct = G > 1 ? nullptr : counts;
         a.accumulate = accumulate;
-        // Non-temporal loads also for R > 1: the chunk's other owners still find
-        // the lines in the XCD's L2 (measured: 50% L2 hits, one HBM fetch per
-        // element) and the stream evicts less useful data.
-        tm.begin(PH_SWEEP);
-        e = p->cw == 32   ? launch_sweep_wg<32>(p, a, stream)
-            : p->cw == 16 ? launch_sweep_wg<16>(p, a, stream)
-                          : launch_sweep_wg<8>(p, a, stream);
-        tm.end(PH_SWEEP);
+        // Non-temporal loads also for R > 1. On the 2^26-element sweeps plain
+        // and non-temporal loads time alike for R > 1 (2^18 uniform bins: 119.2
+        // vs 119.8 us). The co-owners do not always find the lines in the XCD's
+        // L2: on the Zipf 262,144-bin workload (R = 2, 8-bit counters) the
+        // sweep's scaled FETCH_SIZE is 1.8x the input, so most second reads
+        // go to the fabric.
+        const KEv sev = tm.ev(PH_SWEEP);
+        e = p->cw == 32   ? launch_sweep_wg<32>(p, a, stream, sev)
+            : p->cw == 16 ? launch_sweep_wg<16>(p, a, stream, sev)
+                          : launch_sweep_wg<8>(p, a, stream, sev);
         if (e != hipSuccess) return HIST_ERR_HIP;
         if (G > 1) {
-            tm.begin(PH_MERGE);
             // one batch of loads per lane covers 8 rows x 8 rounds per wave
-            e = accumulate ? launch_merge<true>(a.out, G, num_bins, counts, p->nblk, stream)
-                           : launch_merge<false>(a.out, G, num_bins, counts, p->nblk, stream);
-            tm.end(PH_MERGE);
+            const KEv mev = tm.ev(PH_MERGE);
+            e = accumulate ? launch_merge<true>(a.out, G, num_bins, counts, p->nblk, stream, mev)
+                           : launch_merge<false>(a.out, G, num_bins, counts, p->nblk, stream, mev);
             if (e != hipSuccess) return HIST_ERR_HIP;
         }
         return HIST_OK;
@@ -672,47 +690,47 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     // SCATTER
     const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kScatterWG * kScatterVPT));
     if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
-    tm.begin(PH_PART);
-    e = launch_partition(p, in, T, stream);
-    tm.end(PH_PART);
+    e = launch_partition(p, in, T, stream, tm.ev(PH_PART));
     if (e != hipSuccess) return HIST_ERR_HIP;
-    tm.begin(PH_SCAN);
     {
         const uint32_t nseg = ceil_div(T, pca::kScanSeg);
         uint32_t *tpre = reinterpret_cast<uint32_t *>(p->ws + p->off_tpre);
         uint32_t *segtot = reinterpret_cast<uint32_t *>(p->ws + p->off_segtot);
+        // the phase's first kernel carries its start event, the last its stop
         if (p->tile_major)
-            hipLaunchKernelGGL(pca::k_transpose, dim3(ceil_div(p->ranges, 64), ceil_div(T, 64), 2),
-                               dim3(256), 0, stream, tpre,
-                               reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
-                               reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase_tm),
-                               reinterpret_cast<uint32_t *>(p->ws + p->off_tbase), T, p->ranges);
-        hipLaunchKernelGGL(pca::k_seg_scan<1024>, dim3(p->ranges * nseg), dim3(1024), 0, stream,
-                           reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt), T, nseg, tpre,
-                           segtot);
-        hipLaunchKernelGGL(pca::k_seg_fix<256>, dim3(p->ranges * nseg), dim3(256), 0, stream, T, nseg,
-                           tpre, segtot, reinterpret_cast<uint32_t *>(p->ws + p->off_totals));
+            launch(pca::k_transpose, dim3(ceil_div(p->ranges, 64), ceil_div(T, 64), 2), dim3(256), 0,
+                   stream, tm.ev(PH_SCAN, true, false), tpre,
+                   reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt),
+                   reinterpret_cast<const uint32_t *>(p->ws + p->off_tbase_tm),
+                   reinterpret_cast<uint32_t *>(p->ws + p->off_tbase), T, p->ranges);
+        launch(pca::k_seg_scan<1024>, dim3(p->ranges * nseg), dim3(1024), 0, stream,
+               tm.ev(PH_SCAN, !p->tile_major, false),
+               reinterpret_cast<const uint32_t *>(p->ws + p->off_tcnt), T, nseg, tpre, segtot);
+        launch(pca::k_seg_fix<256>, dim3(p->ranges * nseg), dim3(256), 0, stream,
+               tm.ev(PH_SCAN, false, true), T, nseg, tpre, segtot,
+               reinterpret_cast<uint32_t *>(p->ws + p->off_totals));
     }
-    tm.end(PH_SCAN);
     if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
-    tm.begin(PH_OWNER);
-    switch (p->agg) {
-    case 0: e = launch_owner_t<0>(p, T, counts, accumulate, stream); break;
-    case 1: e = launch_owner_t<1>(p, T, counts, accumulate, stream); break;
-    case 2: e = launch_owner_t<2>(p, T, counts, accumulate, stream); break;
-    default: e = launch_owner_t<4>(p, T, counts, accumulate, stream); break;
+    {
+        const KEv oev = tm.ev(PH_OWNER);
+        switch (p->agg) {
+        case 0: e = launch_owner_t<0>(p, T, counts, accumulate, stream, oev); break;
+        case 1: e = launch_owner_t<1>(p, T, counts, accumulate, stream, oev); break;
+        case 2: e = launch_owner_t<2>(p, T, counts, accumulate, stream, oev); break;
+        default: e = launch_owner_t<4>(p, T, counts, accumulate, stream, oev); break;
+        }
     }
-    tm.end(PH_OWNER);
     if (e != hipSuccess) return HIST_ERR_HIP;
-    tm.begin(PH_SLOTS);
-    e = accumulate ? launch_merge_slots<true>(p, num_bins, counts, stream)
-                   : launch_merge_slots<false>(p, num_bins, counts, stream);
-    tm.end(PH_SLOTS);
+    {
+        const KEv sev = tm.ev(PH_SLOTS);
+        e = accumulate ? launch_merge_slots<true>(p, num_bins, counts, stream, sev)
+                       : launch_merge_slots<false>(p, num_bins, counts, stream, sev);
+    }
     if (e != hipSuccess) return HIST_ERR_HIP;
     return HIST_OK;
 }
 
-void fill_info(const hist_plan *p, hist_plan_info_t *info);
+void fill_info(const hist_plan_impl *p, hist_plan_info_t *info);
 
 }  // namespace
 
@@ -737,7 +755,7 @@ hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n, const hist_
     hist_status_t st = check_opts(opts);
     if (st != HIST_OK) return st;
     if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
-    hist_plan p;
+    hist_plan_impl p;
     st = query_device(&p.dev);
     if (st != HIST_OK) return st;
     st = design(&p, num_bins, max_n, opts);
@@ -746,9 +764,8 @@ hist_status_t hist_workspace_size(uint32_t num_bins, uint64_t max_n, const hist_
     return HIST_OK;
 }
 
-hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
-                               const hist_plan_opts_t *opts, void *workspace,
-                               uint64_t workspace_bytes)
+hist_status_t hist_plan(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
+                        const hist_plan_opts_t *opts, void *workspace, uint64_t workspace_bytes)
 {
     if (!plan) return HIST_ERR_INVALID_ARG;
     *plan = nullptr;
@@ -757,7 +774,7 @@ hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t m
     if (st != HIST_OK) return st;
     if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
     if (((uintptr_t)workspace & 255u) != 0) return HIST_ERR_INVALID_ARG;
-    hist_plan *p = new (std::nothrow) hist_plan();
+    hist_plan_impl *p = new (std::nothrow) hist_plan_impl();
     if (!p) return HIST_ERR_INVALID_ARG;
     st = query_device(&p->dev);
     if (st == HIST_OK) st = design(p, num_bins, max_n, opts);
@@ -773,6 +790,12 @@ hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t m
     return HIST_OK;
 }
 
+hist_status_t hist_plan_create(hist_plan_t **plan, uint32_t num_bins, uint64_t max_n,
+                               const hist_plan_opts_t *opts, void *workspace,
+                               uint64_t workspace_bytes)
+{
+    return hist_plan(plan, num_bins, max_n, opts, workspace, workspace_bytes);
+}
 
 hist_status_t hist_run(hist_plan_t *p, uint32_t *counts, const int32_t *input, uint64_t n,
                        uint32_t num_bins, hipStream_t stream)
@@ -803,7 +826,7 @@ hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins
     hist_status_t st = check_opts(opts);
     if (st != HIST_OK) return st;
     if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
-    hist_plan p;
+    hist_plan_impl p;
     p.dev.cu = dev->cu_count;
     p.dev.xcd = dev->xcd_count;
     p.dev.lds = dev->lds_bytes;
@@ -818,7 +841,7 @@ hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins
 
 namespace {
 
-void fill_info(const hist_plan *p, hist_plan_info_t *info)
+void fill_info(const hist_plan_impl *p, hist_plan_info_t *info)
 {
     std::memset(info, 0, sizeof(*info));
     info->path = p->path;

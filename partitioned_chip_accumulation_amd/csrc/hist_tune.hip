@@ -116,8 +116,8 @@ hist_status_t hist_tune(uint32_t num_bins, uint64_t max_n, const int32_t *input,
         if (st == HIST_OK) {
             fits_any = true;
             hist_plan_t *plan = nullptr;
-            st = hist_plan_create(&plan, num_bins, max_n, &e.opts, need ? workspace : nullptr,
-                                  need ? workspace_bytes : 0);
+            st = hist_plan(&plan, num_bins, max_n, &e.opts, need ? workspace : nullptr,
+                           need ? workspace_bytes : 0);
             if (st == HIST_OK) {
                 st = time_plan(plan, counts, input, n, num_bins, reps, stream, &e.ms);
                 hist_plan_destroy(plan);

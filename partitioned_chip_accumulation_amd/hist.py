@@ -85,6 +85,7 @@ def load(path: str = LIBRARY):
     sigs = {
         "hist_status_str": (ctypes.c_char_p, [i32]),
         "hist_workspace_size": (i32, [u32, u64, P(PlanOpts), P(u64)]),
+        "hist_plan": (i32, [P(vp), u32, u64, P(PlanOpts), vp, u64]),
         "hist_plan_create": (i32, [P(vp), u32, u64, P(PlanOpts), vp, u64]),
         "hist_run": (i32, [vp, vp, vp, u64, u32, vp]),
         "hist_run_accumulate": (i32, [vp, vp, vp, u64, u32, vp]),
@@ -196,6 +197,10 @@ class Plan:
             else torch.device(device)
         self.num_bins, self.max_n = int(num_bins), int(max_n)
         self._plan = ctypes.c_void_p()
+        # streams other than the allocation stream that this plan's kernels ran
+        # on: the workspace is recorded on each, so the caching allocator does
+        # not hand it out again before their work is done
+        self._side_streams: set[int] = set()
         lib = library()
         self._run = lib.hist_run
         self._run_acc = lib.hist_run_accumulate
@@ -206,10 +211,9 @@ class Plan:
                                            ctypes.byref(n)), "hist_workspace_size")
             self.workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8,
                                          device=self.device)
-            _check(lib.hist_plan_create(ctypes.byref(self._plan), self.num_bins, self.max_n,
-                                        ctypes.byref(o),
-                                        self.workspace.data_ptr() if n.value else None,
-                                        int(n.value)), "hist_plan_create")
+            _check(lib.hist_plan(ctypes.byref(self._plan), self.num_bins, self.max_n,
+                                 ctypes.byref(o), self.workspace.data_ptr() if n.value else None,
+                                 int(n.value)), "hist_plan")
 
     def run(self, input: torch.Tensor, out: torch.Tensor | None = None,
             accumulate: bool = False, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
@@ -222,6 +226,7 @@ class Plan:
             raise ValueError("input must be an int32 tensor on the plan's device")
         if not input.is_contiguous():
             raise ValueError("input must be contiguous")
+        fresh_out = out is None
         if out is None:
             if accumulate:
                 raise ValueError("accumulate=True needs out")
@@ -244,6 +249,17 @@ class Plan:
                 st = fn(self._plan, out.data_ptr(), input.data_ptr() if n else None, n,
                         self.num_bins, h)
         _check(st, "hist_run_accumulate" if accumulate else "hist_run")
+        if stream is not None:
+            # Memory from torch's caching allocator belongs to the stream that
+            # was current when it was allocated; kernels queued on another
+            # stream must be recorded on it, or a later allocation could reuse
+            # the memory while they still run.
+            h = stream.cuda_stream
+            if h not in self._side_streams:
+                self.workspace.record_stream(stream)
+                self._side_streams.add(h)
+            if fresh_out:
+                out.record_stream(stream)
         return out.view(torch.uint32) if out.dtype == torch.int32 else out
 
     __call__ = run

@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for the histogram kernels.
 
-    python -m partitioned_chip_accumulation_amd.profiling trace DIR --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling trace DIR --cmd "..." --out FILE.md \
+        [--sources A B ...] [--entry "KEY|KERNEL-SUBSTRING|WORKGROUPS" ...]
     python -m partitioned_chip_accumulation_amd.profiling counters DIR [DIR...] --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling matrix FILE.jsonl --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling sweep FILE.jsonl --cmd "..." --out FILE.md
@@ -9,6 +10,11 @@
         --kernel k_sweep --calib-kernel k_copy --calib-bytes N --key KEY --sources A B --out FILE.json
 
 DIR is a rocprofv3 output directory written with ``--output-format csv``.
+``trace`` tabulates kernel durations per (kernel, workgroups of the
+dispatch), so that launches of one kernel on different shapes stay apart,
+stamps the hash of the kernel sources into the summary, and with ``--entry``
+records a dispatch group's durations under KEY in profiles/kernel_times.json
+(for bench.py's cross-check of its live kernel timing).
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE of a kernel by
 what the same counters read for a plain copy kernel of known size in the same
 run (both counters are in KiB per dispatch; on gfx950 FETCH_SIZE reads half
@@ -36,23 +42,68 @@ def short(name: str) -> str:
     return base.replace("void ", "")
 
 
-def kernel_durations(d: str) -> dict[str, list[float]]:
-    by = collections.defaultdict(list)
+def _workgroups(r: dict) -> int | None:
+    """Workgroups of a dispatch from a kernel-trace row (grid sizes are in
+    work-items), or None when the columns are absent."""
+    try:
+        n = 1
+        for ax in "XYZ":
+            g, w = int(r[f"Grid_Size_{ax}"]), int(r[f"Workgroup_Size_{ax}"])
+            n *= (g + w - 1) // w
+        return n
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+RUN_GAP_NS = 500_000_000  # dispatches of one group further apart start a new run
+
+
+def kernel_durations(d: str) -> dict[tuple[str, int | None, int], list[float]]:
+    """Durations in microseconds per (kernel, workgroups of the dispatch, run).
+    A run is a stretch of a group's dispatches with no gap over half a second
+    between them: one program that times several workloads in turn launches
+    the same kernel on the same grid for each, seconds apart (their inputs
+    are generated in between)."""
+    raw = collections.defaultdict(list)
     for f in _csvs(d, "kernel_trace.csv"):
         for r in csv.DictReader(open(f)):
-            by[short(r["Kernel_Name"])].append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            raw[(short(r["Kernel_Name"]), _workgroups(r))].append((t0, (t1 - t0) / 1e3))
+    by = {}
+    for (k, wgs), v in raw.items():
+        v.sort()
+        run, last = 0, None
+        for t0, us in v:
+            if last is not None and t0 - last > RUN_GAP_NS:
+                run += 1
+            last = t0
+            by.setdefault((k, wgs, run), []).append(us)
     return by
 
 
 def trace_table(d: str) -> str:
     by = kernel_durations(d)
-    lines = ["| kernel | calls | avg us | median us | min us | total ms |",
-             "|---|---:|---:|---:|---:|---:|"]
-    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{k}` | {len(v)} | {statistics.mean(v):.2f} | "
-                     f"{statistics.median(v):.2f} | {min(v):.2f} | {sum(v) / 1e3:.3f} |")
+    lines = ["| kernel | workgroups | run | calls | avg us | median us | min us | total ms |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (k, wgs, run), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {wgs if wgs is not None else '?'} | {run} | {len(v)} | "
+                     f"{statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} | "
+                     f"{sum(v) / 1e3:.3f} |")
     return "\n".join(lines)
+
+
+def trace_entry(d: str, pattern: str, workgroups: int, run: int = 0) -> dict:
+    """Duration statistics of run `run` of the dispatches of the kernel
+    matching pattern with that many workgroups."""
+    hits = {k: v for k, v in kernel_durations(d).items()
+            if pattern in k[0] and k[1] == workgroups and k[2] == run}
+    if len(hits) != 1:
+        raise SystemExit(f"{len(hits)} dispatch groups match {pattern!r} x {workgroups} "
+                         f"run {run}: {sorted(hits)}")
+    (name, _, _), v = next(iter(hits.items()))
+    return {"kernel": name, "workgroups": workgroups, "run": run, "calls": len(v),
+            "avg_us": round(statistics.mean(v), 3), "median_us": round(statistics.median(v), 3),
+            "min_us": round(min(v), 3)}
 
 
 def counters_per_dispatch(d: str) -> dict[str, dict[str, float]]:
@@ -197,6 +248,12 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--title", default="Kernel trace")
+    t.add_argument("--sources", nargs="*", default=[],
+                   help="kernel source files whose SHA-256 the summary records")
+    t.add_argument("--entry", action="append", default=[],
+                   help="KEY|KERNEL-SUBSTRING|WORKGROUPS[|RUN]: record that dispatch group's "
+                        "durations (its RUN-th run, default 0) under KEY in --times")
+    t.add_argument("--times", default=os.path.join("profiles", "kernel_times.json"))
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--cmd", required=True, action="append")
@@ -238,9 +295,26 @@ def main():
         open(a.out, "w").write(matrix_markdown(a.jsonl, a.cmd))
         return
     if a.cmd_ == "trace":
+        sha = sources_sha(a.sources) if a.sources else None
+        stamp = "" if not sha else \
+            f"Kernel sources (SHA-256 of {' '.join(a.sources)}): `{sha}`\n\n"
         text = f"# {a.title}\n\nCommand (rocprofv3 kernel trace):\n\n```\n{a.cmd}\n```\n\n" \
-               f"{trace_table(a.dir)}\n"
+               f"{stamp}{trace_table(a.dir)}\n"
         open(a.out, "w").write(text)
+        if a.entry:
+            if not sha:
+                raise SystemExit("--entry needs --sources")
+            data = json.load(open(a.times)) if os.path.exists(a.times) else {}
+            for spec in a.entry:
+                key, pat, wgs, *run = spec.split("|")
+                e = trace_entry(a.dir, pat, int(wgs), int(run[0]) if run else 0)
+                e.update({"profile": a.out, "cmd": a.cmd, "kernel_source_sha": sha,
+                          "sources": a.sources})
+                data[key] = e
+                print(json.dumps({key: e}))
+            with open(a.times, "w") as f:
+                json.dump(data, f, indent=1, sort_keys=True)
+                f.write("\n")
     elif a.cmd_ == "counters":
         cmds = "\n".join(a.cmd)
         text = f"# {a.title}\n\nCommands (one rocprofv3 --pmc pass each):\n\n```\n{cmds}\n```\n\n" \
@@ -258,7 +332,8 @@ def main():
         entry = {"fetch_bytes": round(f_k * 1024 * f_scale), "write_bytes": round(w_k * 1024 * w_scale),
                  "fetch_kib_raw": f_k, "write_kib_raw": w_k, "fetch_scale": f_scale,
                  "write_scale": w_scale, "calib_kernel": a.calib_kernel,
-                 "calib_bytes": a.calib_bytes, "kernel_source_sha": sources_sha(a.sources)}
+                 "calib_bytes": a.calib_bytes, "kernel_source_sha": sources_sha(a.sources),
+                 "sources": a.sources}
         entry["bytes_per_launch"] = entry["fetch_bytes"] + entry["write_bytes"]
         lds = {}
         if a.lds:

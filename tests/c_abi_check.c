@@ -39,9 +39,14 @@ int main(void)
     opts.path = 9;
     expect("workspace_size(bad path)", hist_workspace_size(10, 10, &opts, &bytes),
            HIST_ERR_INVALID_ARG);
-    expect("plan_create(NULL)", hist_plan_create(NULL, 10, 10, NULL, NULL, 0),
+    expect("plan(NULL)", hist_plan(NULL, 10, 10, NULL, NULL, 0), HIST_ERR_INVALID_ARG);
+    expect("plan(num_bins=0)", hist_plan(&plan, 0, 10, NULL, NULL, 0), HIST_ERR_INVALID_ARG);
+    expect("plan(max_n=2^32)", hist_plan(&plan, 10, 1ull << 32, NULL, NULL, 0),
            HIST_ERR_INVALID_ARG);
-    expect("plan_create(num_bins=0)", hist_plan_create(&plan, 0, 10, NULL, NULL, 0),
+    expect("plan(misaligned workspace)", hist_plan(&plan, 10, 10, NULL, (void *)3, 0),
+           HIST_ERR_INVALID_ARG);
+    expect("plan left NULL", plan == NULL, 1);
+    expect("plan_create(NULL)", hist_plan_create(NULL, 10, 10, NULL, NULL, 0),
            HIST_ERR_INVALID_ARG);
     expect("run(NULL)", hist_run(NULL, NULL, NULL, 0, 1, NULL), HIST_ERR_INVALID_ARG);
     expect("run_accumulate(NULL)", hist_run_accumulate(NULL, NULL, NULL, 0, 1, NULL),

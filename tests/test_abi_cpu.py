@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_headers_declare_the_expected_calls():
     names = declared_functions()
-    for must in ["hist_plan_create", "hist_run", "hist_workspace_size", "hist_plan_destroy",
+    for must in ["hist_plan", "hist_plan_create", "hist_run", "hist_workspace_size", "hist_plan_destroy",
                  "hist_status_str", "hist_bench_global_atomic", "hist_plan_preview",
                  "hist_run_accumulate", "hist_tune", "hist_tune_workspace_size"]:
         assert must in names
@@ -65,6 +65,9 @@ def test_argument_errors_before_any_device_call():
         assert lib.hist_workspace_size(10, 10, ctypes.byref(o),
                                        ctypes.byref(n)) == hist.HIST_ERR_INVALID_ARG, field
     p = ctypes.c_void_p()
+    assert lib.hist_plan(None, 10, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan(ctypes.byref(p), 0, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan(ctypes.byref(p), 10, 10, None, 3, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_create(None, 10, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_create(ctypes.byref(p), 0, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_create(ctypes.byref(p), 10, 10, None, 3, 0) == hist.HIST_ERR_INVALID_ARG

@@ -28,12 +28,16 @@ def test_counters_are_used_only_for_the_current_kernel_sources(tmp_path, monkeyp
     assert bench.counters_for(key) == {}
 
 
-def test_committed_counters_match_the_kernel_sources():
-    # the summaries under profiles/ were taken from the kernels as committed
-    with open(bench.TRAFFIC_FILE) as fh:
-        data = json.load(fh)
-    assert data and all(e["kernel_source_sha"] == bench.kernel_source_sha() for e in data.values())
-    assert any(k.startswith("sweep:uniform-64k:") for k in data)
+def test_committed_profiles_match_the_kernel_sources():
+    # the counter and kernel-trace entries under profiles/ were taken from the
+    # kernels as committed (each entry names the sources its hash covers)
+    for path in (bench.TRAFFIC_FILE, bench.KERNEL_TIMES_FILE):
+        with open(path) as fh:
+            data = json.load(fh)
+        stale = [k for k, e in data.items()
+                 if e["kernel_source_sha"] != bench.kernel_source_sha(e.get("sources"))]
+        assert data and not stale, (path, stale)
+        assert any(k.startswith("sweep:uniform-64k:") for k in data)
 
 
 def test_reference_counts_skip_values_outside_the_bins():

@@ -160,3 +160,25 @@ def test_planted_mistake_is_caught(name, tmp_path):
     lib.oracle_hist.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
                                 ctypes.c_void_p]
     assert pin_failures(lib), f"planted mistake {name!r} passed every pin"
+
+
+def test_oracle_counts_match_stored_hashes():
+    """The oracle's counts of each workload's first 2^20 elements hash to the
+    values tests/golden/make_golden.py stored (written from the generator and
+    the oracle only). A change to either shows up here; that each stored
+    histogram is right is what the pins above establish."""
+    import hashlib
+    import json
+
+    from partitioned_chip_accumulation_amd import inputs
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "counts_sha256.json")
+    with open(path) as f:
+        stored = json.load(f)["counts"]
+    assert sorted(stored) == [str(c) for c in sorted(inputs.WORKLOADS)]
+    for cfg, e in stored.items():
+        x = inputs.generate(int(cfg), n=e["n"])
+        counts, dropped = oracle.hist(x, e["num_bins"])
+        assert dropped == e["dropped"], cfg
+        assert int(counts.sum(dtype=np.uint64)) + dropped == e["n"], cfg
+        assert hashlib.sha256(counts.tobytes()).hexdigest() == e["sha256"], cfg

@@ -217,6 +217,44 @@ def test_counter8_carry_events_smaller_workgroups(wg, path, bins, groups):
           wg_size=wg, **({"range_bins": 150_016} if path == "range" else {}))
 
 
+@pytest.mark.parametrize("wg,groups", [(1024, 2), (512, 3), (256, 2), (1024, 1), (256, 1)])
+def test_counter8_every_leaf_of_the_event_application(wg, groups):
+    """8-bit counters: carries out of every count a lane holds at the flush.
+    A wave's flush takes four pairs of 256-bin blocks spaced by the wave count
+    (pairs w, w + NW, w + 2 NW, w + 3 NW for wave w), and a lane holds 8
+    counts (two words) of each: 32 counts, each reached by its own leaf of the
+    event application. Here every one of those counts, for one lane of every
+    wave, gets at least 256 copies in every chunk, so every leaf applies
+    events, with carries out of byte 3 and cascades into the next byte. One
+    chunk takes the direct write, whose application covers one pair (8
+    leaves) at a time."""
+    nw = wg // 64
+    bins = 512 * 4 * nw
+    hot = []
+    for w in range(nw):
+        lane = (7 * w + 3) % 64
+        for j in range(4):
+            for i in range(8):
+                hot.append(512 * (w + j * nw) + 8 * lane + i)
+    copies = 300 * groups + 100  # >= 256 in every chunk of the shuffled input
+    x = np.concatenate([np.repeat(np.array(hot, np.int32), copies), rnd(11, 50_000, 0, bins)])
+    x = x[np.random.default_rng(wg + groups).permutation(x.size)].astype(np.int32)
+    check(x, bins, f"cw8-leaves-wg{wg}-g{groups}", path="full", counter_bits=8, groups=groups,
+          wg_size=wg)
+
+
+@pytest.mark.parametrize("agg", [0, 1])
+@pytest.mark.parametrize("groups", [2, 16])
+def test_zipf_workload_shape_on_8bit_ranges(agg, groups):
+    """The Zipf 262,144-bin workload's recipe at 2^22 elements on its AUTO
+    schedule's kind (8-bit counters, two ranges): hot bytes wrap every 256
+    counts, so the carry events and their application run at scale, in well
+    under the full size's time."""
+    x = inputs.generate(3, n=1 << 22)
+    check(x, 262_144, f"zipf-2^22-range8-agg{agg}-g{groups}", path="range", counter_bits=8,
+          groups=groups, aggregation=agg)
+
+
 @pytest.mark.parametrize("case,bins", [("one-bin-at-the-limit", 155_392),
                                        ("one-bin-at-the-limit", 100_000),
                                        ("one-bin-past-the-limit", 155_392),

@@ -77,7 +77,7 @@ def test_trace_table(tmp_path):
         f.write('"void pca::k_merge<4>(x)",1000,3000\n')
         f.write('"void pca::k_merge<4>(x)",5000,9000\n')
     table = profiling.trace_table(str(d))
-    assert "| `pca::k_merge<4>` | 2 | 3.00 | 3.00 | 2.00 | 0.006 |" in table
+    assert "| `pca::k_merge<4>` | ? | 0 | 2 | 3.00 | 3.00 | 2.00 | 0.006 |" in table  # no shapes
 
 
 def test_sweep_title_names_the_input(tmp_path):
@@ -90,3 +90,28 @@ def test_sweep_title_names_the_input(tmp_path):
     g = tmp_path / "u.jsonl"
     write_lines(g, [cell("bins", 1 << 14, "full16", 2.0)])  # records without the field
     assert "uniform int32 input" in profiling.sweep_markdown(str(g), "cmd").splitlines()[0]
+
+
+def test_trace_groups_dispatches_by_shape_and_records_entries(tmp_path):
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
+            "Grid_Size_Z", "Workgroup_Size_X", "Workgroup_Size_Y", "Workgroup_Size_Z"]
+    rows = [("void pca::k_sweep<1024, 2, 0, 16>(args)", 0, 44000, 262144),
+            ("void pca::k_sweep<1024, 2, 0, 16>(args)", 100000, 146000, 262144),
+            ("void pca::k_sweep<1024, 2, 0, 16>(args)", 0, 5000, 131072),
+            ("void pca::k_merge<4, false>(args)", 0, 5000, 65536),
+            # the same kernel and grid seconds later: a second run
+            ("void pca::k_sweep<1024, 2, 0, 16>(args)", 9 * 10**9, 9 * 10**9 + 90000, 262144)]
+    with open(d / "run_kernel_trace.csv", "w") as f:
+        f.write(",".join(cols) + "\n")
+        for name, t0, t1, grid in rows:
+            wg = 1024 if "sweep" in name else 256
+            f.write(f'"{name}",{t0},{t1},{grid},1,1,{wg},1,1\n')
+    table = profiling.trace_table(str(tmp_path / "trace"))
+    assert "| `pca::k_sweep<1024, 2, 0, 16>` | 256 | 0 | 2 | 45.00 |" in table
+    assert "| `pca::k_sweep<1024, 2, 0, 16>` | 256 | 1 | 1 | 90.00 |" in table
+    assert "| `pca::k_sweep<1024, 2, 0, 16>` | 128 | 0 | 1 | 5.00 |" in table
+    e = profiling.trace_entry(str(tmp_path / "trace"), "k_sweep", 256)
+    assert e["calls"] == 2 and e["avg_us"] == 45.0 and e["kernel"] == "pca::k_sweep<1024, 2, 0, 16>"
+    assert profiling.trace_entry(str(tmp_path / "trace"), "k_sweep", 256, 1)["avg_us"] == 90.0
