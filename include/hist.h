@@ -182,6 +182,39 @@ hist_status_t hist_run(hist_plan_t *plan, uint32_t *counts, const int32_t *input
 hist_status_t hist_run_accumulate(hist_plan_t *plan, uint32_t *counts, const int32_t *input,
                                   uint64_t n, uint32_t num_bins, hipStream_t stream);
 
+/* The histogram with no device allocation at all, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid hipMalloc. It computes what hist_run computes,
+ * counts[b] = #{ i in [0, n) : input[i] == b }, with the same kernels: it
+ * plans like hist_plan with default options for (num_bins, max_n = n) on the
+ * current device, and takes the workspace from a device array the library
+ * holds, HIST_STATIC_SCRATCH_BYTES on each device it runs on, kept until the
+ * process ends. When the default plan's one-pass workspace (its partial rows)
+ * does not fit, it counts the input in fewer, larger chunks.
+ *   counts    device, num_bins uint32, overwritten; 4-byte aligned
+ *   input     device, n int32, read-only; 4-byte aligned; NULL allowed when n == 0
+ *   n         < 2^32
+ *   num_bins  1 .. HIST_MAX_BINS
+ *   stream    the stream to queue on (0 = the null stream)
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * call) and queues kernels only. Every call on a device shares that device's
+ * array, which keeps the last call's contents: calls that overlap on one
+ * device (on different streams, or from several threads without ordering)
+ * race and give wrong counts. Calls ordered on one stream are safe.
+ * Errors: INVALID_ARG as hist_run (null counts, NULL input with n > 0,
+ * num_bins == 0, n >= 2^32, overlapping buffers, misalignment);
+ * UNSUPPORTED when the current device is not gfx950 or num_bins >
+ * HIST_MAX_BINS; WORKSPACE, before anything is queued, when the plan for
+ * (num_bins, n) needs more than HIST_STATIC_SCRATCH_BYTES even in fewer
+ * chunks. On an MI355X every n < 2^32 fits up to 79,616 bins; up to 318,464
+ * bins at least 2^26 elements fit (8-bit counters need a minimum number of
+ * chunks, each a partial row); on the two-phase path (more bins) the routed
+ * slots take about 2n bytes, and at least 2^25 elements fit up to 2^20 bins,
+ * 2^23 up to 2^24 bins. HIP when a launch fails. */
+#define HIST_STATIC_SCRATCH_BYTES (128ull << 20)
+hist_status_t hist_run_static(uint32_t *counts, const int32_t *input, uint64_t n,
+                              uint32_t num_bins, hipStream_t stream);
+
 /* Fill *info. */
 hist_status_t hist_plan_info(const hist_plan_t *plan, hist_plan_info_t *info);
 

@@ -16,9 +16,11 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
+#include "hist_host.hpp"
 #include "hist_kernels.hpp"
 
 namespace {
@@ -732,7 +734,68 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
 
 void fill_info(const hist_plan_impl *p, hist_plan_info_t *info);
 
+// Device numbers for run_in_workspace, taken once per device: the runtime's
+// property query costs far more than the planning arithmetic.
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev_info[kMaxDevices];
+hist_status_t g_dev_status[kMaxDevices];
+
+hist_status_t device_info_cached(int dev, DeviceInfo *d)
+{
+    if (dev < 0 || dev >= kMaxDevices) return HIST_ERR_UNSUPPORTED;
+    std::call_once(g_dev_once[dev], [dev] { g_dev_status[dev] = query_device(&g_dev_info[dev]); });
+    if (g_dev_status[dev] != HIST_OK) return g_dev_status[dev];
+    *d = g_dev_info[dev];
+    return HIST_OK;
+}
+
 }  // namespace
+
+namespace pca_host {
+
+hist_status_t device_supported(int dev)
+{
+    DeviceInfo d;
+    return device_info_cached(dev, &d);
+}
+
+hist_status_t run_in_workspace(uint32_t *counts, const int32_t *input, uint64_t n,
+                               uint32_t num_bins, hipStream_t stream, void *ws, uint64_t ws_bytes,
+                               int dev)
+{
+    if (!counts || (n > 0 && !input) || num_bins == 0 || n > (uint64_t)UINT32_MAX)
+        return HIST_ERR_INVALID_ARG;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    if (!ws || ((uintptr_t)ws & 255u) != 0) return HIST_ERR_WORKSPACE;
+    hist_plan_impl p;  // on the stack: its vectors stay empty, nothing is allocated
+    hist_status_t st = device_info_cached(dev, &p.dev);
+    if (st != HIST_OK) return st;
+    const uint64_t max_n = std::max<uint64_t>(n, 1);
+    st = design(&p, num_bins, max_n, nullptr);
+    if (st != HIST_OK) return st;
+    if (p.need > ws_bytes && p.path != HIST_PATH_SCATTER && p.groups > 1) {
+        // The one-pass paths' workspace is their partial rows, one per input
+        // chunk: take fewer, larger chunks (same kernels, same result).
+        uint32_t g = p.groups;
+        while (g > 1 && partial_bytes(g, p.nblk) > ws_bytes) g = g > 64 ? g - g / 16 : g - 1;
+        if (g >= (uint32_t)p.dev.xcd) g = g / p.dev.xcd * p.dev.xcd;
+        hist_plan_opts_t o{};
+        o.aggregation = -1;
+        o.groups = (int32_t)g;
+        hist_plan_impl q;
+        q.dev = p.dev;
+        st = design(&q, num_bins, max_n, &o);
+        if (st != HIST_OK) return st;
+        p = q;
+    }
+    if (p.need > ws_bytes) return HIST_ERR_WORKSPACE;
+    p.ws = static_cast<char *>(ws);
+    p.ws_bytes = ws_bytes;
+    return run_impl(&p, counts, input, n, num_bins, stream, 0u);
+}
+
+}  // namespace pca_host
 
 extern "C" {
 

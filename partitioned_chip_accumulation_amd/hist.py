@@ -89,6 +89,7 @@ def load(path: str = LIBRARY):
         "hist_plan_create": (i32, [P(vp), u32, u64, P(PlanOpts), vp, u64]),
         "hist_run": (i32, [vp, vp, vp, u64, u32, vp]),
         "hist_run_accumulate": (i32, [vp, vp, vp, u64, u32, vp]),
+        "hist_run_static": (i32, [vp, vp, u64, u32, vp]),
         "hist_plan_info": (i32, [vp, P(PlanInfo)]),
         "hist_plan_preview": (i32, [P(DeviceDesc), u32, u64, P(PlanOpts), P(PlanInfo)]),
         "hist_plan_describe": (i32, [vp, ctypes.c_char_p, u64]),
@@ -351,6 +352,28 @@ def run(input: torch.Tensor, num_bins: int, out: torch.Tensor | None = None,
     if plan is None:
         plan = _cache[key] = Plan(num_bins, max_n, device=input.device, **opts)
     return plan.run(input, out=out, accumulate=accumulate)
+
+
+STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def run_static(input: torch.Tensor, num_bins: int, out: torch.Tensor) -> torch.Tensor:
+    """hist_run_static: the histogram with no device allocation (its
+    workspace is a device array the library holds), on the current stream.
+    ``out`` is required (a contiguous 4-byte tensor of num_bins on the input's
+    device), since allocating it here would defeat the point. Calls that
+    overlap on one device race on the shared array."""
+    if input.dtype != torch.int32 or not input.is_cuda or not input.is_contiguous():
+        raise ValueError("input must be a contiguous int32 CUDA tensor")
+    if out.device != input.device or out.numel() != num_bins or out.element_size() != 4 or \
+            not out.is_contiguous():
+        raise ValueError("out must be a contiguous 4-byte tensor of num_bins on the device")
+    n = input.numel()
+    with torch.cuda.device(input.device):
+        _check(library().hist_run_static(out.data_ptr(), input.data_ptr() if n else None, n,
+                                         int(num_bins), _stream_handle(input.device)),
+               "hist_run_static")
+    return out.view(torch.uint32) if out.dtype == torch.int32 else out
 
 
 # Measurement-only kernels (include/hist_bench.h).

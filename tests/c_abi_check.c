@@ -49,6 +49,11 @@ int main(void)
     expect("plan_create(NULL)", hist_plan_create(NULL, 10, 10, NULL, NULL, 0),
            HIST_ERR_INVALID_ARG);
     expect("run(NULL)", hist_run(NULL, NULL, NULL, 0, 1, NULL), HIST_ERR_INVALID_ARG);
+    expect("run_static(NULL)", hist_run_static(NULL, NULL, 0, 1, NULL), HIST_ERR_INVALID_ARG);
+    expect("run_static(num_bins=0)", hist_run_static((uint32_t *)16, NULL, 0, 0, NULL),
+           HIST_ERR_INVALID_ARG);
+    expect("run_static(input=NULL, n=5)", hist_run_static((uint32_t *)16, NULL, 5, 8, NULL),
+           HIST_ERR_INVALID_ARG);
     expect("run_accumulate(NULL)", hist_run_accumulate(NULL, NULL, NULL, 0, 1, NULL),
            HIST_ERR_INVALID_ARG);
     expect("plan_info(NULL)", hist_plan_info(NULL, &info), HIST_ERR_INVALID_ARG);

@@ -72,6 +72,9 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_plan_create(ctypes.byref(p), 0, 10, None, None, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_create(ctypes.byref(p), 10, 10, None, 3, 0) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_run(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_run_static(None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_run_static(16, None, 5, 8, None) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_run_static(16, None, 0, 0, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_run_accumulate(None, None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_plan_info(None, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_tune_workspace_size(10, 10, None) == hist.HIST_ERR_INVALID_ARG
