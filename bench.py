@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--counter-bits", type=int, default=0)
     ap.add_argument("--lds-copies", type=int, default=0,
                     help="interleaved LDS copies for 32-bit counters (0 = the plan's choice)")
+    ap.add_argument("--pacing", type=int, default=0,
+                    help="RANGE owners' reads: 1 non-temporal, 2 plain, 3.. plain and paced "
+                         "within (pacing - 2) batches (0 = the plan's choice)")
     ap.add_argument("--copies", type=int, default=4, help="input copies used in rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline work (0 = skip)")
@@ -191,6 +194,27 @@ def calibrate(args):
             print(json.dumps({"what": "lds_atomic", "pattern": pattern, "with_return": rtn,
                               "ns_per_wave_instr_per_cu": round(per_instr * 1e9, 3),
                               "cycles_at_2p4GHz": round(per_instr * 2.4e9, 2)}), flush=True)
+    # LDS latency: dependent chains of one wave (each address waits for the
+    # previous return).
+    for pattern in hist.LDS_LATENCY_PATTERNS:
+        r = hist.lds_latency(pattern, 1 << 16, dev)
+        print(json.dumps({"what": "lds_latency", "pattern": pattern,
+                          "cycles_per_op": round(r["cycles_per_op"], 2),
+                          "ns_per_op": round(r["ns_per_op"], 3),
+                          "clock_ghz": round(r["clock_ghz"], 3) if r["clock_ghz"] else None}),
+              flush=True)
+    # Handoff between two workgroups through global memory, on one XCD (partner
+    # 8: workgroups are dealt to the 8 XCDs in turn) and across XCDs (partner 1).
+    for mode in (0, 1):
+        for partner in (8, 1):
+            hist.handoff(partner, mode, 64, dev)  # warm-up
+            r = hist.handoff(partner, mode, 4096, dev)
+            print(json.dumps({"what": "handoff", "mode": ["token", "payload+release/acquire"][mode],
+                              "partner": partner, "same_xcd": r["xcd_wg0"] == r["xcd_partner"],
+                              "round_trip_cycles": round(r["round_trip_cycles"], 1),
+                              "round_trip_ns": round(r["round_trip_ns"], 1),
+                              "timed_out": r["timed_out"], "payload_errors": r["payload_errors"],
+                              "xcds": r["xcds"]}), flush=True)
     # Shared L2: RANGE with the R owners of a chunk on one XCD vs in plain order.
     n, B = 1 << 26, 1 << 17
     x = torch.from_numpy(inputs.uniform(1, n, B)).to(dev)
@@ -544,7 +568,8 @@ def main():
     else:
         plan_opts = dict(path=args.path, groups=args.groups, range_bins=args.range_bins,
                          aggregation=args.agg, wg_size=args.wg, xcd_map=args.xcd_map,
-                         counter_bits=args.counter_bits, lds_copies=args.lds_copies)
+                         counter_bits=args.counter_bits, lds_copies=args.lds_copies,
+                         pacing=args.pacing)
     # One plan (and workspace) and one output per stream: the steps on different
     # streams are independent histograms, so they may overlap on the device.
     nstreams = max(1, args.streams)

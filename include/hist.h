@@ -99,6 +99,14 @@ typedef struct {
                              slice (1, 2, 4, 8, 16; 0 = one); a lane adds to copy lane mod
                              copies, which spreads same-bin lanes of a wave over words and
                              banks at the cost of clearing and summing the copies */
+    int32_t pacing;       /* RANGE with R > 1, 1024-thread workgroups and 16- or 8-bit
+                             counters, how the R owners of a chunk read it: 0 auto, 1
+                             non-temporal loads, each owner at its own pace; 2 plain loads,
+                             own pace; 3..18 plain loads, each owner kept within (pacing - 2)
+                             batches of the next range's owner by a pacer wave, so that the
+                             lines one owner brings into the XCD's L2 serve the other
+                             (bounded waits: an owner whose partner does not move stops
+                             pacing); 2 and above count with 15 of the 16 waves */
 } hist_plan_opts_t;
 
 /* Numeric description of a plan (for logs and benchmarks). */

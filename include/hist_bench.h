@@ -53,6 +53,44 @@ hist_status_t hist_bench_copy(void *dst, const void *src, uint64_t bytes, hipStr
 hist_status_t hist_bench_lds_atomic(uint32_t pattern, uint32_t with_return, uint32_t iters,
                                    uint32_t *sink, uint32_t sink_words, hipStream_t stream);
 
+/* LDS latency (the dependent-access probe of the CREDIT page, "CREDIT:
+ * Cost-guided Reduction-reuse with Efficient DSMEM Inter-CTA Tiling", its
+ * microbenchmark section: each access waits for the one before). One wave
+ * on one CU runs a chain of iters LDS operations, each address depending on
+ * the previous operation's returned value:
+ *   0  ds_add_rtn_u32 from lane 0 alone
+ *   1  ds_add_rtn_u32 from 64 lanes on 64 consecutive words
+ *   2  ds_add_rtn_u32 from 64 lanes on one word
+ *   3  ds_read_b32 from 64 lanes on consecutive words (load latency)
+ * out (device, >= 3 uint64) receives the shader-clock cycles (s_memtime)
+ * over the chain, the ticks of the 100 MHz real-time counter over it, and a
+ * word that keeps the chain live. iters 1 .. 2^24. */
+hist_status_t hist_bench_lds_latency(uint32_t pattern, uint32_t iters, uint64_t *out,
+                                     hipStream_t stream);
+
+/* Handoff latency between two workgroups through global memory: the gfx950
+ * counterpart of the ping-pong of the page "Hopper DSMEM vs HBM" (its
+ * latency test passes a token between two blocks of a cluster and, for
+ * comparison, through global memory). Sixteen one-wave workgroups are
+ * launched cooperatively (all resident at once); workgroup 0 and workgroup
+ * `partner` (1..15) pass a token back and forth iters times, one round trip
+ * per iteration, and every workgroup records the XCD it ran on (workgroups
+ * are dealt to the XCDs in turn, so partner 8 normally shares workgroup 0's
+ * XCD and its L2, and partner 1 does not; the recorded ids say where they
+ * ran).
+ *   mode 0  the token alone: relaxed device-scope atomic store and load
+ *   mode 1  a 256-byte payload stored with plain stores before each token,
+ *           the token a release store read with acquire loads; the receiver
+ *           checks the payload
+ * Every wait gives up after 2^22 polls, so the kernel always ends.
+ * flags: device, >= 80 uint32 (zeroed by the call). out: device, >= 20
+ * uint64: [0] shader-clock cycles over the iterations, [1] 100 MHz ticks,
+ * [2] 1 if a wait gave up, [3] payload words that arrived wrong, [4 + b] the
+ * XCD of workgroup b. iters 1 .. 2^20. UNSUPPORTED if the device cannot
+ * launch cooperatively. */
+hist_status_t hist_bench_handoff(uint32_t partner, uint32_t mode, uint32_t iters, uint32_t *flags,
+                                 uint64_t *out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -125,6 +126,8 @@ struct hist_plan_impl {
     uint32_t cw = 32;    // LDS counter bits
     uint32_t kshift = 0; // 2^kshift interleaved LDS copies (32-bit counters)
     uint32_t ev_cap = 0; // carry-event list entries (8-bit counters)
+    uint32_t pacing = 1; // RANGE: 1 non-temporal loads, 2 plain loads, >= 3 paced (window - 2)
+    uint64_t off_progress = 0;  // RANGE paced: [G][R][16] progress words
     uint64_t max_elems_wg = 1ull << 40;  // elements one sweep workgroup may count
     uint32_t nblk = 0;       // 256-bin blocks per partial row
     uint32_t part_rows = 0;  // partial rows the workspace holds
@@ -160,6 +163,7 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
     if (o->xcd_map < 0 || o->xcd_map > 2) return HIST_ERR_INVALID_ARG;
     if (o->lds_copies < 0 || o->lds_copies > 16 || (o->lds_copies & (o->lds_copies - 1)) != 0)
         return HIST_ERR_INVALID_ARG;
+    if (o->pacing < 0 || o->pacing > 18) return HIST_ERR_INVALID_ARG;
     return HIST_OK;
 }
 
@@ -314,6 +318,14 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
         p->part_rows = G > 1 ? G : 0;
         p->off_partials = off;
         off += partial_bytes(p->part_rows, p->nblk);
+        // How the R owners of a chunk read it (1024-thread workgroups with packed
+        // counters only: the pacer's LDS words sit in the carry-event block).
+        p->pacing = 1;
+        if (R > 1 && wg == 1024 && cw != 32) p->pacing = opts.pacing > 0 ? (uint32_t)opts.pacing : 1u;
+        if (p->pacing >= 3) {
+            p->off_progress = off;
+            off += align_up((uint64_t)G * R * 4, 256);
+        }
         p->need = off;
     } else {
         const uint32_t S = 1u << kScatterShift;
@@ -405,18 +417,34 @@ struct SweepArgs {
     uint32_t accumulate;
 };
 
+// Epoch of the paced sweeps' progress words: a new one per run, so that words
+// an earlier run left read as "not started".
+std::atomic<uint32_t> g_pace_epoch{0};
+
 template <int WG, int AGG, int CW>
 hipError_t launch_sweep_t(const hist_plan_impl *p, const SweepArgs &a, hipStream_t s, const KEv &ev)
 {
     // Packed counters: 2 vectors (8 returning LDS atomics) per thread per
     // iteration stay within the LDS wait counter; measured 12% faster than 4.
-    auto k = pca::k_sweep<WG, CW == 32 ? 4 : 2, AGG, CW>;
+    constexpr int U = CW == 32 ? 4 : 2;
     const uint32_t bytes = sweep_lds_bytes(CW, p->range_bins, CW == 32 ? p->kshift : 0u, p->ev_cap);
+    pca::Pacing pc{nullptr, 0u, 0u};
+    auto k = pca::k_sweep<WG, U, AGG, CW, false>;
+    if constexpr (WG == 1024 && CW != 32) {
+        if (p->pacing >= 2) {
+            k = pca::k_sweep<WG, U, AGG, CW, true>;
+            if (p->pacing >= 3) {
+                pc.prog = reinterpret_cast<uint32_t *>(p->ws + p->off_progress);
+                pc.epoch = g_pace_epoch.fetch_add(1, std::memory_order_relaxed) & 0xFFFu;
+                pc.window = p->pacing - 2;
+            }
+        }
+    }
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     launch(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, ev, a.in, p->num_bins, p->range_bins,
            p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, p->ev_cap, a.out, a.direct,
-           a.accumulate);
+           a.accumulate, pc);
     return hipGetLastError();
 }
 
@@ -904,6 +932,18 @@ hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins
 
 namespace {
 
+// " pace=..." for a RANGE plan whose owners read other than with
+// non-temporal loads at their own pace (empty otherwise, so that the
+// descriptions of plans that do not pace stay as they were).
+const char *pace_tag(const hist_plan_impl *p)
+{
+    static thread_local char buf[32];
+    if (p->path != HIST_PATH_RANGE || p->pacing <= 1) return "";
+    if (p->pacing == 2) return " pace=plain";
+    std::snprintf(buf, sizeof buf, " pace=%u", p->pacing - 2);
+    return buf;
+}
+
 void fill_info(const hist_plan_impl *p, hist_plan_info_t *info)
 {
     std::memset(info, 0, sizeof(*info));
@@ -935,12 +975,12 @@ hist_status_t hist_plan_describe(const hist_plan_t *p, char *buf, uint64_t len)
     static const char *names[] = {"auto", "full", "range", "scatter"};
     std::snprintf(buf, len,
                   "path=%s bins=%u S=%u R=%u %s=%u cw=%u copies=%u wg=%u agg=%d tile=%u cu=%d xcd=%d "
-                  "lds=%u ws=%llu",
+                  "lds=%u ws=%llu%s",
                   names[p->path], p->num_bins, p->range_bins, p->ranges,
                   p->path == HIST_PATH_SCATTER ? "W" : "G", p->groups,
                   p->path == HIST_PATH_SCATTER ? 32u : p->cw, 1u << p->kshift, p->wg, p->agg,
                   p->path == HIST_PATH_SCATTER ? kScatterTile : 0u, p->dev.cu, p->dev.xcd,
-                  p->dev.lds, (unsigned long long)p->need);
+                  p->dev.lds, (unsigned long long)p->need, pace_tag(p));
     return HIST_OK;
 }
 

@@ -11,6 +11,24 @@
 
 namespace pca {
 
+// Co-owner pacing of the RANGE sweep (see k_sweep): where each workgroup keeps
+// its progress word, the run's epoch (the word's top 12 bits, so that words
+// left by an earlier run read as "not started"), and how many batches a
+// workgroup may run ahead of the next range's owner of its chunk.
+struct Pacing {
+    uint32_t *prog;  // [groups][ranges], or null: plain loads without pacing
+    uint32_t epoch;  // 0 .. 4095
+    uint32_t window; // batches
+};
+constexpr uint32_t kPaceDone = 0xFFFFFu;     // batch field of a workgroup that has finished
+constexpr uint32_t kPaceSpin = 4096;         // LDS polls before a wave stops waiting for good
+constexpr uint32_t kPacerRounds = 1u << 20;  // rounds before the pacer wave gives up
+
+__device__ __forceinline__ uint32_t pace_batch(uint32_t word, uint32_t epoch)
+{
+    return (word >> 20) == epoch ? (word & 0xFFFFFu) : 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Sweep: workgroup (g, r) counts chunk g of the input into bin range r.
 //
@@ -34,11 +52,27 @@ namespace pca {
 // of 256), or straight into direct[] (the output) when there is one chunk;
 // accumulate != 0 adds to direct[] instead of overwriting it. ev_cap is the
 // length of the 8-bit counters' carry-event list.
-template <int WG, int UNROLL, int AGG, int CW>
+//
+// PACE (RANGE, R > 1, packed counters): the owners of a chunk read it with
+// plain loads, and each keeps pace with the next range's owner, which reads
+// the same lines, so that the lines the first reader brings into the XCD's
+// L2 are still there for the second. The last wave of the workgroup does no
+// counting: it is the pacer. It publishes the workgroup's progress (the
+// counting waves' average batch, which they add up in LDS) with relaxed
+// device-scope stores, reads the partner's, and leaves it in LDS, where a
+// counting wave that is more than pc.window batches ahead waits for it
+// (s_sleep between LDS polls). The pacer's stores never hold up a counting
+// wave: a wave's stores and loads share one wait counter, and a store that
+// writes through takes microseconds under the input stream. Every wait is
+// bounded (a counting wave stops waiting after kPaceSpin polls, the pacer
+// after kPacerRounds rounds, e.g. when the partner is not resident). The
+// counts do not depend on any of this: every owner counts what it loads.
+template <int WG, int UNROLL, int AGG, int CW, bool PACE = false>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
                                               uint32_t kshift, uint32_t ev_cap, Partials out,
-                                              uint32_t *__restrict__ direct, uint32_t accumulate)
+                                              uint32_t *__restrict__ direct, uint32_t accumulate,
+                                              Pacing pc)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
@@ -61,20 +95,31 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     const i32x4 *body = reinterpret_cast<const i32x4 *>(in.ptr + in.head);
     const uint64_t v0 = (uint64_t)g * in.nvec / groups;
     const uint64_t v1 = (uint64_t)(g + 1) * in.nvec / groups;
-    constexpr uint32_t STEP = WG * UNROLL;
+    static_assert(!PACE || CW != 32, "pacing keeps its LDS words in the carry-event block");
+    constexpr uint32_t CT = PACE ? WG - 64 : WG;  // counting threads (the rest: the pacer wave)
+    constexpr uint32_t NCW = CT / 64;             // counting waves
+    constexpr uint32_t STEP = CT * UNROLL;
+    constexpr bool NT = !PACE;  // paced owners keep the lines in L2 for each other
+    const bool counter = !PACE || tid < CT;
     uint64_t v = v0;
+
+    // PACE: ev_count[1] sums the counting waves' batches, ev_count[2] holds the
+    // partner's batch (the pacer's copy), ev_count[3] counts finished waves
+    bool pace = false;
+    uint32_t kb = 0;
+    if constexpr (PACE) pace = pc.prog != nullptr && ranges > 1;
 
     // The first batch of loads is in flight while the LDS slice is cleared,
     // and every later batch is requested before the previous one is counted,
     // so each wave keeps 2 * UNROLL vector loads outstanding.
     i32x4 nx[UNROLL];
     const bool any_full = v + STEP <= v1;
-    if (any_full) {
+    if (any_full && counter) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + u * WG + tid);
+        for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<NT>(body + v + u * CT + tid);
     }
     zero_lds<WG>(lds, CW == 32 ? (len << kshift) : CW == 16 ? (len + 1) / 2 : (len + 3) / 4);
-    if (CW != 32 && tid == 0) *ev_count = 0u;
+    if (CW != 32 && tid < (PACE ? 4u : 1u)) ev_count[tid] = 0u;
     __syncthreads();
     // 32-bit counters may keep 2^kshift interleaved copies of the slice; a lane
     // adds to copy (lane mod 2^kshift), so lanes of one wave that hit the same
@@ -124,13 +169,31 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
         s = (uint32_t)q.w - lo; count1(s, ok && s < len);
     };
 
+    if (counter) {
     for (; any_full && v + STEP <= v1; v += STEP) {
+        if constexpr (PACE) {
+            if (pace) {
+                uint32_t spins = 0;
+                while (kb > __hip_atomic_load(ev_count + 2, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_WORKGROUP) + pc.window) {
+                    if (++spins > kPaceSpin) {
+                        pace = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+        }
         i32x4 q[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) q[u] = nx[u];
         if (v + 2 * STEP <= v1) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<true>(body + v + STEP + u * WG + tid);
+            for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<NT>(body + v + STEP + u * CT + tid);
+        }
+        if constexpr (PACE) {
+            if (lane_id() == 0) lds_add(ev_count, 1, 1u);
+            ++kb;
         }
         if constexpr (AGG <= 1) {
             uint32_t sl[4 * UNROLL];
@@ -169,10 +232,13 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
             for (int u = 0; u < UNROLL; ++u) count4(q[u], true);
         }
     }
+    if constexpr (PACE) {
+        if (lane_id() == 0) lds_add(ev_count, 3, 1u);  // this wave is done with the stream
+    }
     // Remainder with a wave-uniform trip count.
-    for (; v < v1; v += WG) {
+    for (; v < v1; v += CT) {
         const bool ok = v + tid < v1;
-        const i32x4 q = ok ? load_vec<true>(body + v + tid) : i32x4{0, 0, 0, 0};
+        const i32x4 q = ok ? load_vec<NT>(body + v + tid) : i32x4{0, 0, 0, 0};
         count4(q, ok);
     }
     {
@@ -182,6 +248,31 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
         const bool tok = g == groups - 1 && tid < in.tail;
         const uint32_t ts = (tok ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid] : 0u) - lo;
         count1(ts, tok && ts < len);
+    }
+    } else if constexpr (PACE) {
+        // The pacer wave: publish this workgroup's progress, fetch the
+        // partner's into LDS, until every counting wave is done (or, bounded,
+        // kPacerRounds rounds: then the counting waves stop waiting).
+        uint32_t *my_prog = pc.prog + (uint64_t)g * ranges + r;
+        const uint32_t *pa_prog = pc.prog + (uint64_t)g * ranges + (r + 1) % ranges;
+        for (uint32_t round = 0; pace; ++round) {
+            const uint32_t done =
+                __hip_atomic_load(ev_count + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t mine =
+                __hip_atomic_load(ev_count + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) / NCW;
+            if (lane_id() == 0)
+                __hip_atomic_store(my_prog, (pc.epoch << 20) | (done == NCW ? kPaceDone : mine),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (done == NCW) break;
+            uint32_t pk = pace_batch((uint32_t)__builtin_amdgcn_readfirstlane((int)__hip_atomic_load(
+                                         pa_prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)),
+                                     pc.epoch);
+            if (round >= kPacerRounds) pk = kPaceDone;  // give up: nobody waits any more
+            if (lane_id() == 0)
+                __hip_atomic_store(ev_count + 2, pk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (pk == kPaceDone) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
     }
     hot_flush();
     __syncthreads();

@@ -38,7 +38,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("groups", ctypes.c_int32),
                 ("range_bins", ctypes.c_int32), ("aggregation", ctypes.c_int32),
                 ("wg_size", ctypes.c_int32), ("xcd_map", ctypes.c_int32),
-                ("counter_bits", ctypes.c_int32), ("lds_copies", ctypes.c_int32)]
+                ("counter_bits", ctypes.c_int32), ("lds_copies", ctypes.c_int32),
+                ("pacing", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -104,6 +105,8 @@ def load(path: str = LIBRARY):
         "hist_bench_read": (i32, [vp, u64, vp, vp]),
         "hist_bench_copy": (i32, [vp, vp, u64, vp]),
         "hist_bench_lds_atomic": (i32, [u32, u32, u32, vp, u32, vp]),
+        "hist_bench_lds_latency": (i32, [u32, u32, vp, vp]),
+        "hist_bench_handoff": (i32, [u32, u32, u32, vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -136,12 +139,12 @@ def _stream_handle(device: torch.device) -> int:
 
 
 def _opts(path="auto", groups=0, range_bins=0, aggregation=-1, wg_size=0, xcd_map=0,
-          counter_bits=0, lds_copies=0) -> PlanOpts:
+          counter_bits=0, lds_copies=0, pacing=0) -> PlanOpts:
     o = PlanOpts()
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.groups, o.range_bins, o.aggregation = int(groups), int(range_bins), int(aggregation)
     o.wg_size, o.xcd_map, o.counter_bits = int(wg_size), int(xcd_map), int(counter_bits)
-    o.lds_copies = int(lds_copies)
+    o.lds_copies, o.pacing = int(lds_copies), int(pacing)
     return o
 
 
@@ -412,3 +415,38 @@ def lds_atomic(pattern: str, with_return: bool, iters: int, sink: torch.Tensor):
                                                sink.data_ptr(), sink.numel(),
                                                _stream_handle(sink.device)),
                "hist_bench_lds_atomic")
+
+
+LDS_LATENCY_PATTERNS = {"rtn-one-lane": 0, "rtn-64-words": 1, "rtn-one-word": 2, "read-64-words": 3}
+
+
+def lds_latency(pattern: str, iters: int, device=None) -> dict:
+    """Run the dependent-chain LDS probe (one wave) and return its cycles and
+    nanoseconds per operation. Blocks until done."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        _check(library().hist_bench_lds_latency(LDS_LATENCY_PATTERNS[pattern], int(iters),
+                                                out.data_ptr(), _stream_handle(dev)),
+               "hist_bench_lds_latency")
+    o = out.cpu().tolist()
+    return {"cycles_per_op": o[0] / iters, "ns_per_op": o[1] * 10.0 / iters,
+            "clock_ghz": o[0] / (o[1] * 10.0) if o[1] else None}
+
+
+def handoff(partner: int, mode: int, iters: int, device=None) -> dict:
+    """Run the two-workgroup ping-pong probe and return the round trip in
+    cycles and nanoseconds, the XCDs the two workgroups ran on, and whether
+    a wait gave up or a payload word arrived wrong. Blocks until done."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    flags = torch.zeros(80, dtype=torch.int32, device=dev)
+    out = torch.zeros(20, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        _check(library().hist_bench_handoff(int(partner), int(mode), int(iters), flags.data_ptr(),
+                                            out.data_ptr(), _stream_handle(dev)),
+               "hist_bench_handoff")
+    o = out.cpu().tolist()
+    return {"round_trip_cycles": o[0] / iters, "round_trip_ns": o[1] * 10.0 / iters,
+            "timed_out": bool(o[2]), "payload_errors": int(o[3]),
+            "xcd_wg0": int(o[4]), "xcd_partner": int(o[4 + partner]),
+            "xcds": [int(v) for v in o[4:20]]}

@@ -188,6 +188,31 @@ def calib_markdown(jsonl: str, cmd: str) -> str:
             form = "ds_add_rtn_u32" if r["with_return"] else "ds_add_u32"
             out.append(f"| {names[r['pattern']]} | {form} | {r['ns_per_wave_instr_per_cu']:.2f} | "
                        f"{r['cycles_at_2p4GHz']:.1f} |")
+    lat = [r for r in recs if r["what"] == "lds_latency"]
+    if lat:
+        out += ["", "## LDS latency (one wave; each access's address waits for the previous "
+                "access's return)", "",
+                "| chain | cycles per access | ns per access | shader clock GHz |",
+                "|---|---:|---:|---:|"]
+        lnames = {"rtn-one-lane": "ds_add_rtn_u32, lane 0 alone",
+                  "rtn-64-words": "ds_add_rtn_u32, 64 lanes on 64 consecutive words",
+                  "rtn-one-word": "ds_add_rtn_u32, 64 lanes on one word",
+                  "read-64-words": "ds_read_b32, 64 lanes on 64 consecutive words"}
+        for r in lat:
+            out.append(f"| {lnames.get(r['pattern'], r['pattern'])} | {r['cycles_per_op']:.1f} | "
+                       f"{r['ns_per_op']:.2f} | {r['clock_ghz']} |")
+    ho = [r for r in recs if r["what"] == "handoff"]
+    if ho:
+        out += ["", "## Handoff between two workgroups through global memory (round trip)", "",
+                "| what passes | workgroups | XCDs (wg 0, partner) | cycles | ns | clean |",
+                "|---|---|---|---:|---:|---|"]
+        for r in ho:
+            where = "one XCD" if r["same_xcd"] else "two XCDs"
+            clean = "yes" if not r["timed_out"] and not r["payload_errors"] else \
+                f"NO (timed out {r['timed_out']}, payload errors {r['payload_errors']})"
+            out.append(f"| {r['mode']} | 0 and {r['partner']} ({where}) | "
+                       f"{r['xcds'][0]}, {r['xcds'][r['partner']]} | {r['round_trip_cycles']:.0f} | "
+                       f"{r['round_trip_ns']:.0f} | {clean} |")
     out += ["", "## Owners of a chunk sharing an XCD's L2 (RANGE path)", "",
             "| placement | bins | n | us per run | plan |", "|---|---:|---:|---:|---|"]
     for r in recs:

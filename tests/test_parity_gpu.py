@@ -255,6 +255,26 @@ def test_zipf_workload_shape_on_8bit_ranges(agg, groups):
           groups=groups, aggregation=agg)
 
 
+@pytest.mark.parametrize("pacing", [1, 2, 3, 4, 10])
+@pytest.mark.parametrize("shape", ["zipf-2^22", "uniform-2-ranges", "many-chunks-3-ranges"])
+def test_range_owner_pacing(pacing, shape):
+    """RANGE with the owners of a chunk reading non-temporally (1), with plain
+    loads (2), or paced against each other within 1, 2 or 8 batches (3, 4,
+    10). The counts must not depend on it: every owner counts what it loads.
+    Three ranges pace in a ring; 1,024 chunks put co-owners in different
+    rounds of resident workgroups, so some waits give up. Values outside the
+    bins (negative ones here) are skipped as always."""
+    if shape == "zipf-2^22":
+        x, bins, opts = inputs.generate(3, n=1 << 22), 262_144, {"counter_bits": 8, "groups": 16}
+    elif shape == "uniform-2-ranges":
+        x, bins, opts = rnd(31, (1 << 22) + 5, -3, 300_000), 300_000, {"counter_bits": 8,
+                                                                        "groups": 8}
+    else:
+        x, bins, opts = rnd(32, 1 << 23, 0, 200_000), 200_000, {"counter_bits": 16,
+                                                                 "groups": 1024}
+    check(x, bins, f"pacing{pacing}-{shape}", path="range", pacing=pacing, **opts)
+
+
 @pytest.mark.parametrize("case,bins", [("one-bin-at-the-limit", 155_392),
                                        ("one-bin-at-the-limit", 100_000),
                                        ("one-bin-past-the-limit", 155_392),
