@@ -91,6 +91,10 @@ def parse():
                     help="skip the `workloads` record (the four other workloads at full size)")
     ap.add_argument("--tune", action="store_true",
                     help="time every schedule on the input first (hist_tune) and bench the fastest")
+    ap.add_argument("--select", action="store_true",
+                    help="predict every schedule on the input with the cost model (hist_select: a "
+                         "sample and one stream read, no schedule run) and bench the predicted "
+                         "fastest")
     ap.add_argument("--comparators", action="store_true",
                     help="also time the global-atomic fallback and the stream-read ceiling")
     ap.add_argument("--path-sweep", action="store_true",
@@ -215,6 +219,89 @@ def calibrate(args):
                               "round_trip_ns": round(r["round_trip_ns"], 1),
                               "timed_out": r["timed_out"], "payload_errors": r["payload_errors"],
                               "xcds": r["xcds"]}), flush=True)
+    # Primitives of the cost model (hist_predict): a launch, a sweep's fixed cost,
+    # one 8-bit carry event, the two-phase path's fixed cost. Each comes from the
+    # library's own kernels on synthetic input that isolates one cost, timed on
+    # the device with the events the plan attaches to its kernels (the host's
+    # per-call overhead would hide short kernels).
+    import numpy as np
+
+    def kernel_us(plan, xt, out, reps, phase=None):
+        """Average device time per call: one phase, or all phases summed."""
+        for _ in range(3):
+            plan.run(xt, out)
+        torch.cuda.synchronize(dev)
+        plan.timing_enable(reps)
+        for _ in range(reps):
+            plan.run(xt, out)
+        ph = plan.timing_read()
+        plan.timing_enable(0)
+        if phase is not None:
+            ms, cnt = ph[phase]
+            return ms / cnt * 1e3
+        return sum(ms / cnt for ms, cnt in ph.values()) * 1e3
+
+    empty = torch.empty(0, dtype=torch.int32, device=dev)
+    o256 = torch.empty(256, dtype=torch.int32, device=dev)
+    plan = hist.Plan(256, 1, device=dev)
+    t = kernel_us(plan, empty, o256, 200, "sweep")
+    plan.close()
+    print(json.dumps({"what": "model_primitive", "name": "launch_us", "value": round(t, 3),
+                      "how": "device time of the one kernel of a hist_run with n = 0"}), flush=True)
+    # a sweep's fixed cost: the intercept of one plan's sweep time at n and 2n
+    o64k = torch.empty(65536, dtype=torch.int32, device=dev)
+    plan = hist.Plan(65536, 1 << 25, device=dev, path="full", counter_bits=16)
+    x1 = torch.from_numpy(inputs.uniform(7, 1 << 25, 65536)).to(dev)
+    t1 = kernel_us(plan, x1[:1 << 24], o64k, 50, "sweep")
+    t2 = kernel_us(plan, x1, o64k, 50, "sweep")
+    print(json.dumps({"what": "model_primitive", "name": "sweep_fixed_us",
+                      "value": round(2 * t1 - t2, 3), "t_2p24_us": round(t1, 2),
+                      "t_2p25_us": round(t2, 2), "plan": plan.describe(),
+                      "how": "FULL 16-bit sweep of 2^24 and 2^25 uniform elements over 65,536 "
+                             "bins, 256 chunks: 2 T(n) - T(2n)"}), flush=True)
+    plan.close()
+    del x1
+    # carry events: uniform over 2,048 bins, 2^28 elements in 512 chunks (the
+    # 8-bit event list's bound allows at most 560,490 elements a chunk here), so
+    # a bin takes about 256 adds a chunk and half the bins wrap their byte once;
+    # the 16-bit plan with the same chunks has no events
+    ne, be, ge = 1 << 28, 2048, 512
+    xe_host = inputs.uniform(8, ne, be)
+    xe = torch.from_numpy(xe_host).to(dev)
+    oe = torch.empty(be, dtype=torch.int32, device=dev)
+    p8 = hist.Plan(be, ne, device=dev, path="full", counter_bits=8, groups=ge)
+    p16 = hist.Plan(be, ne, device=dev, path="full", counter_bits=16, groups=ge)
+    assert p8.info().groups == ge and p16.info().groups == ge
+    t8, t16 = kernel_us(p8, xe, oe, 10, "sweep"), kernel_us(p16, xe, oe, 10, "sweep")
+    nvec = ne // 4
+    events = 0
+    for g in range(ge):  # chunk g holds body vectors [g nvec / G, (g + 1) nvec / G)
+        lo, hi = (g * nvec // ge) * 4, ((g + 1) * nvec // ge) * 4
+        events += int((np.bincount(xe_host[lo:hi], minlength=be) // 256).sum())
+    print(json.dumps({"what": "model_primitive", "name": "event_cycles",
+                      "value": round((t8 - t16) * 1e-6 * cu * 2.4e9 / events, 2),
+                      "t8_us": round(t8, 2), "t16_us": round(t16, 2), "events": events,
+                      "plan8": p8.describe(), "plan16": p16.describe(),
+                      "how": "sweep time of FULL 8-bit minus FULL 16-bit on 2^28 uniform elements "
+                             "over 2,048 bins in 512 chunks, per carry event, in cycles of every "
+                             "CU at 2.4 GHz"}), flush=True)
+    p8.close()
+    p16.close()
+    del xe, xe_host
+    # the two-phase path's fixed cost: the intercept of its summed phases at n and 2n
+    o1m = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+    x3 = torch.from_numpy(inputs.uniform(9, 1 << 23, 1 << 20)).to(dev)
+    plan = hist.Plan(1 << 20, 1 << 23, device=dev, path="scatter", aggregation=0)
+    t1 = kernel_us(plan, x3[:1 << 22], o1m, 50)
+    t2 = kernel_us(plan, x3, o1m, 50)
+    print(json.dumps({"what": "model_primitive", "name": "scatter_fixed_us",
+                      "value": round(2 * t1 - t2, 3), "t_2p22_us": round(t1, 2),
+                      "t_2p23_us": round(t2, 2), "plan": plan.describe(),
+                      "how": "two-phase path on 2^22 and 2^23 uniform elements over 2^20 bins, "
+                             "its phases summed: 2 T(n) - T(2n)"}), flush=True)
+    plan.close()
+    del x3, o1m
+    torch.cuda.empty_cache()
     # Shared L2: RANGE with the R owners of a chunk on one XCD vs in plain order.
     n, B = 1 << 26, 1 << 17
     x = torch.from_numpy(inputs.uniform(1, n, B)).to(dev)
@@ -557,7 +644,16 @@ def main():
     out = torch.empty(B, dtype=torch.int32, device=dev)
 
     tuned = None
-    if args.tune:
+    selected = None
+    if args.select:
+        # predicted schedule choice on this input, before and outside the timed region
+        t0 = time.perf_counter()
+        best, rows = hist.select(xs[0], B)
+        selected = {"opts": best, "seconds": round(time.perf_counter() - t0, 4),
+                    "predicted_us": {r["schedule"]: round(r["predicted_us"], 1)
+                                     for r in rows if r["status"] == hist.HIST_OK}}
+        plan_opts = best
+    elif args.tune:
         # measured schedule choice on this input, before and outside the timed region
         best, rows = hist.tune(xs[0], B, max_n=n, reps=3)
         tuned = {"opts": best, "candidates_ms": {
@@ -672,7 +768,7 @@ def main():
     # bit (after the headline, so that nothing runs between its regions).
     workloads = None
     if not args.no_workloads and args.config == 2 and args.n is None and not args.uniform_bins \
-            and nstreams == 1 and not args.tune:
+            and nstreams == 1 and not args.tune and not args.select:
         workloads = {}
         for cfg in (1, 3, 4, 5):
             wk = inputs.WORKLOADS[cfg]
@@ -730,7 +826,8 @@ def main():
         "config": {"workload": f"{w.name}: {w.recipe}; n={n}, {B} uint32 bins",
                    "n": n, "num_bins": B, "plan": plan.describe(),
                    "input_copies": len(xs), "streams": nstreams,
-                   **({"tuned": tuned} if tuned else {})},
+                   **({"tuned": tuned} if tuned else {}),
+                   **({"selected": selected} if selected else {})},
         "phases_ms_per_step": {k: round(v[0] / v[1], 5) for k, v in phases.items()},
         "ms_per_step_with_events": round(elapsed_events / args.steps * 1e3, 5),
         "step_us_event_bracketed": step_us,

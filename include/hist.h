@@ -296,6 +296,92 @@ hist_status_t hist_tune(uint32_t num_bins, uint64_t max_n, const int32_t *input,
                         uint32_t reps, hipStream_t stream, hist_plan_opts_t *best,
                         hist_tune_entry_t *entries, uint32_t capacity, uint32_t *count);
 
+/* Predicted schedule choice: a cost model, not a measurement.
+ *
+ * The cost-guided selection of "CREDIT: Cost-guided Reduction-reuse with
+ * Efficient DSMEM Inter-CTA Tiling" (its cost model section, Eq. 7-9)
+ * predicts whether a schedule pays at a given shape from one baseline timing
+ * at that shape, primitive rates measured once per device, and a static
+ * account of each schedule's traffic, without timing the schedules. Here:
+ *   - the baseline is a stream read of the caller's input: its achieved rate
+ *     prices every pass over the input (Eq. 7 replaces a device peak with the
+ *     rate achieved at the same shape);
+ *   - the primitives (hist_model_calib_t) come from the library's probes:
+ *     copy rate, LDS atomics per wave instruction on random words and the
+ *     surcharge per same-word lane, one launch, a sweep's fixed cost, one
+ *     8-bit carry event, the two-phase path's fixed cost;
+ *   - the traffic: FULL and RANGE read the input once per owned range (each
+ *     pass priced as a full read: cache hits between a chunk's owners are
+ *     not credited) and merge G partial rows; SCATTER reads the input,
+ *     writes and reads back 2-byte slots;
+ *   - a sample of the input gives what the data decides: same-word lanes per
+ *     LDS instruction, expected carry events of packed counters at the
+ *     plan's chunk size, and the hot value the wave hot slot takes.
+ * A schedule's time is its fixed costs + max(passes, LDS atomics) + carry
+ * events + merge.
+ *
+ * Candidates, in their order of preference on equal predictions: FULL with
+ * 16-, 8- and 32-bit counters; RANGE with 8-, 16- and 32-bit counters (2,048
+ * bins and up); SCATTER with the hot slot, then without. */
+#define HIST_MODEL_MAX_ENTRIES 8
+
+typedef struct {
+    double read_gbps;        /* HBM stream read, GB/s (hist_select replaces it with the rate
+                                measured on the caller's input) */
+    double copy_gbps;        /* copy, read + write bytes per second / 1e9 */
+    double clock_ghz;        /* shader clock */
+    double lds_cycles;       /* one wave instruction of LDS atomics on random words, cycles
+                                of one CU */
+    double lds_dup_cycles;   /* added per lane that shares its word with another lane */
+    double launch_us;        /* one kernel launch */
+    double sweep_fixed_us;   /* a sweep beyond its pass over the input: LDS clear, flush, ramp */
+    double event_cycles;     /* one 8-bit carry event, logged and applied, cycles of one CU */
+    double scatter_fixed_us; /* the two-phase path beyond its passes: scans, merge, launches */
+} hist_model_calib_t;
+
+typedef struct {
+    hist_plan_opts_t opts; /* path, counter_bits, aggregation (the rest 0) */
+    double predicted_us;   /* -1 when the bin count does not allow the schedule */
+    double pass_us;        /* passes over the input and the staged slots */
+    double lds_us;         /* LDS atomics */
+    double events_us;      /* 8-bit carry events */
+    double fixed_us;       /* fixed costs and the merge of partial rows */
+    int32_t status;        /* HIST_OK, or HIST_ERR_UNSUPPORTED */
+    int32_t reserved;
+} hist_prediction_t;
+
+/* The primitives as the library's probes measured them on an MI355X
+ * (bench.py --calibrate). */
+hist_status_t hist_model_calibration(hist_model_calib_t *cal);
+
+/* Predict every candidate schedule's time for a histogram of num_bins bins
+ * over n elements on the described device (host only, no device needed).
+ * cal: the primitives (NULL: hist_model_calibration's). sample: host
+ * int32[sample_n], elements of the input in no particular order (a few
+ * thousand to 2^16; sample_n 0 treats the input as uniform and in range).
+ * Writes the fastest predicted candidate's options to *best and the
+ * candidates to entries[0..*count) (at most capacity; entries and count may
+ * be NULL when capacity is 0). Errors: INVALID_ARG for null dev or best,
+ * num_bins == 0, n == 0 or n >= 2^32, a null sample with sample_n > 0, bad
+ * calibration figures; UNSUPPORTED for num_bins > HIST_MAX_BINS. */
+hist_status_t hist_predict(const hist_device_desc_t *dev, const hist_model_calib_t *cal,
+                           uint32_t num_bins, uint64_t n, const int32_t *sample, uint32_t sample_n,
+                           hist_plan_opts_t *best, hist_prediction_t *entries, uint32_t capacity,
+                           uint32_t *count);
+
+/* hist_predict on the current device for the caller's device input: takes a
+ * sample of up to 64 runs of 1,024 elements at evenly spaced places, times
+ * one stream read of the input (the baseline), and predicts. workspace:
+ * device memory of at least HIST_SELECT_WORKSPACE_BYTES, 256-byte aligned
+ * (overwritten). Synchronous. No schedule is run. Errors: as hist_predict,
+ * WORKSPACE for a missing or small workspace, UNSUPPORTED when the current
+ * device is not gfx950, HIP when a launch or copy fails. */
+#define HIST_SELECT_WORKSPACE_BYTES (64u * 1024u * 4u + 16384u)
+hist_status_t hist_select(uint32_t num_bins, const int32_t *input, uint64_t n,
+                          const hist_model_calib_t *cal, void *workspace, uint64_t workspace_bytes,
+                          hipStream_t stream, hist_plan_opts_t *best, hist_prediction_t *entries,
+                          uint32_t capacity, uint32_t *count);
+
 /* Write a one-line description ("path=range R=2 S=32768 G=128 ...") into
  * buf (always NUL-terminated when len > 0). */
 hist_status_t hist_plan_describe(const hist_plan_t *plan, char *buf, uint64_t len);

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libpca_hist.so")
-SOURCES = ["hist_api.hip", "hist_bench.hip", "hist_tune.hip", "hist_static.hip"]
+SOURCES = ["hist_api.hip", "hist_bench.hip", "hist_tune.hip", "hist_static.hip",
+           "hist_model.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

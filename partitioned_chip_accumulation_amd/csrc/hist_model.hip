@@ -1,0 +1,349 @@
+// hist_model.hip -- the cost model of the histogram's schedules, and the
+// selection that uses it (declared in hist.h).
+//
+// The model follows the cost-guided selection of "CREDIT: Cost-guided
+// Reduction-reuse with Efficient DSMEM Inter-CTA Tiling" (its cost model
+// section): the time of a schedule is predicted, not measured, from
+//   - one baseline timing at the caller's own shape: a stream read of the
+//     input, whose achieved rate replaces the device's peak bandwidth (Eq. 7);
+//   - primitive rates measured once per device by the library's probes (LDS
+//     atomics by address pattern, a launch, a sweep's fixed cost, one 8-bit
+//     carry event, the two-phase path's fixed cost);
+//   - static analysis of each schedule: how many times it passes over the
+//     input, what it stages, how many partial rows it merges;
+//   - a sample of the input for what the data decides: duplicate lanes per
+//     LDS instruction (same-word contention), carry events of packed
+//     counters, and the hot value the wave hot slot would take.
+// Nothing is fitted to timings of the schedules themselves.
+#include "hist.h"
+#include "hist_bench.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+// The MI355X figures of the primitives, from the library's probes
+// (bench.py --calibrate): HBM stream read and copy, LDS atomics on random
+// words and in groups of same-word lanes, one launch, a one-chunk sweep, one
+// 8-bit carry event, the two-phase path on a tiny input.
+const hist_model_calib_t kMi355x = {
+    5876.0,  // read_gbps
+    4739.0,  // copy_gbps (read + write bytes)
+    2.4,     // clock_ghz
+    7.3,     // lds_cycles: one wave instruction of LDS atomics on random words, per CU
+    0.407,   // lds_dup_cycles: (30.1 - 7.3) / 56, eight groups of eight same-word lanes
+    4.3,     // launch_us: device time of one fill kernel
+    6.1,     // sweep_fixed_us: 2 T(2^24) - T(2^25), FULL 16-bit over 65,536 bins
+    95.0,    // event_cycles: FULL 8-bit minus 16-bit, 2^28 elements over 2,048 bins
+    42.8,    // scatter_fixed_us: 2 T(2^22) - T(2^23), two-phase over 2^20 bins
+};
+
+// What a sample of the input says, for every schedule.
+struct SampleStats {
+    uint64_t total = 0;            // sample elements
+    uint64_t valid = 0;            // of them in [0, num_bins)
+    std::vector<uint32_t> counts;  // counts of the distinct valid values
+    double dups[3] = {0, 0, 0};    // same-word lanes per LDS instruction, 1/2/4 bins per word
+    double hot_frac = 0;           // share of the valid elements the wave hot slot counts in
+                                   // registers (its value's copies), 0 if it would not latch
+    double dups_hot = 0;           // same-word lanes per instruction of 32-bit words, without
+                                   // the hot value's lanes
+};
+
+// Whether the wave hot slot takes a value that a share p of the elements
+// hold: a check (every 4th vector, first lane's value) latches it when at
+// least 8 of the 64 lanes hold it. Latched within a few checks when that has
+// a chance of 1 in 16 or more.
+bool hot_slot_latches(double p)
+{
+    double tail = 0, term = std::pow(1.0 - p, 64);  // P(Binomial(64, p) = 0)
+    for (int k = 0; k < 64; ++k) {
+        if (k >= 8) tail += term;
+        term *= (64.0 - k) / (k + 1.0) * p / (1.0 - p);
+    }
+    tail += term;
+    return p > 0 && p < 1 ? tail >= 1.0 / 16 : p >= 1;
+}
+
+SampleStats sample_stats(const int32_t *s, uint32_t sn, uint32_t num_bins)
+{
+    SampleStats st;
+    st.total = sn;
+    std::vector<uint32_t> v;
+    v.reserve(sn);
+    for (uint32_t i = 0; i < sn; ++i)
+        if ((uint32_t)s[i] < num_bins) v.push_back((uint32_t)s[i]);
+    st.valid = v.size();
+    // the most frequent value, and whether the hot slot would take it
+    std::vector<uint32_t> sorted(v);
+    std::sort(sorted.begin(), sorted.end());
+    uint32_t hot = 0, hot_n = 0;
+    for (size_t i = 0; i < sorted.size();) {
+        size_t j = i;
+        while (j < sorted.size() && sorted[j] == sorted[i]) ++j;
+        st.counts.push_back((uint32_t)(j - i));
+        if (j - i > hot_n) {
+            hot_n = (uint32_t)(j - i);
+            hot = sorted[i];
+        }
+        i = j;
+    }
+    const bool latched = st.valid && hot_slot_latches((double)hot_n / (double)st.valid);
+    if (latched) st.hot_frac = (double)hot_n / (double)st.valid;
+    // one wave instruction: 64 consecutive elements (the inputs are in no
+    // particular order, so any 64 are like the kernels' 64 lanes)
+    const uint32_t groups = std::min<uint32_t>((uint32_t)(v.size() / 64), 1024);
+    uint32_t w[64];
+    for (uint32_t g = 0; g < groups; ++g) {
+        const uint32_t *row = v.data() + (size_t)g * 64;
+        for (int k = 0; k < 3; ++k) {
+            for (int i = 0; i < 64; ++i) w[i] = row[i] >> k;
+            std::sort(w, w + 64);
+            st.dups[k] += (double)(64 - (std::unique(w, w + 64) - w));
+        }
+        int m = 0;
+        for (int i = 0; i < 64; ++i)
+            if (!latched || row[i] != hot) w[m++] = row[i];
+        std::sort(w, w + m);
+        st.dups_hot += (double)(m - (std::unique(w, w + m) - w));
+    }
+    if (groups) {
+        for (double &d : st.dups) d /= groups;
+        st.dups_hot /= groups;
+    }
+    return st;
+}
+
+// Expected carries out of packed counters of `unit` values (256 for 8-bit)
+// over one chunk of m elements: a bin that receives c adds in a chunk wraps
+// floor(c / unit) times from zero.
+double chunk_events(const SampleStats &st, double m, double unit)
+{
+    if (!st.total) return 0;
+    double e = 0;
+    for (uint32_t k : st.counts) e += std::floor((double)k / (double)st.total * m / unit);
+    return e;
+}
+
+struct Candidate {
+    const char *name;
+    int32_t path, counter_bits, aggregation;
+};
+// In order of preference when predictions tie: one pass before several,
+// 16-bit counters (no carry events short of 65,536 counts) before 8-bit ones,
+// the hot slot on the two-phase path (cheap without a hot value, a large
+// saving with one).
+const Candidate kCandidates[] = {
+    {"full16", HIST_PATH_FULL, 16, 0},    {"full8", HIST_PATH_FULL, 8, 0},
+    {"full32", HIST_PATH_FULL, 32, 0},    {"range8", HIST_PATH_RANGE, 8, 0},
+    {"range16", HIST_PATH_RANGE, 16, 0},  {"range32", HIST_PATH_RANGE, 32, 0},
+    {"scatter+hot", HIST_PATH_SCATTER, 32, 1}, {"scatter", HIST_PATH_SCATTER, 32, 0},
+};
+constexpr uint32_t kNumCandidates = sizeof(kCandidates) / sizeof(kCandidates[0]);
+static_assert(kNumCandidates <= HIST_MODEL_MAX_ENTRIES, "entries");
+
+// One schedule's predicted time (microseconds) and its terms.
+void predict_one(const hist_device_desc_t &dev, const hist_model_calib_t &c, const SampleStats &st,
+                 uint32_t num_bins, uint64_t n, const hist_plan_info_t &info, int32_t aggregation,
+                 hist_prediction_t *e)
+{
+    const double valid = st.total ? (double)st.valid / (double)st.total : 1.0;
+    const double read_us = 4.0 * (double)n / (c.read_gbps * 1e3);  // one pass over the input
+    const double cyc_us = 1.0 / (dev.cu_count * c.clock_ghz * 1e3);  // one cycle of every CU
+    const double instr = valid * (double)n / 64.0;                 // LDS wave instructions
+    if (info.path == HIST_PATH_SCATTER) {
+        // partition: read the input, write 2-byte slots (a copy's rate for the
+        // read and write bytes); owners: read the slots, one 32-bit LDS atomic
+        // per element, the hot slot taking each instruction's hot value
+        const double part = read_us + (2.0 * valid * n + 2.0 * valid * n) / (c.copy_gbps * 1e3);
+        const double slots = 2.0 * valid * (double)n / (c.read_gbps * 1e3);
+        // with the hot slot, the hot value's copies issue no LDS atomic at all
+        const double d = aggregation == 1 ? st.dups_hot : st.dups[0];
+        const double atomics = aggregation == 1 ? instr * (1.0 - st.hot_frac) : instr;
+        const double lds = atomics * (c.lds_cycles + c.lds_dup_cycles * d) * cyc_us;
+        e->pass_us = part + slots;
+        e->lds_us = lds;
+        e->events_us = 0;
+        e->fixed_us = c.scatter_fixed_us;
+        e->predicted_us = c.scatter_fixed_us + part + std::max(slots, lds);
+        return;
+    }
+    const uint32_t cw = info.counter_bits, R = info.ranges, G = info.groups;
+    const int k = cw == 32 ? 0 : cw == 16 ? 1 : 2;  // log2 bins per word
+    // every owner of a chunk reads it (each pass priced as a full read: the
+    // model does not credit cache hits between a chunk's owners, which the
+    // counters show are partial and input-dependent)
+    const double pass = read_us * R;
+    const double lds = instr * (c.lds_cycles + c.lds_dup_cycles * st.dups[k]) * cyc_us;
+    const double m = (double)n / G;
+    const double events = cw == 8 ? chunk_events(st, m, 256.0) * G
+                          : cw == 16 ? chunk_events(st, m, 65536.0) * G : 0.0;
+    const double ev = events * c.event_cycles * cyc_us;
+    // merge: plane 0 (and the planes its counts need) of G partial rows
+    double merge = 0;
+    if (G > 1) {
+        const double per_bin = valid * m / num_bins;
+        const double planes = per_bin < 8 ? 1 : per_bin < 128 ? 2 : per_bin < 32768 ? 4 : 8;
+        const double nblk = std::ceil(num_bins / 256.0);
+        merge = c.launch_us + G * nblk * 128.0 * planes / (c.read_gbps * 1e3);
+    }
+    e->pass_us = pass;
+    e->lds_us = lds;
+    e->events_us = ev;
+    e->fixed_us = c.sweep_fixed_us + merge;
+    e->predicted_us = c.sweep_fixed_us + std::max(pass, lds) + ev + merge;
+}
+
+bool calib_ok(const hist_model_calib_t &c)
+{
+    return c.read_gbps > 0 && c.copy_gbps > 0 && c.clock_ghz > 0 && c.lds_cycles > 0 &&
+           c.lds_dup_cycles >= 0 && c.launch_us >= 0 && c.sweep_fixed_us >= 0 &&
+           c.event_cycles >= 0 && c.scatter_fixed_us >= 0;
+}
+
+// Sample of the input for hist_select: `blocks` runs of 1,024 consecutive
+// elements at evenly spaced starts.
+__global__ void k_gather(const int32_t *__restrict__ in, uint64_t n, uint32_t blocks,
+                         int32_t *__restrict__ out)
+{
+    const uint32_t b = blockIdx.x;
+    const uint64_t span = n / blocks;
+    const uint64_t start = (uint64_t)b * span;
+    for (uint32_t i = threadIdx.x; i < 1024; i += blockDim.x) {
+        const uint64_t j = start + i;
+        out[(size_t)b * 1024 + i] = j < n ? in[j] : -1;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+hist_status_t hist_model_calibration(hist_model_calib_t *cal)
+{
+    if (!cal) return HIST_ERR_INVALID_ARG;
+    *cal = kMi355x;
+    return HIST_OK;
+}
+
+hist_status_t hist_predict(const hist_device_desc_t *dev, const hist_model_calib_t *cal,
+                           uint32_t num_bins, uint64_t n, const int32_t *sample, uint32_t sample_n,
+                           hist_plan_opts_t *best, hist_prediction_t *entries, uint32_t capacity,
+                           uint32_t *count)
+{
+    if (!dev || !best || num_bins == 0 || n == 0 || n > (uint64_t)UINT32_MAX ||
+        (sample_n > 0 && !sample) || (capacity > 0 && (!entries || !count)))
+        return HIST_ERR_INVALID_ARG;
+    if (num_bins > HIST_MAX_BINS) return HIST_ERR_UNSUPPORTED;
+    const hist_model_calib_t c = cal ? *cal : kMi355x;
+    if (!calib_ok(c)) return HIST_ERR_INVALID_ARG;
+    const SampleStats st = sample_stats(sample, sample_n, num_bins);
+    double best_us = 1e300;
+    bool any = false;
+    uint32_t w = 0;
+    for (uint32_t i = 0; i < kNumCandidates; ++i) {
+        const Candidate &cd = kCandidates[i];
+        hist_prediction_t e;
+        std::memset(&e, 0, sizeof e);
+        e.opts.path = cd.path;
+        e.opts.counter_bits = cd.path == HIST_PATH_SCATTER ? 0 : cd.counter_bits;
+        e.opts.aggregation = cd.aggregation;
+        e.predicted_us = -1;
+        hist_plan_info_t info;
+        hist_status_t s = HIST_ERR_UNSUPPORTED;
+        // ranges of fewer than 1,024 bins each are never worth their passes
+        if (cd.path != HIST_PATH_RANGE || num_bins >= 2048)
+            s = hist_plan_preview(dev, num_bins, n, &e.opts, &info);
+        e.status = s;
+        if (s == HIST_OK) {
+            predict_one(*dev, c, st, num_bins, n, info, cd.aggregation, &e);
+            if (e.predicted_us < best_us) {  // strict: ties keep the earlier candidate
+                best_us = e.predicted_us;
+                *best = e.opts;
+                any = true;
+            }
+        } else if (s != HIST_ERR_UNSUPPORTED) {
+            return s;
+        }
+        if (w < capacity) entries[w++] = e;
+    }
+    if (count) *count = w;
+    return any ? HIST_OK : HIST_ERR_UNSUPPORTED;
+}
+
+hist_status_t hist_select(uint32_t num_bins, const int32_t *input, uint64_t n,
+                          const hist_model_calib_t *cal, void *workspace, uint64_t workspace_bytes,
+                          hipStream_t stream, hist_plan_opts_t *best, hist_prediction_t *entries,
+                          uint32_t capacity, uint32_t *count)
+{
+    if (!input || n == 0 || n > (uint64_t)UINT32_MAX || num_bins == 0 || !best ||
+        (capacity > 0 && (!entries || !count)))
+        return HIST_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < HIST_SELECT_WORKSPACE_BYTES) return HIST_ERR_WORKSPACE;
+    if (((uintptr_t)input & 3u) != 0 || ((uintptr_t)workspace & 255u) != 0) return HIST_ERR_INVALID_ARG;
+    int devno = -1;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&devno) != hipSuccess || hipGetDeviceProperties(&prop, devno) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_UNSUPPORTED;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return HIST_ERR_UNSUPPORTED;
+    hist_device_desc_t dev;
+    dev.cu_count = prop.multiProcessorCount;
+    dev.xcd_count = std::max(1, dev.cu_count / 32);
+    int lds = 0;
+    (void)hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, devno);
+    dev.lds_bytes = (uint32_t)std::min(std::max(lds, 65536), 163840);
+    dev.sweep_waves_per_simd = 6;  // the sweep's residency as its registers allow (gfx950)
+
+    // the sample: up to 64 runs of 1,024 elements
+    const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(64, n / 1024));
+    int32_t *dsample = static_cast<int32_t *>(workspace);
+    uint32_t *sink = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + 64 * 1024 * 4);
+    hipLaunchKernelGGL(k_gather, dim3(blocks), dim3(256), 0, stream, input, n, blocks, dsample);
+    if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+    std::vector<int32_t> sample((size_t)blocks * 1024);
+    if (hipMemcpyAsync(sample.data(), dsample, sample.size() * 4, hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_HIP;
+    }
+    // (below 1,024 elements the one run is the whole input, padded with -1)
+    const uint32_t sn = (uint32_t)std::min<uint64_t>(sample.size(), n);
+
+    // the baseline: one stream read of the input's 16-byte aligned body, at its shape
+    hist_model_calib_t c = cal ? *cal : kMi355x;
+    const uintptr_t a0 = (uintptr_t)input, a1 = (a0 + 15u) & ~(uintptr_t)15u;
+    const uint64_t head = (a1 - a0) / 4;
+    const uint64_t nvec = n > head ? (n - head) / 4 : 0;
+    if (nvec >= 4096) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        float ms = 0.f;
+        hist_status_t st = HIST_OK;
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) st = HIST_ERR_HIP;
+        const void *body = reinterpret_cast<const void *>(a1);
+        if (st == HIST_OK) st = hist_bench_read(body, nvec * 16, sink, stream);  // warm-up
+        if (st == HIST_OK && hipEventRecord(e0, stream) != hipSuccess) st = HIST_ERR_HIP;
+        if (st == HIST_OK) st = hist_bench_read(body, nvec * 16, sink, stream);
+        if (st == HIST_OK && (hipEventRecord(e1, stream) != hipSuccess ||
+                              hipEventSynchronize(e1) != hipSuccess ||
+                              hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            st = HIST_ERR_HIP;
+        if (e0) (void)hipEventDestroy(e0);
+        if (e1) (void)hipEventDestroy(e1);
+        if (st != HIST_OK) {
+            (void)hipGetLastError();
+            return st;
+        }
+        if (ms > 0) c.read_gbps = (double)nvec * 16.0 / (ms * 1e-3) / 1e9;
+    }
+    return hist_predict(&dev, &c, num_bins, n, sample.data(), sn, best, entries, capacity, count);
+}
+
+}  // extern "C"

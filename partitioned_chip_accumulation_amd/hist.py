@@ -66,6 +66,25 @@ class TuneEntry(ctypes.Structure):
 TUNE_MAX_ENTRIES = 10
 
 
+class ModelCalib(ctypes.Structure):
+    _fields_ = [("read_gbps", ctypes.c_double), ("copy_gbps", ctypes.c_double),
+                ("clock_ghz", ctypes.c_double), ("lds_cycles", ctypes.c_double),
+                ("lds_dup_cycles", ctypes.c_double), ("launch_us", ctypes.c_double),
+                ("sweep_fixed_us", ctypes.c_double), ("event_cycles", ctypes.c_double),
+                ("scatter_fixed_us", ctypes.c_double)]
+
+
+class Prediction(ctypes.Structure):
+    _fields_ = [("opts", PlanOpts), ("predicted_us", ctypes.c_double), ("pass_us", ctypes.c_double),
+                ("lds_us", ctypes.c_double), ("events_us", ctypes.c_double),
+                ("fixed_us", ctypes.c_double), ("status", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+MODEL_MAX_ENTRIES = 8
+SELECT_WORKSPACE_BYTES = 64 * 1024 * 4 + 16384
+
+
 def mi355x() -> DeviceDesc:
     """MI355X (gfx950) as this library's kernels see it: 256 CUs in 8 XCDs,
     160 KiB of LDS per workgroup, 6 sweep waves per SIMD by registers."""
@@ -97,6 +116,11 @@ def load(path: str = LIBRARY):
         "hist_tune_workspace_size": (i32, [u32, u64, P(u64)]),
         "hist_tune": (i32, [u32, u64, vp, u64, vp, vp, u64, u32, vp, P(PlanOpts), P(TuneEntry),
                             u32, P(u32)]),
+        "hist_model_calibration": (i32, [P(ModelCalib)]),
+        "hist_predict": (i32, [P(DeviceDesc), P(ModelCalib), u32, u64, vp, u32, P(PlanOpts),
+                               P(Prediction), u32, P(u32)]),
+        "hist_select": (i32, [u32, vp, u64, P(ModelCalib), vp, u64, vp, P(PlanOpts),
+                              P(Prediction), u32, P(u32)]),
         "hist_plan_timing_enable": (i32, [vp, u32]),
         "hist_plan_timing_read": (i32, [vp, P(ctypes.c_double), P(u32)]),
         "hist_plan_phase_name": (ctypes.c_char_p, [vp, u32]),
@@ -336,6 +360,68 @@ def tune(input: torch.Tensor, num_bins: int, max_n: int | None = None, reps: int
     rows = [{"opts": _opts_dict(e.opts), "ms": float(e.ms), "status": int(e.status)}
             for e in entries[:count.value]]
     return _opts_dict(best), rows
+
+
+def _schedule_name(o: PlanOpts) -> str:
+    name = PATH_NAMES[o.path]
+    if o.path != PATHS["scatter"]:
+        return f"{name}{o.counter_bits}"
+    return name + ("+hot" if o.aggregation == 1 else "")
+
+
+def _predictions(best: PlanOpts, entries, count: int) -> tuple[dict, list[dict]]:
+    rows = [{"schedule": _schedule_name(e.opts), "opts": _opts_dict(e.opts),
+             "predicted_us": float(e.predicted_us), "pass_us": float(e.pass_us),
+             "lds_us": float(e.lds_us), "events_us": float(e.events_us),
+             "fixed_us": float(e.fixed_us), "status": int(e.status)}
+            for e in entries[:count]]
+    return _opts_dict(best), rows
+
+
+def model_calibration() -> ModelCalib:
+    c = ModelCalib()
+    _check(library().hist_model_calibration(ctypes.byref(c)), "hist_model_calibration")
+    return c
+
+
+def predict(num_bins: int, n: int, sample=None, device: DeviceDesc | None = None,
+            calib: ModelCalib | None = None) -> tuple[dict, list[dict]]:
+    """The cost model's prediction for every candidate schedule (host only).
+    ``sample``: int32 array-like of input elements (or None). Returns the
+    fastest predicted schedule's options and every candidate's terms."""
+    import numpy as np
+    smp = None if sample is None else np.ascontiguousarray(sample, dtype=np.int32)
+    best = PlanOpts()
+    entries = (Prediction * MODEL_MAX_ENTRIES)()
+    count = ctypes.c_uint32(0)
+    _check(library().hist_predict(ctypes.byref(device or mi355x()),
+                                  ctypes.byref(calib) if calib is not None else None,
+                                  int(num_bins), int(n),
+                                  smp.ctypes.data if smp is not None and smp.size else None,
+                                  0 if smp is None else int(smp.size), ctypes.byref(best), entries,
+                                  MODEL_MAX_ENTRIES, ctypes.byref(count)), "hist_predict")
+    return _predictions(best, entries, count.value)
+
+
+def select(input: torch.Tensor, num_bins: int, calib: ModelCalib | None = None,
+           workspace: torch.Tensor | None = None) -> tuple[dict, list[dict]]:
+    """hist_select: sample the device input, time one stream read of it, and
+    predict every schedule (no schedule is run). Blocks until done."""
+    if input.dtype != torch.int32 or not input.is_cuda or not input.is_contiguous():
+        raise ValueError("input must be a contiguous int32 CUDA tensor")
+    with torch.cuda.device(input.device):
+        if workspace is None:
+            workspace = torch.empty(SELECT_WORKSPACE_BYTES, dtype=torch.uint8, device=input.device)
+        best = PlanOpts()
+        entries = (Prediction * MODEL_MAX_ENTRIES)()
+        count = ctypes.c_uint32(0)
+        _check(library().hist_select(int(num_bins), input.data_ptr(), input.numel(),
+                                     ctypes.byref(calib) if calib is not None else None,
+                                     workspace.data_ptr(), workspace.numel(),
+                                     torch.cuda.current_stream().cuda_stream, ctypes.byref(best),
+                                     entries, MODEL_MAX_ENTRIES, ctypes.byref(count)),
+               "hist_select")
+    return _predictions(best, entries, count.value)
 
 
 _cache: dict = {}

@@ -6,6 +6,7 @@
     python -m partitioned_chip_accumulation_amd.profiling matrix FILE.jsonl --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling sweep FILE.jsonl --cmd "..." --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling calib FILE.jsonl --cmd "..." --out FILE.md
+    python -m partitioned_chip_accumulation_amd.profiling model --out FILE.md
     python -m partitioned_chip_accumulation_amd.profiling traffic --fetch DIR --write DIR \
         --kernel k_sweep --calib-kernel k_copy --calib-bytes N --key KEY --sources A B --out FILE.json
 
@@ -257,6 +258,84 @@ def matrix_markdown(jsonl: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def measured_rows(profiles_dir: str) -> dict:
+    """The committed path-selection sweeps and workload matrix as
+    {label: (input kind, bins, n, {schedule: us})} (AUTO's column left out)."""
+    import re
+
+    from partitioned_chip_accumulation_amd import inputs
+    rows = {}
+
+    def read(name, kind_of):
+        hdr = None
+        for line in open(os.path.join(profiles_dir, name)):
+            line = line.rstrip("\n")
+            if line.startswith("| bins") or line.startswith("| workload"):
+                hdr = [c.strip() for c in line.strip("|").split("|")]
+                continue
+            if hdr and line.startswith("| ") and not line.startswith("|---"):
+                cells = [c.strip().replace("**", "") for c in line.strip("|").split("|")]
+                kind, B, n = kind_of(cells[0])
+                rows[f"{name}: {cells[0]}"] = (kind, B, n, {
+                    h: float(c) for h, c in zip(hdr[1:], cells[1:])
+                    if c and "FAIL" not in c and h != "auto"})
+            elif line.startswith("AUTO"):
+                hdr = None
+
+    pow2 = lambda l: 1 << int(re.match(r"2\^(\d+)", l).group(1))
+    read("path_selection_uniform_n2p26.md", lambda l: ("uniform", pow2(l), 1 << 26))
+    read("path_selection_zipf1.1_n2p26.md", lambda l: ("zipf", pow2(l), 1 << 26))
+    cfg = {w.name: c for c, w in inputs.WORKLOADS.items()}
+    read("path_matrix_workloads.md",
+         lambda l: (str(cfg[l]), inputs.WORKLOADS[cfg[l]].num_bins, inputs.WORKLOADS[cfg[l]].n))
+    return rows
+
+
+def model_markdown(profiles_dir: str) -> str:
+    """The cost model's predictions (hist_predict, samples of 2^16 elements
+    from the same generator and seeds) beside the committed measurements."""
+    from partitioned_chip_accumulation_amd import hist, inputs
+
+    def sample(kind, B):
+        if kind == "uniform":
+            return inputs.uniform(1, 1 << 16, B)
+        if kind == "zipf":
+            return inputs.zipf(2, 1 << 16, B, 1.1)
+        return inputs.generate(int(kind), n=1 << 16)
+
+    c = hist.model_calibration()
+    out = ["# The schedule cost model against the measured schedules, one MI355X", "",
+           "`hist_predict` with the library's MI355X primitives (HBM read "
+           f"{c.read_gbps:.0f} GB/s, copy {c.copy_gbps:.0f} GB/s, LDS atomics {c.lds_cycles} cycles "
+           f"a wave instruction + {c.lds_dup_cycles:.3f} per same-word lane, launch "
+           f"{c.launch_us} us, sweep fixed {c.sweep_fixed_us} us, carry event {c.event_cycles} "
+           f"cycles, two-phase fixed {c.scatter_fixed_us} us; `bench.py --calibrate`) on a "
+           "sample of 2^16 elements of each row's input, drawn by the same generator and seed. "
+           "The measured times are the committed path-selection sweeps and workload matrix; no "
+           "schedule was timed to make a prediction, and nothing was fitted to these tables. A "
+           "row is a hit when the schedule predicted fastest (among those the row measured) "
+           "took at most 5% longer than the fastest measured one.", "",
+           "Command:", "", "```",
+           "python -m partitioned_chip_accumulation_amd.profiling model --out "
+           "profiles/model_selection.md", "```", "",
+           "| row | predicted fastest | its predicted us | its measured us | fastest measured | "
+           "us | hit |", "|---|---|---:|---:|---|---:|---|"]
+    hits = 0
+    rows = measured_rows(profiles_dir)
+    for label, (kind, B, n, meas) in rows.items():
+        _, preds = hist.predict(B, n, sample(kind, B))
+        pred = {p["schedule"]: p["predicted_us"] for p in preds
+                if p["status"] == 0 and p["schedule"] in meas}
+        pick = min(pred, key=pred.get)
+        best = min(meas, key=meas.get)
+        hit = meas[pick] <= 1.05 * meas[best]
+        hits += hit
+        out.append(f"| {label.replace('.md', '')} | {pick} | {pred[pick]:.1f} | {meas[pick]:.1f} | "
+                   f"{best} | {meas[best]:.1f} | {'yes' if hit else 'NO'} |")
+    out += ["", f"Hits: {hits} of {len(rows)} rows ({100.0 * hits / len(rows):.0f}%)."]
+    return "\n".join(out) + "\n"
+
+
 def sources_sha(paths: list[str]) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -296,6 +375,9 @@ def main():
     mx.add_argument("jsonl")
     mx.add_argument("--cmd", required=True)
     mx.add_argument("--out", required=True)
+    mo = sub.add_parser("model")
+    mo.add_argument("--out", required=True)
+    mo.add_argument("--profiles", default="profiles")
     tr = sub.add_parser("traffic")
     tr.add_argument("--fetch", required=True)
     tr.add_argument("--write", required=True)
@@ -318,6 +400,9 @@ def main():
         return
     if a.cmd_ == "matrix":
         open(a.out, "w").write(matrix_markdown(a.jsonl, a.cmd))
+        return
+    if a.cmd_ == "model":
+        open(a.out, "w").write(model_markdown(a.profiles))
         return
     if a.cmd_ == "trace":
         sha = sources_sha(a.sources) if a.sources else None

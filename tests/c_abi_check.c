@@ -78,6 +78,26 @@ int main(void)
                                              entries, HIST_TUNE_MAX_ENTRIES, &count),
                HIST_ERR_INVALID_ARG);
     }
+    {
+        /* the cost model needs no device: a prediction on an MI355X description */
+        hist_device_desc_t dev = {256, 8, 163840, 6};
+        hist_model_calib_t cal;
+        hist_plan_opts_t best;
+        hist_prediction_t pred[HIST_MODEL_MAX_ENTRIES];
+        uint32_t count = 0;
+        int32_t sample[4096];
+        int i;
+        for (i = 0; i < 4096; ++i) sample[i] = (int32_t)((i * 2654435761u) % 65536u);
+        expect("model_calibration", hist_model_calibration(&cal), HIST_OK);
+        expect("predict(NULL dev)", hist_predict(NULL, &cal, 10, 10, NULL, 0, &best, NULL, 0, NULL),
+               HIST_ERR_INVALID_ARG);
+        expect("predict(65536 bins)", hist_predict(&dev, &cal, 65536, 1u << 26, sample, 4096, &best,
+                                                   pred, HIST_MODEL_MAX_ENTRIES, &count), HIST_OK);
+        expect("predict count", (int)count, HIST_MODEL_MAX_ENTRIES);
+        expect("predict path", best.path, HIST_PATH_FULL);
+        expect("select(input=NULL)", hist_select(10, NULL, 10, NULL, NULL, 0, NULL, &best, NULL, 0,
+                                                 NULL), HIST_ERR_INVALID_ARG);
+    }
     expect("timing_enable(NULL)", hist_plan_timing_enable(NULL, 1), HIST_ERR_INVALID_ARG);
     expect("timing_read(NULL)", hist_plan_timing_read(NULL, ms, launches), HIST_ERR_INVALID_ARG);
     expect("phase_name(0)", strcmp(hist_plan_phase_name(NULL, 0), "sweep"), 0);
@@ -95,6 +115,8 @@ int main(void)
            offsetof(hist_plan_info_t, event_cap), sizeof(hist_device_desc_t),
            sizeof(hist_tune_entry_t), offsetof(hist_tune_entry_t, ms),
            offsetof(hist_tune_entry_t, status));
+    printf("layout2 %zu %zu %zu %zu\n", sizeof(hist_model_calib_t), sizeof(hist_prediction_t),
+           offsetof(hist_prediction_t, predicted_us), offsetof(hist_prediction_t, status));
     if (failures == 0) printf("ok\n");
     return failures == 0 ? 0 : 1;
 }

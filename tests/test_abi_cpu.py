@@ -30,7 +30,9 @@ def test_headers_declare_the_expected_calls():
     names = declared_functions()
     for must in ["hist_plan", "hist_plan_create", "hist_run", "hist_workspace_size", "hist_plan_destroy",
                  "hist_status_str", "hist_bench_global_atomic", "hist_plan_preview",
-                 "hist_run_accumulate", "hist_tune", "hist_tune_workspace_size"]:
+                 "hist_run_accumulate", "hist_tune", "hist_tune_workspace_size", "hist_run_static",
+                 "hist_predict", "hist_select", "hist_model_calibration",
+                 "hist_bench_lds_latency", "hist_bench_handoff"]:
         assert must in names
 
 
@@ -149,3 +151,6 @@ def test_plain_c_client_compiles_links_and_gets_documented_errors(tmp_path):
                       hist.PlanInfo.max_group_elems.offset, hist.PlanInfo.event_cap.offset,
                       ctypes.sizeof(hist.DeviceDesc), ctypes.sizeof(hist.TuneEntry),
                       hist.TuneEntry.ms.offset, hist.TuneEntry.status.offset]
+    layout2 = [int(v) for v in lines[lines.index("layout2") + 1:lines.index("layout2") + 5]]
+    assert layout2 == [ctypes.sizeof(hist.ModelCalib), ctypes.sizeof(hist.Prediction),
+                       hist.Prediction.predicted_us.offset, hist.Prediction.status.offset]

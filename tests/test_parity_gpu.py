@@ -891,3 +891,20 @@ def test_tune_skips_schedules_the_workspace_cannot_hold():
     with pytest.raises(hist.HistError) as e:
         hist.tune(xt, num_bins, reps=1, workspace=tiny)
     assert e.value.status == hist.HIST_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_select_predicts_a_schedule_that_is_exact(cfg):
+    """hist_select samples the device input, times one stream read of it and
+    predicts every schedule without running any; the schedule it names is
+    then run, and must be exact like any other."""
+    x = inputs.generate(cfg, n=1 << 21)
+    B = inputs.WORKLOADS[cfg].num_bins
+    xt = torch.from_numpy(x).to(DEV)
+    best, rows = hist.select(xt, B)
+    assert rows and all(r["status"] in (hist.HIST_OK, hist.HIST_ERR_UNSUPPORTED) for r in rows)
+    ok = [r for r in rows if r["status"] == hist.HIST_OK]
+    assert ok and min(ok, key=lambda r: r["predicted_us"])["opts"] == best
+    say(f"select cfg {cfg}: {best} " + " ".join(f"{r['schedule']}:{r['predicted_us']:.1f}"
+                                                  for r in ok))
+    check(x, B, f"selected-cfg{cfg}", **best)
