@@ -214,6 +214,12 @@ def calib_markdown(jsonl: str, cmd: str) -> str:
             out.append(f"| {r['mode']} | 0 and {r['partner']} ({where}) | "
                        f"{r['xcds'][0]}, {r['xcds'][r['partner']]} | {r['round_trip_cycles']:.0f} | "
                        f"{r['round_trip_ns']:.0f} | {clean} |")
+    prim = [r for r in recs if r["what"] == "model_primitive"]
+    if prim:
+        out += ["", "## Primitives of the schedule cost model (hist_model_calibration)", "",
+                "| primitive | value | how |", "|---|---:|---|"]
+        for r in prim:
+            out.append(f"| {r['name']} | {r['value']} | {r['how']} |")
     out += ["", "## Owners of a chunk sharing an XCD's L2 (RANGE path)", "",
             "| placement | bins | n | us per run | plan |", "|---|---:|---:|---:|---|"]
     for r in recs:
