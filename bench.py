@@ -62,7 +62,7 @@ def parse():
                     help="instead of a workload, uniform int32 over this many bins (sweeps)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run one plain copy of this many MiB (for counter scaling)")
-    ap.add_argument("--path", default="auto", choices=["auto", "full", "range", "scatter"])
+    ap.add_argument("--path", default="auto", choices=["auto", "full", "range", "scatter", "stream"])
     ap.add_argument("--groups", type=int, default=0)
     ap.add_argument("--range-bins", type=int, default=0)
     ap.add_argument("--agg", type=int, default=-1)
@@ -353,6 +353,8 @@ def workload_matrix(args):
             cells.append(("range8+hot", {"path": "range", "counter_bits": 8, "aggregation": 1}))
         cells.append(("scatter", {"path": "scatter", "aggregation": 0}))
         cells.append(("scatter+hot", {"path": "scatter", "aggregation": 1}))
+        if B <= 1 << 21:
+            cells.append(("stream", {"path": "stream"}))
         cells.append(("auto", {}))  # last: the first cell after an upload runs slow
         steps = max(10, min(args.steps, int(4e9 / (4 * w.n))))
         settle_clocks(B, w.n, xs, out)
@@ -416,6 +418,8 @@ def path_sweep(args):
         cells.append(("scatter", {"path": "scatter"}))
         if args.sweep_zipf > 0:
             cells.append(("scatter+hot", {"path": "scatter", "aggregation": 1}))
+        if B <= 1 << 21:
+            cells.append(("stream", {"path": "stream"}))
         cells.append(("auto", {}))  # last: the first cell after an upload runs slow
         settle_clocks(B, n, xs, out)
         for name, opts in cells:
@@ -484,7 +488,7 @@ def dominant_kernel(phases: dict, n: int, B: int):
     partition read each element once (4 bytes); the owner kernel reads its
     2-byte routed slots; the merges write the 4-byte bins."""
     name, (ms, launches) = max(phases.items(), key=lambda kv: kv[1][0])
-    if name in ("sweep", "partition"):
+    if name in ("sweep", "partition", "stream"):
         nbytes = 4 * n
     elif name == "owner_hist":
         nbytes = 2 * n

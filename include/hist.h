@@ -74,14 +74,19 @@ typedef enum {
     HIST_PATH_AUTO = 0,
     HIST_PATH_FULL = 1,    /* every workgroup holds all bins in LDS (num_bins <= LDS capacity) */
     HIST_PATH_RANGE = 2,   /* bin-range ownership: R workgroups per input chunk, one range each */
-    HIST_PATH_SCATTER = 3  /* two-phase: scatter by owning range, then per-owner LDS histograms */
+    HIST_PATH_SCATTER = 3, /* two-phase: scatter by owning range, then per-owner LDS histograms */
+    HIST_PATH_STREAM = 4   /* one persistent kernel: producers route tiles to the ranges that own
+                              their bins and publish them; owners count each range in LDS as the
+                              tiles arrive, moving to the ranges with the most work left
+                              (num_bins <= 2^21; never chosen by AUTO) */
 } hist_path_t;
 
 /* Plan options. Zero-initialise and set only what you want to force;
  * 0 (or -1 for aggregation) means "choose automatically". */
 typedef struct {
     int32_t path;       /* hist_path_t */
-    int32_t groups;     /* FULL/RANGE: input chunks G; SCATTER: owner workgroups W */
+    int32_t groups;     /* FULL/RANGE: input chunks G; SCATTER: owner workgroups W; STREAM:
+                           producer workgroups P (the rest start as owners) */
     int32_t range_bins; /* RANGE: bins per owned range (multiple of 256, <= LDS capacity:
                            40960 with 32-bit counters, 79616 with 16-bit, 155392 with
                            8-bit) */
@@ -107,6 +112,9 @@ typedef struct {
                              lines one owner brings into the XCD's L2 serve the other
                              (bounded waits: an owner whose partner does not move stops
                              pacing); 2 and above count with 15 of the 16 waves */
+    int32_t spin_log2;    /* STREAM: a wait (for a tile, for a range's lock) gives up after
+                             2^spin_log2 polls (0 = 2^22, seconds), sets the plan's give-up
+                             flag (hist_plan_check) and moves on; 1..30 */
 } hist_plan_opts_t;
 
 /* Numeric description of a plan (for logs and benchmarks). */
@@ -396,10 +404,35 @@ hist_status_t hist_plan_describe(const hist_plan_t *plan, char *buf, uint64_t le
  * then clears the record. Phase names come from hist_plan_phase_name.
  * capacity bounds the number of hist_run calls recorded (older ones beyond
  * it are not recorded). Enabling allocates host-side HIP events only. */
-#define HIST_MAX_PHASES 6
+#define HIST_MAX_PHASES 7
 hist_status_t hist_plan_timing_enable(hist_plan_t *plan, uint32_t capacity);
 hist_status_t hist_plan_timing_read(hist_plan_t *plan, double *ms, uint32_t *launches);
 const char *hist_plan_phase_name(const hist_plan_t *plan, uint32_t phase);
+
+/* Whether a bounded wait of the plan's last run gave up (STREAM plans; 0
+ * for every other path). Waits for the stream first. A give-up means the
+ * counts of that run are incomplete; it cannot happen unless a wait outlasts
+ * its bound (spin_log2). Errors: INVALID_ARG for a null argument, HIP when
+ * the copy fails. */
+hist_status_t hist_plan_check(hist_plan_t *plan, hipStream_t stream, uint32_t *gave_up);
+
+/* The timeline of a STREAM plan's last run, one record of
+ * HIST_STREAM_TRACE_WORDS 32-bit words per workgroup of its persistent
+ * kernel, in the order the workgroups started (record i is the workgroup
+ * that took ticket i; tickets below the plan's producer count are the
+ * producers). Words: 0 ticket, 1 start, 2 end of its producer part (0 for an
+ * owner from the start), 3 end, 4 tiles routed, 5 blocks counted, 6 stints
+ * written to the pool, 7 ticks waiting for tiles' flags, 8 moves to another
+ * range denied by the move budget (0 or 1), 9 ticks writing stints, 10 ticks
+ * counting blocks, 11 range scans; 12..15 zero. Times are the low 32 bits of the
+ * 100 MHz constant clock (s_memrealtime), so differences are taken modulo
+ * 2^32. Waits for the stream, then copies into out (host memory of capacity
+ * words) and sets *workgroups; 0 workgroups for other paths. Errors:
+ * INVALID_ARG for a null plan or workgroups pointer, or a capacity below
+ * workgroups x HIST_STREAM_TRACE_WORDS; HIP when the copy fails. */
+#define HIST_STREAM_TRACE_WORDS 16
+hist_status_t hist_plan_stream_trace(hist_plan_t *plan, hipStream_t stream, uint32_t *out,
+                                     uint32_t capacity, uint32_t *workgroups);
 
 void hist_plan_destroy(hist_plan_t *plan);
 

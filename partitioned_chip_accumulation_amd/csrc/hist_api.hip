@@ -30,7 +30,8 @@ constexpr uint32_t kMaxLdsBins = 40960;      // 160 KiB of uint32 counters
 constexpr uint32_t kMaxLdsBins16 = 79616;    // 16-bit counters + the carry-event list
 constexpr uint64_t kMaxElemsPerWG16 = 1ull << 24;  // bounds the carry-event list
 constexpr uint32_t kMaxLdsBins8 = 155392;    // 8-bit counters + the shortest carry-event list
-constexpr uint32_t kScatterShift = 15;       // SCATTER range = 32768 bins (128 KiB)
+constexpr uint32_t kScatterShift = 15;
+constexpr uint32_t S_STREAM = 1u << kScatterShift;       // SCATTER range = 32768 bins (128 KiB)
 // From this many ranges the partition writes its run tables tile-major and a
 // transpose makes them range-major. Range-major stores from a tile land a row
 // apart: at 2,048 ranges (2^26 bins) the partition wrote 827 MiB for 192 MiB
@@ -47,12 +48,27 @@ constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slot
 // (141 us against 220 with 16-bit and 111 with 8-bit counters, the latter
 // at 1,528 us against 912 on the half-Gaussian 512K-bin workload).
 constexpr uint32_t kRangeMaxR = 4;
+// STREAM: at most this many ranges (an owner scans them all when it moves);
+// blocks of 8 tiles per range (about 8 x 16,384 elements of a range when the
+// ranges are even), 16 to 256 tiles, per owner claim; and the polls a wait
+// makes before it gives up (2^22: seconds).
+constexpr uint32_t kStreamMaxRanges = 64;
+constexpr uint32_t kStreamMinBlockTiles = 16, kStreamMaxBlockTiles = 256;
+constexpr uint32_t kStreamSpinLog2 = 22;
+// STREAM: threads per workgroup. One workgroup fits a CU (the owner's slice
+// takes 128 KiB of LDS); 8 waves leave each up to 256 VGPRs, which a
+// producer wave's two sub-tiles in registers and 33 ranks in flight need.
+constexpr uint32_t kStreamWG = 512;
+// STREAM: moves an owner may make to another range, over all workgroups, per
+// workgroup (the stint pool holds workgroups x (1 + this) slots at most)
+constexpr uint32_t kStreamMovesPerWG = 3;
 constexpr uint32_t kMinElemsPerGroup = 4096;
 constexpr int kMaxWavesPerCU = 32;
 
-enum Phase { PH_SWEEP = 0, PH_MERGE = 1, PH_PART = 2, PH_SCAN = 3, PH_OWNER = 4, PH_SLOTS = 5 };
+enum Phase { PH_SWEEP = 0, PH_MERGE = 1, PH_PART = 2, PH_SCAN = 3, PH_OWNER = 4, PH_SLOTS = 5,
+             PH_STREAM = 6 };
 const char *kPhaseNames[HIST_MAX_PHASES] = {"sweep", "merge", "partition", "range_scan",
-                                            "owner_hist", "slot_merge"};
+                                            "owner_hist", "slot_merge", "stream"};
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
@@ -131,8 +147,13 @@ struct hist_plan_impl {
     uint64_t max_elems_wg = 1ull << 40;  // elements one sweep workgroup may count
     uint32_t nblk = 0;       // 256-bin blocks per partial row
     uint32_t part_rows = 0;  // partial rows the workspace holds
-    // SCATTER
+    // SCATTER (and STREAM: tiles, qlog)
     uint32_t tiles = 0, owners = 0, qlog = 0;
+    // STREAM
+    uint32_t producers = 0, bt = 0, spin = 0, uwords = 0, grid = 0, rstride = 0, glog = 0;
+    uint32_t pool_slots = 0, move_budget = 0;
+    uint64_t off_pool = 0, off_slot_range = 0;
+    uint64_t off_ctl = 0, off_trace = 0;
     // workspace
     char *ws = nullptr;
     uint64_t ws_bytes = 0, need = 0;
@@ -150,7 +171,8 @@ namespace {
 hist_status_t check_opts(const hist_plan_opts_t *o)
 {
     if (!o) return HIST_OK;
-    if (o->path < 0 || o->path > 3) return HIST_ERR_INVALID_ARG;
+    if (o->path < 0 || o->path > 4) return HIST_ERR_INVALID_ARG;
+    if (o->spin_log2 < 0 || o->spin_log2 > 30) return HIST_ERR_INVALID_ARG;
     if (o->groups < 0 || o->groups > 65536) return HIST_ERR_INVALID_ARG;
     if (o->range_bins < 0 || (o->range_bins % 256) != 0 || o->range_bins > (int)kMaxLdsBins8)
         return HIST_ERR_INVALID_ARG;
@@ -326,6 +348,58 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
             p->off_progress = off;
             off += align_up((uint64_t)G * R * 4, 256);
         }
+        p->need = off;
+    } else if (path == HIST_PATH_STREAM) {
+        const uint32_t S = 1u << kScatterShift;
+        const uint32_t R = ceil_div(num_bins, S);
+        if (R > kStreamMaxRanges) return HIST_ERR_UNSUPPORTED;
+        const uint32_t T = std::max<uint32_t>(1, ceil_div(max_n / 4, pca::kStreamTileVecs));
+        // one workgroup per CU (each holds a 128 KiB slice), and at least one
+        // per range, so that every range has an owner from the first tickets
+        // on; by default 5/8 of them start as producers
+        const uint32_t W = std::max<uint32_t>((uint32_t)d.cu, R);
+        const uint32_t P = opts.groups > 0 ? std::min<uint32_t>((uint32_t)opts.groups, W)
+                                           : std::max<uint32_t>(1, W * 5 / 8);
+        p->range_bins = S;
+        p->ranges = R;
+        p->tiles = T;
+        p->qlog = 0;
+        p->grid = W;
+        p->producers = P;
+        p->groups = P;
+        p->bt = std::min(kStreamMaxBlockTiles,
+                         std::max(kStreamMinBlockTiles, (8u * R + 15u) & ~15u));
+        // a sub-tile's run of one range holds about 2048 / R slots, 256 / R
+        // chunks: that many lanes per run (a power of two, 1 to 64)
+        uint32_t glog = 0;
+        while (glog < 6 && (R << (glog + 1)) <= 256u) ++glog;
+        p->glog = glog;
+        p->spin = 1u << (opts.spin_log2 > 0 ? (uint32_t)opts.spin_log2 : kStreamSpinLog2);
+        p->uwords = std::max<uint32_t>(S, (kStreamWG / 64) * pca::kStreamWaveWords);
+        p->wg = kStreamWG;
+        p->nblk = S / pca::kBlockBins;
+        if ((p->uwords + pca::kStreamShWords) * 4 > d.lds) return HIST_ERR_UNSUPPORTED;
+        uint64_t off = 0;
+        p->off_ctl = off;
+        off += align_up((uint64_t)(pca::kCtlWords + R + T) * 4, 256);
+        // run-table rows of whole 128-byte lines, one per sub-tile
+        p->rstride = (R + 31u) & ~31u;
+        const uint64_t subs = (uint64_t)T * pca::kStreamSubsPerTile;
+        p->off_tcnt = off;
+        off += subs * p->rstride * 4;
+        p->off_stage = off;
+        off += subs * pca::kStreamSubCap * 2;
+        p->off_trace = off;
+        off += align_up((uint64_t)W * pca::kStreamTraceWords * 4, 256);
+        // the stint pool: a stint holds at least one block, and there are at
+        // most W + the move budget of them
+        p->move_budget = kStreamMovesPerWG * W;
+        const uint64_t blocks = (uint64_t)R * ceil_div(T, p->bt);
+        p->pool_slots = (uint32_t)std::min<uint64_t>(W + p->move_budget, blocks);
+        p->off_pool = off;
+        off += (uint64_t)p->pool_slots * S * 4;
+        p->off_slot_range = off;
+        off += align_up((uint64_t)p->pool_slots * 4, 256);
         p->need = off;
     } else {
         const uint32_t S = 1u << kScatterShift;
@@ -717,6 +791,46 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         return HIST_OK;
     }
 
+    if (p->path == HIST_PATH_STREAM) {
+        const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, pca::kStreamTileVecs));
+        if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
+        uint32_t *ctl = reinterpret_cast<uint32_t *>(p->ws + p->off_ctl);
+        const uint32_t words = pca::kCtlWords + p->ranges + T;
+        launch(pca::k_stream_prepare, dim3(std::min<uint32_t>(1024, ceil_div(words, 256))), dim3(256),
+               0, stream, tm.ev(PH_STREAM, true, false), ctl, words);
+        pca::StreamArgs sa;
+        sa.in = in;
+        sa.num_bins = num_bins;
+        sa.ranges = p->ranges;
+        sa.tiles = T;
+        sa.bt = p->bt;
+        sa.nblocks = ceil_div(T, p->bt);
+        sa.producers = p->producers;
+        sa.spin = p->spin;
+        sa.uwords = p->uwords;
+        sa.ctl = ctl;
+        sa.rows = reinterpret_cast<uint32_t *>(p->ws + p->off_tcnt);
+        sa.stage = reinterpret_cast<uint16_t *>(p->ws + p->off_stage);
+        sa.trace = reinterpret_cast<uint32_t *>(p->ws + p->off_trace);
+        sa.rstride = p->rstride;
+        sa.glog = p->glog;
+        sa.counts = counts;
+        sa.accumulate = accumulate;
+        sa.pool = reinterpret_cast<uint32_t *>(p->ws + p->off_pool);
+        sa.slot_range = reinterpret_cast<uint32_t *>(p->ws + p->off_slot_range);
+        sa.pool_slots = p->pool_slots;
+        sa.move_budget = p->move_budget;
+        auto k = pca::k_stream<kStreamWG>;
+        const uint32_t bytes = (p->uwords + pca::kStreamShWords) * 4;
+        e = allow_lds(k, bytes);
+        if (e != hipSuccess) return HIST_ERR_HIP;
+        launch(k, dim3(p->grid), dim3(kStreamWG), bytes, stream, tm.ev(PH_STREAM, false, false), sa);
+        launch(pca::k_stream_merge<256>, dim3(p->ranges * (S_STREAM / pca::kStreamMergeBins)), dim3(256), 0,
+               stream, tm.ev(PH_STREAM, false, true), (const uint32_t *)ctl, (const uint32_t *)sa.pool,
+               (const uint32_t *)sa.slot_range, p->pool_slots, num_bins, counts, accumulate);
+        return hipGetLastError() == hipSuccess ? HIST_OK : HIST_ERR_HIP;
+    }
+
     // SCATTER
     const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kScatterWG * kScatterVPT));
     if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
@@ -957,12 +1071,13 @@ void fill_info(const hist_plan_impl *p, hist_plan_info_t *info)
     info->groups = p->groups;
     info->wg_size = p->wg;
     info->aggregation = p->agg;
-    info->tile_elems = p->path == HIST_PATH_SCATTER ? kScatterTile : 0;
-    info->counter_bits = p->path == HIST_PATH_SCATTER ? 32 : p->cw;
+    const bool routed = p->path == HIST_PATH_SCATTER || p->path == HIST_PATH_STREAM;
+    info->tile_elems = routed ? kScatterTile : 0;
+    info->counter_bits = routed ? 32 : p->cw;
     info->max_n = p->max_n;
     info->workspace_bytes = p->need;
-    info->max_group_elems = p->path == HIST_PATH_SCATTER ? 0 : p->max_elems_wg;
-    info->event_cap = p->path == HIST_PATH_SCATTER ? 0 : p->ev_cap;
+    info->max_group_elems = routed ? 0 : p->max_elems_wg;
+    info->event_cap = routed ? 0 : p->ev_cap;
 }
 
 }  // namespace
@@ -972,14 +1087,14 @@ extern "C" {
 hist_status_t hist_plan_describe(const hist_plan_t *p, char *buf, uint64_t len)
 {
     if (!p || !buf || len == 0) return HIST_ERR_INVALID_ARG;
-    static const char *names[] = {"auto", "full", "range", "scatter"};
+    static const char *names[] = {"auto", "full", "range", "scatter", "stream"};
     std::snprintf(buf, len,
                   "path=%s bins=%u S=%u R=%u %s=%u cw=%u copies=%u wg=%u agg=%d tile=%u cu=%d xcd=%d "
                   "lds=%u ws=%llu%s",
                   names[p->path], p->num_bins, p->range_bins, p->ranges,
-                  p->path == HIST_PATH_SCATTER ? "W" : "G", p->groups,
-                  p->path == HIST_PATH_SCATTER ? 32u : p->cw, 1u << p->kshift, p->wg, p->agg,
-                  p->path == HIST_PATH_SCATTER ? kScatterTile : 0u, p->dev.cu, p->dev.xcd,
+                  p->path == HIST_PATH_SCATTER ? "W" : p->path == HIST_PATH_STREAM ? "P" : "G",
+                  p->groups, p->path >= HIST_PATH_SCATTER ? 32u : p->cw, 1u << p->kshift, p->wg,
+                  p->agg, p->path >= HIST_PATH_SCATTER ? kScatterTile : 0u, p->dev.cu, p->dev.xcd,
                   p->dev.lds, (unsigned long long)p->need, pace_tag(p));
     return HIST_OK;
 }
@@ -1032,6 +1147,38 @@ const char *hist_plan_phase_name(const hist_plan_t *p, uint32_t phase)
 {
     (void)p;
     return phase < HIST_MAX_PHASES ? kPhaseNames[phase] : "";
+}
+
+hist_status_t hist_plan_check(hist_plan_t *p, hipStream_t stream, uint32_t *gave_up)
+{
+    if (!p || !gave_up) return HIST_ERR_INVALID_ARG;
+    *gave_up = 0;
+    if (p->path != HIST_PATH_STREAM) return HIST_OK;
+    const uint32_t *err = reinterpret_cast<const uint32_t *>(p->ws + p->off_ctl) + pca::kCtlError;
+    if (hipMemcpyAsync(gave_up, err, 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_HIP;
+    }
+    return HIST_OK;
+}
+
+hist_status_t hist_plan_stream_trace(hist_plan_t *p, hipStream_t stream, uint32_t *out,
+                                     uint32_t capacity, uint32_t *workgroups)
+{
+    if (!p || !workgroups || (capacity && !out)) return HIST_ERR_INVALID_ARG;
+    *workgroups = 0;
+    if (p->path != HIST_PATH_STREAM) return HIST_OK;
+    const uint32_t words = p->grid * pca::kStreamTraceWords;
+    if (capacity < words) return HIST_ERR_INVALID_ARG;
+    if (hipMemcpyAsync(out, p->ws + p->off_trace, (size_t)words * 4, hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return HIST_ERR_HIP;
+    }
+    *workgroups = p->grid;
+    return HIST_OK;
 }
 
 void hist_plan_destroy(hist_plan_t *p)

@@ -28,6 +28,7 @@
 //   hist_partials.hpp    partial-slice layout, flush and exclusive-owner merge
 //   hist_sweep.hpp       the single-pass sweep (FULL, RANGE)
 //   hist_scatter.hpp     the two-phase path (SCATTER)
+//   hist_stream.hpp      the streaming owner-queue path (STREAM)
 #pragma once
 
 #include "hist_common.hpp"
@@ -36,3 +37,4 @@
 #include "hist_partials.hpp"
 #include "hist_sweep.hpp"
 #include "hist_scatter.hpp"
+#include "hist_stream.hpp"

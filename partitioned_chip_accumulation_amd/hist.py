@@ -18,9 +18,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libpca_hist.so")
 
 HIST_OK, HIST_ERR_INVALID_ARG, HIST_ERR_UNSUPPORTED, HIST_ERR_WORKSPACE, HIST_ERR_HIP = range(5)
-PATHS = {"auto": 0, "full": 1, "range": 2, "scatter": 3}
+PATHS = {"auto": 0, "full": 1, "range": 2, "scatter": 3, "stream": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
-MAX_PHASES = 6
+MAX_PHASES = 7
+STREAM_TRACE_WORDS = 16
+STREAM_TRACE_FIELDS = ("ticket", "start", "produced", "end", "tiles", "blocks", "stints",
+                       "flag_wait", "moves_denied", "stint_write", "count", "scans")
 MAX_BINS = 1 << 26
 
 
@@ -39,7 +42,7 @@ class PlanOpts(ctypes.Structure):
                 ("range_bins", ctypes.c_int32), ("aggregation", ctypes.c_int32),
                 ("wg_size", ctypes.c_int32), ("xcd_map", ctypes.c_int32),
                 ("counter_bits", ctypes.c_int32), ("lds_copies", ctypes.c_int32),
-                ("pacing", ctypes.c_int32)]
+                ("pacing", ctypes.c_int32), ("spin_log2", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -124,6 +127,8 @@ def load(path: str = LIBRARY):
         "hist_plan_timing_enable": (i32, [vp, u32]),
         "hist_plan_timing_read": (i32, [vp, P(ctypes.c_double), P(u32)]),
         "hist_plan_phase_name": (ctypes.c_char_p, [vp, u32]),
+        "hist_plan_check": (i32, [vp, vp, P(u32)]),
+        "hist_plan_stream_trace": (i32, [vp, vp, P(u32), u32, P(u32)]),
         "hist_plan_destroy": (None, [vp]),
         "hist_bench_global_atomic": (i32, [vp, vp, u64, u32, vp]),
         "hist_bench_read": (i32, [vp, u64, vp, vp]),
@@ -163,12 +168,12 @@ def _stream_handle(device: torch.device) -> int:
 
 
 def _opts(path="auto", groups=0, range_bins=0, aggregation=-1, wg_size=0, xcd_map=0,
-          counter_bits=0, lds_copies=0, pacing=0) -> PlanOpts:
+          counter_bits=0, lds_copies=0, pacing=0, spin_log2=0) -> PlanOpts:
     o = PlanOpts()
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.groups, o.range_bins, o.aggregation = int(groups), int(range_bins), int(aggregation)
     o.wg_size, o.xcd_map, o.counter_bits = int(wg_size), int(xcd_map), int(counter_bits)
-    o.lds_copies, o.pacing = int(lds_copies), int(pacing)
+    o.lds_copies, o.pacing, o.spin_log2 = int(lds_copies), int(pacing), int(spin_log2)
     return o
 
 
@@ -312,6 +317,32 @@ class Plan:
         lib = library()
         return {lib.hist_plan_phase_name(self._plan, k).decode(): (ms[k], cnt[k])
                 for k in range(MAX_PHASES) if cnt[k]}
+
+    def check(self, stream: torch.cuda.Stream | None = None) -> bool:
+        """True when a bounded wait of the plan's last runs gave up (STREAM
+        plans; always False for the other paths). Waits for the stream."""
+        v = ctypes.c_uint32(0)
+        with torch.cuda.device(self.device):
+            h = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+            _check(library().hist_plan_check(self._plan, h, ctypes.byref(v)), "hist_plan_check")
+        return bool(v.value)
+
+    def stream_trace(self, stream: torch.cuda.Stream | None = None):
+        """The last run's per-workgroup timeline of a STREAM plan, a
+        (workgroups, STREAM_TRACE_WORDS) uint32 array (None for other
+        paths); the columns are STREAM_TRACE_FIELDS. Waits for the stream."""
+        import numpy as np
+        cap = self.info().cu_count * STREAM_TRACE_WORDS
+        buf = (ctypes.c_uint32 * cap)()
+        wg = ctypes.c_uint32(0)
+        with torch.cuda.device(self.device):
+            h = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+            _check(library().hist_plan_stream_trace(self._plan, h, buf, cap, ctypes.byref(wg)),
+                   "hist_plan_stream_trace")
+        if not wg.value:
+            return None
+        return np.frombuffer(buf, dtype=np.uint32)[:wg.value * STREAM_TRACE_WORDS].reshape(
+            wg.value, STREAM_TRACE_WORDS).copy()
 
     def close(self):
         if self._plan:

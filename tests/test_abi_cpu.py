@@ -32,7 +32,8 @@ def test_headers_declare_the_expected_calls():
                  "hist_status_str", "hist_bench_global_atomic", "hist_plan_preview",
                  "hist_run_accumulate", "hist_tune", "hist_tune_workspace_size", "hist_run_static",
                  "hist_predict", "hist_select", "hist_model_calibration",
-                 "hist_bench_lds_latency", "hist_bench_handoff"]:
+                 "hist_bench_lds_latency", "hist_bench_handoff", "hist_plan_check",
+                 "hist_plan_stream_trace"]:
         assert must in names
 
 
@@ -97,6 +98,9 @@ def test_argument_errors_before_any_device_call():
     assert lib.hist_tune(10, 10, 8, 5, 8, None, 0, 1, None, ctypes.byref(best), None, 1,
                          ctypes.byref(cnt)) == hist.HIST_ERR_INVALID_ARG  # no entries
     assert lib.hist_plan_timing_enable(None, 4) == hist.HIST_ERR_INVALID_ARG
+    g = ctypes.c_uint32(7)
+    assert lib.hist_plan_check(None, None, ctypes.byref(g)) == hist.HIST_ERR_INVALID_ARG
+    assert lib.hist_plan_stream_trace(None, None, None, 0, ctypes.byref(g)) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_global_atomic(None, None, 0, 1, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_copy(None, None, 16, None) == hist.HIST_ERR_INVALID_ARG
     assert lib.hist_bench_lds_atomic(4, 0, 1, None, 0, None) == hist.HIST_ERR_INVALID_ARG

@@ -908,3 +908,77 @@ def test_select_predicts_a_schedule_that_is_exact(cfg):
     say(f"select cfg {cfg}: {best} " + " ".join(f"{r['schedule']}:{r['predicted_us']:.1f}"
                                                   for r in ok))
     check(x, B, f"selected-cfg{cfg}", **best)
+
+
+STREAM_CASES = [  # (label, input, bins, producers)
+    ("hot-bin shape 2^22", lambda: inputs.generate(4, n=1 << 22), 1 << 20, 0),
+    ("half-Gaussian shape 2^22", lambda: inputs.generate(5, n=1 << 22), 1 << 19, 0),
+    ("uniform 2^21 bins, ragged", lambda: rnd(41, 3_000_001, -7, (1 << 21) + 9), 1 << 21, 0),
+    ("one range, one tile", lambda: rnd(42, 10_000, 0, 5000), 5000, 0),
+    ("partial last range", lambda: rnd(43, 500_003, 0, 100_003), 100_003, 0),
+    ("every range empty but one", lambda: np.full(700_001, 65_537, np.int32), 1 << 20, 0),
+    ("one producer", lambda: inputs.generate(4, n=1 << 21), 1 << 20, 1),
+    ("all producers", lambda: inputs.generate(5, n=1 << 21), 1 << 19, 256),
+    ("eight producers", lambda: rnd(44, 1 << 22, 0, 1 << 20), 1 << 20, 8),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_stream_path(case):
+    """The streaming owner-queue path (STREAM) against the oracle: producers
+    route tiles and publish them, owners count each range as its tiles arrive
+    and move to the ranges with the most work left, adding their counts under
+    the range's lock. Every bounded wait must have ended on its own."""
+    label, make, bins, producers = case
+    x = make()
+    for offset in (0, 1):
+        ref, dropped = oracle.hist(x, bins)
+        say(f"case stream {label}: n={x.size} bins={bins} offset={offset} P={producers}")
+        buf = torch.full((x.size + offset + 4,), -1, dtype=torch.int32, device=DEV)
+        xt = buf[offset:offset + x.size]
+        xt.copy_(torch.from_numpy(x))
+        plan = hist.Plan(bins, max(1, x.size), device=DEV, path="stream", groups=producers)
+        got = plan.run(xt).cpu().numpy()
+        assert not plan.check(), f"{label}: a wait gave up"
+        assert np.array_equal(got, ref), f"{label} ({plan.describe()})"
+        # a second run on the same workspace, accumulating onto the first
+        acc = torch.from_numpy(got.view(np.int32).copy()).to(DEV)
+        plan.run(xt, out=acc, accumulate=True)
+        assert not plan.check()
+        got2 = acc.cpu().numpy().view(np.uint32).astype(np.int64)
+        assert np.array_equal(got2, 2 * ref.astype(np.int64)), label
+        plan.close()
+
+
+def test_stream_accumulates_and_repeats():
+    x = inputs.generate(4, n=1 << 21)
+    bins = 1 << 20
+    ref, _ = oracle.hist(x, bins)
+    plan = hist.Plan(bins, x.size, device=DEV, path="stream")
+    xt = torch.from_numpy(x).to(DEV)
+    out = torch.full((bins,), 3, dtype=torch.int32, device=DEV)
+    for _ in range(3):
+        plan.run(xt, out, accumulate=True)
+    got = out.cpu().numpy().view(np.uint32).astype(np.int64)
+    assert np.array_equal(got, 3 + 3 * ref.astype(np.int64))
+    for _ in range(3):  # overwriting runs in a row reuse the workspace
+        assert np.array_equal(plan.run(xt).cpu().numpy(), ref)
+    assert not plan.check()
+    plan.close()
+
+
+def test_stream_waits_that_give_up_are_reported():
+    """A poll bound of 2 makes owners give up on tiles not yet published (a
+    forced failure of the bounded wait, from the host): the kernel still ends,
+    and the plan reports the give-up."""
+    x = inputs.generate(4, n=1 << 22)
+    bins = 1 << 20
+    plan = hist.Plan(bins, x.size, device=DEV, path="stream", spin_log2=1, groups=8)
+    xt = torch.from_numpy(x).to(DEV)
+    gave_up = False
+    for _ in range(3):
+        plan.run(xt)
+        gave_up = gave_up or plan.check()
+    say(f"stream spin 2: gave up {gave_up}")
+    assert gave_up
+    plan.close()
