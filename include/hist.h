@@ -112,9 +112,9 @@ typedef struct {
                              lines one owner brings into the XCD's L2 serve the other
                              (bounded waits: an owner whose partner does not move stops
                              pacing); 2 and above count with 15 of the 16 waves */
-    int32_t spin_log2;    /* STREAM: a wait (for a tile, for a range's lock) gives up after
-                             2^spin_log2 polls (0 = 2^22, seconds), sets the plan's give-up
-                             flag (hist_plan_check) and moves on; 1..30 */
+    int32_t spin_log2;    /* STREAM: a wait for a block's tiles gives up after 2^spin_log2
+                             polls (0 = 2^22, seconds), sets the plan's give-up flag
+                             (hist_plan_check) and moves on; 1..30 */
 } hist_plan_opts_t;
 
 /* Numeric description of a plan (for logs and benchmarks). */

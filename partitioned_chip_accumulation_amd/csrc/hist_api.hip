@@ -55,10 +55,9 @@ constexpr uint32_t kRangeMaxR = 4;
 constexpr uint32_t kStreamMaxRanges = 64;
 constexpr uint32_t kStreamMinBlockTiles = 16, kStreamMaxBlockTiles = 256;
 constexpr uint32_t kStreamSpinLog2 = 22;
-// STREAM: threads per workgroup. One workgroup fits a CU (the owner's slice
-// takes 128 KiB of LDS); 8 waves leave each up to 256 VGPRs, which a
-// producer wave's two sub-tiles in registers and 33 ranks in flight need.
-constexpr uint32_t kStreamWG = 512;
+// STREAM: threads per workgroup, set by the sub-tile a producer wave holds in
+// registers; one workgroup fits a CU (the owner's slice takes 128 KiB of LDS)
+constexpr uint32_t kStreamWG = pca::kStreamWG;
 // STREAM: moves an owner may make to another range, over all workgroups, per
 // workgroup (the stint pool holds workgroups x (1 + this) slots at most)
 constexpr uint32_t kStreamMovesPerWG = 3;
@@ -150,7 +149,7 @@ struct hist_plan_impl {
     // SCATTER (and STREAM: tiles, qlog)
     uint32_t tiles = 0, owners = 0, qlog = 0;
     // STREAM
-    uint32_t producers = 0, bt = 0, spin = 0, uwords = 0, grid = 0, rstride = 0, glog = 0;
+    uint32_t producers = 0, bt = 0, spin = 0, uwords = 0, grid = 0, rstride = 0;
     uint32_t pool_slots = 0, move_budget = 0;
     uint64_t off_pool = 0, off_slot_range = 0;
     uint64_t off_ctl = 0, off_trace = 0;
@@ -369,13 +368,9 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
         p->groups = P;
         p->bt = std::min(kStreamMaxBlockTiles,
                          std::max(kStreamMinBlockTiles, (8u * R + 15u) & ~15u));
-        // a sub-tile's run of one range holds about 2048 / R slots, 256 / R
-        // chunks: that many lanes per run (a power of two, 1 to 64)
-        uint32_t glog = 0;
-        while (glog < 6 && (R << (glog + 1)) <= 256u) ++glog;
-        p->glog = glog;
         p->spin = 1u << (opts.spin_log2 > 0 ? (uint32_t)opts.spin_log2 : kStreamSpinLog2);
-        p->uwords = std::max<uint32_t>(S, (kStreamWG / 64) * pca::kStreamWaveWords);
+        // the owner's slice and a trash word per lane; the producers' waves
+        p->uwords = std::max<uint32_t>(S + 64, (kStreamWG / 64) * pca::kStreamWaveWords);
         p->wg = kStreamWG;
         p->nblk = S / pca::kBlockBins;
         if ((p->uwords + pca::kStreamShWords) * 4 > d.lds) return HIST_ERR_UNSUPPORTED;
@@ -813,7 +808,6 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         sa.stage = reinterpret_cast<uint16_t *>(p->ws + p->off_stage);
         sa.trace = reinterpret_cast<uint32_t *>(p->ws + p->off_trace);
         sa.rstride = p->rstride;
-        sa.glog = p->glog;
         sa.counts = counts;
         sa.accumulate = accumulate;
         sa.pool = reinterpret_cast<uint32_t *>(p->ws + p->off_pool);

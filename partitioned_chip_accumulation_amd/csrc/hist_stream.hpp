@@ -22,7 +22,7 @@ namespace pca {
 //   - the first P workgroups to start are producers, and each of their waves
 //     works on its own, with no workgroup barrier: it claims input tiles of
 //     16,384 elements in turn (an atomic tile counter) and routes a tile in
-//     eight sub-tiles of 2,048 elements. For a sub-tile it ranks every
+//     sub-tiles of 2,048 elements. For a sub-tile it ranks every
 //     element within its range with wave-private LDS counters, lays the
 //     ranges' runs of 16-bit slots (bin & (S - 1)) out one after another,
 //     each padded to whole 16-byte chunks with the slot kStreamPad, and
@@ -83,25 +83,35 @@ enum StreamTrace : uint32_t {
 constexpr uint32_t kStreamShWords = 8 + kStreamTraceWords;  // LDS words after the shared area
 // the slot value that pads a run (slots hold bin & (S - 1) < S)
 constexpr uint16_t kStreamPad = 0xFFFFu;
-// owner runs per lane in a set (each one 16-byte chunk load per pass)
-constexpr uint32_t kStreamOwnerU = 8;
-
 __device__ __forceinline__ uint32_t ceil_div_u(uint32_t a, uint32_t b) { return (a + b - 1u) / b; }
-// A producer wave's sub-tile: 2,048 elements (8 vectors per lane), eight to a
-// tile. Its stage area holds them, a head or tail of up to 3 + 3 elements
-// and up to 7 padding slots for each of up to 64 ranges, in whole 256-byte
-// units: 2,560 slots, copied out as at most 5 chunks of 16 bytes per lane.
-constexpr uint32_t kStreamSubVecs = 512, kStreamSubsPerTile = 8;
-constexpr uint32_t kStreamTileVecs = kStreamSubVecs * kStreamSubsPerTile;
-constexpr uint32_t kStreamSubCap = 2560, kStreamSubChunksPerLane = 5;
+// A producer wave's sub-tile: kStreamLaneVecs vectors per lane, a tile
+// (4,096 vectors, 16,384 elements) in kStreamSubsPerTile of them. Its stage
+// area holds its elements, a head or tail of up to 3 + 3 elements and up to 7
+// padding slots for each of up to 64 ranges, in whole 256-byte units, and is
+// copied out as at most kStreamSubChunksPerLane chunks of 16 bytes per lane.
+// The workgroup size goes with it: a lane holds two sub-tiles' elements and
+// their positions in registers, which 8 vectors per lane fit only with
+// 256-VGPR waves (512 threads), 4 with 128-VGPR waves (1,024 threads).
+constexpr uint32_t kStreamLaneVecs = 8;
+constexpr uint32_t kStreamWG = kStreamLaneVecs > 4 ? 512 : 1024;
+constexpr uint32_t kStreamLaneElems = 4 * kStreamLaneVecs + 1;
+constexpr uint32_t kStreamSubVecs = 64 * kStreamLaneVecs;
+constexpr uint32_t kStreamTileVecs = 4096, kStreamSubsPerTile = kStreamTileVecs / kStreamSubVecs;
+constexpr uint32_t kStreamSubCap = (4 * kStreamSubVecs + 8 + 7 * 64 + 127) / 128 * 128;
+constexpr uint32_t kStreamSubChunksPerLane = (kStreamSubCap / 8 + 63) / 64;
 // per producer wave, in LDS: counters [65][4] (ranges 0..63, and 64 for the
 // elements to drop), their bases (range 64's all the trash slot), the
 // staged slots (whose last slot takes the dropped elements: a sub-tile
-// stages at most 2,051 + 7 x 64 slots). A counter ranks at most 16 lanes x
-// 33 elements, so a rank fits 10 bits.
+// stages at most 4 kStreamSubVecs + 3 + 7 x 64 slots). A counter ranks at
+// most 16 lanes x kStreamLaneElems elements, so a rank fits 10 bits.
 constexpr uint32_t kStreamWaveCnt = 260;
 constexpr uint32_t kStreamWaveWords = 2 * kStreamWaveCnt + kStreamSubCap / 2;
 constexpr uint32_t kStreamTrashSlot = kStreamSubCap - 1;
+static_assert(16 * kStreamLaneElems < 1024, "ranks must fit 10 bits");
+static_assert(4 * kStreamSubVecs + 3 + 7 * 64 < kStreamTrashSlot, "the trash slot must stay unused");
+// owner runs per lane in a set (each one 16-byte chunk load per pass); two
+// sets in flight take 2 x 6 U VGPRs
+constexpr uint32_t kStreamOwnerU = kStreamWG == 512 ? 8 : 4;
 constexpr uint32_t kStreamDropRange = 64;
 
 struct StreamArgs {
@@ -113,13 +123,12 @@ struct StreamArgs {
     uint32_t spin;     // polls a wait makes before it gives up
     uint32_t uwords;   // LDS words shared by the producer's and the owner's state
     uint32_t rstride;  // words per run-table row (ranges, padded to 32)
-    uint32_t glog;     // owner lanes per run: 1 << glog
     uint32_t *ctl;     // control words, then claim[R], flag[T]
     uint32_t *pool;    // [pool_slots][S] stints' counts
     uint32_t *slot_range;  // [pool_slots] the range of each written slot
     uint32_t pool_slots, move_budget;
-    uint32_t *rows;    // [tiles * 8][rstride] per range: start << 16 | length
-    uint16_t *stage;   // [tiles * 8][kStreamSubCap] slots grouped by range
+    uint32_t *rows;    // [tiles * kStreamSubsPerTile][rstride] per range: start << 16 | length
+    uint16_t *stage;   // [tiles * kStreamSubsPerTile][kStreamSubCap] slots grouped by range
     uint32_t *counts;
     uint32_t accumulate;
     uint32_t *trace;  // [workgroups][kStreamTraceWords]
@@ -182,13 +191,13 @@ __device__ __forceinline__ uint32_t tile_vecs(const StreamArgs &a, uint32_t t)
 // step drops by index, so that no use follows a load at once) and w[32], the
 // head (tile 0, sub-tile 0) or tail (last tile, last sub-tile) element of
 // the first lanes, else -1.
-__device__ __forceinline__ void load_sub(uint32_t (&w)[33], const StreamArgs &a, uint32_t t,
+__device__ __forceinline__ void load_sub(uint32_t (&w)[kStreamLaneElems], const StreamArgs &a, uint32_t t,
                                          uint32_t sub, uint32_t lane, int32_t head_x, int32_t tail_x)
 {
     const __amdgpu_buffer_rsrc_t r =
         buffer_of(a.in.ptr + a.in.head + (uint64_t)t * kStreamTileVecs * 4, tile_vecs(a, t) * 16u);
 #pragma unroll
-    for (uint32_t u = 0; u < 8; ++u) {
+    for (uint32_t u = 0; u < kStreamLaneVecs; ++u) {
         const u32x4 q = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (sub * kStreamSubVecs + u * 64 + lane) * 16, 0, 0));
         w[4 * u + 0] = q.x;
@@ -196,7 +205,7 @@ __device__ __forceinline__ void load_sub(uint32_t (&w)[33], const StreamArgs &a,
         w[4 * u + 2] = q.z;
         w[4 * u + 3] = q.w;
     }
-    w[32] = (uint32_t)((t == 0 && sub == 0) ? head_x
+    w[kStreamLaneElems - 1] = (uint32_t)((t == 0 && sub == 0) ? head_x
                        : (t == a.tiles - 1 && sub == kStreamSubsPerTile - 1) ? tail_x : -1);
 }
 
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
     constexpr uint32_t S = 32768;  // bins an owner holds
     extern __shared__ u32x4 smem4[];
     uint32_t *const slice = reinterpret_cast<uint32_t *>(smem4);  // owner: S counters
-    uint32_t *const sh = slice + a.uwords;  // broadcast words
+    uint32_t *const sh = slice + a.uwords;  // broadcast words (past the owner's S + 64 trash words)
     uint32_t *const tr = sh + 8;            // this workgroup's timeline (thread 0)
     auto now = []() { return (uint32_t)wall_clock64(); };
     const uint32_t tid = threadIdx.x, lane = lane_id();
@@ -248,18 +257,20 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
         // Route sub-tile `sub` of tile t, held in cur, after sending out the
         // loads of the one after it (sub + 1 of t, or the first of tile tn,
         // which reads as empty past the last tile) into nxt.
-        auto route = [&](uint32_t (&cur)[33], uint32_t (&nxt)[33], uint32_t t, uint32_t sub, uint32_t tn,
+        auto route = [&](uint32_t (&cur)[kStreamLaneElems], uint32_t (&nxt)[kStreamLaneElems], uint32_t t,
+                         uint32_t sub, uint32_t tn,
                          uint32_t nv) {
             const bool last = sub + 1 == kStreamSubsPerTile;
             load_sub(nxt, a, last ? tn : t, last ? 0u : sub + 1, lane, head_x, tail_x);
             // rank each element within its range's counter q and pack range
             // (bits 25..31; kStreamDropRange for an element outside the bins
             // or past the body), rank (15..24) and slot (0..14) into one
-            // word. No branch, so that the 33 atomics go out back to back.
+            // word. No branch, so that the atomics go out back to back.
 #pragma unroll
-            for (uint32_t k = 0; k < 33; ++k) {
+            for (uint32_t k = 0; k < kStreamLaneElems; ++k) {
                 const uint32_t x = cur[k];
-                const bool ok = (k == 32 || sub * kStreamSubVecs + (k >> 2) * 64 + lane < nv) && x < a.num_bins;
+                const bool ok = (k == kStreamLaneElems - 1 || sub * kStreamSubVecs + (k >> 2) * 64 + lane < nv) &&
+                                x < a.num_bins;
                 const uint32_t r = ok ? x >> 15 : kStreamDropRange;
                 const uint32_t rk = lds_add_rtn(wcnt, (r << 2) | q, 1u);
                 cur[k] = (r << 25) | ((rk & 1023u) << 15) | (x & (S - 1u));
@@ -283,14 +294,14 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
             // every position first, then every slot: the reads of the bases
             // and the writes of the slots each go out back to back (a dropped
             // element's base is the trash slot, so min() keeps it there)
-            uint32_t pos[33];
+            uint32_t pos[kStreamLaneElems];
 #pragma unroll
-            for (uint32_t k = 0; k < 33; ++k) {
+            for (uint32_t k = 0; k < kStreamLaneElems; ++k) {
                 const uint32_t e = cur[k];
                 pos[k] = min(wbase[((e >> 25) << 2) | q] + ((e >> 15) & 1023u), kStreamTrashSlot);
             }
 #pragma unroll
-            for (uint32_t k = 0; k < 33; ++k) wst[pos[k]] = (uint16_t)(cur[k] & (S - 1u));
+            for (uint32_t k = 0; k < kStreamLaneElems; ++k) wst[pos[k]] = (uint16_t)(cur[k] & (S - 1u));
             wave_lds_order();
             // copy the staged slots out: chunks past the total are dropped
             const __amdgpu_buffer_rsrc_t out = buffer_of(a.stage + sub_id * kStreamSubCap, total * 2);
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
             wave_lds_order();
         };
         uint32_t t = __builtin_amdgcn_readfirstlane(claim_issue());
-        uint32_t ea[33], eb[33];
+        uint32_t ea[kStreamLaneElems], eb[kStreamLaneElems];
         load_sub(ea, a, t, 0, lane, head_x, tail_x);  // reads as empty when t >= T
         while (t < T) {
             // sub-tiles in pairs, ea and eb taking turns; the next tile is
@@ -363,8 +374,22 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
                 if (!ok && lane == 0)
                     __hip_atomic_store(a.ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                // lanes per run for this block: the next power of two at or
+                // above the mean chunks per run of range cur in 16 sampled
+                // sub-tiles (runs of a heavy range are longer than the mean
+                // over the ranges)
+                const uint32_t nsub_b = nt * kStreamSubsPerTile;
+                uint32_t nch = 0;
+                if (ok && lane < 16) {
+                    const uint64_t js = (uint64_t)t0 * kStreamSubsPerTile + (uint64_t)lane * nsub_b / 16;
+                    nch = ((dev_load(a.rows + js * a.rstride + cur) & 0xFFFFu) + 7u) >> 3;
+                }
+                const uint32_t mean = (wave_sum(nch) + 15u) / 16u;
+                uint32_t glog = 0;
+                while (glog < 6 && (1u << glog) < mean) ++glog;
                 if (lane == 0) {
                     sh[3] = ok;
+                    sh[5] = glog;
                     const uint32_t w1 = now();
                     tr[kTrFlagWait] += w1 - w0;
                     tr[kTrCount] -= w1;  // plus the time after the block's closing barrier
@@ -382,7 +407,7 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
                 // Two sets take turns in registers: the next set's row words
                 // and first pass are in flight while one is counted.
                 constexpr uint32_t U = kStreamOwnerU, NW = WG / 64;
-                const uint32_t glog = a.glog, G = 1u << glog, gl = lane & (G - 1u), gi = lane >> glog;
+                const uint32_t glog = sh[5], G = 1u << glog, gl = lane & (G - 1u), gi = lane >> glog;
                 const uint32_t NG = 64u >> glog, per = NG * U, nsub = nt * kStreamSubsPerTile;
                 const uint64_t sub0 = (uint64_t)t0 * kStreamSubsPerTile;
                 const __amdgpu_buffer_rsrc_t rs =
@@ -396,19 +421,36 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
                         pk[u] = j < nsub ? dev_load(rowb + (uint64_t)j * a.rstride) : 0u;
                     }
                 };
-                auto issue = [&](u32x4 (&v)[U], const uint32_t (&pk)[U], uint32_t k, uint32_t pass) {
-                    const uint32_t j0 = (wave + NW * k) * per + gi;
+                // a set in flight: its runs' chunk counts and byte offsets
+                // (this lane's first chunk), and the first pass's chunks
+                struct Set {
+                    u32x4 v[U];
+                    uint32_t nch[U], off[U];
+                };
+                auto load_pass = [&](Set &st, uint32_t pass) {
 #pragma unroll
                     for (uint32_t u = 0; u < U; ++u) {
                         const uint32_t c = gl + G * pass;
-                        const uint32_t nch = ((pk[u] & 0xFFFFu) + 7u) >> 3;
-                        const uint32_t off = ((j0 + NG * u) * kStreamSubCap + (pk[u] >> 16)) * 2 + c * 16;
-                        v[u] = c < nch ? dev_load16(rs, off) : u32x4{~0u, ~0u, ~0u, ~0u};
+                        st.v[u] = c < st.nch[u] ? dev_load16(rs, st.off[u] + G * pass * 16)
+                                                : u32x4{~0u, ~0u, ~0u, ~0u};
                     }
+                };
+                auto start = [&](Set &st, const uint32_t (&pk)[U], uint32_t k) {
+                    const uint32_t j0 = (wave + NW * k) * per + gi;
+#pragma unroll
+                    for (uint32_t u = 0; u < U; ++u) {
+                        st.nch[u] = ((pk[u] & 0xFFFFu) + 7u) >> 3;
+                        st.off[u] = ((j0 + NG * u) * kStreamSubCap + (pk[u] >> 16)) * 2 + gl * 16;
+                    }
+                    load_pass(st, 0);
                 };
                 // a hot slot (a bin holding many lanes of a wave) is counted in
                 // registers and added once per switch (HotSlot), as the
-                // two-phase path's owners do; padding slots are >= S
+                // two-phase path's owners do. Every other slot is one LDS add
+                // with no branch: a padding slot (>= S) or a hot one adds into
+                // the lane's own word past the slice, so that nothing waits
+                // on an exec-mask change (with two waves per SIMD, those
+                // dependencies were what bound the loop)
                 auto count = [&](const u32x4 (&v)[U]) {
 #pragma unroll
                     for (uint32_t u = 0; u < U; ++u) {
@@ -425,38 +467,38 @@ __global__ __launch_bounds__(WG) void k_stream(StreamArgs a)
                             const uint32_t slot = (w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                             const bool m = slot == h;
                             hs.c += m ? 1u : 0u;
-                            if (slot < S && !m) lds_add(slice, slot, 1u);
+                            lds_add(slice, slot < S && !m ? slot : S + lane, 1u);
                         }
                     }
                 };
-                // the passes after the first of a set whose runs are longer than G chunks
-                auto rest = [&](const uint32_t (&pk)[U], uint32_t k) {
+                // count a set: its first pass, then the passes of runs longer than G chunks
+                auto finish = [&](Set &st) {
+                    count(st.v);
                     uint32_t most = 0;
 #pragma unroll
-                    for (uint32_t u = 0; u < U; ++u) most = max(most, ((pk[u] & 0xFFFFu) + 7u) >> 3);
+                    for (uint32_t u = 0; u < U; ++u) most = max(most, st.nch[u]);
                     for (uint32_t pass = 1; __any(gl + G * pass < most); ++pass) {
-                        u32x4 v[U];
-                        issue(v, pk, k, pass);
-                        count(v);
+                        load_pass(st, pass);
+                        count(st.v);
                     }
                 };
+                // sets k and k + 1 take turns in sa and sb; the row words of the
+                // set after next load while one set is counted
                 const uint32_t sets = ceil_div_u(nsub, per);  // sets over the workgroup
-                u32x4 va[U], vb[U];
-                uint32_t pa[U], pb[U];
+                Set sa, sb;
+                uint32_t pr[U];
                 uint32_t k = 0;
-                rows(pa, k);
-                issue(va, pa, k, 0);
-                rows(pb, k + 1);
+                rows(pr, k);
+                start(sa, pr, k);
+                rows(pr, k + 1);
                 for (; wave + NW * k < sets; k += 2) {
-                    issue(vb, pb, k + 1, 0);
-                    count(va);
-                    rest(pa, k);
+                    start(sb, pr, k + 1);
+                    rows(pr, k + 2);
+                    finish(sa);
                     if (wave + NW * (k + 1) >= sets) break;
-                    rows(pa, k + 2);
-                    issue(va, pa, k + 2, 0);
-                    count(vb);
-                    rest(pb, k + 1);
-                    rows(pb, k + 3);
+                    start(sa, pr, k + 2);
+                    rows(pr, k + 3);
+                    finish(sb);
                 }
                 const uint32_t tk = hot_take(hs);
                 if (lane == 0 && tk != 0u) lds_add(slice, hs.h, tk);
