@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--pacing", type=int, default=0,
                     help="RANGE owners' reads: 1 non-temporal, 2 plain, 3.. plain and paced "
                          "within (pacing - 2) batches (0 = the plan's choice)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="SCATTER's in-place window: 0 auto, 1 off, 2 always")
     ap.add_argument("--copies", type=int, default=4, help="input copies used in rotation")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the CPU-baseline work (0 = skip)")
@@ -669,7 +671,7 @@ def main():
         plan_opts = dict(path=args.path, groups=args.groups, range_bins=args.range_bins,
                          aggregation=args.agg, wg_size=args.wg, xcd_map=args.xcd_map,
                          counter_bits=args.counter_bits, lds_copies=args.lds_copies,
-                         pacing=args.pacing)
+                         pacing=args.pacing, window=args.window)
     # One plan (and workspace) and one output per stream: the steps on different
     # streams are independent histograms, so they may overlap on the device.
     nstreams = max(1, args.streams)

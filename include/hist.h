@@ -115,7 +115,15 @@ typedef struct {
     int32_t spin_log2;    /* STREAM: a wait for a block's tiles gives up after 2^spin_log2
                              polls (0 = 2^22, seconds), sets the plan's give-up flag
                              (hist_plan_check) and moves on; 1..30 */
+    int32_t window;       /* SCATTER: a window of HIST_WINDOW_BINS consecutive bins counted in
+                             place by the partition workgroups (their elements are never
+                             staged), at the heaviest place a 4,096-element sample of each
+                             run's input shows: 0 auto (from 2^22 elements, used when the
+                             window holds at least a quarter of the sample), 1 never, 2 always */
 } hist_plan_opts_t;
+
+/* Bins of SCATTER's in-place window (hist_plan_opts_t.window). */
+#define HIST_WINDOW_BINS 8192
 
 /* Numeric description of a plan (for logs and benchmarks). */
 typedef struct {

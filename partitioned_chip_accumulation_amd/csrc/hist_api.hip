@@ -48,6 +48,16 @@ constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slot
 // (141 us against 220 with 16-bit and 111 with 8-bit counters, the latter
 // at 1,528 us against 912 on the half-Gaussian 512K-bin workload).
 constexpr uint32_t kRangeMaxR = 4;
+// SCATTER's in-place window: AUTO samples for it from this many elements on,
+// and uses it when it holds at least 1 / kWindowMinShare of the sample. On
+// the half-Gaussian 512K-bin workload an 8,192-bin window holds 51% of the
+// input, and the owners' time halves (2^29 elements: 896 -> 794 us end to
+// end). A window that is heavy because of one hot bin does not pay: the
+// owners' hot slot already takes that bin in registers, while in the
+// partition its adds pile onto one LDS word (the hot-bin workload's window
+// holds 11%: 472 -> 576 us), hence a quarter.
+constexpr uint64_t kWindowMinElems = 1ull << 22;
+constexpr uint32_t kWindowMinShare = 4;
 // STREAM: at most this many ranges (an owner scans them all when it moves);
 // blocks of 8 tiles per range (about 8 x 16,384 elements of a range when the
 // ranges are even), 16 to 256 tiles, per owner claim; and the polls a wait
@@ -151,6 +161,10 @@ struct hist_plan_impl {
     // STREAM
     uint32_t producers = 0, bt = 0, spin = 0, uwords = 0, grid = 0, rstride = 0;
     uint32_t pool_slots = 0, move_budget = 0;
+    // SCATTER's in-place window: mode (0 auto, 1 never, 2 always), width, the
+    // chosen base word and the partition workgroups' rows
+    uint32_t window = 1, wbins = 0, wrows = 0;
+    uint64_t off_wsel = 0, off_wpart = 0;
     uint64_t off_pool = 0, off_slot_range = 0;
     uint64_t off_ctl = 0, off_trace = 0;
     // workspace
@@ -172,6 +186,7 @@ hist_status_t check_opts(const hist_plan_opts_t *o)
     if (!o) return HIST_OK;
     if (o->path < 0 || o->path > 4) return HIST_ERR_INVALID_ARG;
     if (o->spin_log2 < 0 || o->spin_log2 > 30) return HIST_ERR_INVALID_ARG;
+    if (o->window < 0 || o->window > 2) return HIST_ERR_INVALID_ARG;
     if (o->groups < 0 || o->groups > 65536) return HIST_ERR_INVALID_ARG;
     if (o->range_bins < 0 || (o->range_bins % 256) != 0 || o->range_bins > (int)kMaxLdsBins8)
         return HIST_ERR_INVALID_ARG;
@@ -440,6 +455,16 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
         p->part_rows = W + R;
         p->off_partials = off;
         off += partial_bytes(p->part_rows, p->nblk);
+        // the in-place window, sized for the partition's largest grid
+        p->window = opts.window == 1 ? 1u : opts.window == 2 ? 2u : 0u;
+        if (p->window != 1) {
+            p->wbins = HIST_WINDOW_BINS;
+            p->wrows = std::min<uint32_t>(T, 2u * (uint32_t)d.cu);
+            p->off_wsel = off;
+            off += 256;
+            p->off_wpart = off;
+            off += align_up((uint64_t)p->wrows * p->wbins * 4, 256);
+        }
         p->need = off;
     }
     return HIST_OK;
@@ -581,11 +606,11 @@ uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes)
 }
 
 hipError_t launch_partition(const hist_plan_impl *p, pca::InputView in, uint32_t T, hipStream_t s,
-                            const KEv &ev)
+                            const KEv &ev, bool window)
 {
     auto k = pca::k_partition<kScatterWG, kScatterVPT>;
     const uint32_t npad = ((p->ranges << p->qlog) + 3u) & ~3u;
-    const uint32_t bytes = (2 * npad + 64) * 4 + kScatterCap * 2;
+    const uint32_t bytes = (2 * npad + 64) * 4 + kScatterCap * 2 + (window ? p->wbins * 4 : 0u);
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     // persistent: a grid of two workgroups per CU, each walking tiles (at its
@@ -597,7 +622,9 @@ hipError_t launch_partition(const hist_plan_impl *p, pca::InputView in, uint32_t
     const uint32_t rstride = p->tile_major ? 1u : T, tstride = p->tile_major ? p->ranges : 1u;
     launch(k, dim3(grid), dim3(kScatterWG), bytes, s, ev, in, p->num_bins, kScatterShift, p->ranges,
            p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage), kScatterCap, tcnt, tbase,
-           rstride, tstride);
+           rstride, tstride,
+           window ? reinterpret_cast<const uint32_t *>(p->ws + p->off_wsel) : (const uint32_t *)nullptr,
+           p->wbins, reinterpret_cast<uint32_t *>(p->ws + p->off_wpart));
     return hipGetLastError();
 }
 
@@ -828,7 +855,15 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     // SCATTER
     const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kScatterWG * kScatterVPT));
     if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
-    e = launch_partition(p, in, T, stream, tm.ev(PH_PART));
+    // the in-place window: chosen on the device from a sample of this input
+    // (AUTO leaves it out below 2^22 elements, where the pick's few
+    // microseconds would not pay)
+    const bool window = p->window == 2 || (p->window == 0 && n >= kWindowMinElems);
+    uint32_t *wsel = reinterpret_cast<uint32_t *>(p->ws + p->off_wsel);
+    if (window)
+        launch(pca::k_window_pick<1024>, dim3(1), dim3(1024), 0, stream, tm.ev(PH_PART, true, false),
+               in.ptr, n, num_bins, p->wbins, p->window == 2 ? 0u : kWindowMinShare, wsel);
+    e = launch_partition(p, in, T, stream, tm.ev(PH_PART, !window, true), window);
     if (e != hipSuccess) return HIST_ERR_HIP;
     {
         const uint32_t nseg = ceil_div(T, pca::kScanSeg);
@@ -860,11 +895,20 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     }
     if (e != hipSuccess) return HIST_ERR_HIP;
     {
-        const KEv sev = tm.ev(PH_SLOTS);
+        const KEv sev = tm.ev(PH_SLOTS, true, !window);
         e = accumulate ? launch_merge_slots<true>(p, num_bins, counts, stream, sev)
                        : launch_merge_slots<false>(p, num_bins, counts, stream, sev);
     }
     if (e != hipSuccess) return HIST_ERR_HIP;
+    if (window) {
+        // after the owners and the slot merge: the window's bins hold the
+        // staged elements' counts (none), to which the rows are added
+        launch(pca::k_window_merge<1024>, dim3(ceil_div(p->wbins, 64)), dim3(1024), 0, stream,
+               tm.ev(PH_SLOTS, false, true), (const uint32_t *)wsel,
+               reinterpret_cast<const uint32_t *>(p->ws + p->off_wpart),
+               std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu), p->wbins, num_bins, counts);
+        if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
+    }
     return HIST_OK;
 }
 
@@ -1084,12 +1128,13 @@ hist_status_t hist_plan_describe(const hist_plan_t *p, char *buf, uint64_t len)
     static const char *names[] = {"auto", "full", "range", "scatter", "stream"};
     std::snprintf(buf, len,
                   "path=%s bins=%u S=%u R=%u %s=%u cw=%u copies=%u wg=%u agg=%d tile=%u cu=%d xcd=%d "
-                  "lds=%u ws=%llu%s",
+                  "lds=%u ws=%llu%s%s",
                   names[p->path], p->num_bins, p->range_bins, p->ranges,
                   p->path == HIST_PATH_SCATTER ? "W" : p->path == HIST_PATH_STREAM ? "P" : "G",
                   p->groups, p->path >= HIST_PATH_SCATTER ? 32u : p->cw, 1u << p->kshift, p->wg,
                   p->agg, p->path >= HIST_PATH_SCATTER ? kScatterTile : 0u, p->dev.cu, p->dev.xcd,
-                  p->dev.lds, (unsigned long long)p->need, pace_tag(p));
+                  p->dev.lds, (unsigned long long)p->need, pace_tag(p),
+                  p->path != HIST_PATH_SCATTER ? "" : p->window == 1 ? " win=off" : p->window == 2 ? " win=on" : " win=auto");
     return HIST_OK;
 }
 

@@ -159,13 +159,17 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
 // write, so the tables are written tile-major (rstride = 1, tstride = ranges)
 // and k_transpose turns them range-major. Element order inside a run is
 // whatever the atomics gave; counts do not depend on it.
+// no in-place window (k_window_pick found none worth it, or none was asked for)
+constexpr uint32_t kNoWindow = 0xFFFFFFFFu;
+
 template <int WG, int VPT>
 __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
                                                   uint32_t ranges, uint32_t qlog, uint32_t tiles,
                                                   uint16_t *__restrict__ stage, uint32_t stage_cap,
                                                   uint32_t *__restrict__ tcnt,
                                                   uint32_t *__restrict__ tbase, uint32_t rstride,
-                                                  uint32_t tstride)
+                                                  uint32_t tstride, const uint32_t *__restrict__ wsel,
+                                                  uint32_t wbins, uint32_t *__restrict__ wpart)
 {
     extern __shared__ u32x4 smem4[];
     const uint32_t nsub = ranges << qlog;  // <= 2 * WG
@@ -174,6 +178,10 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
     uint32_t *base = cnt + npad;
     uint32_t *scratch = base + npad;  // block scan scratch + total
     uint16_t *st = reinterpret_cast<uint16_t *>(scratch + 64);
+    // the in-place window: bins [w0, w0 + hw) are counted here, not staged
+    uint32_t *win = reinterpret_cast<uint32_t *>(st + stage_cap);
+    const uint32_t w0 = wsel ? *wsel : kNoWindow;
+    const uint32_t hw = w0 == kNoWindow ? 0u : min(wbins, num_bins - w0);
     const uint32_t tid = threadIdx.x;
     const uint32_t mask = (1u << shift) - 1u;
     const uint32_t q = lane_id() & ((1u << qlog) - 1u);
@@ -201,6 +209,7 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
     uint32_t t = blockIdx.x;
     if (t < tiles) load_tile(t);
     for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
+    for (uint32_t i = tid; i < hw; i += WG) win[i] = 0u;
     __syncthreads();
 
     for (; t < tiles; t += gridDim.x) {
@@ -208,6 +217,20 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
 #pragma unroll
         for (int e = 0; e < E + 2; ++e) x[e] = nx[e];
         if (t + gridDim.x < tiles) load_tile(t + gridDim.x);
+        if (hw) {
+            // the window's elements first: counted, then neither ranked nor
+            // staged. The add alone sits under the branch and the marking is
+            // a select: a register written under a branch would make the
+            // compiler copy the whole array there and wait for the next
+            // tile's loads.
+#pragma unroll
+            for (int e = 0; e < E + 2; ++e) {
+                const uint32_t wi = x[e] - w0;
+                if (wi < hw) lds_add(win, wi, 1u);
+            }
+#pragma unroll
+            for (int e = 0; e < E + 2; ++e) x[e] = x[e] - w0 < hw ? 0xFFFFFFFFu : x[e];
+        }
 #pragma unroll
         for (int e = 0; e < E + 2; ++e) {
             rk[e] = 0u;
@@ -245,6 +268,117 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
         u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)t * stage_cap);
         for (uint32_t i = tid; i < nv; i += WG) d4[i] = s4[i];
         __syncthreads();  // staging and counters are reused by the next tile
+    }
+    // the workgroup's window counts: its row of the window partials
+    if (hw) {
+        __syncthreads();
+        for (uint32_t i = tid; i < hw; i += WG) wpart[(uint64_t)blockIdx.x * wbins + i] = win[i];
+    }
+}
+
+// The heaviest window of wbins consecutive bins, from a sample of the input,
+// for k_partition to count in place. One workgroup: 4 samples per thread at
+// evenly spaced indices (4,096 scattered lines are what one CU fetches in a
+// few microseconds while the rest of the GPU waits), counted into coarse
+// buckets (256 bins, or more so that there are at most 8,192), then the
+// window of wbins / bucket buckets with the most samples (the first such,
+// from a prefix sum). *wsel gets the window's first bin when it holds at
+// least samples / min_div of the sample (min_div 0: always), else kNoWindow.
+template <int WG>
+__global__ __launch_bounds__(WG) void k_window_pick(const int32_t *__restrict__ x, uint64_t n,
+                                                   uint32_t num_bins, uint32_t wbins,
+                                                   uint32_t min_div, uint32_t *__restrict__ wsel)
+{
+    constexpr uint32_t kSamples = 4 * WG, kMaxBuckets = 8192, PER = kMaxBuckets / WG;
+    __shared__ uint32_t hist[kMaxBuckets];
+    __shared__ uint32_t scratch[64];
+    const uint32_t tid = threadIdx.x;
+    uint32_t blog = 8;
+    while ((((uint64_t)num_bins + (1u << blog) - 1u) >> blog) > kMaxBuckets) ++blog;
+    const uint32_t nb = (uint32_t)(((uint64_t)num_bins + (1u << blog) - 1u) >> blog);
+    for (uint32_t i = tid; i < kMaxBuckets; i += WG) hist[i] = 0u;
+    // every sample's load goes out before any is counted
+    uint32_t v[kSamples / WG];
+#pragma unroll
+    for (uint32_t i = 0; i < kSamples / WG; ++i)
+        v[i] = (uint32_t)x[(uint64_t)(tid + i * WG) * n / kSamples];
+    __syncthreads();
+#pragma unroll
+    for (uint32_t i = 0; i < kSamples / WG; ++i)
+        if (v[i] < num_bins) lds_add(hist, v[i] >> blog, 1u);
+    __syncthreads();
+    // inclusive prefix over the buckets, PER per thread
+    uint32_t local[PER], run = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        run += hist[tid * PER + k];
+        local[k] = run;
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan<WG>(run, scratch, &total);
+    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) hist[tid * PER + k] = before + local[k];
+    __syncthreads();
+    // window sums: buckets [j, j + wb) = P[j + wb - 1] - P[j - 1]
+    const uint32_t wb = max(1u, wbins >> blog);
+    uint32_t best = 0;  // sum << 13 | (8191 - j): the largest sum, then the first j
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        const uint32_t j = tid * PER + k;
+        if (j < nb) {
+            const uint32_t hi = hist[min(j + wb, nb) - 1u], lo = j ? hist[j - 1u] : 0u;
+            best = max(best, ((hi - lo) << 13) | (kMaxBuckets - 1u - j));
+        }
+    }
+    __syncthreads();
+    // block max through the scratch words
+    const uint32_t lane = lane_id(), w = tid >> 6;
+    for (int d = 32; d >= 1; d >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, d, 64));
+    if (lane == 0) scratch[w] = best;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t m = 0;
+        for (uint32_t i = 0; i < WG / 64; ++i) m = max(m, scratch[i]);
+        const uint32_t sum = m >> 13, j = kMaxBuckets - 1u - (m & (kMaxBuckets - 1u));
+        *wsel = (min_div == 0 || (uint64_t)sum * min_div >= kSamples) ? (j << blog) : kNoWindow;
+    }
+}
+
+// counts[w0 + b] += the sum of the window partials' rows at b, for the bins
+// of the window k_window_pick chose (none: nothing). Each workgroup takes 64
+// bins; its waves sum every (WG / 64)-th row, 8 loads in flight per lane, then
+// one wave adds the partial sums: the counts of a bin are written by one
+// thread, with no atomic.
+template <int WG>
+__global__ __launch_bounds__(WG) void k_window_merge(const uint32_t *__restrict__ wsel,
+                                                    const uint32_t *__restrict__ wpart, uint32_t rows,
+                                                    uint32_t wbins, uint32_t num_bins,
+                                                    uint32_t *__restrict__ counts)
+{
+    constexpr uint32_t PH = WG / 64, U = 8;
+    __shared__ uint32_t part[WG];
+    const uint32_t w0 = *wsel;
+    if (w0 == kNoWindow) return;
+    const uint32_t hw = min(wbins, num_bins - w0);
+    const uint32_t b = blockIdx.x * 64 + (threadIdx.x & 63u), ph = threadIdx.x >> 6;
+    uint32_t sum = 0;
+    if (b < hw) {
+        uint32_t r = ph;
+        for (; r + PH * (U - 1) < rows; r += PH * U) {
+            uint32_t v[U];
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) v[u] = wpart[(uint64_t)(r + PH * u) * wbins + b];
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) sum += v[u];
+        }
+        for (; r < rows; r += PH) sum += wpart[(uint64_t)r * wbins + b];
+    }
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    if (ph == 0 && b < hw) {
+        for (uint32_t k = 1; k < PH; ++k) sum += part[k * 64 + threadIdx.x];
+        counts[w0 + b] += sum;
     }
 }
 

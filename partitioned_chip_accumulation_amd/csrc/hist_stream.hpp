@@ -8,7 +8,6 @@
 #pragma once
 
 #include "hist_common.hpp"
-#include "hist_scatter.hpp"
 
 namespace pca {
 

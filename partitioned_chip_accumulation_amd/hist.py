@@ -21,6 +21,7 @@ HIST_OK, HIST_ERR_INVALID_ARG, HIST_ERR_UNSUPPORTED, HIST_ERR_WORKSPACE, HIST_ER
 PATHS = {"auto": 0, "full": 1, "range": 2, "scatter": 3, "stream": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 MAX_PHASES = 7
+WINDOW_BINS = 8192  # HIST_WINDOW_BINS
 STREAM_TRACE_WORDS = 16
 STREAM_TRACE_FIELDS = ("ticket", "start", "produced", "end", "tiles", "blocks", "stints",
                        "flag_wait", "moves_denied", "stint_write", "count", "scans")
@@ -42,7 +43,8 @@ class PlanOpts(ctypes.Structure):
                 ("range_bins", ctypes.c_int32), ("aggregation", ctypes.c_int32),
                 ("wg_size", ctypes.c_int32), ("xcd_map", ctypes.c_int32),
                 ("counter_bits", ctypes.c_int32), ("lds_copies", ctypes.c_int32),
-                ("pacing", ctypes.c_int32), ("spin_log2", ctypes.c_int32)]
+                ("pacing", ctypes.c_int32), ("spin_log2", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -168,12 +170,13 @@ def _stream_handle(device: torch.device) -> int:
 
 
 def _opts(path="auto", groups=0, range_bins=0, aggregation=-1, wg_size=0, xcd_map=0,
-          counter_bits=0, lds_copies=0, pacing=0, spin_log2=0) -> PlanOpts:
+          counter_bits=0, lds_copies=0, pacing=0, spin_log2=0, window=0) -> PlanOpts:
     o = PlanOpts()
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.groups, o.range_bins, o.aggregation = int(groups), int(range_bins), int(aggregation)
     o.wg_size, o.xcd_map, o.counter_bits = int(wg_size), int(xcd_map), int(counter_bits)
     o.lds_copies, o.pacing, o.spin_log2 = int(lds_copies), int(pacing), int(spin_log2)
+    o.window = int(window)
     return o
 
 

@@ -982,3 +982,49 @@ def test_stream_waits_that_give_up_are_reported():
     say(f"stream spin 2: gave up {gave_up}")
     assert gave_up
     plan.close()
+
+
+def top_cluster(seed, n, num_bins):
+    """Half the elements in the last 3,000 bins and 100 values past them, the
+    rest uniform over the bins, some negative: the heaviest window runs past
+    num_bins and must be cut there."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-50, num_bins, size=n, dtype=np.int64)
+    hot = rng.random(n) < 0.5
+    x[hot] = rng.integers(num_bins - 3000, num_bins + 100, size=int(hot.sum()))
+    return x.astype(np.int32)
+
+
+WINDOW_CASES = [  # (label, input, bins)
+    ("half-Gaussian shape 2^22", lambda: inputs.generate(5, n=1 << 22), 1 << 19),
+    ("hot-bin shape 2^22", lambda: inputs.generate(4, n=1 << 22), 1 << 20),
+    ("cluster at the last bins", lambda: top_cluster(51, (1 << 22) + 5, 700_001), 700_001),
+    ("uniform 2^21 bins", lambda: rnd(52, 1 << 22, 0, 1 << 21), 1 << 21),
+    ("below the sampling size", lambda: top_cluster(53, 100_003, 300_000), 300_000),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_scatter_in_place_window(case):
+    """SCATTER with its in-place window: the partition workgroups count the
+    heaviest 8,192 bins a sample shows in LDS and never stage them; their
+    rows are added after the owners. Auto, off and forced must all be exact,
+    at an aligned and a misaligned start, overwriting and accumulating."""
+    label, make, bins = case
+    x = make()
+    ref, _ = oracle.hist(x, bins)
+    for window in (0, 1, 2):
+        for offset in (0, 1):
+            say(f"case window {label}: n={x.size} bins={bins} window={window} offset={offset}")
+            buf = torch.full((x.size + offset + 4,), -1, dtype=torch.int32, device=DEV)
+            xt = buf[offset:offset + x.size]
+            xt.copy_(torch.from_numpy(x))
+            plan = hist.Plan(bins, x.size, device=DEV, path="scatter", window=window)
+            assert ("win=auto", "win=off", "win=on")[window] in plan.describe()
+            got = plan.run(xt).cpu().numpy()
+            assert np.array_equal(got, ref), f"{label} window={window} offset={offset}"
+            acc = torch.from_numpy(got.view(np.int32).copy()).to(DEV)
+            plan.run(xt, out=acc, accumulate=True)
+            got2 = acc.cpu().numpy().view(np.uint32).astype(np.int64)
+            assert np.array_equal(got2, 2 * ref.astype(np.int64)), f"{label} accumulate"
+            plan.close()

@@ -84,18 +84,23 @@ def test_scatter_sizes():
     assert i.workspace_bytes > partial_bytes(256 + 32, 32768) + tiles * 16392 * 2
 
 
-def scatter_workspace(num_bins, max_n, owners=256):
+def scatter_workspace(num_bins, max_n, owners=256, window=True):
     """The SCATTER workspace, region by region, each 256-byte aligned, in the
     plan's order: staged slots, run tables (counts, starts, prefix), range totals,
     segment totals, range starts, from 1,024 ranges a tile-major copy of the
-    run starts, then W + R partial rows of 32,768-bin slices."""
+    run starts, W + R partial rows of 32,768-bin slices, then (unless the
+    in-place window is off) the window's base word and one 16,384-bin row per
+    partition workgroup (min(tiles, 2 x CUs) of them)."""
     R = -(-num_bins // 32768)
     T = max(1, -(-(max_n // 4) // 4096))
     b = align(T * 16392 * 2) + 3 * align(R * T * 4) + align(R * 4)
     b += align(R * -(-T // 4096) * 4) + align((R + 1) * 8)
     if R >= 1024:
         b += align(R * T * 4)
-    return b + partial_bytes(owners + R, 32768)
+    b += partial_bytes(owners + R, 32768)
+    if window:
+        b += 256 + align(min(T, 512) * hist.WINDOW_BINS * 4)
+    return b
 
 
 @pytest.mark.parametrize("num_bins,max_n", [
@@ -107,6 +112,16 @@ def test_scatter_workspace_layout(num_bins, max_n):
     i = hist.preview(num_bins, max_n, path="scatter")
     assert i.ranges == -(-num_bins // 32768)
     assert i.workspace_bytes == scatter_workspace(num_bins, max_n)
+    for w, on in ((1, False), (2, True)):
+        assert hist.preview(num_bins, max_n, path="scatter", window=w).workspace_bytes == \
+            scatter_workspace(num_bins, max_n, window=on)
+
+
+def test_window_option_is_checked():
+    for bad in (-1, 3):
+        with pytest.raises(hist.HistError) as e:
+            hist.preview(1 << 20, N, path="scatter", window=bad)
+        assert e.value.status == hist.HIST_ERR_INVALID_ARG
 
 
 def test_forced_options():
