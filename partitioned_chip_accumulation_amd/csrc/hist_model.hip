@@ -53,6 +53,9 @@ struct SampleStats {
                                    // registers (its value's copies), 0 if it would not latch
     double dups_hot = 0;           // same-word lanes per instruction of 32-bit words, without
                                    // the hot value's lanes
+    double win_frac = 0;           // share of all the elements in the heaviest window of
+                                   // HIST_WINDOW_BINS bins (at 256-bin steps, as the
+                                   // two-phase path's own sampling places it)
 };
 
 // Whether the wave hot slot takes a value that a share p of the elements
@@ -116,6 +119,18 @@ SampleStats sample_stats(const int32_t *s, uint32_t sn, uint32_t num_bins)
         for (double &d : st.dups) d /= groups;
         st.dups_hot /= groups;
     }
+    // the heaviest window, from 256-bin buckets (more per bucket above 8,192
+    // buckets) and a prefix sum over them, as k_window_pick finds it
+    uint32_t blog = 8;
+    while ((((uint64_t)num_bins + (1u << blog) - 1) >> blog) > 8192) ++blog;
+    const uint32_t nb = (uint32_t)(((uint64_t)num_bins + (1u << blog) - 1) >> blog);
+    const uint32_t wb = std::max<uint32_t>(1, HIST_WINDOW_BINS >> blog);
+    std::vector<uint64_t> pre(nb + 1, 0);
+    for (uint32_t x : v) ++pre[(x >> blog) + 1];
+    for (uint32_t b = 0; b < nb; ++b) pre[b + 1] += pre[b];
+    uint64_t best = 0;
+    for (uint32_t j = 0; j < nb; ++j) best = std::max(best, pre[std::min(j + wb, nb)] - pre[j]);
+    st.win_frac = st.total ? (double)best / (double)st.total : 0.0;
     return st;
 }
 
@@ -157,20 +172,31 @@ void predict_one(const hist_device_desc_t &dev, const hist_model_calib_t &c, con
     const double cyc_us = 1.0 / (dev.cu_count * c.clock_ghz * 1e3);  // one cycle of every CU
     const double instr = valid * (double)n / 64.0;                 // LDS wave instructions
     if (info.path == HIST_PATH_SCATTER) {
+        // the in-place window (AUTO's rule): from 2^22 elements, when the
+        // heaviest window holds a quarter of the input, its elements are
+        // counted by the partition and never staged; its rows (one per
+        // partition workgroup) are read back by the window merge
+        const bool win = n >= (1ull << 22) && st.win_frac >= 0.25;
+        const double staged = win ? std::max(0.0, valid - st.win_frac) : valid;
+        const double tiles = std::ceil((double)n / 16384.0);
+        const double rows = std::min(tiles, 2.0 * dev.cu_count);
+        const double win_us = win ? c.launch_us + rows * HIST_WINDOW_BINS * 4.0 / (c.read_gbps * 1e3) : 0.0;
         // partition: read the input, write 2-byte slots (a copy's rate for the
         // read and write bytes); owners: read the slots, one 32-bit LDS atomic
         // per element, the hot slot taking each instruction's hot value
-        const double part = read_us + (2.0 * valid * n + 2.0 * valid * n) / (c.copy_gbps * 1e3);
-        const double slots = 2.0 * valid * (double)n / (c.read_gbps * 1e3);
+        const double part = read_us + (2.0 * staged * n + 2.0 * staged * n) / (c.copy_gbps * 1e3);
+        const double slots = 2.0 * staged * (double)n / (c.read_gbps * 1e3);
         // with the hot slot, the hot value's copies issue no LDS atomic at all
+        // (the window, when it holds the hot value, already took them)
         const double d = aggregation == 1 ? st.dups_hot : st.dups[0];
-        const double atomics = aggregation == 1 ? instr * (1.0 - st.hot_frac) : instr;
+        const double owned = valid > 0 ? staged / valid : 0.0;
+        const double atomics = instr * owned * (aggregation == 1 && !win ? 1.0 - st.hot_frac : 1.0);
         const double lds = atomics * (c.lds_cycles + c.lds_dup_cycles * d) * cyc_us;
         e->pass_us = part + slots;
         e->lds_us = lds;
         e->events_us = 0;
-        e->fixed_us = c.scatter_fixed_us;
-        e->predicted_us = c.scatter_fixed_us + part + std::max(slots, lds);
+        e->fixed_us = c.scatter_fixed_us + win_us;
+        e->predicted_us = c.scatter_fixed_us + win_us + part + std::max(slots, lds);
         return;
     }
     const uint32_t cw = info.counter_bits, R = info.ranges, G = info.groups;
