@@ -117,7 +117,7 @@ typedef struct {
                              (hist_plan_check) and moves on; 1..30 */
     int32_t window;       /* SCATTER: a window of HIST_WINDOW_BINS consecutive bins counted in
                              place by the partition workgroups (their elements are never
-                             staged), at the heaviest place a 4,096-element sample of each
+                             staged), at the heaviest place a 1,024-element sample of each
                              run's input shows: 0 auto (from 2^22 elements, used when the
                              window holds at least a quarter of the sample), 1 never, 2 always */
 } hist_plan_opts_t;

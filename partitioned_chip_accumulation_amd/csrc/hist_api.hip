@@ -641,7 +641,7 @@ pca::Partials plan_partials(const hist_plan_impl *p)
 
 template <int AGG>
 hipError_t launch_owner_t(const hist_plan_impl *p, uint32_t T, uint32_t *counts, uint32_t accumulate,
-                          hipStream_t s, const KEv &ev)
+                          hipStream_t s, const KEv &ev, const uint32_t *hot_seen)
 {
     auto k = pca::k_bucket_hist<kScatterWG, 8, AGG>;
     const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + 4 * 4;
@@ -654,7 +654,7 @@ hipError_t launch_owner_t(const hist_plan_impl *p, uint32_t T, uint32_t *counts,
            reinterpret_cast<const uint32_t *>(p->ws + p->off_tpre),
            reinterpret_cast<const uint32_t *>(p->ws + p->off_totals), p->ranges, T, p->range_bins,
            p->num_bins, p->owners, plan_partials(p),
-           reinterpret_cast<uint64_t *>(p->ws + p->off_starts), counts, accumulate);
+           reinterpret_cast<uint64_t *>(p->ws + p->off_starts), counts, accumulate, hot_seen);
     return hipGetLastError();
 }
 
@@ -886,11 +886,13 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
     {
         const KEv oev = tm.ev(PH_OWNER);
+        // the pick's verdict on a hot value, when it ran
+        const uint32_t *hot = window ? wsel + 1 : nullptr;
         switch (p->agg) {
-        case 0: e = launch_owner_t<0>(p, T, counts, accumulate, stream, oev); break;
-        case 1: e = launch_owner_t<1>(p, T, counts, accumulate, stream, oev); break;
-        case 2: e = launch_owner_t<2>(p, T, counts, accumulate, stream, oev); break;
-        default: e = launch_owner_t<4>(p, T, counts, accumulate, stream, oev); break;
+        case 0: e = launch_owner_t<0>(p, T, counts, accumulate, stream, oev, hot); break;
+        case 1: e = launch_owner_t<1>(p, T, counts, accumulate, stream, oev, hot); break;
+        case 2: e = launch_owner_t<2>(p, T, counts, accumulate, stream, oev, hot); break;
+        default: e = launch_owner_t<4>(p, T, counts, accumulate, stream, oev, hot); break;
         }
     }
     if (e != hipSuccess) return HIST_ERR_HIP;
@@ -903,7 +905,7 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     if (window) {
         // after the owners and the slot merge: the window's bins hold the
         // staged elements' counts (none), to which the rows are added
-        launch(pca::k_window_merge<1024>, dim3(ceil_div(p->wbins, 64)), dim3(1024), 0, stream,
+        launch(pca::k_window_merge<1024>, dim3(ceil_div(p->wbins, pca::kWindowMergeBins)), dim3(1024), 0, stream,
                tm.ev(PH_SLOTS, false, true), (const uint32_t *)wsel,
                reinterpret_cast<const uint32_t *>(p->ws + p->off_wpart),
                std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu), p->wbins, num_bins, counts);

@@ -277,19 +277,23 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
 }
 
 // The heaviest window of wbins consecutive bins, from a sample of the input,
-// for k_partition to count in place. One workgroup: 4 samples per thread at
-// evenly spaced indices (4,096 scattered lines are what one CU fetches in a
-// few microseconds while the rest of the GPU waits), counted into coarse
+// for k_partition to count in place. One workgroup: one sample per thread at
+// evenly spaced indices (1,024 scattered lines, which one CU fetches in a
+// few microseconds while the rest of the GPU waits: 4,096 took 12 us; the
+// share's standard error is then under 1.6%), counted into coarse
 // buckets (256 bins, or more so that there are at most 8,192), then the
 // window of wbins / bucket buckets with the most samples (the first such,
-// from a prefix sum). *wsel gets the window's first bin when it holds at
-// least samples / min_div of the sample (min_div 0: always), else kNoWindow.
+// from a prefix sum). wsel[0] gets the window's first bin when it holds at
+// least samples / min_div of the sample (min_div 0: always), else kNoWindow;
+// wsel[1] gets whether some value outside that window holds 8 or more of one
+// wave's 64 samples, the share at which the owners' hot slot latches (0: the
+// owners leave the hot slot off for this run).
 template <int WG>
 __global__ __launch_bounds__(WG) void k_window_pick(const int32_t *__restrict__ x, uint64_t n,
                                                    uint32_t num_bins, uint32_t wbins,
                                                    uint32_t min_div, uint32_t *__restrict__ wsel)
 {
-    constexpr uint32_t kSamples = 4 * WG, kMaxBuckets = 8192, PER = kMaxBuckets / WG;
+    constexpr uint32_t kSamples = WG, kMaxBuckets = 8192, PER = kMaxBuckets / WG;
     __shared__ uint32_t hist[kMaxBuckets];
     __shared__ uint32_t scratch[64];
     const uint32_t tid = threadIdx.x;
@@ -341,27 +345,48 @@ __global__ __launch_bounds__(WG) void k_window_pick(const int32_t *__restrict__ 
         uint32_t m = 0;
         for (uint32_t i = 0; i < WG / 64; ++i) m = max(m, scratch[i]);
         const uint32_t sum = m >> 13, j = kMaxBuckets - 1u - (m & (kMaxBuckets - 1u));
-        *wsel = (min_div == 0 || (uint64_t)sum * min_div >= kSamples) ? (j << blog) : kNoWindow;
+        hist[0] = (min_div == 0 || (uint64_t)sum * min_div >= kSamples) ? (j << blog) : kNoWindow;
+    }
+    __syncthreads();
+    // the most copies of one value among a wave's samples outside the window
+    const uint32_t w0 = hist[0];
+    const uint32_t hw = w0 == kNoWindow ? 0u : min(wbins, num_bins - w0);
+    const uint32_t mine = v[0];
+    const bool counted = mine < num_bins && !(mine - w0 < hw);
+    uint32_t most = 0;
+    for (uint32_t k = 0; k < 64; ++k) {
+        const uint32_t vk = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)k);
+        most = max(most, (uint32_t)__popcll(__ballot(counted && mine == vk)));
+    }
+    __syncthreads();
+    if (lane == 0) scratch[w] = most;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t m = 0;
+        for (uint32_t i = 0; i < WG / 64; ++i) m = max(m, scratch[i]);
+        wsel[0] = w0;
+        wsel[1] = m >= 8u ? 1u : 0u;
     }
 }
 
 // counts[w0 + b] += the sum of the window partials' rows at b, for the bins
-// of the window k_window_pick chose (none: nothing). Each workgroup takes 64
-// bins; its waves sum every (WG / 64)-th row, 8 loads in flight per lane, then
-// one wave adds the partial sums: the counts of a bin are written by one
-// thread, with no atomic.
+// of the window k_window_pick chose (none: nothing). Each workgroup takes
+// kWindowMergeBins bins; its thread groups sum every (WG / kWindowMergeBins)-th
+// row, 8 loads in flight per lane, then one group adds the partial sums: the
+// counts of a bin are written by one thread, with no atomic.
+constexpr uint32_t kWindowMergeBins = 64;
 template <int WG>
 __global__ __launch_bounds__(WG) void k_window_merge(const uint32_t *__restrict__ wsel,
                                                     const uint32_t *__restrict__ wpart, uint32_t rows,
                                                     uint32_t wbins, uint32_t num_bins,
                                                     uint32_t *__restrict__ counts)
 {
-    constexpr uint32_t PH = WG / 64, U = 8;
+    constexpr uint32_t NB = kWindowMergeBins, PH = WG / NB, U = 8;
     __shared__ uint32_t part[WG];
     const uint32_t w0 = *wsel;
     if (w0 == kNoWindow) return;
     const uint32_t hw = min(wbins, num_bins - w0);
-    const uint32_t b = blockIdx.x * 64 + (threadIdx.x & 63u), ph = threadIdx.x >> 6;
+    const uint32_t b = blockIdx.x * NB + (threadIdx.x & (NB - 1u)), ph = threadIdx.x / NB;
     uint32_t sum = 0;
     if (b < hw) {
         uint32_t r = ph;
@@ -377,7 +402,7 @@ __global__ __launch_bounds__(WG) void k_window_merge(const uint32_t *__restrict_
     part[threadIdx.x] = sum;
     __syncthreads();
     if (ph == 0 && b < hw) {
-        for (uint32_t k = 1; k < PH; ++k) sum += part[k * 64 + threadIdx.x];
+        for (uint32_t k = 1; k < PH; ++k) sum += part[k * NB + threadIdx.x];
         counts[w0 + b] += sum;
     }
 }
@@ -495,10 +520,13 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint32_t *__restrict__ tbase, const uint32_t *__restrict__ tpre,
     const uint32_t *__restrict__ totals, uint32_t ranges, uint32_t tiles, uint32_t range_bins,
     uint32_t num_bins, uint32_t owners, Partials out, uint64_t *__restrict__ starts,
-    uint32_t *__restrict__ counts, uint32_t accumulate)
+    uint32_t *__restrict__ counts, uint32_t accumulate, const uint32_t *__restrict__ hot_seen)
 {
     extern __shared__ u32x4 lds4[];
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
+    // the hot slot, unless this run's sample showed no value that it would
+    // take (k_window_pick): then its checks would cost and find nothing
+    const bool hot_on = AGG == 1 && (!hot_seen || *hot_seen != 0u);
     uint64_t *bs = reinterpret_cast<uint64_t *>(lds + range_bins);  // [ranges + 1]
     uint32_t *misc = reinterpret_cast<uint32_t *>(bs + ranges + 1);  // [0] ta [1] tb
     const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
@@ -692,8 +720,8 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                                                (uint32_t)qv[k].z, (uint32_t)qv[k].w};
                     if constexpr (AGG == 1) {
                         uint32_t nxt;
-                        if (hot_should_switch(hs, words[0] & 0xFFFFu, first[k] == 0u && last[k] > 0u,
-                                              &nxt)) {
+                        if (hot_on && hot_should_switch(hs, words[0] & 0xFFFFu,
+                                                        first[k] == 0u && last[k] > 0u, &nxt)) {
                             const uint32_t tk = hot_take(hs);
                             if (lane == 0 && tk != 0u) lds_add(lds, hs.h, tk);
                             hs.h = nxt;
