@@ -119,7 +119,10 @@ typedef struct {
                              place by the partition workgroups (their elements are never
                              staged), at the heaviest place a 1,024-element sample of each
                              run's input shows: 0 auto (from 2^22 elements, used when the
-                             window holds at least a quarter of the sample), 1 never, 2 always */
+                             window holds at least a quarter of the sample), 1 never, 2 always.
+                             Unless 1, the same sample also names a hot value outside the
+                             window (a thirty-second of the sample or more), which the
+                             partition counts in registers and never stages. */
 } hist_plan_opts_t;
 
 /* Bins of SCATTER's in-place window (hist_plan_opts_t.window). */

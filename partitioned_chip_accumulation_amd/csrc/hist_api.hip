@@ -39,9 +39,15 @@ constexpr uint32_t S_STREAM = 1u << kScatterShift;       // SCATTER range = 3276
 // range-major: 2^26 bins 567 vs 672 us, 2^25 360 vs 404, 2^24 263.3 vs 262.2
 // (the transpose's cost equals the partition's saving there).
 constexpr uint32_t kTileMajorRanges = 1024;
-constexpr uint32_t kScatterWG = 1024;
+constexpr uint32_t kScatterWG = 1024;        // the owners' workgroup
+constexpr uint32_t kPartWG = 1024;           // the partition's workgroup
+// The partition's persistent grid, per CU: at its register count one
+// 1024-thread workgroup is resident per CU, and a second one per CU would
+// start cold after the first (on 2^26 uniform elements over 2^20 bins the
+// partition took 92 us with one per CU against 98 with two).
+constexpr uint32_t kPartPerCU = 1;
 constexpr uint32_t kScatterVPT = 4;          // vectors per thread in a scatter tile
-constexpr uint32_t kScatterTile = kScatterWG * kScatterVPT * 4;  // 16384 elements
+constexpr uint32_t kScatterTile = kPartWG * kScatterVPT * 4;  // 16384 elements
 constexpr uint32_t kScatterCap = kScatterTile + 8;               // staging slots per tile
 // AUTO uses RANGE up to this many 16-bit ranges' worth of bins (318,464) and
 // SCATTER beyond: on 2^26 uniform elements SCATTER wins from 2^19 bins on
@@ -415,13 +421,13 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
         const uint32_t S = 1u << kScatterShift;
         const uint32_t R = ceil_div(num_bins, S);
         const uint64_t nvec_max = max_n / 4;
-        const uint32_t T = std::max<uint32_t>(1, ceil_div(nvec_max, kScatterWG * kScatterVPT));
+        const uint32_t T = std::max<uint32_t>(1, ceil_div(nvec_max, kPartWG * kScatterVPT));
         uint32_t W = (uint32_t)opts.groups;
         if (W == 0) W = (uint32_t)d.cu;
         // Sub-counters per range in the partition's rank atomics: up to 16,
-        // within 2,048 counters per tile.
+        // within two counters per partition thread.
         uint32_t qlog = 4;
-        while (qlog > 0 && (R << qlog) > 2048) --qlog;
+        while (qlog > 0 && (R << qlog) > 2 * kPartWG) --qlog;
         p->range_bins = S;
         p->ranges = R;
         p->tiles = T;
@@ -459,11 +465,11 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
         p->window = opts.window == 1 ? 1u : opts.window == 2 ? 2u : 0u;
         if (p->window != 1) {
             p->wbins = HIST_WINDOW_BINS;
-            p->wrows = std::min<uint32_t>(T, 2u * (uint32_t)d.cu);
+            p->wrows = std::min<uint32_t>(T, kPartPerCU * (uint32_t)d.cu);
             p->off_wsel = off;
             off += 256;
             p->off_wpart = off;
-            off += align_up((uint64_t)p->wrows * p->wbins * 4, 256);
+            off += align_up((uint64_t)p->wrows * (p->wbins + pca::kWindowRowPad) * 4, 256);
         }
         p->need = off;
     }
@@ -608,19 +614,18 @@ uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes)
 hipError_t launch_partition(const hist_plan_impl *p, pca::InputView in, uint32_t T, hipStream_t s,
                             const KEv &ev, bool window)
 {
-    auto k = pca::k_partition<kScatterWG, kScatterVPT>;
+    auto k = pca::k_partition<kPartWG, kScatterVPT>;
     const uint32_t npad = ((p->ranges << p->qlog) + 3u) & ~3u;
-    const uint32_t bytes = (2 * npad + 64) * 4 + kScatterCap * 2 + (window ? p->wbins * 4 : 0u);
+    const uint32_t bytes = (3 * npad + 64) * 4 + 2 * kScatterCap * 2 + (window ? p->wbins * 4 + 16 : 0u);
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
-    // persistent: a grid of two workgroups per CU, each walking tiles (at its
-    // register count one 1024-thread workgroup is resident per CU at a time)
-    const uint32_t grid = std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu);
+    // persistent: kPartPerCU workgroups per CU, each walking tiles
+    const uint32_t grid = std::min<uint32_t>(T, kPartPerCU * (uint32_t)p->dev.cu);
     uint32_t *tcnt = reinterpret_cast<uint32_t *>(p->ws + (p->tile_major ? p->off_tpre : p->off_tcnt));
     uint32_t *tbase =
         reinterpret_cast<uint32_t *>(p->ws + (p->tile_major ? p->off_tbase_tm : p->off_tbase));
     const uint32_t rstride = p->tile_major ? 1u : T, tstride = p->tile_major ? p->ranges : 1u;
-    launch(k, dim3(grid), dim3(kScatterWG), bytes, s, ev, in, p->num_bins, kScatterShift, p->ranges,
+    launch(k, dim3(grid), dim3(kPartWG), bytes, s, ev, in, p->num_bins, kScatterShift, p->ranges,
            p->qlog, T, reinterpret_cast<uint16_t *>(p->ws + p->off_stage), kScatterCap, tcnt, tbase,
            rstride, tstride,
            window ? reinterpret_cast<const uint32_t *>(p->ws + p->off_wsel) : (const uint32_t *)nullptr,
@@ -853,7 +858,7 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     }
 
     // SCATTER
-    const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kScatterWG * kScatterVPT));
+    const uint32_t T = std::max<uint32_t>(1, ceil_div(in.nvec, kPartWG * kScatterVPT));
     if (T > p->tiles) return HIST_ERR_INVALID_ARG;  // cannot happen for n <= max_n
     // the in-place window: chosen on the device from a sample of this input
     // (AUTO leaves it out below 2^22 elements, where the pick's few
@@ -887,7 +892,7 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
     {
         const KEv oev = tm.ev(PH_OWNER);
         // the pick's verdict on a hot value, when it ran
-        const uint32_t *hot = window ? wsel + 1 : nullptr;
+        const uint32_t *hot = window ? wsel + pca::kSelOwnersHot : nullptr;
         switch (p->agg) {
         case 0: e = launch_owner_t<0>(p, T, counts, accumulate, stream, oev, hot); break;
         case 1: e = launch_owner_t<1>(p, T, counts, accumulate, stream, oev, hot); break;
@@ -908,7 +913,7 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         launch(pca::k_window_merge<1024>, dim3(ceil_div(p->wbins, pca::kWindowMergeBins)), dim3(1024), 0, stream,
                tm.ev(PH_SLOTS, false, true), (const uint32_t *)wsel,
                reinterpret_cast<const uint32_t *>(p->ws + p->off_wpart),
-               std::min<uint32_t>(T, 2u * (uint32_t)p->dev.cu), p->wbins, num_bins, counts);
+               std::min<uint32_t>(T, kPartPerCU * (uint32_t)p->dev.cu), p->wbins, num_bins, counts);
         if (hipGetLastError() != hipSuccess) return HIST_ERR_HIP;
     }
     return HIST_OK;

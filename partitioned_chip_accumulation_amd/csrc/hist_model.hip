@@ -13,7 +13,8 @@
 //     input, what it stages, how many partial rows it merges;
 //   - a sample of the input for what the data decides: duplicate lanes per
 //     LDS instruction (same-word contention), carry events of packed
-//     counters, and the hot value the wave hot slot would take.
+//     counters, the hot value the wave hot slot would take, and what the
+//     two-phase path's own sampling counts in place (a window, a hot value).
 // Nothing is fitted to timings of the schedules themselves.
 #include "hist.h"
 #include "hist_bench.h"
@@ -23,6 +24,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 namespace {
@@ -43,6 +45,18 @@ const hist_model_calib_t kMi355x = {
     42.8,    // scatter_fixed_us: 2 T(2^22) - T(2^23), two-phase over 2^20 bins
 };
 
+// What the two-phase path's owners see once k_window_pick has chosen (from
+// 2^22 elements): the window's and the hot value's elements are counted by
+// the partition and never staged.
+struct PickStats {
+    bool window = false;  // the window is taken (a quarter of the sample or more)
+    double win_frac = 0;  // share of all the elements the window counts
+    double hv_frac = 0;   // share of all the elements the partition counts in registers
+    double hot_frac = 0;  // share of the staged elements the owners' hot slot counts
+    double dups = 0;      // same-word lanes per owner instruction (32-bit words)
+    double dups_hot = 0;  // the same without the hot slot's lanes
+};
+
 // What a sample of the input says, for every schedule.
 struct SampleStats {
     uint64_t total = 0;            // sample elements
@@ -56,7 +70,48 @@ struct SampleStats {
     double win_frac = 0;           // share of all the elements in the heaviest window of
                                    // HIST_WINDOW_BINS bins (at 256-bin steps, as the
                                    // two-phase path's own sampling places it)
+    PickStats pick;
 };
+
+// Same-word lanes per 64-lane instruction over v (consecutive groups of 64,
+// at most 1,024 of them), with and without the lanes holding `hot`.
+void lane_dups(const std::vector<uint32_t> &v, int shift, bool drop, uint32_t hot, double *all,
+               double *without)
+{
+    const uint32_t groups = std::min<uint32_t>((uint32_t)(v.size() / 64), 1024);
+    double a = 0, b = 0;
+    uint32_t w[64];
+    for (uint32_t g = 0; g < groups; ++g) {
+        const uint32_t *row = v.data() + (size_t)g * 64;
+        for (int i = 0; i < 64; ++i) w[i] = row[i] >> shift;
+        std::sort(w, w + 64);
+        a += (double)(64 - (std::unique(w, w + 64) - w));
+        int m = 0;
+        for (int i = 0; i < 64; ++i)
+            if (!drop || row[i] != hot) w[m++] = row[i] >> shift;
+        std::sort(w, w + m);
+        b += (double)(m - (std::unique(w, w + m) - w));
+    }
+    *all = groups ? a / groups : 0.0;
+    if (without) *without = groups ? b / groups : 0.0;
+}
+
+// The most frequent value of v and its copies (0, 0 when v is empty).
+std::pair<uint32_t, uint32_t> most_frequent(std::vector<uint32_t> v)
+{
+    std::sort(v.begin(), v.end());
+    uint32_t best = 0, best_n = 0;
+    for (size_t i = 0; i < v.size();) {
+        size_t j = i;
+        while (j < v.size() && v[j] == v[i]) ++j;
+        if (j - i > best_n) {
+            best_n = (uint32_t)(j - i);
+            best = v[i];
+        }
+        i = j;
+    }
+    return {best, best_n};
+}
 
 // Whether the wave hot slot takes a value that a share p of the elements
 // hold: a check (every 4th vector, first lane's value) latches it when at
@@ -100,25 +155,9 @@ SampleStats sample_stats(const int32_t *s, uint32_t sn, uint32_t num_bins)
     if (latched) st.hot_frac = (double)hot_n / (double)st.valid;
     // one wave instruction: 64 consecutive elements (the inputs are in no
     // particular order, so any 64 are like the kernels' 64 lanes)
-    const uint32_t groups = std::min<uint32_t>((uint32_t)(v.size() / 64), 1024);
-    uint32_t w[64];
-    for (uint32_t g = 0; g < groups; ++g) {
-        const uint32_t *row = v.data() + (size_t)g * 64;
-        for (int k = 0; k < 3; ++k) {
-            for (int i = 0; i < 64; ++i) w[i] = row[i] >> k;
-            std::sort(w, w + 64);
-            st.dups[k] += (double)(64 - (std::unique(w, w + 64) - w));
-        }
-        int m = 0;
-        for (int i = 0; i < 64; ++i)
-            if (!latched || row[i] != hot) w[m++] = row[i];
-        std::sort(w, w + m);
-        st.dups_hot += (double)(m - (std::unique(w, w + m) - w));
-    }
-    if (groups) {
-        for (double &d : st.dups) d /= groups;
-        st.dups_hot /= groups;
-    }
+    lane_dups(v, 0, latched, hot, &st.dups[0], &st.dups_hot);
+    lane_dups(v, 1, false, 0, &st.dups[1], nullptr);
+    lane_dups(v, 2, false, 0, &st.dups[2], nullptr);
     // the heaviest window, from 256-bin buckets (more per bucket above 8,192
     // buckets) and a prefix sum over them, as k_window_pick finds it
     uint32_t blog = 8;
@@ -129,8 +168,37 @@ SampleStats sample_stats(const int32_t *s, uint32_t sn, uint32_t num_bins)
     for (uint32_t x : v) ++pre[(x >> blog) + 1];
     for (uint32_t b = 0; b < nb; ++b) pre[b + 1] += pre[b];
     uint64_t best = 0;
-    for (uint32_t j = 0; j < nb; ++j) best = std::max(best, pre[std::min(j + wb, nb)] - pre[j]);
+    uint32_t best_j = 0;
+    for (uint32_t j = 0; j < nb; ++j)
+        if (pre[std::min(j + wb, nb)] - pre[j] > best) {
+            best = pre[std::min(j + wb, nb)] - pre[j];
+            best_j = j;
+        }
     st.win_frac = st.total ? (double)best / (double)st.total : 0.0;
+    // what the pick leaves to the owners: the window when it holds a quarter,
+    // then the most frequent value outside it when that holds a thirty-second
+    // of all the elements; the owners' hot slot then looks for the next value
+    PickStats &pk = st.pick;
+    pk.window = st.win_frac >= 0.25;
+    pk.win_frac = pk.window ? st.win_frac : 0.0;
+    const uint64_t w0 = (uint64_t)best_j << blog, w1 = w0 + HIST_WINDOW_BINS;
+    std::vector<uint32_t> outside;
+    outside.reserve(v.size());
+    for (uint32_t x : v)
+        if (!pk.window || x < w0 || x >= w1) outside.push_back(x);
+    const auto top = most_frequent(outside);
+    const bool hv = st.total && (double)top.second * 32.0 >= (double)st.total;
+    pk.hv_frac = hv ? (double)top.second / (double)st.total : 0.0;
+    std::vector<uint32_t> staged;
+    staged.reserve(outside.size());
+    for (uint32_t x : outside)
+        if (!hv || x != top.first) staged.push_back(x);
+    // the owners' slot runs only when that next value holds a thirty-second too
+    const auto next = most_frequent(staged);
+    const bool next_latched = !staged.empty() && (double)next.second * 32.0 >= (double)st.total &&
+                              hot_slot_latches((double)next.second / (double)staged.size());
+    pk.hot_frac = next_latched ? (double)next.second / (double)staged.size() : 0.0;
+    lane_dups(staged, 0, next_latched, next.first, &pk.dups, &pk.dups_hot);
     return st;
 }
 
@@ -176,10 +244,12 @@ void predict_one(const hist_device_desc_t &dev, const hist_model_calib_t &c, con
         // heaviest window holds a quarter of the input, its elements are
         // counted by the partition and never staged; its rows (one per
         // partition workgroup) are read back by the window merge
-        const bool win = n >= (1ull << 22) && st.win_frac >= 0.25;
-        const double staged = win ? std::max(0.0, valid - st.win_frac) : valid;
+        const bool picked = n >= (1ull << 22);
+        const bool win = picked && st.pick.window;
+        const double staged =
+            picked ? std::max(0.0, valid - st.pick.win_frac - st.pick.hv_frac) : valid;
         const double tiles = std::ceil((double)n / 16384.0);
-        const double rows = std::min(tiles, 2.0 * dev.cu_count);
+        const double rows = std::min(tiles, (double)dev.cu_count);
         const double win_us = win ? c.launch_us + rows * HIST_WINDOW_BINS * 4.0 / (c.read_gbps * 1e3) : 0.0;
         // partition: read the input, write 2-byte slots (a copy's rate for the
         // read and write bytes); owners: read the slots, one 32-bit LDS atomic
@@ -187,10 +257,13 @@ void predict_one(const hist_device_desc_t &dev, const hist_model_calib_t &c, con
         const double part = read_us + (2.0 * staged * n + 2.0 * staged * n) / (c.copy_gbps * 1e3);
         const double slots = 2.0 * staged * (double)n / (c.read_gbps * 1e3);
         // with the hot slot, the hot value's copies issue no LDS atomic at all
-        // (the window, when it holds the hot value, already took them)
-        const double d = aggregation == 1 ? st.dups_hot : st.dups[0];
+        // (from 2^22 elements the pick's window and hot value already took the
+        // hottest, and the slot looks for the next)
+        const double hot = picked ? st.pick.hot_frac : st.hot_frac;
+        const double d = picked ? (aggregation == 1 ? st.pick.dups_hot : st.pick.dups)
+                                : (aggregation == 1 ? st.dups_hot : st.dups[0]);
         const double owned = valid > 0 ? staged / valid : 0.0;
-        const double atomics = instr * owned * (aggregation == 1 && !win ? 1.0 - st.hot_frac : 1.0);
+        const double atomics = instr * owned * (aggregation == 1 ? 1.0 - hot : 1.0);
         const double lds = atomics * (c.lds_cycles + c.lds_dup_cycles * d) * cyc_us;
         e->pass_us = part + slots;
         e->lds_us = lds;

@@ -34,6 +34,30 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     return scratch[NW + w] + incl - v;
 }
 
+// The same with one barrier: every wave scans the per-wave totals itself.
+// scratch holds WG / 64 words, which the caller must not write again before
+// its next barrier.
+template <int WG>
+__device__ __forceinline__ uint32_t block_exclusive_scan_1b(uint32_t v, uint32_t *scratch,
+                                                            uint32_t *total)
+{
+    constexpr int NW = WG / 64;
+    const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane == 63) scratch[w] = incl;
+    __syncthreads();
+    const uint32_t s = lane < (uint32_t)NW ? scratch[lane] : 0u;
+    uint32_t si = s;
+#pragma unroll
+    for (int d = 1; d < NW; d <<= 1) {
+        const uint32_t o = __shfl_up(si, d, 64);
+        if (lane >= (uint32_t)d) si += o;
+    }
+    *total = (uint32_t)__builtin_amdgcn_readlane((int)si, NW - 1);
+    const uint32_t before = (uint32_t)__shfl((int)(si - s), (int)w, 64);
+    return before + incl - v;
+}
+
 // Phase 1b: per range r, tpre[r][t] = sum of tcnt[r][t'] over t' < t, and
 // totals[r] = the range's element count. Two passes, both spread over
 // (range, segment of kScanSeg tiles) workgroups so that every CU takes part:
@@ -136,6 +160,14 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
     return (uint32_t)(((p + 1) * W - 1) / N);
 }
 
+// no in-place window (k_window_pick found none worth it, or none was asked for)
+constexpr uint32_t kNoWindow = 0xFFFFFFFFu;
+// k_window_pick's words: the window's first bin, whether the owners' hot slot
+// has a value to take, the hot value the partition counts in registers
+constexpr uint32_t kSelWindow = 0, kSelOwnersHot = 1, kSelHotValue = 2;
+// a window-partials row: the window's bins, then the hot value's total
+constexpr uint32_t kWindowRowPad = 64;
+
 // Phase 1: route every element of a tile to its owning range.
 //
 // Tile t is body vectors [t * WG * VPT, ...) (tile 0 also takes the head
@@ -146,7 +178,11 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
 // exclusive scan of the counts gives each range's start, so the tile's slots
 // are grouped by range in an LDS staging buffer and copied out with full
 // 16-byte stores to stage[t * stage_cap ...]. Only the 16-bit slot is kept:
-// the range is implied by the position.
+// the range is implied by the position. Counters and staging buffers come in
+// pairs that alternate between tiles, so a tile's copy-out and the clearing
+// of its counters wait for no barrier of their own: they run after the next
+// tile's ranks, and a tile takes three barriers (ranks done, wave totals
+// posted, starts posted).
 //
 // Returning atomics on one LDS word are served one lane at a time (each lane
 // needs its own rank), so every range's counter is split into 2^qlog
@@ -159,8 +195,6 @@ __device__ __forceinline__ uint32_t owner_of(uint64_t p, uint64_t N, uint32_t W)
 // write, so the tables are written tile-major (rstride = 1, tstride = ranges)
 // and k_transpose turns them range-major. Element order inside a run is
 // whatever the atomics gave; counts do not depend on it.
-// no in-place window (k_window_pick found none worth it, or none was asked for)
-constexpr uint32_t kNoWindow = 0xFFFFFFFFu;
 
 template <int WG, int VPT>
 __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
@@ -174,14 +208,17 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
     extern __shared__ u32x4 smem4[];
     const uint32_t nsub = ranges << qlog;  // <= 2 * WG
     const uint32_t npad = (nsub + 3u) & ~3u;
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem4);
-    uint32_t *base = cnt + npad;
-    uint32_t *scratch = base + npad;  // block scan scratch + total
-    uint16_t *st = reinterpret_cast<uint16_t *>(scratch + 64);
-    // the in-place window: bins [w0, w0 + hw) are counted here, not staged
-    uint32_t *win = reinterpret_cast<uint32_t *>(st + stage_cap);
-    const uint32_t w0 = wsel ? *wsel : kNoWindow;
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem4);  // two sets of npad
+    uint32_t *base = cnt + 2 * npad;
+    uint32_t *scratch = base + npad;  // block scan scratch
+    uint16_t *st = reinterpret_cast<uint16_t *>(scratch + 64);  // two buffers of stage_cap
+    // the in-place window: bins [w0, w0 + hw) are counted here, not staged;
+    // so is the hot value hv (k_window_pick), in a register of each lane
+    uint32_t *win = reinterpret_cast<uint32_t *>(st + 2 * stage_cap);  // [wbins], then the hot total
+    const uint32_t w0 = wsel ? wsel[kSelWindow] : kNoWindow;
     const uint32_t hw = w0 == kNoWindow ? 0u : min(wbins, num_bins - w0);
+    const uint32_t hv = wsel ? wsel[kSelHotValue] : kNoWindow;
+    uint32_t hc = 0;
     const uint32_t tid = threadIdx.x;
     const uint32_t mask = (1u << shift) - 1u;
     const uint32_t q = lane_id() & ((1u << qlog) - 1u);
@@ -206,13 +243,24 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
         nx[E + 1] = (t == tiles - 1 && tid < in.tail) ? (uint32_t)in.ptr[in.head + 4 * in.nvec + tid]
                                                       : 0xFFFFFFFFu;
     };
+    // the previous tile's slots, still in its staging buffer: 16-byte vectors, tile
+    uint32_t prev_nv = 0, prev_t = 0;
+    auto copy_out = [&](uint32_t buf) {
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(st + buf * stage_cap);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)prev_t * stage_cap);
+        for (uint32_t i = tid; i < prev_nv; i += WG) d4[i] = s4[i];
+    };
     uint32_t t = blockIdx.x;
     if (t < tiles) load_tile(t);
-    for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
+    for (uint32_t i = tid; i < 2 * npad; i += WG) cnt[i] = 0u;
     for (uint32_t i = tid; i < hw; i += WG) win[i] = 0u;
+    if (wsel && tid == 0) win[wbins] = 0u;
     __syncthreads();
 
-    for (; t < tiles; t += gridDim.x) {
+    uint32_t b = 0;  // this tile's counters and staging buffer
+    for (; t < tiles; t += gridDim.x, b ^= 1u) {
+        uint32_t *cb = cnt + b * npad;
+        uint16_t *sb = st + b * stage_cap;
         uint32_t x[E + 2], rk[E + 2];
 #pragma unroll
         for (int e = 0; e < E + 2; ++e) x[e] = nx[e];
@@ -231,24 +279,36 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
 #pragma unroll
             for (int e = 0; e < E + 2; ++e) x[e] = x[e] - w0 < hw ? 0xFFFFFFFFu : x[e];
         }
+        if (hv != kNoWindow) {  // the hot value's copies: a register count, no LDS
+#pragma unroll
+            for (int e = 0; e < E + 2; ++e) {
+                const bool m = x[e] == hv;
+                hc += m ? 1u : 0u;
+                x[e] = m ? 0xFFFFFFFFu : x[e];
+            }
+        }
 #pragma unroll
         for (int e = 0; e < E + 2; ++e) {
             rk[e] = 0u;
-            if (x[e] < num_bins) rk[e] = lds_add_rtn(cnt, ((x[e] >> shift) << qlog) | q, 1u);
+            if (x[e] < num_bins) rk[e] = lds_add_rtn(cb, ((x[e] >> shift) << qlog) | q, 1u);
         }
-        __syncthreads();
+        __syncthreads();  // this tile's ranks are in; the previous tile's slots are staged
 
+        // the previous tile goes out, and its counters are cleared for the next
+        copy_out(b ^ 1u);
+        {
+            uint32_t *co = cnt + (b ^ 1u) * npad;
+            for (uint32_t i = tid; i < nsub; i += WG) co[i] = 0u;
+        }
+        uint32_t nvalid;
         {
             const uint32_t i0 = 2 * tid, i1 = 2 * tid + 1;
-            const uint32_t c0 = i0 < nsub ? cnt[i0] : 0u, c1 = i1 < nsub ? cnt[i1] : 0u;
-            uint32_t total;
-            const uint32_t ex = block_exclusive_scan<WG>(c0 + c1, scratch, &total);
+            const uint32_t c0 = i0 < nsub ? cb[i0] : 0u, c1 = i1 < nsub ? cb[i1] : 0u;
+            const uint32_t ex = block_exclusive_scan_1b<WG>(c0 + c1, scratch, &nvalid);
             if (i0 < nsub) base[i0] = ex;
             if (i1 < nsub) base[i1] = ex + c0;
-            if (tid == 0) scratch[63] = total;
         }
-        __syncthreads();
-        const uint32_t nvalid = scratch[63];
+        __syncthreads();  // the starts are posted
         for (uint32_t r = tid; r < ranges; r += WG) {
             const uint32_t b0 = base[r << qlog];
             const uint32_t b1 = r + 1 < ranges ? base[(r + 1) << qlog] : nvalid;
@@ -256,60 +316,104 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
             tcnt[at] = b1 - b0;
             tbase[at] = b0;
         }
+        // every element's start is read, its own counter's or counter 0's, so
+        // that a group of reads waits once; then the valid ones are stored
+        constexpr int G = (E + 2) % 6 == 0 ? 6 : 1;
 #pragma unroll
-        for (int e = 0; e < E + 2; ++e)
-            if (x[e] < num_bins) st[base[((x[e] >> shift) << qlog) | q] + rk[e]] = (uint16_t)(x[e] & mask);
-        __syncthreads();
-
-        // counters are free again: clear them for the next tile while copying out
-        for (uint32_t i = tid; i < nsub; i += WG) cnt[i] = 0u;
-        const uint32_t nv = (nvalid + 7u) >> 3;
-        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(st);
-        u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)t * stage_cap);
-        for (uint32_t i = tid; i < nv; i += WG) d4[i] = s4[i];
-        __syncthreads();  // staging and counters are reused by the next tile
+        for (int g = 0; g < E + 2; g += G) {
+            uint32_t at[G];
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const uint32_t xe = x[g + k];
+                at[k] = base[xe < num_bins ? ((xe >> shift) << qlog) | q : 0u] + rk[g + k];
+            }
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+                if (x[g + k] < num_bins) sb[at[k]] = (uint16_t)(x[g + k] & mask);
+        }
+        prev_nv = (nvalid + 7u) >> 3;
+        prev_t = t;
     }
-    // the workgroup's window counts: its row of the window partials
-    if (hw) {
+    // the last tile's slots
+    __syncthreads();
+    copy_out(b ^ 1u);
+    // the workgroup's window counts and hot-value total: its row of the
+    // window partials (kWindowRowPad words past the window's bins)
+    if (wsel) {
+        const uint32_t hsum = wave_sum(hc);
+        if (lane_id() == 0 && hsum) lds_add(win, wbins, hsum);
         __syncthreads();
-        for (uint32_t i = tid; i < hw; i += WG) wpart[(uint64_t)blockIdx.x * wbins + i] = win[i];
+        uint32_t *row = wpart + (uint64_t)blockIdx.x * (wbins + kWindowRowPad);
+        for (uint32_t i = tid; i < hw; i += WG) row[i] = win[i];
+        if (tid == 0) row[wbins] = win[wbins];
     }
 }
 
 // The heaviest window of wbins consecutive bins, from a sample of the input,
-// for k_partition to count in place. One workgroup: one sample per thread at
-// evenly spaced indices (1,024 scattered lines, which one CU fetches in a
-// few microseconds while the rest of the GPU waits: 4,096 took 12 us; the
-// share's standard error is then under 1.6%), counted into coarse
-// buckets (256 bins, or more so that there are at most 8,192), then the
-// window of wbins / bucket buckets with the most samples (the first such,
-// from a prefix sum). wsel[0] gets the window's first bin when it holds at
-// least samples / min_div of the sample (min_div 0: always), else kNoWindow;
-// wsel[1] gets whether some value outside that window holds 8 or more of one
-// wave's 64 samples, the share at which the owners' hot slot latches (0: the
-// owners leave the hot slot off for this run).
+// for k_partition to count in place, and the hottest value outside it. One
+// workgroup samples 1,024 elements, 1024 / WG consecutive ones at each of WG
+// evenly spaced places (with WG = 1024, 1,024 scattered lines, which one CU
+// fetches in a few microseconds while the rest of the GPU waits; a share's
+// standard error is then under 1.6%). The samples are counted into coarse buckets (256
+// bins, or more so that there are at most 8,192) and, by value, into an LDS
+// hash table; the window is the run of wbins / bucket buckets with the most
+// samples (the first such, from a prefix sum). wsel[kSelWindow] gets its
+// first bin when it holds at least samples / min_div of the sample (min_div
+// 0: always), else kNoWindow. Among the values outside the window, the one
+// with the most copies (the largest such value on a tie, so the choice does
+// not depend on the order of the atomics), when it holds at least 1/32 of
+// the samples, is the hot value (wsel[kSelHotValue], else kNoWindow) that the
+// partition counts in registers; wsel[kSelOwnersHot] says whether the next
+// value holds at least 1/32 of them too (0: the owners leave their hot slot
+// off for this run; its checks would find nothing to take: on Zipf s = 1.1
+// over 2^18 bins, whose second value holds 6%, the slot still took a run
+// from 598 to 489 us, while on the half-Gaussian it cost 8 us).
 template <int WG>
 __global__ __launch_bounds__(WG) void k_window_pick(const int32_t *__restrict__ x, uint64_t n,
                                                    uint32_t num_bins, uint32_t wbins,
                                                    uint32_t min_div, uint32_t *__restrict__ wsel)
 {
-    constexpr uint32_t kSamples = WG, kMaxBuckets = 8192, PER = kMaxBuckets / WG;
+    constexpr uint32_t S = 1024 / WG, kSamples = S * WG, kMaxBuckets = 8192, PER = kMaxBuckets / WG;
+    constexpr uint32_t kSlots = 2 * kSamples, kEmpty = 0xFFFFFFFFu, NW = WG / 64;
+    static_assert(kSlots == 2048, "the hash gives 11 bits");
     __shared__ uint32_t hist[kMaxBuckets];
+    __shared__ uint32_t keys[kSlots], cnts[kSlots];
     __shared__ uint32_t scratch[64];
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    // every sample's load goes out before the tables are cleared
+    uint32_t v[S];
+    const uint64_t at = (uint64_t)tid * n / WG;
+#pragma unroll
+    for (uint32_t k = 0; k < S; ++k) v[k] = (uint32_t)x[min(at + k, n - 1u)];
     uint32_t blog = 8;
     while ((((uint64_t)num_bins + (1u << blog) - 1u) >> blog) > kMaxBuckets) ++blog;
     const uint32_t nb = (uint32_t)(((uint64_t)num_bins + (1u << blog) - 1u) >> blog);
     for (uint32_t i = tid; i < kMaxBuckets; i += WG) hist[i] = 0u;
-    // every sample's load goes out before any is counted
-    uint32_t v[kSamples / WG];
-#pragma unroll
-    for (uint32_t i = 0; i < kSamples / WG; ++i)
-        v[i] = (uint32_t)x[(uint64_t)(tid + i * WG) * n / kSamples];
+    for (uint32_t i = tid; i < kSlots; i += WG) {
+        keys[i] = kEmpty;
+        cnts[i] = 0u;
+    }
     __syncthreads();
+    // buckets, and counts by value (linear probing; at most kSamples of the
+    // 2 * kSamples slots fill, so every probe ends)
 #pragma unroll
-    for (uint32_t i = 0; i < kSamples / WG; ++i)
-        if (v[i] < num_bins) lds_add(hist, v[i] >> blog, 1u);
+    for (uint32_t k = 0; k < S; ++k) {
+        const uint32_t val = v[k];
+        if (val < num_bins) {
+            lds_add(hist, val >> blog, 1u);
+            uint32_t h = (val * 2654435761u) >> (32 - 11);  // Knuth's multiplicative hash
+            for (;;) {
+                uint32_t old = kEmpty;
+                const bool took = __hip_atomic_compare_exchange_strong(
+                    keys + h, &old, val, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (took || old == val) {
+                    lds_add(cnts, h, 1u);
+                    break;
+                }
+                h = (h + 1u) & (kSlots - 1u);
+            }
+        }
+    }
     __syncthreads();
     // inclusive prefix over the buckets, PER per thread
     uint32_t local[PER], run = 0;
@@ -335,37 +439,56 @@ __global__ __launch_bounds__(WG) void k_window_pick(const int32_t *__restrict__ 
             best = max(best, ((hi - lo) << 13) | (kMaxBuckets - 1u - j));
         }
     }
-    __syncthreads();
-    // block max through the scratch words
-    const uint32_t lane = lane_id(), w = tid >> 6;
     for (int d = 32; d >= 1; d >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, d, 64));
     if (lane == 0) scratch[w] = best;
     __syncthreads();
-    if (tid == 0) {
-        uint32_t m = 0;
-        for (uint32_t i = 0; i < WG / 64; ++i) m = max(m, scratch[i]);
-        const uint32_t sum = m >> 13, j = kMaxBuckets - 1u - (m & (kMaxBuckets - 1u));
-        hist[0] = (min_div == 0 || (uint64_t)sum * min_div >= kSamples) ? (j << blog) : kNoWindow;
-    }
-    __syncthreads();
-    // the most copies of one value among a wave's samples outside the window
-    const uint32_t w0 = hist[0];
+    uint32_t m = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < NW; ++i) m = max(m, scratch[i]);
+    const uint32_t bsum = m >> 13, bj = kMaxBuckets - 1u - (m & (kMaxBuckets - 1u));
+    const uint32_t w0 = (min_div == 0 || (uint64_t)bsum * min_div >= kSamples) ? (bj << blog) : kNoWindow;
     const uint32_t hw = w0 == kNoWindow ? 0u : min(wbins, num_bins - w0);
-    const uint32_t mine = v[0];
-    const bool counted = mine < num_bins && !(mine - w0 < hw);
-    uint32_t most = 0;
-    for (uint32_t k = 0; k < 64; ++k) {
-        const uint32_t vk = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)k);
-        most = max(most, (uint32_t)__popcll(__ballot(counted && mine == vk)));
+    // the two (copies << 32 | value) maxima among the values outside the window
+    uint64_t a1 = 0, a2 = 0;
+    for (uint32_t i = tid; i < kSlots; i += WG) {
+        const uint32_t c = cnts[i], key = keys[i];
+        if (c && !(key - w0 < hw)) {
+            const uint64_t e = ((uint64_t)c << 32) | key;
+            a2 = max(a2, min(a1, e));
+            a1 = max(a1, e);
+        }
+    }
+    auto merge2 = [&](uint64_t b1, uint64_t b2) {
+        a2 = max(max(a2, b2), min(a1, b1));
+        a1 = max(a1, b1);
+    };
+    for (int d = 32; d >= 1; d >>= 1) {
+        auto xchg = [&](uint64_t q) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)q, d, 64);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(q >> 32), d, 64);
+            return ((uint64_t)hi << 32) | lo;
+        };
+        const uint64_t b1 = xchg(a1), b2 = xchg(a2);
+        merge2(b1, b2);
+    }
+    __syncthreads();  // every wave has read the window maxima
+    if (lane == 0) {
+        scratch[4 * w + 0] = (uint32_t)a1;
+        scratch[4 * w + 1] = (uint32_t)(a1 >> 32);
+        scratch[4 * w + 2] = (uint32_t)a2;
+        scratch[4 * w + 3] = (uint32_t)(a2 >> 32);
     }
     __syncthreads();
-    if (lane == 0) scratch[w] = most;
-    __syncthreads();
     if (tid == 0) {
-        uint32_t m = 0;
-        for (uint32_t i = 0; i < WG / 64; ++i) m = max(m, scratch[i]);
-        wsel[0] = w0;
-        wsel[1] = m >= 8u ? 1u : 0u;
+        a1 = a2 = 0;
+        for (uint32_t i = 0; i < NW; ++i)
+            merge2(((uint64_t)scratch[4 * i + 1] << 32) | scratch[4 * i],
+                   ((uint64_t)scratch[4 * i + 3] << 32) | scratch[4 * i + 2]);
+        const bool hot = (uint32_t)(a1 >> 32) * 32u >= kSamples;
+        wsel[kSelWindow] = w0;
+        wsel[kSelHotValue] = hot ? (uint32_t)a1 : kNoWindow;
+        // the next value: the second maximum, or the first when there is no hot one
+        wsel[kSelOwnersHot] = (uint32_t)((hot ? a2 : a1) >> 32) * 32u >= kSamples ? 1u : 0u;
     }
 }
 
@@ -383,7 +506,23 @@ __global__ __launch_bounds__(WG) void k_window_merge(const uint32_t *__restrict_
 {
     constexpr uint32_t NB = kWindowMergeBins, PH = WG / NB, U = 8;
     __shared__ uint32_t part[WG];
-    const uint32_t w0 = *wsel;
+    const uint32_t w0 = wsel[kSelWindow], hv = wsel[kSelHotValue];
+    if (w0 == kNoWindow && hv == kNoWindow) return;
+    const uint64_t stride = wbins + kWindowRowPad;
+    if (blockIdx.x == 0 && hv != kNoWindow) {
+        // the hot value's total over the rows, by the first workgroup
+        uint32_t h = 0;
+        for (uint32_t r = threadIdx.x; r < rows; r += WG) h += wpart[(uint64_t)r * stride + wbins];
+        h = wave_sum(h);
+        if (lane_id() == 0) part[threadIdx.x >> 6] = h;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t t = 0;
+            for (uint32_t k = 0; k < WG / 64; ++k) t += part[k];
+            counts[hv] += t;
+        }
+        __syncthreads();  // part is reused below
+    }
     if (w0 == kNoWindow) return;
     const uint32_t hw = min(wbins, num_bins - w0);
     const uint32_t b = blockIdx.x * NB + (threadIdx.x & (NB - 1u)), ph = threadIdx.x / NB;
@@ -393,11 +532,11 @@ __global__ __launch_bounds__(WG) void k_window_merge(const uint32_t *__restrict_
         for (; r + PH * (U - 1) < rows; r += PH * U) {
             uint32_t v[U];
 #pragma unroll
-            for (uint32_t u = 0; u < U; ++u) v[u] = wpart[(uint64_t)(r + PH * u) * wbins + b];
+            for (uint32_t u = 0; u < U; ++u) v[u] = wpart[(uint64_t)(r + PH * u) * stride + b];
 #pragma unroll
             for (uint32_t u = 0; u < U; ++u) sum += v[u];
         }
-        for (; r < rows; r += PH) sum += wpart[(uint64_t)r * wbins + b];
+        for (; r < rows; r += PH) sum += wpart[(uint64_t)r * stride + b];
     }
     part[threadIdx.x] = sum;
     __syncthreads();

@@ -72,16 +72,25 @@ def test_carry_events_appear_only_where_counts_wrap():
 
 
 def test_same_word_lanes_and_the_hot_slot():
-    n, B = 1 << 26, 1 << 20
-    uni = by_name(hist.predict(B, n, inputs.uniform(1, MS, B))[1])
-    # a tenth of the input on one value: lanes collide on its word, and the hot
-    # slot takes them out of the LDS atomics again
+    B = 1 << 20
     x = inputs.uniform(1, MS, B)
-    x[::10] = 524287
+    x[::10] = 524287  # a tenth of the input on one value
+    # below 2^22 elements the two-phase path samples nothing: the hot value's
+    # lanes collide on its word, and the owners' hot slot takes them out of
+    # the LDS atomics again
+    n = 1 << 21
+    uni = by_name(hist.predict(B, n, inputs.uniform(1, MS, B))[1])
     hot = by_name(hist.predict(B, n, x)[1])
     assert hot["scatter"]["lds_us"] > uni["scatter"]["lds_us"]
     assert hot["scatter+hot"]["lds_us"] < hot["scatter"]["lds_us"]
     assert uni["scatter+hot"]["lds_us"] == pytest.approx(uni["scatter"]["lds_us"], rel=0.02)
+    # from 2^22 the sample names the value, the partition counts it in
+    # registers, and the owners see the other nine tenths with no contention
+    n = 1 << 26
+    uni = by_name(hist.predict(B, n, inputs.uniform(1, MS, B))[1])
+    hot = by_name(hist.predict(B, n, x)[1])
+    assert hot["scatter"]["lds_us"] == pytest.approx(0.9 * uni["scatter"]["lds_us"], rel=0.03)
+    assert hot["scatter"]["pass_us"] < uni["scatter"]["pass_us"]
 
 
 def test_values_outside_the_bins_cost_no_atomics():

@@ -995,19 +995,43 @@ def top_cluster(seed, n, num_bins):
     return x.astype(np.int32)
 
 
+def hot_values(seed, n, num_bins, hot, cluster=None):
+    """Uniform over the bins, some negative and some past the last bin, with
+    each (value, share) of hot holding that share of the elements and, when
+    cluster is (first bin, bins, share), that share spread over those bins."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-50, num_bins + 50, size=n, dtype=np.int64)
+    u = rng.random(n)
+    lo = 0.0
+    for value, share in hot:
+        x[(u >= lo) & (u < lo + share)] = value
+        lo += share
+    if cluster:
+        first, width, share = cluster
+        m = (u >= lo) & (u < lo + share)
+        x[m] = first + rng.integers(0, width, size=int(m.sum()))
+    return x.astype(np.int32)
+
+
 WINDOW_CASES = [  # (label, input, bins)
     ("half-Gaussian shape 2^22", lambda: inputs.generate(5, n=1 << 22), 1 << 19),
     ("hot-bin shape 2^22", lambda: inputs.generate(4, n=1 << 22), 1 << 20),
     ("cluster at the last bins", lambda: top_cluster(51, (1 << 22) + 5, 700_001), 700_001),
     ("uniform 2^21 bins", lambda: rnd(52, 1 << 22, 0, 1 << 21), 1 << 21),
     ("below the sampling size", lambda: top_cluster(53, 100_003, 300_000), 300_000),
+    ("two hot values, no window", lambda: hot_values(54, (1 << 22) + 3, 1 << 22, [(777, 0.12), (3_000_001, 0.09)]),
+     1 << 22),
+    ("hot value beside a window",
+     lambda: hot_values(55, 1 << 22, 1 << 20, [(900_000, 0.08)], cluster=(1000, 4000, 0.4)), 1 << 20),
+    ("hot value at the last bin", lambda: hot_values(56, (1 << 22) + 1, 500_000, [(499_999, 0.2)]), 500_000),
 ]
 
 
 @pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
 def test_scatter_in_place_window(case):
     """SCATTER with its in-place window: the partition workgroups count the
-    heaviest 8,192 bins a sample shows in LDS and never stage them; their
+    heaviest 8,192 bins a sample shows in LDS, and a value that holds a
+    thirty-second of the sample in registers, and never stage either; their
     rows are added after the owners. Auto, off and forced must all be exact,
     at an aligned and a misaligned start, overwriting and accumulating."""
     label, make, bins = case

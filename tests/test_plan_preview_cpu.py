@@ -89,8 +89,9 @@ def scatter_workspace(num_bins, max_n, owners=256, window=True):
     plan's order: staged slots, run tables (counts, starts, prefix), range totals,
     segment totals, range starts, from 1,024 ranges a tile-major copy of the
     run starts, W + R partial rows of 32,768-bin slices, then (unless the
-    in-place window is off) the window's base word and one 16,384-bin row per
-    partition workgroup (min(tiles, 2 x CUs) of them)."""
+    in-place window is off) the pick's words and, per partition workgroup
+    (min(tiles, CUs) of them), a row of the window's 8,192 bins and 64
+    words more, the first of which holds the hot value's total."""
     R = -(-num_bins // 32768)
     T = max(1, -(-(max_n // 4) // 4096))
     b = align(T * 16392 * 2) + 3 * align(R * T * 4) + align(R * 4)
@@ -99,7 +100,7 @@ def scatter_workspace(num_bins, max_n, owners=256, window=True):
         b += align(R * T * 4)
     b += partial_bytes(owners + R, 32768)
     if window:
-        b += 256 + align(min(T, 512) * hist.WINDOW_BINS * 4)
+        b += 256 + align(min(T, 256) * (hist.WINDOW_BINS + 64) * 4)
     return b
 
 
