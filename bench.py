@@ -486,10 +486,14 @@ def counters_for(key: str) -> dict:
 
 def dominant_kernel(phases: dict, n: int, B: int):
     """(phase name, algorithmic bytes per launch, average launch seconds,
-    launches) of the phase with the most device time. The sweep and the
-    partition read each element once (4 bytes); the owner kernel reads its
-    2-byte routed slots; the merges write the 4-byte bins."""
-    name, (ms, launches) = max(phases.items(), key=lambda kv: kv[1][0])
+    launches) of the kernel that reads the input (sweep, partition or
+    stream), else of the phase with the most device time. On a launch-bound
+    input the merge can take as long as the sweep; the roofline still
+    describes the sweep. The sweep and the partition read each element once
+    (4 bytes); the owner kernel reads its 2-byte routed slots; the merges
+    write the 4-byte bins."""
+    readers = {k: v for k, v in phases.items() if k in ("sweep", "partition", "stream")}
+    name, (ms, launches) = max((readers or phases).items(), key=lambda kv: kv[1][0])
     if name in ("sweep", "partition", "stream"):
         nbytes = 4 * n
     elif name == "owner_hist":

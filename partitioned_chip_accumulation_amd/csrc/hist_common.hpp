@@ -25,14 +25,26 @@ struct InputView {
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// Inclusive sums by DPP, one VALU add a step with no LDS round trip: row
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes (a lane shifted in
+// from outside the row reads 0), then, across rows, lane 15 of rows 0 and 2
+// into rows 1 and 3 (row_bcast:15) and lane 31 into rows 2 and 3
+// (row_bcast:31). Every lane of the wave must be active: DPP reads the
+// source lane's register whether or not that lane runs.
+__device__ __forceinline__ uint32_t row_inclusive_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    return v;
+}
+
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
 {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o = __shfl_up(v, d, 64);
-        if (lane >= (uint32_t)d) v += o;
-    }
+    v = row_inclusive_scan(v);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return v;
 }
 
@@ -99,11 +111,10 @@ struct HotSlot {
     uint32_t tick = 0;     // wave-uniform: candidates are checked every 4th vector
 };
 
+// The sum over the wave's 64 lanes, in every lane (all lanes active).
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(v), 63);
 }
 
 // The wave's pending count for h, summed (whole wave, convergent).

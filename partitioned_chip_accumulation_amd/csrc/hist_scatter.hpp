@@ -46,15 +46,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_1b(uint32_t v, uint32_t
     const uint32_t incl = wave_inclusive_scan(v);
     if (lane == 63) scratch[w] = incl;
     __syncthreads();
+    static_assert(NW <= 16, "the wave totals fit one row of 16 lanes");
     const uint32_t s = lane < (uint32_t)NW ? scratch[lane] : 0u;
-    uint32_t si = s;
-#pragma unroll
-    for (int d = 1; d < NW; d <<= 1) {
-        const uint32_t o = __shfl_up(si, d, 64);
-        if (lane >= (uint32_t)d) si += o;
-    }
+    const uint32_t si = row_inclusive_scan(s);
     *total = (uint32_t)__builtin_amdgcn_readlane((int)si, NW - 1);
-    const uint32_t before = (uint32_t)__shfl((int)(si - s), (int)w, 64);
+    const uint32_t before = (uint32_t)__builtin_amdgcn_readlane(
+        (int)(si - s), __builtin_amdgcn_readfirstlane((int)w));
     return before + incl - v;
 }
 

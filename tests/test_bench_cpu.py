@@ -8,6 +8,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -50,3 +51,18 @@ def test_more_than_one_gpu_is_refused_before_any_device_call():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_the_roofline_follows_the_kernel_that_reads_the_input():
+    # a launch-bound input whose merge took as long as its sweep
+    name, nbytes, avg_s, launches = bench.dominant_kernel(
+        {"sweep": (4.31, 1), "merge": (4.84, 1)}, n=1 << 20, B=8192)
+    assert (name, nbytes, launches) == ("sweep", 4 << 20, 1)
+    assert avg_s == pytest.approx(4.31e-3)
+    # the two-phase path: the partition, not the longer owner phase
+    name, nbytes, _, _ = bench.dominant_kernel(
+        {"partition": (3.0, 10), "owner_hist": (4.0, 10), "slot_merge": (0.2, 10)}, n=1000, B=10)
+    assert (name, nbytes) == ("partition", 4000)
+    # no reader timed: the longest phase, priced at the bins it writes
+    name, nbytes, _, _ = bench.dominant_kernel({"merge": (1.0, 2)}, n=1000, B=10)
+    assert (name, nbytes) == ("merge", 40)
