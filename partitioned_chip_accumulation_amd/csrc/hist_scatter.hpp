@@ -108,6 +108,61 @@ __global__ __launch_bounds__(WG) void k_seg_fix(uint32_t tiles, uint32_t nseg,
     for (uint32_t t = s0 + tid; t < s1; t += WG) p[t] += off;
 }
 
+// The same in one pass for a range of at most WG * PER tiles: one
+// workgroup per range loads all its run lengths at once, row by row (tile k
+// * WG + thread, so every load and store is one contiguous row), scans each
+// row across its waves, and wave 0 scans the (row, wave) totals in row-major
+// order, which is the tiles' order. Two barriers and one memory round trip,
+// where the two passes above take two kernels.
+template <int WG, int PER>
+__global__ __launch_bounds__(WG) void k_range_scan(const uint32_t *__restrict__ tcnt, uint32_t tiles,
+                                                   uint32_t *__restrict__ tpre,
+                                                   uint32_t *__restrict__ totals)
+{
+    constexpr uint32_t NW = WG / 64, NT = PER * NW;
+    static_assert(NT % 64 == 0 && NT <= 64 * 8, "wave 0 scans the totals, 8 per lane");
+    __shared__ uint32_t tot[NT + 1];
+    const uint32_t r = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+    const uint32_t *c = tcnt + (uint64_t)r * tiles;
+    uint32_t *p = tpre + (uint64_t)r * tiles;
+    const uint32_t rows = (tiles + WG - 1) / WG;  // <= PER
+    uint32_t v[PER], incl[PER];
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) v[k] = k < rows && k * WG + tid < tiles ? c[k * WG + tid] : 0u;
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k) {
+        incl[k] = 0u;
+        if (k < rows) {  // uniform
+            incl[k] = wave_inclusive_scan(v[k]);
+            if (lane == 63) tot[k * NW + w] = incl[k];
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        constexpr uint32_t E = NT / 64;
+        uint32_t a[E], sum = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < E; ++i) {
+            const uint32_t at = lane * E + i;
+            a[i] = at < rows * NW ? tot[at] : 0u;
+            sum += a[i];
+        }
+        const uint32_t in = wave_inclusive_scan(sum);
+        uint32_t run = in - sum;
+#pragma unroll
+        for (uint32_t i = 0; i < E; ++i) {
+            tot[lane * E + i] = run;
+            run += a[i];
+        }
+        if (lane == 63) tot[NT] = in;
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < PER; ++k)
+        if (k < rows && k * WG + tid < tiles) p[k * WG + tid] = tot[k * NW + w] + incl[k] - v[k];
+    if (tid == 0) totals[r] = tot[NT];
+}
+
 // Two [rows][cols] uint32 tables (blockIdx.z picks which) to [cols][rows],
 // through LDS in 64 x 64 tiles: reads and writes are both 256-byte rows.
 __global__ __launch_bounds__(256) void k_transpose(const uint32_t *__restrict__ src0,
