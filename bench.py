@@ -15,6 +15,12 @@ histograms a series of batches with a plan per stream. (`--streams 2` makes
 that the timed mode; the roofline's per-launch durations then include the
 overlap.)
 
+Before the W warm-up steps of each timed region, 0.3 s of untimed runs of
+the same plan let the clocks settle: with K = 20 a region lasts about a
+millisecond, and a fresh box's first milliseconds run below the settled clock
+(20-step runs measured 52.3-53.0 us per step without this, 500-step runs
+50.2).
+
 Prints one JSON line (rank 0). Throughput `value` is Gelem/s over the K timed
 steps (wall clock between two device synchronisations, no instrumentation in
 between). `roofline` is for the dominant kernel, timed live over a second run
@@ -137,6 +143,19 @@ def reference_counts(x, num_bins: int):
     import numpy as np
     v = x[(x >= 0) & (x < num_bins)]
     return np.bincount(v, minlength=num_bins).astype(np.uint32)
+
+
+def settle(run, seconds: float = 0.3):
+    """Call run(k) untimed for about `seconds` (in groups of 8, synchronised),
+    so that the timed steps after it meet settled clocks."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            run(k)
+            k += 1
+        torch.cuda.synchronize()
 
 
 def settle_clocks(B, n, xs, out, seconds: float = 0.3):
@@ -539,6 +558,7 @@ def time_workload(cfg: int, steps: int, warmup: int, dev, check: bool = True,
         xs += [xs[0].clone() for _ in range(3)]  # as the headline: four copies in rotation
     out = torch.empty(w.num_bins, dtype=torch.int32, device=dev)
     plan = hist.Plan(w.num_bins, w.n, device=dev)
+    settle(lambda k: plan.run(xs[k % len(xs)], out))
     for k in range(warmup):
         plan.run(xs[k % len(xs)], out)
     torch.cuda.synchronize(dev)
@@ -709,6 +729,7 @@ def main():
     def timed(events: bool, ns: int):
         for p in plans[:ns]:
             p.timing_enable((args.steps + args.warmup) if events else 0)
+        settle(lambda k: step(k, ns))
         for k in range(args.warmup):
             step(k, ns)
         torch.cuda.synchronize(dev)
