@@ -58,6 +58,27 @@ __device__ __forceinline__ uint32_t lds_add_rtn(uint32_t *lds, uint32_t slot, ui
     return __hip_atomic_fetch_add(lds + slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// v << (sh mod 32), the shift as the hardware does it: VOP shifts read only
+// the low five bits of the amount, so a caller need not mask it (in C++ a
+// shift by 32 or more is undefined, and a mask would cost an instruction).
+__device__ __forceinline__ uint32_t shl_mod32(uint32_t v, uint32_t sh)
+{
+    uint32_t r;
+    asm("v_lshlrev_b32_e64 %0, %1, %2" : "=v"(r) : "v"(sh), "v"(v));
+    return r;
+}
+
+// A returning add to the dynamic LDS word at byte address a. A kernel that
+// declares no static LDS has its dynamic block at LDS address 0, so an offset
+// into the block is the address itself and needs no base added per access.
+// Only kernels with no static LDS may use this; a compiler check keeps them so.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ uint32_t dyn_lds_add_rtn(uint32_t a, uint32_t v)
+{
+    return __hip_atomic_fetch_add((lds_u32 *)(uintptr_t)a, v, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Add one to lds[slot] for every lane with valid set.
 //
 // ROUNDS > 0 adds a bounded wave-level duplicate aggregation in front of the

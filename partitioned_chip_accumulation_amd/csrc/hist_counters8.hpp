@@ -61,69 +61,60 @@ __device__ __forceinline__ void add8(uint32_t *words, uint32_t *evlist, uint32_t
     log_carries8(evlist, ev_count, cap, s >> 2, old, delta);
 }
 
-// Unaggregated 8-bit counting of N elements at once (all ds_add_rtn_u32 are
-// issued before any returned value is examined; N <= 15). An add of 1 can
-// carry only when the byte it increments was 0xFF, which one bit-field
-// extract tests. The carries then take one wave-uniform branch that logs all
-// of the wave's events with a single LDS atomic: each lane's offset in the
-// wave's block is the sum of its lower lanes' event counts, taken from one
-// ballot per event a lane has (mostly one). Skewed input, whose hot bins
-// wrap a byte every 256 counts, takes this branch often.
-template <int N>
-__device__ __forceinline__ void count8_batch(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
-                                             uint32_t cap, const uint32_t (&s)[N],
-                                             const bool (&ok)[N])
+// Log the carries of an add of one to byte q0 = t / 8 (t mod 32 its bit
+// offset) of the word at slot offset a (a multiple of 4), which returned old
+// with that byte 0xFF (one lane on its own). The carry leaves byte q0 and runs
+// on through every 0xFF byte above it, up to byte 3: n >= 1 events, entries
+// a | q0 .. a | (q0 + n - 1). The bytes of ~old above bit t are zero exactly
+// where old's are 0xFF, so n is the count of whole zero bytes at the bottom
+// of ~old >> t, capped at the word's top byte.
+__device__ __forceinline__ void log_carry_chain8(uint32_t *evlist, uint32_t *ev_count, uint32_t cap,
+                                                 uint32_t a, uint32_t old, uint32_t t)
 {
-    uint32_t old[N], sh[N];
+    const uint32_t q0 = (t >> 3) & 3u;
+    const uint32_t y = ~old >> (t & 31u);
+    const uint32_t n = y == 0u ? 4u - q0 : min((uint32_t)__builtin_ctz(y) >> 3, 4u - q0);
+    uint32_t i = lds_add_rtn(ev_count, 0, n);
+    if (i < cap) evlist[i] = a | q0;
+    for (uint32_t j = 1; j < n; ++j)
+        if (i + j < cap) evlist[i + j] = a | (q0 + j);
+}
+
+// Unaggregated 8-bit counting of N elements at once (all ds_add_rtn_u32 are
+// issued before any returned value is examined; N <= 15), into the counters
+// at the start of the dynamic LDS block. The byte of slot s sits at bit
+// 8 (s mod 4) of the word at byte offset s & ~3, and t = 8 s holds that bit
+// offset in its low five bits, the only ones the shift and the bit-field
+// extract below read. An add of 1 can carry only when the byte it increments
+// was 0xFF. A batch in which some lane carried takes one wave-uniform branch,
+// where each lane logs its own carries with one LDS atomic on the list length
+// per element that carried (mostly one element of one lane). Skewed input,
+// whose hot bins wrap a byte every 256 counts, takes this branch often, so it
+// stays short.
+template <int N>
+__device__ __forceinline__ void count8_batch(uint32_t *evlist, uint32_t *ev_count, uint32_t cap,
+                                             const uint32_t (&s)[N], const bool (&ok)[N])
+{
+    uint32_t old[N], t[N], a[N];
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-        sh[e] = (s[e] & 3u) << 3;
-        old[e] = 0u;
-        if (ok[e]) old[e] = lds_add_rtn(words, s[e] >> 2, 1u << sh[e]);
+        t[e] = s[e] << 3;
+        a[e] = s[e] & ~3u;
+        // a lane that does not count keeps the increment, which is dead after
+        // the add (the returned value can take its register: no copy)
+        old[e] = shl_mod32(1u, t[e]);
+        if (ok[e]) old[e] = dyn_lds_add_rtn(a[e], old[e]);
     }
     bool hit[N], any = false;
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-        hit[e] = ok[e] && __builtin_amdgcn_ubfe(old[e], sh[e], 8) == 0xFFu;
+        hit[e] = ok[e] && __builtin_amdgcn_ubfe(old[e], t[e], 8) == 0xFFu;
         any = any || hit[e];
     }
     if (__ballot(any)) {
-        // carry bits only for the elements some lane carried on (mostly one or two)
-        uint32_t bits[N], tot = 0;
-        uint64_t hm[N];
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-            bits[e] = 0u;
-            hm[e] = __ballot(hit[e]);
-            if (hm[e]) {
-                bits[e] = hit[e] ? carry_bits8(old[e], 1u << sh[e]) : 0u;
-                tot += (uint32_t)__popc(bits[e]);
-            }
-        }
-        uint32_t pre = 0, sum = 0;
-        for (uint32_t j = 0;; ++j) {
-            const uint64_t m = __ballot(tot > j);
-            if (m == 0) break;
-            pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            sum += (uint32_t)__popcll(m);
-        }
-        const int first = __builtin_ctzll(__ballot(true));
-        uint32_t b = 0u;
-        if (lane_id() == (uint32_t)first) b = lds_add_rtn(ev_count, 0, sum);
-        uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)b, first) + pre;
-#pragma unroll
-        for (int e = 0; e < N; ++e) {
-            if (hm[e]) {  // a hit has at least the bit of its own byte
-#pragma unroll
-                for (uint32_t q = 0; q < 4; ++q) {
-                    if ((bits[e] >> q) & 1u) {
-                        if (slot < cap) evlist[slot] = (s[e] & ~3u) | q;
-                        ++slot;
-                    }
-                }
-            }
-        }
+        for (int e = 0; e < N; ++e)
+            if (hit[e]) log_carry_chain8(evlist, ev_count, cap, a[e], old[e], t[e]);
     }
 }
 

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
             if constexpr (CW == 16) {
                 count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
             } else if constexpr (CW == 8) {
-                count8_batch<4 * UNROLL>(lds, evlist, ev_count, ev_cap, sl, ok);
+                count8_batch<4 * UNROLL>(evlist, ev_count, ev_cap, sl, ok);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4 * UNROLL; ++e) lds_count<0>(lds, (sl[e] << kshift) | rep, ok[e]);

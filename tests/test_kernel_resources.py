@@ -94,3 +94,17 @@ def test_no_run_time_register_indexing(device_build):
     bad = {k: v[:3] for k, v in bad.items() if v}
     assert not bad, bad
 
+
+
+def test_sweep_kernels_declare_no_static_lds(device_build):
+    """The sweep addresses its counters by their offset into the dynamic LDS
+    block, with no base added, which holds only while the block starts at
+    LDS address 0: the kernel must declare no static LDS of its own."""
+    source, kernels, _ = device_build
+    if source != "hist_api.hip":
+        pytest.skip("the sweep kernels live in the library source")
+    sweeps = {k: v for k, v in kernels.items() if "k_sweep" in k}
+    assert sweeps, "no sweep kernel in the resource remarks"
+    assert all("LDS Size" in v for v in sweeps.values()), sweeps
+    bad = {k: v["LDS Size"] for k, v in sweeps.items() if v["LDS Size"] != 0}
+    assert not bad, bad

@@ -168,6 +168,28 @@ def test_counter8_identical_events_in_a_window(path, bins, groups):
     check(x, bins, f"identical-events-{path}-g{groups}", path=path, counter_bits=8, groups=groups)
 
 
+@pytest.mark.parametrize("agg", [0, 1])
+@pytest.mark.parametrize("path,bins", [("full", 150_000), ("range", 262_144)])
+def test_counter8_carry_chains(agg, path, bins):
+    """8-bit counters, one chunk: words whose bytes above the first one end
+    one short of a wrap (255 adds each) while the first byte wraps once
+    (256 adds). Whichever add comes last decides where the carries start:
+    when the first byte's wrap comes after the others' adds it carries
+    through every byte above it, out of the word's top byte, in one add. The
+    chains start at byte 0, 1 and 2 in different words."""
+    words = np.arange(37, 37 + 3 * 1400, 3, dtype=np.int64) % (bins // 4)
+    adds = {0: [256, 255, 255, 255], 1: [0, 256, 255, 255], 2: [0, 0, 256, 255]}
+    parts = []
+    for k, w in enumerate(words):
+        for q, c in enumerate(adds[k % 3]):
+            parts.append(np.full(c, 4 * w + q, np.int64))
+    parts.append(rnd(12, 100_000, 0, bins).astype(np.int64))
+    x = np.concatenate(parts)
+    x = x[np.random.default_rng(13 + agg).permutation(x.size)].astype(np.int32)
+    check(x, bins, f"cw8-chains-{path}-agg{agg}", path=path, counter_bits=8, groups=1,
+          aggregation=agg, **({"range_bins": 131_072} if path == "range" else {}))
+
+
 @pytest.mark.parametrize("agg", [0, 1, 4])
 @pytest.mark.parametrize("path,bins", [("full", 65536), ("range", 200_000)])
 def test_counter16_carry_events(agg, path, bins):
