@@ -106,8 +106,9 @@ typedef struct {
                              banks at the cost of clearing and summing the copies */
     int32_t pacing;       /* RANGE with R > 1, 1024-thread workgroups and 16- or 8-bit
                              counters, how the R owners of a chunk read it: 0 auto, 1
-                             non-temporal loads, each owner at its own pace; 2 plain loads,
-                             own pace; 3..18 plain loads, each owner kept within (pacing - 2)
+                             plain loads, each owner at its own pace; 2 the same, with the
+                             last wave idle (the paced kernel without its partner); 3..18
+                             plain loads, each owner kept within (pacing - 2)
                              batches of the next range's owner by a pacer wave, so that the
                              lines one owner brings into the XCD's L2 serve the other
                              (bounded waits: an owner whose partner does not move stops

@@ -160,7 +160,7 @@ struct hist_plan_impl {
     uint32_t cw = 32;    // LDS counter bits
     uint32_t kshift = 0; // 2^kshift interleaved LDS copies (32-bit counters)
     uint32_t ev_cap = 0; // carry-event list entries (8-bit counters)
-    uint32_t pacing = 1; // RANGE: 1 non-temporal loads, 2 plain loads, >= 3 paced (window - 2)
+    uint32_t pacing = 1; // RANGE: 1 own pace, 2 own pace with a pacer wave, >= 3 paced (window - 2)
     uint64_t off_progress = 0;  // RANGE paced: [G][R][16] progress words
     uint64_t max_elems_wg = 1ull << 40;  // elements one sweep workgroup may count
     uint32_t nblk = 0;       // 256-bin blocks per partial row
@@ -534,6 +534,11 @@ hipError_t launch_sweep_t(const hist_plan_impl *p, const SweepArgs &a, hipStream
     pca::Pacing pc{nullptr, 0u, 0u};
     auto k = pca::k_sweep<WG, U, AGG, CW, false>;
     if constexpr (WG == 1024 && CW != 32) {
+        // R > 1 owners at their own pace: plain loads. Measured against
+        // non-temporal ones: the Zipf 262,144-bin workload 373 against
+        // 380-395 us, 2^18 uniform bins at 2^26 elements 59.0 against 62-69 us
+        // (with one owner the two time alike: 48.8 us on the headline).
+        if (p->pacing == 1 && p->ranges > 1) k = pca::k_sweep<WG, U, AGG, CW, false, false>;
         if (p->pacing >= 2) {
             k = pca::k_sweep<WG, U, AGG, CW, true>;
             if (p->pacing >= 3) {
@@ -800,12 +805,9 @@ hist_status_t run_impl(hist_plan_t *p, uint32_t *counts, const int32_t *input, u
         a.out = plan_partials(p);
         a.direct = G > 1 ? nullptr : counts;
         a.accumulate = accumulate;
-        // Non-temporal loads also for R > 1. On the 2^26-element sweeps plain
-        // and non-temporal loads time alike for R > 1 (2^18 uniform bins: 119.2
-        // vs 119.8 us). The co-owners do not always find the lines in the XCD's
-        // L2: on the Zipf 262,144-bin workload (R = 2, 8-bit counters) the
-        // sweep's scaled FETCH_SIZE is 1.8x the input, so most second reads
-        // go to the fabric.
+        // The co-owners of a chunk (R > 1) do not always find its lines in the
+        // XCD's L2: on the Zipf 262,144-bin workload (R = 2, 8-bit counters)
+        // the sweep's scaled FETCH_SIZE is 1.8x the input.
         const KEv sev = tm.ev(PH_SWEEP);
         e = p->cw == 32   ? launch_sweep_wg<32>(p, a, stream, sev)
             : p->cw == 16 ? launch_sweep_wg<16>(p, a, stream, sev)
@@ -1110,14 +1112,14 @@ hist_status_t hist_plan_preview(const hist_device_desc_t *dev, uint32_t num_bins
 
 namespace {
 
-// " pace=..." for a RANGE plan whose owners read other than with
-// non-temporal loads at their own pace (empty otherwise, so that the
-// descriptions of plans that do not pace stay as they were).
+// " pace=..." for a RANGE plan whose owners do not each read at their own
+// pace with all waves counting (empty otherwise, so that the descriptions of
+// plans that do not pace stay as they were).
 const char *pace_tag(const hist_plan_impl *p)
 {
     static thread_local char buf[32];
     if (p->path != HIST_PATH_RANGE || p->pacing <= 1) return "";
-    if (p->pacing == 2) return " pace=plain";
+    if (p->pacing == 2) return " pace=idle-wave";
     std::snprintf(buf, sizeof buf, " pace=%u", p->pacing - 2);
     return buf;
 }

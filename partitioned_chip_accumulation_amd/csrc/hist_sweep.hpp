@@ -53,6 +53,11 @@ __device__ __forceinline__ uint32_t pace_batch(uint32_t word, uint32_t epoch)
 // accumulate != 0 adds to direct[] instead of overwriting it. ev_cap is the
 // length of the 8-bit counters' carry-event list.
 //
+// NTL: non-temporal input loads (the lines are not kept for a later reader).
+// With false the loads are plain, so that when R > 1 owners read a chunk
+// each at its own pace the second reader finds more of the lines still in
+// the XCD's L2.
+//
 // PACE (RANGE, R > 1, packed counters): the owners of a chunk read it with
 // plain loads, and each keeps pace with the next range's owner, which reads
 // the same lines, so that the lines the first reader brings into the XCD's
@@ -67,7 +72,7 @@ __device__ __forceinline__ uint32_t pace_batch(uint32_t word, uint32_t epoch)
 // bounded (a counting wave stops waiting after kPaceSpin polls, the pacer
 // after kPacerRounds rounds, e.g. when the partner is not resident). The
 // counts do not depend on any of this: every owner counts what it loads.
-template <int WG, int UNROLL, int AGG, int CW, bool PACE = false>
+template <int WG, int UNROLL, int AGG, int CW, bool PACE = false, bool NTL = true>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
                                               uint32_t kshift, uint32_t ev_cap, Partials out,
@@ -99,7 +104,8 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     constexpr uint32_t CT = PACE ? WG - 64 : WG;  // counting threads (the rest: the pacer wave)
     constexpr uint32_t NCW = CT / 64;             // counting waves
     constexpr uint32_t STEP = CT * UNROLL;
-    constexpr bool NT = !PACE;  // paced owners keep the lines in L2 for each other
+    constexpr bool NT = NTL && !PACE;
+    auto ld = [&](const i32x4 *a) __attribute__((always_inline)) { return load_vec<NT>(a); };
     const bool counter = !PACE || tid < CT;
     uint64_t v = v0;
 
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     const bool any_full = v + STEP <= v1;
     if (any_full && counter) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<NT>(body + v + u * CT + tid);
+        for (int u = 0; u < UNROLL; ++u) nx[u] = ld(body + v + u * CT + tid);
     }
     zero_lds<WG>(lds, CW == 32 ? (len << kshift) : CW == 16 ? (len + 1) / 2 : (len + 3) / 4);
     if (CW != 32 && tid < (PACE ? 4u : 1u)) ev_count[tid] = 0u;
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
         for (int u = 0; u < UNROLL; ++u) q[u] = nx[u];
         if (v + 2 * STEP <= v1) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) nx[u] = load_vec<NT>(body + v + STEP + u * CT + tid);
+            for (int u = 0; u < UNROLL; ++u) nx[u] = ld(body + v + STEP + u * CT + tid);
         }
         if constexpr (PACE) {
             if (lane_id() == 0) lds_add(ev_count, 1, 1u);
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     // Remainder with a wave-uniform trip count.
     for (; v < v1; v += CT) {
         const bool ok = v + tid < v1;
-        const i32x4 q = ok ? load_vec<NT>(body + v + tid) : i32x4{0, 0, 0, 0};
+        const i32x4 q = ok ? ld(body + v + tid) : i32x4{0, 0, 0, 0};
         count4(q, ok);
     }
     {
