@@ -405,10 +405,14 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
 
 // The heaviest window of wbins consecutive bins, from a sample of the input,
 // for k_partition to count in place, and the hottest value outside it. One
-// workgroup samples 1,024 elements, 1024 / WG consecutive ones at each of WG
-// evenly spaced places (with WG = 1024, 1,024 scattered lines, which one CU
-// fetches in a few microseconds while the rest of the GPU waits; a share's
-// standard error is then under 1.6%). The samples are counted into coarse buckets (256
+// workgroup samples 1,024 elements, 64 runs of 16 S consecutive ones at
+// evenly spaced places (S = 1024 / WG per thread; with WG = 1024, 64 lines on
+// 64 pages, which one CU fetches in a few microseconds while the rest of the
+// GPU waits; single elements from 1,024 pages took the half-Gaussian 2^19-bin
+// workload 652 against 644 us, the page walks setting the time). For input in
+// random order a share's standard error stays under 1.6%; on ordered input
+// the runs make the estimate coarser, which can only cost time, never
+// exactness. The samples are counted into coarse buckets (256
 // bins, or more so that there are at most 8,192) and, by value, into an LDS
 // hash table; the window is the run of wbins / bucket buckets with the most
 // samples (the first such, from a prefix sum). wsel[kSelWindow] gets its
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(WG) void k_window_pick(const int32_t *__restrict__ 
     const uint32_t tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
     // every sample's load goes out before the tables are cleared
     uint32_t v[S];
-    const uint64_t at = (uint64_t)tid * n / WG;
+    const uint64_t at = (uint64_t)(tid >> 4) * n / (WG >> 4) + (tid & 15u) * S;
 #pragma unroll
     for (uint32_t k = 0; k < S; ++k) v[k] = (uint32_t)x[min(at + k, n - 1u)];
     uint32_t blog = 8;
