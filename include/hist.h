@@ -150,7 +150,8 @@ typedef struct {
                                  ceil(n / max_group_elems) chunks (packed counters: this
                                  bounds each workgroup's carry events) */
     uint32_t event_cap;       /* FULL/RANGE with 8-bit counters: carry-event list entries
-                                 per workgroup (the LDS its slice leaves); otherwise 0 */
+                                 per workgroup (the LDS its slice leaves, then 512 more in
+                                 the workspace); otherwise 0 */
 } hist_plan_info_t;
 
 typedef struct hist_plan_impl hist_plan_t; /* opaque, host memory only */

@@ -162,6 +162,7 @@ struct hist_plan_impl {
     uint32_t ev_cap = 0; // carry-event list entries (8-bit counters)
     uint32_t pacing = 1; // RANGE: 1 own pace, 2 own pace with a pacer wave, >= 3 paced (window - 2)
     uint64_t off_progress = 0;  // RANGE paced: [G][R][16] progress words
+    uint64_t off_spill = 0;     // 8-bit counters: [G R][kEvSpill8] carry events past the LDS list
     uint64_t max_elems_wg = 1ull << 40;  // elements one sweep workgroup may count
     uint32_t nblk = 0;       // 256-bin blocks per partial row
     uint32_t part_rows = 0;  // partial rows the workspace holds
@@ -347,7 +348,11 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
             // large slice (one workgroup per CU) lets a workgroup count more.
             const uint32_t occ = std::max<uint32_t>(1, lds_dyn / sweep_lds_bytes(8, S, 0, pca::kMinEventCap8));
             ev_cap = (lds_dyn / occ - S) / 4 - 4;
-            max_elems_wg = 255ull * (ev_cap - 16);
+            // the list goes on in the workspace for kEvSpill8 entries, so
+            // that the Zipf 2^18-bin workload's 2^21-element chunks (one
+            // round of 128 chunks, R = 2) fit: measured 353 against 371 us
+            // with 256 chunks at 266,000,000 elements
+            max_elems_wg = 255ull * (ev_cap + pca::kEvSpill8 - 16);
         }
         G = chunks_for(sweep_lds_bytes(cw, S, kshift, ev_cap), max_elems_wg, &wg);
         p->range_bins = S;
@@ -370,6 +375,10 @@ hist_status_t design(hist_plan_impl *p, uint32_t num_bins, uint64_t max_n, const
         if (p->pacing >= 3) {
             p->off_progress = off;
             off += align_up((uint64_t)G * R * 4, 256);
+        }
+        if (cw == 8) {
+            p->off_spill = off;
+            off += align_up((uint64_t)G * R * pca::kEvSpill8 * 4, 256);
         }
         p->need = off;
     } else if (path == HIST_PATH_STREAM) {
@@ -551,7 +560,8 @@ hipError_t launch_sweep_t(const hist_plan_impl *p, const SweepArgs &a, hipStream
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;
     launch(k, dim3(a.G * p->ranges), dim3(WG), bytes, s, ev, a.in, p->num_bins, p->range_bins,
-           p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, p->ev_cap, a.out, a.direct,
+           p->ranges, a.G, a.xcds, CW == 32 ? p->kshift : 0u, p->ev_cap,
+           CW == 8 ? reinterpret_cast<uint32_t *>(p->ws + p->off_spill) : nullptr, a.out, a.direct,
            a.accumulate, pc);
     return hipGetLastError();
 }
@@ -1143,7 +1153,7 @@ void fill_info(const hist_plan_impl *p, hist_plan_info_t *info)
     info->max_n = p->max_n;
     info->workspace_bytes = p->need;
     info->max_group_elems = routed ? 0 : p->max_elems_wg;
-    info->event_cap = routed ? 0 : p->ev_cap;
+    info->event_cap = routed ? 0 : p->cw == 8 ? p->ev_cap + pca::kEvSpill8 : p->ev_cap;
 }
 
 }  // namespace

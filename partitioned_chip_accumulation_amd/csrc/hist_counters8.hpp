@@ -25,8 +25,39 @@ namespace pca {
 // q are the adds to bin q plus the carries out of byte q - 1, so from zero a
 // workgroup that counts E elements logs at most E / 255 events. The list
 // takes the LDS the slice leaves (at least kMinEventCap8 entries, cap in
-// all), and the host keeps E <= 255 (cap - 16), which bounds it.
+// all) and goes on for kEvSpill8 entries in the workgroup's own area of the
+// workspace, and the host keeps E <= 255 (cap + kEvSpill8 - 16), which
+// bounds it.
 constexpr uint32_t kMinEventCap8 = 2048;
+constexpr uint32_t kEvSpill8 = 512;
+
+// A workgroup's carry-event list: cap entries in LDS, then (spill not null)
+// kEvSpill8 more in global memory, written with plain stores and read by the
+// same workgroup after a barrier. The 16-bit counters use lds, count and cap
+// only.
+struct EvList {
+    uint32_t *lds;
+    uint32_t *count;  // LDS word: entries logged
+    uint32_t cap;
+    uint32_t *spill;
+};
+
+__device__ __forceinline__ void put_event8(const EvList &ev, uint32_t i, uint32_t x)
+{
+    if (i < ev.cap) ev.lds[i] = x;
+    else if (ev.spill != nullptr && i - ev.cap < kEvSpill8) ev.spill[i - ev.cap] = x;
+}
+
+__device__ __forceinline__ uint32_t event8_at(const EvList &ev, uint32_t e)
+{
+    return e < ev.cap ? ev.lds[e] : ev.spill[e - ev.cap];
+}
+
+// Entries logged that the list holds.
+__device__ __forceinline__ uint32_t events8_held(const EvList &ev)
+{
+    return min(*ev.count, ev.cap + (ev.spill != nullptr ? kEvSpill8 : 0u));
+}
 
 // Bit q set: the add of delta to a word that held old carried out of byte q.
 __device__ __forceinline__ uint32_t carry_bits8(uint32_t old, uint32_t delta)
@@ -38,27 +69,26 @@ __device__ __forceinline__ uint32_t carry_bits8(uint32_t old, uint32_t delta)
 
 // Log the carries of an add of delta = k << 8p to word w that returned old
 // (one lane on its own).
-__device__ __forceinline__ void log_carries8(uint32_t *evlist, uint32_t *ev_count, uint32_t cap,
-                                             uint32_t w, uint32_t old, uint32_t delta)
+__device__ __forceinline__ void log_carries8(const EvList &ev, uint32_t w, uint32_t old,
+                                             uint32_t delta)
 {
     const uint32_t bits = carry_bits8(old, delta);
     if (bits == 0u) return;
-    uint32_t i = lds_add_rtn(ev_count, 0, (uint32_t)__popc(bits));
+    uint32_t i = lds_add_rtn(ev.count, 0, (uint32_t)__popc(bits));
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         if ((bits >> q) & 1u) {
-            if (i < cap) evlist[i] = (w << 2) | q;
+            put_event8(ev, i, (w << 2) | q);
             ++i;
         }
     }
 }
 
-__device__ __forceinline__ void add8(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
-                                     uint32_t cap, uint32_t s, uint32_t k)
+__device__ __forceinline__ void add8(uint32_t *words, const EvList &ev, uint32_t s, uint32_t k)
 {
     const uint32_t delta = k << ((s & 3u) << 3);
     const uint32_t old = lds_add_rtn(words, s >> 2, delta);
-    log_carries8(evlist, ev_count, cap, s >> 2, old, delta);
+    log_carries8(ev, s >> 2, old, delta);
 }
 
 // Log the carries of an add of one to byte q0 = t / 8 (t mod 32 its bit
@@ -68,16 +98,15 @@ __device__ __forceinline__ void add8(uint32_t *words, uint32_t *evlist, uint32_t
 // a | q0 .. a | (q0 + n - 1). The bytes of ~old above bit t are zero exactly
 // where old's are 0xFF, so n is the count of whole zero bytes at the bottom
 // of ~old >> t, capped at the word's top byte.
-__device__ __forceinline__ void log_carry_chain8(uint32_t *evlist, uint32_t *ev_count, uint32_t cap,
-                                                 uint32_t a, uint32_t old, uint32_t t)
+__device__ __forceinline__ void log_carry_chain8(const EvList &ev, uint32_t a, uint32_t old,
+                                                 uint32_t t)
 {
     const uint32_t q0 = (t >> 3) & 3u;
     const uint32_t y = ~old >> (t & 31u);
     const uint32_t n = y == 0u ? 4u - q0 : min((uint32_t)__builtin_ctz(y) >> 3, 4u - q0);
-    uint32_t i = lds_add_rtn(ev_count, 0, n);
-    if (i < cap) evlist[i] = a | q0;
-    for (uint32_t j = 1; j < n; ++j)
-        if (i + j < cap) evlist[i + j] = a | (q0 + j);
+    uint32_t i = lds_add_rtn(ev.count, 0, n);
+    put_event8(ev, i, a | q0);
+    for (uint32_t j = 1; j < n; ++j) put_event8(ev, i + j, a | (q0 + j));
 }
 
 // Unaggregated 8-bit counting of N elements at once (all ds_add_rtn_u32 are
@@ -92,8 +121,8 @@ __device__ __forceinline__ void log_carry_chain8(uint32_t *evlist, uint32_t *ev_
 // whose hot bins wrap a byte every 256 counts, takes this branch often, so it
 // stays short.
 template <int N>
-__device__ __forceinline__ void count8_batch(uint32_t *evlist, uint32_t *ev_count, uint32_t cap,
-                                             const uint32_t (&s)[N], const bool (&ok)[N])
+__device__ __forceinline__ void count8_batch(const EvList &ev, const uint32_t (&s)[N],
+                                             const bool (&ok)[N])
 {
     uint32_t old[N], t[N], a[N];
 #pragma unroll
@@ -114,16 +143,16 @@ __device__ __forceinline__ void count8_batch(uint32_t *evlist, uint32_t *ev_coun
     if (__ballot(any)) {
 #pragma unroll
         for (int e = 0; e < N; ++e)
-            if (hit[e]) log_carry_chain8(evlist, ev_count, cap, a[e], old[e], t[e]);
+            if (hit[e]) log_carry_chain8(ev, a[e], old[e], t[e]);
     }
 }
 
 template <int ROUNDS>
-__device__ __forceinline__ void lds_count8(uint32_t *words, uint32_t *evlist, uint32_t *ev_count,
-                                           uint32_t cap, uint32_t slot, bool valid)
+__device__ __forceinline__ void lds_count8(uint32_t *words, const EvList &ev, uint32_t slot,
+                                           bool valid)
 {
     if constexpr (ROUNDS == 0) {
-        if (valid) add8(words, evlist, ev_count, cap, slot, 1u);
+        if (valid) add8(words, ev, slot, 1u);
     } else {
         bool pending = valid;
 #pragma unroll
@@ -135,11 +164,11 @@ __device__ __forceinline__ void lds_count8(uint32_t *words, uint32_t *evlist, ui
             const bool mine = pending && slot == lead;
             const uint64_t m = __ballot(mine);
             if (mine && lane_id() == (uint32_t)leader)
-                add8(words, evlist, ev_count, cap, lead, (uint32_t)__popcll(m));  // <= 64
+                add8(words, ev, lead, (uint32_t)__popcll(m));  // <= 64
             pending = pending && !mine;
             if (__popcll(m) == 1) break;
         }
-        if (pending) add8(words, evlist, ev_count, cap, slot, 1u);
+        if (pending) add8(words, ev, slot, 1u);
     }
 }
 
@@ -199,7 +228,7 @@ __device__ __forceinline__ void carry_at(Counts32 &c, uint32_t k, uint32_t add, 
 // which only the owning lane's values change (its copies in the window are
 // added at once). Whole wave, convergent; p0 uniform.
 template <int J, int STRIDE>
-__device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t nev, uint32_t p0,
+__device__ __forceinline__ void apply_events8(const EvList &ev, uint32_t nev, uint32_t p0,
                                               Counts32 &c)
 {
     const uint32_t lane = lane_id();
@@ -208,7 +237,7 @@ __device__ __forceinline__ void apply_events8(const uint32_t *evlist, uint32_t n
     p0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)p0);
     for (uint32_t e0 = 0; e0 < nev; e0 += 64) {
         const uint32_t e = e0 + lane;
-        const uint32_t ent = e < nev ? evlist[e] : 0xFFFFFFFFu;
+        const uint32_t ent = e < nev ? event8_at(ev, e) : 0xFFFFFFFFu;
         const uint32_t dp = (ent >> 9) - p0;  // pair of the entry's word, from p0
         uint64_t m = __ballot(dp < (uint32_t)(STRIDE * J) && dp % STRIDE == 0u);
         while (m != 0) {

@@ -204,7 +204,7 @@ __device__ __forceinline__ void mask_octet(uint32_t p, uint32_t len, uint32_t (&
 // lane stays inside it. With 8-bit counters the whole wave must call it
 // (uniform p): the carry events are applied by the wave together.
 template <int CW>
-__device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t *evlist,
+__device__ __forceinline__ void slice_octet(const uint32_t *lds, const EvList &ev,
                                             uint32_t nev, uint32_t p, uint32_t len,
                                             uint32_t kshift, uint32_t (&c)[8])
 {
@@ -213,7 +213,7 @@ __device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t 
         Counts32 cv;
         octet8_raw<0>(lds, p, len, cv);
         // a carry out of the last valid byte lands in an invalid one: mask after
-        apply_events8<1, 1>(evlist, nev, p, cv);
+        apply_events8<1, 1>(ev, nev, p, cv);
         octet_of<0>(cv, c);
         mask_octet(p, len, c);
         return;
@@ -246,7 +246,7 @@ __device__ __forceinline__ void slice_octet(const uint32_t *lds, const uint32_t 
         const uint32_t w0 = b0 / 2;
         // constant indices only: a variable index would move c[] to scratch memory
         for (uint32_t e = 0; e < nev; ++e) {
-            const uint32_t ent = evlist[e];
+            const uint32_t ent = ev.lds[e];
             const uint32_t d = (ent & 0x3FFFFFFFu) - w0;
             const uint32_t add_lo = (ent & kEvLoWrap) ? 65536u : 0u;
             const uint32_t add_hi = ((ent & kEvCarry) ? 65536u : 0u) - ((ent & kEvLoWrap) ? 1u : 0u);
@@ -271,7 +271,7 @@ constexpr uint32_t kFlushBatch = 4;
 
 template <int WG, int CW>
 __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uint32_t blk0,
-                                            const uint32_t *lds, const uint32_t *evlist,
+                                            const uint32_t *lds, const EvList &ev,
                                             uint32_t nev, uint32_t len, uint32_t kshift)
 {
     const uint32_t nblk_slice = (len + kBlockBins - 1) / kBlockBins;
@@ -297,7 +297,7 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
             }
             if (full < npairs && w == (full / kFlushBatch) % NW) {
                 uint32_t c[8];
-                slice_octet<CW>(lds, evlist, nev, full, len, kshift, c);
+                slice_octet<CW>(lds, ev, nev, full, len, kshift, c);
                 write_pair(P, row_blk + 2 * full, min(2u, nblk_slice - 2 * full), c);
             }
             return;
@@ -320,7 +320,7 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
             }
             if (full < npairs && w == (full / kFlushBatch) % NW) {
                 uint32_t c[8];
-                slice_octet<CW>(lds, evlist, nev, full, len, kshift, c);
+                slice_octet<CW>(lds, ev, nev, full, len, kshift, c);
                 write_pair(P, row_blk + 2 * full, min(2u, nblk_slice - 2 * full), c);
             }
             return;
@@ -336,7 +336,7 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
             octet8_raw<1>(lds, p0 + 1 * NW, len, cv);
             octet8_raw<2>(lds, p0 + 2 * NW, len, cv);
             octet8_raw<3>(lds, p0 + 3 * NW, len, cv);
-            apply_events8<kFlushBatch, NW>(evlist, nev, p0, cv);
+            apply_events8<kFlushBatch, NW>(ev, nev, p0, cv);
             uint32_t c[kFlushBatch][8];
             octet_of<0>(cv, c[0]);
             octet_of<1>(cv, c[1]);
@@ -356,7 +356,7 @@ __device__ __forceinline__ void flush_slice(const Partials &P, uint64_t row, uin
         uint32_t c[kFlushBatch][8];
 #pragma unroll
         for (uint32_t j = 0; j < kFlushBatch; ++j)
-            slice_octet<CW>(lds, evlist, nev, p0 + j < npairs ? p0 + j : npairs, len, kshift, c[j]);
+            slice_octet<CW>(lds, ev, nev, p0 + j < npairs ? p0 + j : npairs, len, kshift, c[j]);
 #pragma unroll
         for (uint32_t j = 0; j < kFlushBatch; ++j) {
             if (p0 + j >= npairs) break;  // uniform

@@ -670,7 +670,7 @@ __device__ __forceinline__ void finish_range(const Partials &out, uint32_t row, 
                                              uint32_t accumulate)
 {
     if (!whole) {
-        flush_slice<WG, 32>(out, row, 0, lds, nullptr, 0, len, 0);
+        flush_slice<WG, 32>(out, row, 0, lds, EvList{nullptr, nullptr, 0u, nullptr}, 0, len, 0);
         return;
     }
     // 16-byte stores where the range's counts start 16-byte aligned (counts

@@ -51,7 +51,8 @@ __device__ __forceinline__ uint32_t pace_batch(uint32_t word, uint32_t epoch)
 // The slice goes to partial row g in 256-bin blocks (range_bins is a multiple
 // of 256), or straight into direct[] (the output) when there is one chunk;
 // accumulate != 0 adds to direct[] instead of overwriting it. ev_cap is the
-// length of the 8-bit counters' carry-event list.
+// LDS length of the 8-bit counters' carry-event list, and ev_spill (or null)
+// holds kEvSpill8 more entries per workgroup, workgroup b's at b kEvSpill8.
 //
 // NTL: non-temporal input loads (the lines are not kept for a later reader).
 // With false the loads are plain, so that when R > 1 owners read a chunk
@@ -75,7 +76,8 @@ __device__ __forceinline__ uint32_t pace_batch(uint32_t word, uint32_t epoch)
 template <int WG, int UNROLL, int AGG, int CW, bool PACE = false, bool NTL = true>
 __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, uint32_t range_bins,
                                               uint32_t ranges, uint32_t groups, uint32_t xcds,
-                                              uint32_t kshift, uint32_t ev_cap, Partials out,
+                                              uint32_t kshift, uint32_t ev_cap,
+                                              uint32_t *__restrict__ ev_spill, Partials out,
                                               uint32_t *__restrict__ direct, uint32_t accumulate,
                                               Pacing pc)
 {
@@ -83,6 +85,9 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     uint32_t *lds = reinterpret_cast<uint32_t *>(lds4);
     uint32_t *ev_count = lds + range_bins * CW / 32;  // CW < 32 only
     uint32_t *evlist = ev_count + 4;
+    const EvList ev{evlist, ev_count, CW == 8 ? ev_cap : kEventCap,
+                    CW == 8 && ev_spill != nullptr ? ev_spill + (uint64_t)blockIdx.x * kEvSpill8
+                                                   : nullptr};
     const uint32_t tid = threadIdx.x;
     const uint32_t b = blockIdx.x;
     uint32_t g, r;
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     auto count1 = [&](uint32_t s, bool ok) {
         if constexpr (CW == 32) lds_count<PEEL>(lds, (s << kshift) | rep, ok);
         else if constexpr (CW == 16) lds_count16<PEEL>(lds, evlist, ev_count, s, ok);
-        else lds_count8<PEEL>(lds, evlist, ev_count, ev_cap, s, ok);
+        else lds_count8<PEEL>(lds, ev, s, ok);
     };
     HotSlot hs;
     auto hot_flush = [&]() {
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
                     while (t != 0u) {
                         const uint32_t kk = min(t, CW == 16 ? 32768u : 255u);
                         if constexpr (CW == 16) add16(lds, evlist, ev_count, hs.h, kk);
-                        else add8(lds, evlist, ev_count, ev_cap, hs.h, kk);
+                        else add8(lds, ev, hs.h, kk);
                         t -= kk;
                     }
                 }
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
             if constexpr (CW == 16) {
                 count16_batch<4 * UNROLL>(lds, evlist, ev_count, sl, ok);
             } else if constexpr (CW == 8) {
-                count8_batch<4 * UNROLL>(evlist, ev_count, ev_cap, sl, ok);
+                count8_batch<4 * UNROLL>(ev, sl, ok);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4 * UNROLL; ++e) lds_count<0>(lds, (sl[e] << kshift) | rep, ok[e]);
@@ -283,12 +288,14 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
     hot_flush();
     __syncthreads();
 
-    const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : CW == 8 ? min(*ev_count, ev_cap) : 0u;
+    // (the barrier above also makes the spilled entries, plain global stores
+    // of this workgroup, visible to all its waves)
+    const uint32_t nev = CW == 16 ? min(*ev_count, kEventCap) : CW == 8 ? events8_held(ev) : 0u;
     if (direct) {
         const uint32_t npairs = (len + 511) / 512;
         for (uint32_t p = tid >> 6; p < npairs; p += WG / 64) {
             uint32_t c[8];
-            slice_octet<CW>(lds, evlist, nev, p, len, kshift, c);
+            slice_octet<CW>(lds, ev, nev, p, len, kshift, c);
             const uint32_t b0 = lo + p * 512 + lane_id() * 8;
 #pragma unroll
             for (uint32_t i = 0; i < 8; ++i)
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(WG) void k_sweep(InputView in, uint32_t num_bins, u
                     direct[b0 + i] = (accumulate ? direct[b0 + i] : 0u) + c[i];
         }
     } else {
-        flush_slice<WG, CW>(out, g, lo / kBlockBins, lds, evlist, nev, len, kshift);
+        flush_slice<WG, CW>(out, g, lo / kBlockBins, lds, ev, nev, len, kshift);
     }
 }
 

@@ -323,6 +323,24 @@ def test_counter8_event_list_bound(case, bins):
               aggregation=agg)
 
 
+@pytest.mark.parametrize("bins", [100_000, 155_392])
+def test_counter8_event_spill_in_partial_rows(bins):
+    """Two chunks, each at the list's bound and all in one bin: each
+    workgroup logs past its LDS list into its spill area in the workspace,
+    and the partial-row flush applies both parts (the bound test above covers
+    the direct write of one chunk)."""
+    probe = hist.Plan(bins, 1, device=DEV, path="full", counter_bits=8, groups=2)
+    info = probe.info()
+    probe.close()
+    limit = info.max_group_elems
+    assert limit == 255 * (info.event_cap - 16) and info.event_cap > 512
+    x = np.full(2 * limit, bins - 3, np.int32)
+    x[::97] = 7
+    for agg in (0, 1):
+        check(x, bins, f"cw8-spill-{bins}-agg{agg}", path="full", counter_bits=8, groups=2,
+              aggregation=agg)
+
+
 AUTO_CASES = [  # bin count -> (path, counter bits, ranges) the measured thresholds give
     (8192, ("full", 16, 1)), (20480, ("full", 16, 1)), (20481, ("full", 32, 1)),
     (40960, ("full", 32, 1)), (40961, ("full", 16, 1)), (79616, ("full", 16, 1)),

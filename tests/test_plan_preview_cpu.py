@@ -40,7 +40,10 @@ def test_sweep_plans_fill_the_chip_once(num_bins):
     assert i.path in ("full", "range")
     # one resident 1024-thread workgroup per CU (registers), XCD-aligned chunks
     assert i.wg_size == 1024 and i.groups * i.ranges <= 256 and i.groups % 8 == 0
-    assert i.workspace_bytes == partial_bytes(i.groups, num_bins)
+    # the partial rows, and with 8-bit counters each workgroup's 512 spilled
+    # carry-event entries
+    spill = align(i.groups * i.ranges * 512 * 4) if i.counter_bits == 8 else 0
+    assert i.workspace_bytes == partial_bytes(i.groups, num_bins) + spill
     assert i.range_bins % 256 == 0 and i.range_bins * i.ranges >= num_bins
 
 
@@ -60,9 +63,10 @@ def test_small_inputs_take_few_chunks():
 def test_8bit_event_bound(num_bins, max_n):
     i = hist.preview(num_bins, max_n)
     assert i.counter_bits == 8
-    # the list takes the LDS the slice leaves; each chunk may log at most cap - 16
-    # events, one per 255 counted elements
-    assert i.event_cap == (163840 - i.range_bins) // 4 - 4
+    # the list takes the LDS the slice leaves, then 512 entries in the
+    # workspace; each chunk may log at most cap - 16 events, one per 255
+    # counted elements
+    assert i.event_cap == (163840 - i.range_bins) // 4 - 4 + 512
     assert i.max_group_elems == 255 * (i.event_cap - 16)
     assert i.groups * i.max_group_elems >= max_n
     slots = 256 // i.ranges // 8 * 8
