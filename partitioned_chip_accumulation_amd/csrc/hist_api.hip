@@ -43,6 +43,17 @@ constexpr uint32_t kScatterWG = 1024;        // the owners' workgroup
 // The one-pass range scan up to this many ranges (each one workgroup); at
 // 2,048 ranges of 4,096 tiles the two passes were faster (61 against 69 us).
 constexpr uint32_t kRangeScanMaxRanges = 256;
+// The MI355X's Infinity Cache (the memory-side cache in front of HBM). Data
+// read once is loaded or stored non-temporally only when it outgrows it;
+// smaller buffers stay cacheable, so that their later readers can find them
+// there. Measured on the two-phase path's staged slots (2 bytes per element):
+// non-temporal stores and loads took the hot-bin 2^20-bin workload (2^28
+// elements) from 446 to 430 us and the half-Gaussian one (2^29) from 673 to
+// 655 us, but 2^22 uniform bins at 2^26 elements from 199 to 247 us. On the
+// RANGE sweep's input with R > 1 owners plain loads took the Zipf 2^18-bin
+// workload (1 GiB) from 381-384 to 374-376 us but 2^18 uniform bins at 2^26
+// elements (256 MiB) from 63 to 68 us.
+constexpr uint64_t kMallBytes = 256ull << 20;
 constexpr uint32_t kPartWG = 1024;           // the partition's workgroup
 // The partition's persistent grid, per CU: at its register count one
 // 1024-thread workgroup is resident per CU, and a second one per CU would
@@ -547,7 +558,8 @@ hipError_t launch_sweep_t(const hist_plan_impl *p, const SweepArgs &a, hipStream
         // non-temporal ones: the Zipf 262,144-bin workload 373 against
         // 380-395 us, 2^18 uniform bins at 2^26 elements 59.0 against 62-69 us
         // (with one owner the two time alike: 48.8 us on the headline).
-        if (p->pacing == 1 && p->ranges > 1) k = pca::k_sweep<WG, U, AGG, CW, false, false>;
+        if (p->pacing == 1 && p->ranges > 1 && a.in.nvec * 16 > kMallBytes)
+            k = pca::k_sweep<WG, U, AGG, CW, false, false>;
         if (p->pacing >= 2) {
             k = pca::k_sweep<WG, U, AGG, CW, true>;
             if (p->pacing >= 3) {
@@ -632,7 +644,10 @@ uint32_t sweep_resident(uint32_t cw, uint32_t wg, int agg, uint32_t lds_bytes)
 hipError_t launch_partition(const hist_plan_impl *p, pca::InputView in, uint32_t T, hipStream_t s,
                             const KEv &ev, bool window)
 {
-    auto k = pca::k_partition<kPartWG, kScatterVPT>;
+    // staged slots: 2 bytes per element
+    auto k = 2 * ((uint64_t)in.nvec * 4 + in.head + in.tail) > kMallBytes
+                 ? pca::k_partition<kPartWG, kScatterVPT, true>
+                 : pca::k_partition<kPartWG, kScatterVPT, false>;
     const uint32_t npad = ((p->ranges << p->qlog) + 3u) & ~3u;
     const uint32_t bytes = (3 * npad + 64) * 4 + 2 * kScatterCap * 2 + (window ? p->wbins * 4 + 16 : 0u);
     hipError_t e = allow_lds(k, bytes);
@@ -666,7 +681,9 @@ template <int AGG>
 hipError_t launch_owner_t(const hist_plan_impl *p, uint32_t T, uint32_t *counts, uint32_t accumulate,
                           hipStream_t s, const KEv &ev, const uint32_t *hot_seen)
 {
-    auto k = pca::k_bucket_hist<kScatterWG, 8, AGG>;
+    // the staged slots of T tiles, as the partition chose to store them
+    auto k = 2 * (uint64_t)T * kScatterTile > kMallBytes ? pca::k_bucket_hist<kScatterWG, 8, AGG, true>
+                                                          : pca::k_bucket_hist<kScatterWG, 8, AGG, false>;
     const uint32_t bytes = p->range_bins * 4 + (p->ranges + 1) * 8 + 4 * 4;
     hipError_t e = allow_lds(k, bytes);
     if (e != hipSuccess) return e;

@@ -248,7 +248,7 @@ constexpr uint32_t kWindowRowPad = 64;
 // and k_transpose turns them range-major. Element order inside a run is
 // whatever the atomics gave; counts do not depend on it.
 
-template <int WG, int VPT>
+template <int WG, int VPT, bool NTS = true>
 __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bins, uint32_t shift,
                                                   uint32_t ranges, uint32_t qlog, uint32_t tiles,
                                                   uint16_t *__restrict__ stage, uint32_t stage_cap,
@@ -297,12 +297,16 @@ __global__ __launch_bounds__(WG) void k_partition(InputView in, uint32_t num_bin
     };
     // the previous tile's slots, still in its staging buffer: 16-byte vectors, tile
     uint32_t prev_nv = 0, prev_t = 0;
-    // (non-temporal stores: against plain ones the half-Gaussian 2^19-bin
-    // workload took 656-658 against 669-670 us, the hot-bin one 431 against 432)
+    // NTS: non-temporal stores, for staged slots that outgrow the
+    // Infinity Cache (the host's choice); plain ones keep smaller runs there
+    // for the owners
     auto copy_out = [&](uint32_t buf) {
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(st + buf * stage_cap);
         u32x4 *d4 = reinterpret_cast<u32x4 *>(stage + (uint64_t)prev_t * stage_cap);
-        for (uint32_t i = tid; i < prev_nv; i += WG) __builtin_nontemporal_store(s4[i], d4 + i);
+        for (uint32_t i = tid; i < prev_nv; i += WG) {
+            if constexpr (NTS) __builtin_nontemporal_store(s4[i], d4 + i);
+            else d4[i] = s4[i];
+        }
     };
     uint32_t t = blockIdx.x;
     if (t < tiles) load_tile(t);
@@ -711,7 +715,7 @@ __device__ __forceinline__ void finish_range(const Partials &out, uint32_t row, 
 // about equally long for shuffled inputs, so the slots stay busy and the
 // waves balanced. With no workgroup barrier until the slice is flushed, the
 // waves drift apart and one wave's loads overlap the others' counting.
-template <int WG, int UNROLL, int AGG>
+template <int WG, int UNROLL, int AGG, bool NTS = true>
 __global__ __launch_bounds__(WG) void k_bucket_hist(
     const uint16_t *__restrict__ stage, uint32_t stage_cap, const uint32_t *__restrict__ tcnt,
     const uint32_t *__restrict__ tbase, const uint32_t *__restrict__ tpre,
@@ -749,9 +753,9 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
         }
         r = lo;
     }
-    // The staged slots are read once, here: non-temporal loads (measured
-    // against plain ones: the hot-bin 2^20-bin workload 431 against 446 us,
-    // the half-Gaussian 2^19-bin one 661 against 670 us).
+    // The staged slots are read once, here: NTS, non-temporal loads, for
+    // slots that outgrow the Infinity Cache (the host's choice, as for the
+    // partition's stores).
     const i32x4 *stage_vec = reinterpret_cast<const i32x4 *>(stage);
     for (; r < ranges && bs[r] < e1; ++r) {
         const uint64_t rb = bs[r], re = bs[r + 1];
@@ -814,8 +818,8 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                 if (nv > kLaneRunVecs) nv = 0u;
                 for (uint32_t v = 0; v < nv; v += 2u) {
                     const bool two = v + 1u < nv;
-                    const i32x4 qa = load_vec<true>(stage_vec + ((uint64_t)vlo + v));
-                    const i32x4 qb = two ? load_vec<true>(stage_vec + ((uint64_t)vlo + v + 1u)) : i32x4{0, 0, 0, 0};
+                    const i32x4 qa = load_vec<NTS>(stage_vec + ((uint64_t)vlo + v));
+                    const i32x4 qb = two ? load_vec<NTS>(stage_vec + ((uint64_t)vlo + v + 1u)) : i32x4{0, 0, 0, 0};
 #pragma unroll
                     for (uint32_t k = 0; k < 2; ++k) {
                         const i32x4 q = k == 0 ? qa : qb;
@@ -835,7 +839,7 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                     const uint32_t ls = (uint32_t)__builtin_amdgcn_readlane((int)skip, m);
                     const uint32_t lu = (uint32_t)__builtin_amdgcn_readlane((int)used, m);
                     for (uint32_t d = lane; d < ln; d += 64u) {
-                        const i32x4 q = load_vec<true>(stage_vec + ((uint64_t)lv + d));
+                        const i32x4 q = load_vec<NTS>(stage_vec + ((uint64_t)lv + d));
                         const uint32_t k8 = d * 8u;
                         const uint32_t first = k8 < ls ? ls - k8 : 0u;
                         const uint32_t last = min(8u, ls + lu - k8);
@@ -912,7 +916,7 @@ __global__ __launch_bounds__(WG) void k_bucket_hist(
                     const bool ok = d < run_n[m];
                     first[m] = ok ? (k8 < run_s[m] ? run_s[m] - k8 : 0u) : 8u;
                     last[m] = ok ? min(8u, run_s[m] + run_u[m] - k8) : 0u;
-                    qv[m] = ok ? load_vec<true>(stage_vec + ((uint64_t)run_v[m] + d)) : i32x4{0, 0, 0, 0};
+                    qv[m] = ok ? load_vec<NTS>(stage_vec + ((uint64_t)run_v[m] + d)) : i32x4{0, 0, 0, 0};
                 }
 #pragma unroll
                 for (uint32_t k = 0; k < RPW; ++k) {
